@@ -1,0 +1,239 @@
+"""Reference operations in float64 (numpy).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Each function is the plain definition of what the pages say the library
+computes, with the scale granularity and layouts of the workload
+(A: one fp32 scale per row per 128-wide K block; B: one fp32 scale per
+128x128 block).  Operands are dequantised exactly and multiplied in float64.
+Because every block scale is constant over its 128 K-indices, dequantise-then-
+matmul equals "per-block dot product times sa*sb, summed over blocks".
+
+Layouts (row-major, last index contiguous):
+  a    uint8 [M, K]           e4m3fn codes
+  sfa  float32 [K/128, M]     A scales, K-block-major
+  b    uint8 [N, K]           e4m3fn codes (NT: B is stored N x K)
+  sfb  float32 [ceil(N/128), K/128]
+  c    uint16 [M, N] bf16 bits, or None (treated as zero)
+"""
+
+import numpy as np
+
+from .formats import (
+    E4M3_MAX,
+    bf16_bits_to_f64,
+    decode_e4m3,
+    encode_e4m3_rne,
+    pow2_scale_exponent,
+    unpack_e2m1,
+    unpack_ue8m0_int32,
+)
+
+BLOCK_K = 128
+
+
+def dequant_a(a, sfa) -> np.ndarray:
+    """A[m,k] * sfa[k//128, m] in float64."""
+    a = np.asarray(a)
+    M, K = a.shape
+    s = np.asarray(sfa, dtype=np.float64)                 # [K/128, M]
+    s_full = np.repeat(s.T, BLOCK_K, axis=1)[:, :K]       # [M, K]
+    return decode_e4m3(a) * s_full
+
+
+def dequant_b(b, sfb) -> np.ndarray:
+    """B[n,k] * sfb[n//128, k//128] in float64."""
+    b = np.asarray(b)
+    N, K = b.shape
+    s = np.asarray(sfb, dtype=np.float64)                 # [ceil(N/128), K/128]
+    s_full = np.repeat(np.repeat(s, BLOCK_K, axis=0), BLOCK_K, axis=1)[:N, :K]
+    return decode_e4m3(b) * s_full
+
+
+def fp8_gemm_nt(a, sfa, b, sfb, c=None) -> np.ndarray:
+    """Dense NT GEMM: D = C + A . B^T, returned unrounded in float64 [M, N].
+
+    Usage guide, "五、使用方法 / 基础非分组 FP8 GEMM": the naming is D = C + A @ B with
+    A not transposed and B transposed (NT); SM90 takes fp32 scale factors.
+    """
+    ref = dequant_a(a, sfa) @ dequant_b(b, sfb).T
+    if c is not None:
+        ref = ref + bf16_bits_to_f64(c)
+    return ref
+
+
+def m_grouped_contiguous(a, sfa, b, sfb, m_indices):
+    """M-grouped GEMM, contiguous layout (usage guide, "分组 GEMM（MoE）").
+
+    Grouping is along M only; N and K are shared by all groups.  Row r with
+    g = m_indices[r] >= 0 gets A[r] . B[g]^T; rows with -1 are padding and are
+    not part of the result.
+
+    a [M, K], sfa [K/128, M], b [G, N, K], sfb [G, ceil(N/128), K/128],
+    m_indices int32 [M].  Returns (ref float64 [M, N] with NaN in padding rows,
+    written bool [M]).
+    """
+    a = np.asarray(a)
+    m_idx = np.asarray(m_indices).astype(np.int64)
+    G = np.asarray(b).shape[0]
+    M = a.shape[0]
+    N = np.asarray(b).shape[1]
+    ref = np.full((M, N), np.nan)
+    written = np.zeros(M, dtype=bool)
+    sfa = np.asarray(sfa)
+    for g in range(G):
+        rows = np.nonzero(m_idx == g)[0]
+        if rows.size == 0:
+            continue
+        ref[rows] = fp8_gemm_nt(a[rows], sfa[:, rows], b[g], sfb[g])
+        written[rows] = True
+    return ref, written
+
+
+def m_grouped_masked(a, sfa, b, sfb, masked_m):
+    """M-grouped GEMM, masked layout (usage guide, "分组 GEMM（MoE）": decode).
+
+    a [G, max_m, K], sfa [G, K/128, max_m], b [G, N, K],
+    sfb [G, ceil(N/128), K/128], masked_m int [G] (valid rows per group).
+    For r < masked_m[g]: D[g, r] = A[g, r] . B[g]^T; other rows are not part
+    of the result.  Returns (ref float64 [G, max_m, N] with NaN outside,
+    written bool [G, max_m]).
+    """
+    a = np.asarray(a)
+    G, max_m, K = a.shape
+    N = np.asarray(b).shape[1]
+    ref = np.full((G, max_m, N), np.nan)
+    written = np.zeros((G, max_m), dtype=bool)
+    for g in range(G):
+        mg = int(masked_m[g])
+        if mg <= 0:
+            continue
+        ref[g, :mg] = fp8_gemm_nt(a[g, :mg], np.asarray(sfa)[g][:, :mg], b[g], sfb[g])
+        written[g, :mg] = True
+    return ref, written
+
+
+def fp8_gemm_nt_entries(a, sfa, b, sfb, c, rows, cols) -> np.ndarray:
+    """Selected entries D[rows[i], cols[i]] of the dense NT GEMM, one by one.
+
+    For spot checks at full size, where the whole product is too large for the
+    oracle: each entry is its own dot product over K in float64.
+    """
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    urows, rinv = np.unique(rows, return_inverse=True)
+    ucols, cinv = np.unique(cols, return_inverse=True)
+    A = dequant_a(np.asarray(a)[urows], np.asarray(sfa)[:, urows])
+    sfb = np.asarray(sfb, dtype=np.float64)
+    K = np.asarray(a).shape[1]
+    Bd = decode_e4m3(np.asarray(b)[ucols])
+    sb = np.repeat(sfb[ucols // BLOCK_K], BLOCK_K, axis=1)[:, :K]
+    B = Bd * sb
+    out = np.einsum("ik,ik->i", A[rinv], B[cinv])
+    if c is not None:
+        out = out + bf16_bits_to_f64(np.asarray(c)[rows, cols])
+    return out
+
+
+# ----------------------------------------------------------------------------
+# FP8 x FP4 expert FFN (linear1 -> SwiGLU -> requant -> linear2 -> weighted sum)
+# ----------------------------------------------------------------------------
+
+def dequant_x_ue8m0(x, x_sf) -> np.ndarray:
+    """e4m3 activations [T, H] with UE8M0 scales per 1x128 packed 4 per int32 [T, H/512]."""
+    x = np.asarray(x)
+    T, H = x.shape
+    s = unpack_ue8m0_int32(x_sf)[:, : H // 128]            # [T, H/128]
+    return decode_e4m3(x) * np.repeat(s, 128, axis=1)
+
+
+def dequant_w_fp4(w, w_sf) -> np.ndarray:
+    """E2M1 weights [R, C/2] bytes with UE8M0 scales per 1x32 packed 4 per int32 [R, C/128]."""
+    vals = unpack_e2m1(w)                                   # [R, C]
+    C = vals.shape[1]
+    s = unpack_ue8m0_int32(w_sf)[:, : C // 32]              # [R, C/32]
+    return vals * np.repeat(s, 32, axis=1)
+
+
+def silu(x):
+    """silu(x) = x * sigmoid(x) = x / (1 + exp(-x))."""
+    return x / (1.0 + np.exp(-x))
+
+
+def requant_e4m3_pow2(s32) -> tuple:
+    """Requantise rows of SwiGLU outputs to e4m3 with one power-of-two scale per 1x128.
+
+    The scale rule is 2**ceil(log2(amax/448)) (an all-zero block gets scale 1);
+    codes are round-to-nearest-even of s / scale, which cannot exceed 448.
+    Input float32 [P, I]; returns (codes uint8 [P, I], exponents int64 [P, I/128]).
+    The decision is taken on the float32 values, the precision of the kernel's
+    accumulator, so both sides round the same numbers.
+    """
+    s32 = np.asarray(s32, dtype=np.float32)
+    P, I = s32.shape
+    blocks = s32.reshape(P, I // 128, 128).astype(np.float64)
+    amax = np.abs(blocks).max(axis=2)                       # exact (max of fp32 values)
+    e = pow2_scale_exponent(amax, E4M3_MAX)                 # [P, I/128]
+    scaled = np.ldexp(blocks, -e[:, :, None])               # exact power-of-two scaling
+    codes = encode_e4m3_rne(scaled).reshape(P, I)
+    return codes, e
+
+
+def expert_ffn(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, expert_offset,
+               num_local_experts, return_intermediate=False):
+    """Single-GPU share of the fused FP8xFP4 MoE layer.
+
+    News page on the update ("Mega MoE：把整个 MoE 层融成一个核函数"): per expert,
+    linear1 -> SwiGLU -> linear2, then combine; activations FP8, weights FP4
+    with UE8M0 scales packed four per int32 ("FP4 精度支持").  Only the compute
+    of the local experts is modelled (dispatch/combine across GPUs is not).
+
+    Step order per (token t, slot k) whose expert e = topk_idx[t,k] - offset is
+    local:
+      1. h = dequant(x[t])                               (e4m3 * UE8M0 per 128)
+      2. u = h . W1_e^T, W1_e dequantised (E2M1 * UE8M0 per 32)   [2I]
+      3. gate = u[:I], up = u[I:]; both rounded to float32 (accumulator precision)
+      4. s = float32(silu(gate) * up)
+      5. requantise s per 1x128 to e4m3 with a power-of-two scale
+      6. o = dequant(q) . W2_e^T                          [H]
+      7. y[t] += topk_w[t,k] * o
+    Finally y is rounded once to bf16.  Tokens with no local hit give y = 0.
+
+    Returns (y_ref float64 [T, H], info dict).  info holds, per local expert,
+    the pair list (token, slot) and the intermediate codes/exponents when
+    ``return_intermediate`` is set.
+    """
+    x = np.asarray(x)
+    T, H = x.shape
+    idx = np.asarray(topk_idx).astype(np.int64)
+    wts = np.asarray(topk_w, dtype=np.float64)
+    I2 = np.asarray(w1).shape[1]
+    I = I2 // 2
+    y = np.zeros((T, H), dtype=np.float64)
+    info = {"pairs": [], "codes": [], "exps": []}
+    h_all = None
+    for e in range(num_local_experts):
+        tok, slot = np.nonzero(idx == e + expert_offset)
+        info["pairs"].append((tok, slot))
+        if tok.size == 0:
+            if return_intermediate:
+                info["codes"].append(np.zeros((0, I), np.uint8))
+                info["exps"].append(np.zeros((0, I // 128), np.int64))
+            continue
+        if h_all is None:
+            h_all = dequant_x_ue8m0(x, x_sf)
+        h = h_all[tok]                                                 # [m_e, H]
+        W1 = dequant_w_fp4(np.asarray(w1)[e], np.asarray(w1_sf)[e])    # [2I, H]
+        u = h @ W1.T                                                   # [m_e, 2I] float64
+        gate = u[:, :I].astype(np.float32).astype(np.float64)
+        up = u[:, I:].astype(np.float32).astype(np.float64)
+        s32 = (silu(gate) * up).astype(np.float32)
+        codes, ex = requant_e4m3_pow2(s32)
+        if return_intermediate:
+            info["codes"].append(codes)
+            info["exps"].append(ex)
+        q = decode_e4m3(codes) * np.repeat(np.ldexp(1.0, ex), 128, axis=1)
+        W2 = dequant_w_fp4(np.asarray(w2)[e], np.asarray(w2_sf)[e])    # [H, I]
+        o = q @ W2.T                                                   # [m_e, H]
+        np.add.at(y, tok, wts[tok, slot][:, None] * o)
+    return y, info
