@@ -1,0 +1,204 @@
+// C-ABI entry points (declared in include/dg.h): argument validation, device
+// facts, tile planning and kernel launch.  Validation runs on the host before
+// any HIP call; no exception crosses the boundary.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/dg.h"
+#include "dg_internal.hpp"
+
+namespace dg {
+
+static std::atomic<int> g_cu_cap{0};
+static std::mutex g_dev_mu;
+struct DevCache {
+  bool probed = false;
+  bool ok = false;
+  int num_cus = 0;
+};
+static DevCache g_dev_cache[64];
+
+DeviceInfo current_device_info() {
+  DeviceInfo info{-1, 0, false};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return info;
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevCache& c = g_dev_cache[dev];
+  if (!c.probed) {
+    c.probed = true;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+      c.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+      c.num_cus = prop.multiProcessorCount;
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  info.device = dev;
+  info.ok = c.ok;
+  info.num_cus = c.num_cus;
+  return info;
+}
+
+static int effective_cus(const DeviceInfo& di) {
+  int cap = g_cu_cap.load();
+  if (cap <= 0) {
+    const char* env = std::getenv("DG_NUM_CUS");
+    if (env) cap = std::atoi(env);
+  }
+  if (cap > 0 && cap < di.num_cus) return cap;
+  return di.num_cus;
+}
+
+static bool log_enabled() {
+  const char* env = std::getenv("DG_LOG");
+  return env && env[0] == '1';
+}
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream, const char* name) {
+  DeviceInfo di = current_device_info();
+  if (!di.ok) return DG_ERR_NO_DEVICE;
+  int cus = effective_cus(di);
+  GemmPlan plan = plan_fp8_gemm(p.m, p.n, p.k, p.num_groups, mode, cus, expected_m);
+  if (plan.kernel_id < 0) return DG_ERR_UNSUPPORTED;
+  p.tiles_m = plan.tiles_m;
+  p.tiles_n = plan.tiles_n;
+  p.total_tiles = plan.num_tiles;
+  p.group_m = 8;
+  if (log_enabled())
+    std::fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %dx%d (kernel %d), %d tiles, %d workgroups\n",
+                 name, p.m, p.n, p.k, p.num_groups, plan.block_m, plan.block_n, plan.kernel_id,
+                 plan.num_tiles, plan.num_workgroups);
+  hipError_t e = launch_fp8_gemm(p, plan, mode, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DG_OK : DG_ERR_HIP;
+}
+
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" {
+
+int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
+  try {
+    if (!a || !sfa || !b || !sfb || !d) return DG_ERR_INVALID_ARG;
+    if (m <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sfa, 4) || !aligned(sfb, 4) ||
+        (c && !aligned(c, 2)))
+      return DG_ERR_INVALID_ARG;
+    if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
+    Fp8GemmParams p{};
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = c; p.d = d;
+    p.m = m; p.n = n; p.k = k; p.num_groups = 1;
+    return run_fp8_gemm(p, MODE_DENSE, 0, stream, "fp8_gemm_nt");
+  } catch (...) {
+    return DG_ERR_HIP;
+  }
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                        const float* sfb, const int32_t* m_indices, uint16_t* d,
+                                        int m, int n, int k, int num_groups, void* stream) {
+  try {
+    if (!a || !sfa || !b || !sfb || !m_indices || !d) return DG_ERR_INVALID_ARG;
+    if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sfa, 4) || !aligned(sfb, 4) ||
+        !aligned(m_indices, 4))
+      return DG_ERR_INVALID_ARG;
+    if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
+    Fp8GemmParams p{};
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
+    p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
+    return run_fp8_gemm(p, MODE_CONTIG, 0, stream, "m_grouped_fp8_gemm_nt_contiguous");
+  } catch (...) {
+    return DG_ERR_HIP;
+  }
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                    const float* sfb, const int32_t* masked_m, uint16_t* d,
+                                    int num_groups, int max_m, int n, int k, int expected_m,
+                                    void* stream) {
+  try {
+    if (!a || !sfa || !b || !sfb || !masked_m || !d) return DG_ERR_INVALID_ARG;
+    if (num_groups <= 0 || max_m <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sfa, 4) || !aligned(sfb, 4) ||
+        !aligned(masked_m, 4))
+      return DG_ERR_INVALID_ARG;
+    if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
+    // the whole tile grid must be addressable with 32-bit tile ids
+    long long tiles = (long long)num_groups * ((max_m + 15) / 16) * ((n + 15) / 16);
+    if (tiles > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
+    Fp8GemmParams p{};
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
+    p.m = max_m; p.n = n; p.k = k; p.num_groups = num_groups;
+    return run_fp8_gemm(p, MODE_MASKED, expected_m, stream, "m_grouped_fp8_gemm_nt_masked");
+  } catch (...) {
+    return DG_ERR_HIP;
+  }
+}
+
+int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+int dg_set_num_cus(int n) {
+  if (n < 0) return DG_ERR_INVALID_ARG;
+  if (n > 0) {
+    DeviceInfo di = current_device_info();
+    if (di.ok && n > di.num_cus) return DG_ERR_INVALID_ARG;
+  }
+  g_cu_cap.store(n);
+  return DG_OK;
+}
+
+int dg_get_num_cus(void) {
+  DeviceInfo di = current_device_info();
+  if (di.num_cus <= 0) return 0;
+  return effective_cus(di);
+}
+
+int dg_num_tiles(int m, int n, int block_m, int block_n) {
+  if (m <= 0 || n <= 0 || block_m <= 0 || block_n <= 0) return 0;
+  return ((m + block_m - 1) / block_m) * ((n + block_n - 1) / block_n);
+}
+
+int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out) {
+  if (!out || m <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERR_INVALID_ARG;
+  if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
+  if (num_cus <= 0) {
+    DeviceInfo di = current_device_info();
+    if (!di.ok) return DG_ERR_NO_DEVICE;
+    num_cus = effective_cus(di);
+  }
+  int mode = num_groups > 1 ? MODE_MASKED : MODE_DENSE;
+  GemmPlan p = plan_fp8_gemm(m, n, k, num_groups, mode, num_cus, 0);
+  out->block_m = p.block_m;
+  out->block_n = p.block_n;
+  out->num_tiles = p.num_tiles;
+  out->num_workgroups = p.num_workgroups;
+  out->kernel_id = p.kernel_id;
+  return DG_OK;
+}
+
+const char* dg_status_string(int status) {
+  switch (status) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID_ARG: return "invalid argument";
+    case DG_ERR_UNSUPPORTED: return "unsupported shape";
+    case DG_ERR_HIP: return "HIP runtime error";
+    case DG_ERR_NO_DEVICE: return "no gfx950 device";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, the CDNA4
+// F8F6F4 matrix-core builtins, bf16 rounding, and the LDS swizzle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Operand formats of the F8F6F4 matrix instructions (cbsz/blgp fields).
+enum MfmaFmt : int { FMT_E4M3 = 0, FMT_E5M2 = 1, FMT_E2M3 = 2, FMT_E3M2 = 3, FMT_E2M1 = 4 };
+
+// 16x16x128 e4m3 x e4m3 -> fp32.  A lane holds 32 K-consecutive bytes of one
+// row (lane % 16) of A / column of B, K chunk (lane / 16); the 16x16 result has
+// rows 4*(lane/16) + i (i = 0..3) and column lane % 16 in element i.
+// With zero scale operands the compiler emits the unscaled instruction.
+__device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_E4M3, FMT_E4M3, 0, 0, 0, 0);
+}
+
+// 16x16x128 e4m3 (A) x e2m1 (B) with hardware block scales: each lane supplies
+// one UE8M0 byte for its 32-element K chunk of A and one for its chunk of B
+// (byte 0 of the given word).  B's 32 FP4 values occupy the low 4 dwords.
+__device__ __forceinline__ v4f mfma_scaled_e4m3_e2m1_16x16x128(const v8i& a, int sa, const v8i& b,
+                                                               int sb, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_E4M3, FMT_E2M1, 0, sa, 0, sb);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// LDS layout of a K-block tile: each row is 128 bytes = 8 chunks of 16 bytes;
+// chunk c of row r lives at position c ^ swz(r).  swz spreads any 8 (and any 16)
+// consecutive rows that read the same logical chunk over distinct bank groups.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+}  // namespace dg

@@ -1,0 +1,63 @@
+// Host-side declarations shared by the C-ABI layer, the planner and the kernel
+// launchers.  Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dg {
+
+enum GemmMode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
+
+// Arguments of one FP8 block-scaled GEMM launch (dense or grouped).
+struct Fp8GemmParams {
+  const uint8_t* a;
+  const float* sfa;
+  const uint8_t* b;
+  const float* sfb;
+  const uint16_t* c;          // dense only; may be null
+  uint16_t* d;
+  const int32_t* m_indices;   // contiguous only
+  const int32_t* masked_m;    // masked only
+  int m;                      // rows (dense / contiguous) or max_m (masked)
+  int n, k;
+  int num_groups;             // 1 for dense
+  int tiles_m, tiles_n;       // tile grid of one group (masked: over max_m)
+  int total_tiles;            // all groups
+  int group_m;                // raster: tiles along M visited before moving along N
+};
+
+// Tile shapes compiled into the library (kernel_id indexes this table).
+struct TileConfig {
+  int block_m, block_n;
+  int waves_per_simd;   // occupancy of the compiled kernel (VGPR bound)
+};
+int num_tile_configs();
+TileConfig tile_config(int kernel_id);
+
+// Device facts the planner and launchers need (cached per device).
+struct DeviceInfo {
+  int device;
+  int num_cus;
+  bool ok;
+};
+DeviceInfo current_device_info();
+
+// Plan for one GEMM call.
+struct GemmPlan {
+  int kernel_id;
+  int block_m, block_n;
+  int tiles_m, tiles_n;
+  int num_tiles;
+  int num_workgroups;
+};
+GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m);
+
+// Launches the kernel chosen by plan on stream; returns a hipError_t.
+hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mode, hipStream_t stream);
+
+// Workgroups per CU the given kernel reaches (cached; computed on first use).
+int fp8_gemm_blocks_per_cu(int kernel_id, int mode);
+
+}  // namespace dg

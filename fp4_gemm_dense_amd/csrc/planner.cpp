@@ -1,0 +1,70 @@
+// Host-side tile heuristic for the FP8 GEMM kernels.
+//
+// The release article ("DeepSeek 开源第三弹 ... DeepGEMM", 优化技术 / 完全 JIT 设计
+// and 非对齐块大小) describes a deterministic, autotune-free choice of block sizes,
+// and notes that power-of-two blocks can leave compute units idle (its example:
+// M=256, N=7168 with 128x128 blocks gives 112 tiles on a 132-unit part, while a
+// 112-wide block gives 128).  Here the same idea is applied to 256 CUs: among
+// the compiled tile shapes, prefer the one whose tile count fills the chip with
+// the least padding, and launch at most (CUs x workgroups per CU) persistent
+// workgroups.
+#include <algorithm>
+
+#include "dg_internal.hpp"
+
+namespace dg {
+
+static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Resident workgroups per CU for each compiled tile shape: the smaller of the
+// LDS bound (160 KB per CU) and the VGPR bound of the compiled kernel, which
+// the tile table records.
+static int blocks_per_cu_for(int kernel_id) {
+  TileConfig tc = tile_config(kernel_id);
+  int lds = 2 * (tc.block_m + tc.block_n) * 128;
+  int by_lds = (160 * 1024) / lds;
+  return std::max(1, std::min(tc.waves_per_simd, by_lds));
+}
+
+GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m) {
+  (void)k;
+  GemmPlan best{};
+  best.kernel_id = -1;
+  // rows each group contributes (masked: the expected count if given, else capacity)
+  int rows = m;
+  if (mode == MODE_MASKED) rows = expected_m > 0 ? std::min(expected_m, m) : m;
+
+  double best_score = -1.0;
+  for (int id = 0; id < num_tile_configs(); ++id) {
+    TileConfig tc = tile_config(id);
+    if (mode == MODE_CONTIG && (128 % tc.block_m) != 0) continue;   // blocks must be group-pure
+    int tm = cdiv(rows, tc.block_m);
+    int tn = cdiv(n, tc.block_n);
+    long long tiles = (long long)tm * tn * (mode == MODE_DENSE ? 1 : (mode == MODE_MASKED ? num_groups : 1));
+    // useful fraction of the MFMA work (padding in M and N is wasted)
+    double util = (double)rows / (tm * tc.block_m) * (double)n / (tn * tc.block_n);
+    // wave quantisation: fraction of the last wave of tiles that is busy
+    int slots = num_cus * blocks_per_cu_for(id);
+    long long waves = (tiles + slots - 1) / slots;
+    double fill = (double)tiles / (double)(waves * slots);
+    // bigger tiles re-read less from L2/HBM: weight by tile area (arithmetic intensity)
+    double intensity = (double)tc.block_m * tc.block_n / (tc.block_m + tc.block_n);
+    double score = util * fill * intensity;
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best.kernel_id = id;
+    }
+  }
+  TileConfig tc = tile_config(best.kernel_id);
+  best.block_m = tc.block_m;
+  best.block_n = tc.block_n;
+  best.tiles_m = cdiv(m, tc.block_m);
+  best.tiles_n = cdiv(n, tc.block_n);
+  long long total = (long long)best.tiles_m * best.tiles_n * (mode == MODE_MASKED ? num_groups : 1);
+  best.num_tiles = (int)std::min<long long>(total, 0x7fffffff);
+  long long slots = (long long)num_cus * blocks_per_cu_for(best.kernel_id);
+  best.num_workgroups = (int)std::min<long long>(total, slots);
+  return best;
+}
+
+}  // namespace dg

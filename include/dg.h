@@ -1,0 +1,199 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) fine-grained-scaled FP8 / FP8xFP4 GEMM library.
+ *
+ * Operations (sources are the DeepGEMM pages):
+ *   - dense NT GEMM D = C + A.B^T with e4m3 operands and fp32 block scales
+ *     (usage guide "DeepGEMM：统一高性能张量核心 GEMM 计算库编译与使用指南",
+ *      section 五、使用方法 / 基础非分组 FP8 GEMM: naming D = C + A @ B, NT layout,
+ *      fp32 scale factors on SM90);
+ *   - the M-grouped contiguous and masked forms for MoE experts
+ *     (same page, 分组 GEMM（MoE）: grouping along M only, N and K shared);
+ *   - the FP8xFP4 expert FFN, the single-GPU compute share of the fused MoE layer
+ *     (news page "DeepSeek 发布 DeepGEMM 重大更新：Mega MoE 融合算子与 FP4 精度支持",
+ *      sections Mega MoE and FP4 精度支持: linear1 -> SwiGLU -> linear2 -> combine,
+ *      FP4 weights with UE8M0 scales packed four per int32).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers to dense row-major arrays (last index
+ *     contiguous).  Sizes are element counts.  Operand and output pointers must
+ *     be 16-byte aligned; scale pointers 4-byte aligned.
+ *   - The caller owns every buffer, including outputs and workspaces.  The
+ *     library never allocates or frees device memory on these calls and keeps
+ *     only host-side state (a device-property cache and the CU cap).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     There is no host synchronisation and no host read of device data, so the
+ *     calls may be captured in a HIP graph.
+ *   - e4m3 means OCP e4m3fn (bias 7, max 448, NaN = 0x7F/0xFF).  bf16 values
+ *     are passed as their uint16 bit patterns.  Outputs are rounded from fp32
+ *     to bf16 with round-to-nearest-even.
+ *   - Every function returns a dg_status.  Arguments are validated on the host
+ *     before any HIP call; on an error nothing is enqueued and nothing is
+ *     written.  No C++ exception crosses this boundary and the library never
+ *     aborts, so a caller can fall back to another path.
+ *   - Malformed device metadata cannot cause out-of-bounds access: group ids
+ *     outside [0, num_groups) are treated as -1 (row skipped) and masked_m
+ *     values are clamped to [0, max_m].
+ *   - Scale layouts are part of the interface (the explainer page
+ *     "算子与编译器：DeepGEMM：FP8 GEMM 与 Mega-MoE", section 难点解释, treats the
+ *     scale layout as API semantics): A's scales are stored K-block-major so the
+ *     scales of one K block for consecutive rows are contiguous.
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dg_status {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, misalignment, small workspace */
+  DG_ERR_UNSUPPORTED = 2,   /* shape outside what the kernels support (e.g. K % 128 != 0)   */
+  DG_ERR_HIP = 3,           /* a HIP runtime error while launching                            */
+  DG_ERR_NO_DEVICE = 4      /* no usable gfx950 device is current                             */
+} dg_status;
+
+/*
+ * Dense NT GEMM: d[m][n] = bf16( c[m][n] + sum_k A[m][k] * B[n][k] ), where the
+ * dequantised operands are A[m][k] = e4m3(a[m][k]) * sfa[k/128][m] and
+ * B[n][k] = e4m3(b[n][k]) * sfb[n/128][k/128].  Accumulation is fp32: each 128-wide
+ * K block is reduced by the matrix cores into a fresh fp32 partial that is then
+ * scaled by sfa*sfb and added to the fp32 accumulator.
+ *
+ *   a    [m, k]               e4m3 codes
+ *   sfa  [k/128, m]           fp32, one scale per row per 128-wide K block
+ *   b    [n, k]               e4m3 codes (B is stored N x K: the "T" of NT)
+ *   sfb  [ceil(n/128), k/128] fp32, one scale per 128x128 block
+ *   c    [m, n]               bf16, or NULL for C = 0
+ *   d    [m, n]               bf16 output (may alias c only if identical)
+ * Requirements: m, n, k > 0; k % 128 == 0; n % 16 == 0.
+ */
+int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+
+/*
+ * M-grouped GEMM, contiguous layout (prefill / training forward).  Rows of all
+ * groups are concatenated along M; group g's rows are padded up to a multiple of
+ * dg_get_mk_alignment_for_contiguous_layout() and the padding rows carry group
+ * index -1.  For every row r with g = m_indices[r] in [0, num_groups):
+ *   d[r][n] = bf16( sum_k A[r][k] * B_g[n][k] )
+ * Rows with m_indices[r] == -1 (or out of range) are NOT written.  Each
+ * 128-row-aligned block of rows must belong to one group (or be padding); a row
+ * whose index differs from its block's first row is not written either.
+ *
+ *   a         [m, k]                            e4m3
+ *   sfa       [k/128, m]                        fp32
+ *   b         [num_groups, n, k]                e4m3
+ *   sfb       [num_groups, ceil(n/128), k/128]  fp32
+ *   m_indices [m]                               int32, device memory
+ *   d         [m, n]                            bf16
+ * Requirements: m, n, k, num_groups > 0; k % 128 == 0; n % 16 == 0.
+ */
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                        const float* sfb, const int32_t* m_indices, uint16_t* d,
+                                        int m, int n, int k, int num_groups, void* stream);
+
+/*
+ * M-grouped GEMM, masked layout (decode).  Each group has a fixed-capacity
+ * buffer of max_m rows, of which the first masked_m[g] are valid:
+ *   d[g][r][n] = bf16( sum_k A_g[r][k] * B_g[n][k] )   for r < masked_m[g]
+ * Rows r >= masked_m[g] are NOT written.  masked_m lives in device memory and
+ * is never read by the host.  expected_m is an optional host-side hint of the
+ * typical masked_m (<= 0: unknown) used only to choose tile sizes.
+ *
+ *   a        [num_groups, max_m, k]            e4m3
+ *   sfa      [num_groups, k/128, max_m]        fp32
+ *   b        [num_groups, n, k]                e4m3
+ *   sfb      [num_groups, ceil(n/128), k/128]  fp32
+ *   masked_m [num_groups]                      int32, device memory
+ *   d        [num_groups, max_m, n]            bf16
+ * Requirements: num_groups, max_m, n, k > 0; k % 128 == 0; n % 16 == 0.
+ */
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                    const float* sfb, const int32_t* masked_m, uint16_t* d,
+                                    int num_groups, int max_m, int n, int k, int expected_m,
+                                    void* stream);
+
+/*
+ * Bytes of device workspace dg_fp8_fp4_expert_ffn needs for these sizes
+ * (routing lists, the requantised intermediate and per-pair outputs).
+ * Returns 0 for invalid sizes.
+ */
+size_t dg_fp8_fp4_expert_ffn_workspace_bytes(int num_tokens, int num_topk, int num_local_experts,
+                                             int hidden, int intermediate);
+
+/*
+ * Single-GPU FP8 x FP4 expert FFN over the local experts
+ * [expert_offset, expert_offset + num_local_experts):
+ *   for each token t and slot j with e = topk_idx[t][j] - expert_offset in range:
+ *     h = e4m3(x[t]) * 2^(x_sf exponent per 128)
+ *     u = h . W1_e^T                       (W1_e = E2M1 * UE8M0 per 1x32, [2I, H])
+ *     s = silu(u[0:I]) * u[I:2I]           (gate rows first, then up rows)
+ *     q, sq = e4m3 requantisation of s per 1x128 with scale 2^ceil(log2(amax/448))
+ *     o = (q * sq) . W2_e^T                (W2_e = E2M1 * UE8M0 per 1x32, [H, I])
+ *     y[t] += topk_w[t][j] * o
+ *   y = bf16(y), with y[t] = 0 for tokens without a local hit.  Every row of y is written.
+ *
+ *   x         [T, H]            e4m3 activations
+ *   x_sf      [T, H/512]        int32, four UE8M0 scales per word (1x128 blocks);
+ *                               byte i (from the least significant) of word j is block 4j+i
+ *   topk_idx  [T, num_topk]     int32 global expert ids (any value; out-of-range ids ignored)
+ *   topk_w    [T, num_topk]     fp32
+ *   w1        [E, 2I, H/2]      E2M1 pairs; element 2i in the low nibble of byte i
+ *   w1_sf     [E, 2I, H/128]    int32, four UE8M0 scales per word (1x32 blocks)
+ *   w2        [E, H, I/2]       E2M1 pairs
+ *   w2_sf     [E, H, I/128]     int32
+ *   y         [T, H]            bf16 output
+ *   workspace device buffer of at least dg_fp8_fp4_expert_ffn_workspace_bytes(...) bytes,
+ *             256-byte aligned; its contents on entry are ignored
+ * Requirements: T, num_topk, E > 0; H % 512 == 0; I % 128 == 0.
+ */
+int dg_fp8_fp4_expert_ffn(const uint8_t* x, const int32_t* x_sf, const int32_t* topk_idx,
+                          const float* topk_w, const uint8_t* w1, const int32_t* w1_sf,
+                          const uint8_t* w2, const int32_t* w2_sf, uint16_t* y, int num_tokens,
+                          int num_topk, int num_local_experts, int expert_offset, int hidden,
+                          int intermediate, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Row alignment of each group in the contiguous layout (usage guide, 工具函数). Returns 128. */
+int dg_get_mk_alignment_for_contiguous_layout(void);
+
+/*
+ * Cap the number of compute units the persistent kernels use (usage guide, 工具函数:
+ * the SM-count setter/getter).  1 <= n <= CUs of the current device; n = 0 restores
+ * the default (all CUs).  Returns DG_OK or DG_ERR_INVALID_ARG.  dg_get_num_cus
+ * returns the cap in force (the device's CU count when none is set, or 0 when no
+ * device is visible).
+ */
+int dg_set_num_cus(int n);
+int dg_get_num_cus(void);
+
+/*
+ * The tile plan the heuristic picks for an M x N x K problem split over
+ * num_groups groups (1 for dense), on num_cus compute units (<= 0: current cap).
+ * Host-only: no HIP call is made when num_cus > 0.  Fills block_m, block_n,
+ * the number of output tiles and the number of workgroups launched.
+ * Exposed so callers can log the choice (DG_LOG=1 prints it on every call).
+ */
+typedef struct dg_plan {
+  int block_m;
+  int block_n;
+  int num_tiles;
+  int num_workgroups;
+  int kernel_id;
+} dg_plan;
+int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out);
+
+/* Number of output tiles for a tile shape: ceil(m/block_m) * ceil(n/block_n). Host-only. */
+int dg_num_tiles(int m, int n, int block_m, int block_n);
+
+/* Static description of a status code. */
+const char* dg_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H_ */

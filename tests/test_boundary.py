@@ -1,0 +1,99 @@
+"""Host-side checks of the C-ABI library: it loads, exports every symbol that
+include/dg.h declares, and rejects invalid arguments before any HIP call.
+No compute is launched here (these tests run without a GPU)."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import fp4_gemm_dense_amd as dgm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dgm.load_library()
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), name
+    # the binding wraps every one of them under the same name
+    for name in names:
+        assert callable(getattr(dgm, name)), name
+
+
+def test_status_strings_and_constants():
+    lib = dgm.load_library()
+    for s in range(5):
+        assert lib.dg_status_string(s)
+    assert lib.dg_get_mk_alignment_for_contiguous_layout() == 128
+
+
+def test_tile_count_golden_from_pages():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "tile_counts.json")))
+    for c in g["cases"]:
+        assert dgm.dg_num_tiles(c["m"], c["n"], c["block_m"], c["block_n"]) == c["tiles"]
+        assert c["tiles"] <= c["units"]
+
+
+A16 = 0x10000   # fake 16-byte-aligned "device" addresses: never dereferenced on the host
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, A16, A16, A16, 0, A16, 64, 64, 128), 1),          # null a
+    ((A16, A16, A16, A16, 0, A16, 0, 64, 128), 1),         # m = 0
+    ((A16, A16, A16, A16, 0, A16, 64, -1, 128), 1),        # n < 0
+    ((A16 + 4, A16, A16, A16, 0, A16, 64, 64, 128), 1),    # misaligned a
+    ((A16, A16 + 2, A16, A16, 0, A16, 64, 64, 128), 1),    # misaligned sfa
+    ((A16, A16, A16, A16, 0, A16, 64, 64, 100), 2),        # K % 128 != 0
+    ((A16, A16, A16, A16, 0, A16, 64, 40, 128), 2),        # N % 16 != 0
+])
+def test_dense_argument_validation(args, status):
+    lib = dgm.load_library()
+    assert lib.dg_fp8_gemm_nt(*args, None) == status
+
+
+def test_grouped_and_ffn_argument_validation():
+    lib = dgm.load_library()
+    f = lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    assert f(A16, A16, A16, A16, 0, A16, 256, 64, 128, 4, None) == 1            # null m_indices
+    assert f(A16, A16, A16, A16, A16, A16, 256, 64, 128, 0, None) == 1          # no groups
+    assert f(A16, A16, A16, A16, A16, A16, 256, 64, 384 + 1, 4, None) == 2
+    g = lib.dg_m_grouped_fp8_gemm_nt_masked
+    assert g(A16, A16, A16, A16, 0, A16, 4, 256, 64, 128, 0, None) == 1         # null masked_m
+    assert g(A16, A16, A16, A16, A16, A16, 4, 0, 64, 128, 0, None) == 1         # max_m = 0
+    assert g(A16, A16, A16, A16, A16, A16, 4, 256, 72, 128, 0, None) == 2       # N % 16
+    h = lib.dg_fp8_fp4_expert_ffn
+    ws = lib.dg_fp8_fp4_expert_ffn_workspace_bytes(64, 8, 4, 512, 256)
+    assert lib.dg_fp8_fp4_expert_ffn_workspace_bytes(0, 8, 4, 512, 256) == 0
+    common = (A16, A16, A16, A16, A16, A16, A16, A16, A16)
+    assert h(*common, 64, 8, 4, 0, 500, 256, A16, ws, None) == 2                # H % 512
+    assert h(*common, 64, 8, 4, 0, 512, 200, A16, ws, None) == 2                # I % 128
+    assert h(*common, 64, 8, 4, 0, 512, 256, A16, max(ws, 1) - 1, None) in (1, 2)  # workspace too small
+    assert h(*common, 64, 0, 4, 0, 512, 256, A16, ws, None) == 1                # no slots
+    assert h(0, *common[1:], 64, 8, 4, 0, 512, 256, A16, ws, None) == 1         # null x
+
+
+def test_set_num_cus_rejects_negative():
+    lib = dgm.load_library()
+    assert lib.dg_set_num_cus(-3) == 1
+    assert lib.dg_set_num_cus(0) == 0
+
+
+def test_planner_is_host_only_and_fills_the_chip():
+    # with an explicit CU count the plan needs no device
+    for (m, n, k) in [(4096, 7168, 2048), (4096, 2112, 7168), (64, 32768, 512), (128, 2112, 7168)]:
+        p = dgm.dg_query_plan(m, n, k, 1, 256)
+        assert p["num_tiles"] == dgm.dg_num_tiles(m, n, p["block_m"], p["block_n"])
+        assert 0 < p["num_workgroups"] <= max(p["num_tiles"], 1)
+        assert p["num_workgroups"] <= 256 * 4

@@ -1,0 +1,119 @@
+"""Parity of the dense NT GEMM (dg_fp8_gemm_nt) against the oracle on the GPU."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import ref as R
+from tests.helpers import bits, check_bit_exact, check_parity, sentinel_like
+from tests.test_oracle import make_exact_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x):
+    """numpy -> device tensor (uint16 bf16 bit patterns travel as int16)."""
+    if x is None:
+        return None
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        x = x.view(np.int16)
+    return torch.from_numpy(x).cuda()
+
+
+def _run(dg, a, sfa, b, sfb, c):
+    M, N = a.shape[0], b.shape[0]
+    d = sentinel_like((M, N))
+    dg.dg_fp8_gemm_nt(_dev(a), _dev(sfa), _dev(b), _dev(sfb), _dev(c), d)
+    torch.cuda.synchronize()
+    return bits(d)
+
+
+@pytest.mark.parametrize("M,N,K,with_c", [(9, 144, 384, True), (200, 272, 384, False), (130, 400, 1024, True),
+                                          (256, 256, 256, True), (1, 16, 128, False)])
+def test_dense_exact_integer_case_bit_exact(dg, M, N, K, with_c):
+    rng = np.random.default_rng(M + N + K)
+    a, sfa, b, sfb, c, exact = make_exact_case(rng, M, N, K, with_c)
+    check_bit_exact(_run(dg, a, sfa, b, sfb, c), exact, f"exact {M}x{N}x{K}")
+
+
+def test_dense_all_256_e4m3_codes_decode_like_ocp(dg):
+    """Row 0 of A holds every finite e4m3 code once; B is the identity, scales 1:
+    D[0, n] must be the OCP e4m3fn value of code n (exact in bf16)."""
+    K = N = 256
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0
+    a = np.zeros((3, K), np.uint8)
+    a[0] = codes
+    a[1] = codes[::-1]
+    b = np.zeros((N, K), np.uint8)
+    b[np.arange(N), np.arange(N)] = 0x38
+    sfa = np.ones((K // 128, 3), np.float32)
+    sfb = np.ones((2, 2), np.float32)
+    d = _run(dg, a, sfa, b, sfb, None)
+    want = R.fp8_gemm_nt(a, sfa, b, sfb)
+    assert np.array_equal(want[0], F.decode_e4m3(codes))
+    check_bit_exact(d, want, "256 codes")
+
+
+def test_dense_identity_b_and_all_ones(dg):
+    rng = np.random.default_rng(3)
+    M, N, K = 70, 256, 256
+    g = synth.gen_dense(M, N, K, seed=77, with_c=False)
+    a, sfa = synth.to_numpy(g["a"]), synth.to_numpy(g["sfa"])
+    b = np.zeros((N, K), np.uint8)
+    b[np.arange(N), np.arange(N)] = 0x38
+    sfb = rng.uniform(0.5, 2, (2, 2)).astype(np.float32)
+    d = _run(dg, a, sfa, b, sfb, None)
+    check_bit_exact(d, R.fp8_gemm_nt(a, sfa, b, sfb), "identity-B")
+    # all ones with C: D = C + K * sa * sb
+    M, N, K = 33, 160, 512
+    a = np.full((M, K), 0x38, np.uint8)
+    b = np.full((N, K), 0x38, np.uint8)
+    sfa = np.full((K // 128, M), 0.5, np.float32)
+    sfb = np.full((2, K // 128), 0.25, np.float32)
+    c = synth.to_numpy(synth.bf16_bits(torch.full((M, N), 3.0)))
+    d = _run(dg, a, sfa, b, sfb, c)
+    assert np.all(F.bf16_bits_to_f64(d) == K * 0.5 * 0.25 + 3.0)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (17, 144, 384), (64, 528, 1024), (130, 2112, 256),
+                                   (300, 400, 640), (513, 1040, 384)])
+def test_dense_random_parity(dg, M, N, K):
+    g = synth.gen_dense(M, N, K, seed=M * 7 + N + K, with_c=True)
+    a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+    d = _run(dg, a, sfa, b, sfb, c)
+    assert not (d == 0xFFFF).any(), "every output element must be written"
+    check_parity(d, R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"{M}x{N}x{K}")
+
+
+def test_dense_config0_full_parity(dg):
+    """M=128, N=2112, K=7168, C = 0 (passed as NULL): the whole output vs the oracle."""
+    g = synth.gen_dense(128, 2112, 7168, seed=synth.seed_for(0, 0), with_c=False)
+    a, sfa, b, sfb = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb"))
+    d = _run(dg, a, sfa, b, sfb, None)
+    check_parity(d, R.fp8_gemm_nt(a, sfa, b, sfb), what="config0")
+
+
+@pytest.mark.parametrize("mi,nki", [(m, j) for m in range(2) for j in range(6)])
+def test_dense_sweep_full_size_sampled(dg, mi, nki):
+    """The dense sweep shapes at full size, generated on the device; the oracle
+    evaluates 4096 sampled outputs one by one (all rows for M=64)."""
+    M = synth.DENSE_M[mi]
+    N, K = synth.DENSE_NK[nki]
+    g = synth.gen_dense(M, N, K, seed=synth.seed_for(1, mi * 6 + nki), backend="torch", device="cuda")
+    d = sentinel_like((M, N))
+    dg.dg_fp8_gemm_nt(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
+    torch.cuda.synchronize()
+    db = bits(d)
+    assert not (db == 0xFFFF).any()
+    rng = np.random.default_rng(mi * 6 + nki)
+    rows = rng.integers(0, M, 4096)
+    cols = rng.integers(0, N, 4096)
+    rows[:8] = M - 1
+    cols[:8] = N - 1
+    a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+    ref = R.fp8_gemm_nt_entries(a, sfa, b, sfb, c, rows, cols)
+    check_parity(db[rows, cols], ref, what=f"sweep M={M} N={N} K={K}")
