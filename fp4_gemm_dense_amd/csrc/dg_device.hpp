@@ -43,7 +43,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 
 // LDS layout of a K-block tile: each row is 128 bytes = 8 chunks of 16 bytes;
 // chunk c of row r lives at position c ^ swz(r).  swz spreads any 8 (and any 16)
-// consecutive rows that read the same logical chunk over distinct bank groups.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// consecutive rows that read the same logical chunk over distinct bank groups,
+// and depends only on r % 16, so rows r and r + 16k share one pattern (their
+// addresses differ by a constant that fits an instruction offset).
+__device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 
 }  // namespace dg

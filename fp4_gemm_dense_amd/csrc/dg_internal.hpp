@@ -31,7 +31,9 @@ struct Fp8GemmParams {
 // Tile shapes compiled into the library (kernel_id indexes this table).
 struct TileConfig {
   int block_m, block_n;
-  int waves_per_simd;   // occupancy of the compiled kernel (VGPR bound)
+  int blocks_per_cu;    // resident workgroups per CU of the compiled kernel
+  int threads;          // workgroup size
+  int lds_bytes;        // dynamic LDS per workgroup
 };
 int num_tile_configs();
 TileConfig tile_config(int kernel_id);

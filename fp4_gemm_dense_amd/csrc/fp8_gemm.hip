@@ -26,24 +26,60 @@
 
 namespace dg {
 
-template <int MT, int NT, int WM, int WN, int MODE>
-__global__ void __launch_bounds__(256, 1) fp8_gemm_kernel(Fp8GemmParams p) {
+// Waits until at most n vector-memory operations of this wave are outstanding.
+// (gfx9 encoding: vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at max.)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies: the
+// fence would wait for every outstanding load, including the LDS-DMA loads of
+// later pipeline stages.  The empty asm keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copies: lane l's 16 (or 4) bytes land at
+// lds_base + 16*l (or 4*l).  lds_base must be the same for the whole wave.
+__device__ __forceinline__ void dma16_to_lds(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4_to_lds(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
+}
+
+template <int MT, int NT, int WM, int WN, int STAGES, int MODE>
+__global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams p) {
+  constexpr int NW = WM * WN;                 // waves per workgroup
   constexpr int BM = WM * MT * 16;
   constexpr int BN = WN * NT * 16;
   constexpr int A_BYTES = BM * 128;
   constexpr int B_BYTES = BN * 128;
-  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  constexpr int A_CHUNKS = BM * 8;    // 16-byte chunks per A tile
-  constexpr int B_CHUNKS = BN * 8;
-  constexpr int A_LD = (A_CHUNKS + 255) / 256;
-  constexpr int B_LD = (B_CHUNKS + 255) / 256;
-  static_assert(WM * WN == 4, "four waves per workgroup");
+  constexpr int SA_BYTES = BM * 4;
+  constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
+  // Each wave copies RA 8-row regions (1 KB) of A, RB of B and SPW A scales per stage.
+  static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "regions must split evenly over waves");
+  constexpr int RA = BM / 8 / NW;
+  constexpr int RB = BN / 8 / NW;
+  constexpr int SPW = BM / NW;
+  static_assert(SPW <= 64, "scale copy must fit one instruction per wave");
+  constexpr int LPS = RA + RB + 1;            // DMA instructions per wave per stage
+  // the 16 columns of every accumulator block lie in one 128-wide B-scale block;
+  // when all of a wave's columns do, one sb serves the whole wave
+  constexpr bool ONE_SB = (128 % (NT * 16) == 0) && (BN % 128 == 0 || 128 % BN == 0);
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  typedef const __attribute__((address_space(4))) float cfloat;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave / WN;
   const int wave_n = wave % WN;
   const int lrow = lane & 15;     // operand row / output column inside a 16x16 block
@@ -53,7 +89,20 @@ __global__ void __launch_bounds__(256, 1) fp8_gemm_kernel(Fp8GemmParams p) {
   const int KB = K >> 7;
   const int NB = (N + 127) >> 7;
 
-  // XCD-aware remap of the persistent block id.
+  // Per-lane LDS read offsets (slot 0); blocks mt / nt add mt*2048 / nt*2048
+  // and the slot adds slot*STAGE.  The swizzle depends on row % 16 only.
+  const int sw = swz(lrow);
+  const uint32_t a_lo = (wave_m * MT * 16 + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
+  const uint32_t a_hi = (wave_m * MT * 16 + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
+  const uint32_t b_lo = A_BYTES + (wave_n * NT * 16 + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
+  const uint32_t b_hi = A_BYTES + (wave_n * NT * 16 + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
+  const uint32_t sa_rd = A_BYTES + B_BYTES + (wave_m * MT * 16 + 4 * lgrp) * 4;
+  // Per-lane DMA row inside an 8-row region; the swizzled chunk depends on the
+  // tile row's bit 3 as well, i.e. on the region's parity.
+  const int dma_row = lane >> 3;
+
+  // XCD-aware remap of the persistent block id: workgroups are dealt to the
+  // 8 XCDs round-robin, so give XCD x a contiguous stretch of the raster.
   const int G = gridDim.x;
   int vb = blockIdx.x;
   if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
@@ -80,7 +129,7 @@ __global__ void __launch_bounds__(256, 1) fp8_gemm_kernel(Fp8GemmParams p) {
     if (MODE == MODE_MASKED) {
       int mm = p.masked_m[g];
       rows_valid = mm < 0 ? 0 : (mm > M ? M : mm);
-      if (m0 >= rows_valid) continue;           // empty tile: whole block skips
+      if (m0 >= rows_valid) continue;           // empty tile: the whole workgroup skips it
     }
     if (MODE == MODE_CONTIG) {
       g = p.m_indices[m0];
@@ -100,58 +149,44 @@ __global__ void __launch_bounds__(256, 1) fp8_gemm_kernel(Fp8GemmParams p) {
       SB += (size_t)g * NB * KB;
     }
 
-    // ---------------- global -> register staging ----------------
-    v4i ra[A_LD], rb[B_LD];
-    const v4i* a_src[A_LD];
-    const v4i* b_src[B_LD];
-    int a_dst[A_LD], b_dst[B_LD];
+    // ---------------- DMA sources of this wave ----------------
+    // A region (wave*RA + j) covers tile rows 8*(wave*RA+j) .. +7; lane l fills
+    // LDS bytes [16l, 16l+16) of it: row + l/8, position l%8, which holds
+    // logical chunk (l%8) ^ swz(row).  Offsets are 32-bit, relative to A / B.
+    uint32_t a_off[RA], b_off[RB];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      int ch = tid + i * 256;
-      int row = ch >> 3, c = ch & 7;
-      if (ch >= A_CHUNKS) row = 0;
-      int gr = min(m0 + row, M - 1);
-      a_src[i] = reinterpret_cast<const v4i*>(A + (size_t)gr * K + c * 16);
-      a_dst[i] = row * 128 + ((c ^ swz(row)) << 4);
+    for (int j = 0; j < RA; ++j) {
+      const int row = (wave * RA + j) * 8 + dma_row;
+      a_off[j] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4);
     }
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      int ch = tid + i * 256;
-      int row = ch >> 3, c = ch & 7;
-      if (ch >= B_CHUNKS) row = 0;
-      int gc = min(n0 + row, N - 1);
-      b_src[i] = reinterpret_cast<const v4i*>(B + (size_t)gc * K + c * 16);
-      b_dst[i] = A_BYTES + row * 128 + ((c ^ swz(row)) << 4);
+    for (int j = 0; j < RB; ++j) {
+      const int row = (wave * RB + j) * 8 + dma_row;
+      b_off[j] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4);
     }
-    auto gload = [&](int kb) {
+    const uint32_t sa_off = (uint32_t)min(m0 + wave * SPW + (lane < SPW ? lane : 0), M - 1) * 4;
+    const uint32_t a_dst = wave * RA * 1024;
+    const uint32_t b_dst = A_BYTES + wave * RB * 1024;
+    const uint32_t sa_dst = A_BYTES + B_BYTES + wave * SPW * 4;
+
+    auto issue = [&](int kb, uint32_t slot_off) {
+      const uint8_t* ak = A + (size_t)kb * 128;
+      const uint8_t* bk = B + (size_t)kb * 128;
+      const uint8_t* sk = reinterpret_cast<const uint8_t*>(SA + (size_t)kb * M);
 #pragma unroll
-      for (int i = 0; i < A_LD; ++i)
-        if (A_CHUNKS % 256 == 0 || tid + i * 256 < A_CHUNKS) ra[i] = a_src[i][kb * 8];
+      for (int j = 0; j < RA; ++j) dma16_to_lds(ak + a_off[j], smem + slot_off + a_dst + j * 1024);
 #pragma unroll
-      for (int i = 0; i < B_LD; ++i)
-        if (B_CHUNKS % 256 == 0 || tid + i * 256 < B_CHUNKS) rb[i] = b_src[i][kb * 8];
-    };
-    auto lstore = [&](int buf) {
-      uint8_t* base = smem + buf * STAGE_BYTES;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i)
-        if (A_CHUNKS % 256 == 0 || tid + i * 256 < A_CHUNKS) *reinterpret_cast<v4i*>(base + a_dst[i]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i)
-        if (B_CHUNKS % 256 == 0 || tid + i * 256 < B_CHUNKS) *reinterpret_cast<v4i*>(base + b_dst[i]) = rb[i];
+      for (int j = 0; j < RB; ++j) dma16_to_lds(bk + b_off[j], smem + slot_off + b_dst + j * 1024);
+      if (SPW == 64 || lane < SPW) dma4_to_lds(sk + sa_off, smem + slot_off + sa_dst);
     };
 
-    // per-lane scale addresses
-    int sa_row[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sa_row[mt][i] = min(m0 + wave_m * MT * 16 + mt * 16 + 4 * lgrp + i, M - 1);
-    int sb_blk[NT];
+    // B-scale indices are wave-uniform; reading them through the constant
+    // address space makes the per-K-block reads scalar loads (not counted by vmcnt)
+    cfloat* SBc = (cfloat*)(uintptr_t)(SB);
+    int sb_idx[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      sb_blk[nt] = (min(n0 + wave_n * NT * 16 + nt * 16, N - 1) >> 7) * KB;
+      sb_idx[nt] = __builtin_amdgcn_readfirstlane((min(n0 + wave_n * NT * 16 + nt * 16, N - 1) >> 7) * KB);
 
     v4f acc[MT][NT];
 #pragma unroll
@@ -159,42 +194,55 @@ __global__ void __launch_bounds__(256, 1) fp8_gemm_kernel(Fp8GemmParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    // prologue: stages 0 .. STAGES-2 in flight
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KB) issue(s, s * STAGE);
 
+    uint32_t rd_slot = 0;                          // slot of stage kb
+    uint32_t wr_slot = (STAGES - 1) * STAGE;       // slot of stage kb + STAGES - 1
     for (int kb = 0; kb < KB; ++kb) {
-      const int cur = kb & 1;
-      if (kb + 1 < KB) gload(kb + 1);
+      // stage kb has landed once at most (#stages issued after it) DMA ops remain
+      const int after = min(STAGES - 2, KB - 1 - kb);
+      if (STAGES >= 4 && after >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS>();
+      else if (STAGES >= 3 && after >= 1) wait_vmcnt<(STAGES >= 3 ? 1 : 0) * LPS>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      if (kb + STAGES - 1 < KB) issue(kb + STAGES - 1, wr_slot);
 
-      float sa[MT][4], sb[NT];
+      float sbv[NT];
+      if (ONE_SB) {
+        const float s0 = SBc[sb_idx[0] + kb];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int nt = 0; nt < NT; ++nt) sbv[nt] = s0;
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sa[mt][i] = SA[(size_t)kb * M + sa_row[mt][i]];
+        for (int nt = 0; nt < NT; ++nt) sbv[nt] = SBc[sb_idx[nt] + kb];
+      }
+      const uint8_t* ra_lo = smem + rd_slot + a_lo;
+      const uint8_t* ra_hi = smem + rd_slot + a_hi;
+      const uint8_t* rb_lo = smem + rd_slot + b_lo;
+      const uint8_t* rb_hi = smem + rd_slot + b_hi;
+      const uint8_t* rsa = smem + rd_slot + sa_rd;
+      v4f sa[MT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sb[nt] = SB[sb_blk[nt] + kb];
-
-      const uint8_t* sA = smem + cur * STAGE_BYTES;
-      const uint8_t* sB = sA + A_BYTES;
+      for (int mt = 0; mt < MT; ++mt) sa[mt] = *reinterpret_cast<const v4f*>(rsa + mt * 64);
       v8i af[MT], bf[NT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int row = wave_m * MT * 16 + mt * 16 + lrow;
-        const uint8_t* rp = sA + row * 128;
-        const int s = swz(row);
-        v4i lo = *reinterpret_cast<const v4i*>(rp + (((2 * lgrp) ^ s) << 4));
-        v4i hi = *reinterpret_cast<const v4i*>(rp + (((2 * lgrp + 1) ^ s) << 4));
+        v4i lo = *reinterpret_cast<const v4i*>(ra_lo + mt * 2048);
+        v4i hi = *reinterpret_cast<const v4i*>(ra_hi + mt * 2048);
         af[mt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int row = wave_n * NT * 16 + nt * 16 + lrow;
-        const uint8_t* rp = sB + row * 128;
-        const int s = swz(row);
-        v4i lo = *reinterpret_cast<const v4i*>(rp + (((2 * lgrp) ^ s) << 4));
-        v4i hi = *reinterpret_cast<const v4i*>(rp + (((2 * lgrp + 1) ^ s) << 4));
+        v4i lo = *reinterpret_cast<const v4i*>(rb_lo + nt * 2048);
+        v4i hi = *reinterpret_cast<const v4i*>(rb_hi + nt * 2048);
         bf[nt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+      if (ONE_SB) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) sa[mt] *= sbv[0];
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -202,13 +250,16 @@ __global__ void __launch_bounds__(256, 1) fp8_gemm_kernel(Fp8GemmParams p) {
         for (int nt = 0; nt < NT; ++nt) {
           v4f part = mfma_e4m3_16x16x128(af[mt], bf[nt], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(part[i], sa[mt][i] * sb[nt], acc[mt][nt][i]);
+          for (int i = 0; i < 4; ++i) {
+            const float sc = ONE_SB ? sa[mt][i] : sa[mt][i] * sbv[nt];
+            acc[mt][nt][i] = fmaf(part[i], sc, acc[mt][nt][i]);
+          }
         }
       }
-
-      if (kb + 1 < KB) lstore(cur ^ 1);
-      __syncthreads();
+      rd_slot = (rd_slot + STAGE == STAGES * STAGE) ? 0u : rd_slot + STAGE;
+      wr_slot = (wr_slot + STAGE == STAGES * STAGE) ? 0u : wr_slot + STAGE;
     }
+    block_barrier();   // every wave is done with the LDS ring before the next tile refills it
 
     // ---------------- epilogue: + C, bf16 RNE, predicated stores ----------------
     uint16_t* D = p.d;
@@ -238,14 +289,16 @@ __global__ void __launch_bounds__(256, 1) fp8_gemm_kernel(Fp8GemmParams p) {
 // tile-config table and launcher
 // ---------------------------------------------------------------------------
 
-// id, MT, NT, WM, WN, waves per SIMD reached by the compiled kernel
-#define DG_TILE_CONFIGS(X) \
-  X(0, 4, 4, 2, 2, 1)      \
-  X(1, 2, 4, 2, 2, 2)      \
-  X(2, 2, 2, 2, 2, 3)
+// id, MT, NT, WM, WN, STAGES, workgroups per CU
+#define DG_TILE_CONFIGS(X)    \
+  X(0, 4, 4, 4, 2, 3, 1)      \
+  X(1, 4, 4, 2, 4, 3, 1)      \
+  X(2, 4, 4, 2, 2, 3, 1)      \
+  X(3, 4, 2, 1, 4, 4, 1)
 
 static const TileConfig kTileConfigs[] = {
-#define X(id, MT, NT, WM, WN, OCC) {WM * MT * 16, WN * NT * 16, OCC},
+#define X(id, MT, NT, WM, WN, ST, OCC) {WM * MT * 16, WN * NT * 16, OCC, WM * WN * 64, \
+                                        ST * ((WM * MT * 16 + WN * NT * 16) * 128 + WM * MT * 16 * 4)},
     DG_TILE_CONFIGS(X)
 #undef X
 };
@@ -256,10 +309,17 @@ TileConfig tile_config(int id) { return kTileConfigs[id]; }
 template <int MODE>
 static hipError_t launch_mode(const Fp8GemmParams& p, int kernel_id, int grid, hipStream_t stream) {
   switch (kernel_id) {
-#define X(id, MT, NT, WM, WN, OCC)                                                            \
-  case id:                                                                                    \
-    hipLaunchKernelGGL((fp8_gemm_kernel<MT, NT, WM, WN, MODE>), dim3(grid), dim3(256), 0, stream, p); \
-    break;
+#define X(id, MT, NT, WM, WN, ST, OCC)                                                              \
+  case id: {                                                                                      \
+    const TileConfig& tc = kTileConfigs[id];                                                      \
+    static const hipError_t attr = hipFuncSetAttribute(                                           \
+        reinterpret_cast<const void*>(&fp8_gemm_kernel<MT, NT, WM, WN, ST, MODE>),                \
+        hipFuncAttributeMaxDynamicSharedMemorySize, tc.lds_bytes);                                \
+    if (attr != hipSuccess) return attr;                                                          \
+    hipLaunchKernelGGL((fp8_gemm_kernel<MT, NT, WM, WN, ST, MODE>), dim3(grid), dim3(tc.threads), \
+                       tc.lds_bytes, stream, p);                                                  \
+    break;                                                                                        \
+  }
     DG_TILE_CONFIGS(X)
 #undef X
     default:

@@ -17,13 +17,11 @@ namespace dg {
 static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Resident workgroups per CU for each compiled tile shape: the smaller of the
-// LDS bound (160 KB per CU) and the VGPR bound of the compiled kernel, which
-// the tile table records.
+// LDS bound (160 KB per CU) and the occupancy the tile table records.
 static int blocks_per_cu_for(int kernel_id) {
   TileConfig tc = tile_config(kernel_id);
-  int lds = 2 * (tc.block_m + tc.block_n) * 128;
-  int by_lds = (160 * 1024) / lds;
-  return std::max(1, std::min(tc.waves_per_simd, by_lds));
+  int by_lds = (160 * 1024) / tc.lds_bytes;
+  return std::max(1, std::min(tc.blocks_per_cu, by_lds));
 }
 
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m) {
