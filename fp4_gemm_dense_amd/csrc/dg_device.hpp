@@ -48,4 +48,32 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 // addresses differ by a constant that fits an instruction offset).
 __device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 
+// Waits until at most n vector-memory operations of this wave are outstanding.
+// (gfx9 encoding: vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at max.)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies: the
+// fence would wait for every outstanding load, including the LDS-DMA loads of
+// later pipeline stages.  The empty asm keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copies: lane l's 16 (or 4) bytes land at
+// lds_base + 16*l (or 4*l).  lds_base must be the same for the whole wave.
+__device__ __forceinline__ void dma16_to_lds(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4_to_lds(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
+}
+
 }  // namespace dg

@@ -1,0 +1,242 @@
+"""Parity of the FP8xFP4 expert FFN (dg_fp8_fp4_expert_ffn) against the oracle on the GPU.
+
+Tolerance for this path: per element |y - ref| <= 2e-2 * max(|ref|, rms(ref)),
+Frobenius relative error <= 8e-3.
+
+The requantised intermediate is a rounding decision taken in fp32 on both
+sides.  The kernel's fp32 linear1 accumulates in another order than the
+oracle's float64 product rounded to fp32, so where a value lies within fp32
+accumulation error of an e4m3 rounding midpoint the two codes can legitimately
+differ by one step.  The tests therefore check (1) that codes agree except for
+such neighbours, each of which must sit at a midpoint of the oracle's own
+value, (2) y against the oracle's linear2 + weighted sum evaluated on the
+kernel's codes, at the tolerance above, and (3) y against the plain oracle in
+Frobenius norm.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ref as R
+from tests.helpers import bits, check_parity
+
+pytestmark = pytest.mark.gpu
+
+ELEM_TOL, FRO_TOL = 2e-2, 8e-3
+
+
+def _to_dev(g):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in g.items()}
+
+
+def _run(dg, g, topk_w=None, offset=None, ws_extra=0):
+    T, H = g["x"].shape
+    E, I2 = g["w1"].shape[0], g["w1"].shape[1]
+    k = g["topk_idx"].shape[1]
+    nbytes = dg.dg_fp8_fp4_expert_ffn_workspace_bytes(T, k, E, H, I2 // 2)
+    ws = torch.zeros(nbytes + ws_extra, dtype=torch.uint8, device="cuda")
+    y = torch.full((T, H), -1, dtype=torch.int16, device="cuda")      # sentinel 0xFFFF
+    dg.dg_fp8_fp4_expert_ffn(g["x"], g["x_sf"], g["topk_idx"], g["topk_w"] if topk_w is None else topk_w,
+                             g["w1"], g["w1_sf"], g["w2"], g["w2_sf"], y,
+                             g["expert_offset"] if offset is None else offset, ws)
+    torch.cuda.synchronize()
+    return bits(y), ws
+
+
+def _oracle(g, offset=None, topk_w=None, codes_override=None):
+    n = {k: synth.to_numpy(g[k]) for k in ("x", "x_sf", "topk_idx", "topk_w", "w1", "w1_sf", "w2", "w2_sf")}
+    if topk_w is not None:
+        n["topk_w"] = topk_w
+    return R.expert_ffn(n["x"], n["x_sf"], n["topk_idx"], n["topk_w"], n["w1"], n["w1_sf"], n["w2"], n["w2_sf"],
+                        g["expert_offset"] if offset is None else offset, g["E"], return_intermediate=True,
+                        codes_override=codes_override)
+
+
+def _check_ffn(g, y, ws, what):
+    ref, info = _oracle(g)
+    kern = _kernel_intermediate(g, ws, info)
+    _check_codes(kern, info, g)
+    ref_k, _ = _oracle(g, codes_override=kern)
+    idx = synth.to_numpy(g["topk_idx"])
+    off, E = g["expert_offset"], g["E"]
+    hit = ((idx >= off) & (idx < off + E)).any(1)
+    if hit.any():
+        check_parity(y[hit], ref_k[hit], ELEM_TOL, FRO_TOL, what=what + " (oracle on kernel codes)")
+        check_parity(y[hit], ref[hit], np.inf, FRO_TOL, what=what + " (plain oracle, Frobenius)")
+    return hit
+
+
+def _kernel_intermediate(g, ws, info):
+    """The kernel's requantised intermediate (codes, exponents) per local expert, in
+    the oracle's pair order, read from the workspace (regions in the order the
+    library documents: counts, starts, pair tokens, pair index, codes, exponents)."""
+    T, k = g["topk_idx"].shape
+    E, I = g["E"], g["I"]
+    P = T * k
+    sq_stride = ((I // 128) + 3) & ~3
+
+    def a256(v):
+        return (v + 255) & ~255
+    off = a256(a256(0 + E * 4) + (E + 1) * 4)
+    off = a256(off + P * 4)                  # pair tokens
+    pair_of_off = off
+    off = a256(off + P * 4)
+    q_off = off
+    sq_off = a256(off + P * I)
+    w = ws.cpu().numpy()
+    pair_of = w[pair_of_off:pair_of_off + P * 4].view(np.int32).reshape(T, k)
+    q = w[q_off:q_off + P * I].reshape(P, I)
+    sq = w[sq_off:sq_off + P * sq_stride].reshape(P, sq_stride)
+    out = {}
+    for e in range(E):
+        tok, slot = info["pairs"][e]
+        pr = pair_of[tok, slot]
+        out[e] = (q[pr], sq[pr, : I // 128].astype(np.int64) - 127)
+    return out
+
+
+def _value_rank():
+    """Sorted distinct finite e4m3 values, and each code's rank among them (+0 and -0 share one)."""
+    from oracle.formats import E4M3_TABLE
+    vals = np.where(np.isnan(E4M3_TABLE), np.inf, E4M3_TABLE)
+    distinct = np.unique(vals[np.isfinite(vals)])
+    return distinct, np.searchsorted(distinct, vals).astype(np.int64)
+
+
+_DISTINCT, _RANK = _value_rank()
+
+
+def _mfma_error_bound(h, w):
+    """Bound on |matrix-core dot product - exact| for rows of h . w (elementwise pairs).
+
+    The gfx950 F8F6F4 matrix instructions reduce products in groups of 8
+    consecutive K positions aligned to the group's largest product and keep 13
+    bits below its leading bit (measured on MI355X: 2^4 + 2^-9 in one group is
+    exact, 2^5 + 2^-9 drops the small term; groups are k = 8j .. 8j+7).  Each
+    product can therefore lose less than 2^(e_max - 13) with e_max the exponent
+    of its group's largest |product|; fp32 accumulation of the group sums adds
+    a tree-sum term.
+    """
+    t = np.abs(h * w)                                     # [n, K]
+    n, K = t.shape
+    gmax = t.reshape(n, K // 8, 8).max(axis=2)
+    _, ex = np.frexp(np.where(gmax > 0, gmax, 1.0))       # gmax < 2^ex
+    per_group = np.where(gmax > 0, 8 * np.ldexp(1.0, ex - 1 - 13), 0.0)
+    return per_group.sum(axis=1) + (np.ceil(np.log2(K)) + 4) * 2.0 ** -24 * t.sum(axis=1)
+
+
+def _check_codes(kern, info, g):
+    """Codes agree with the oracle's except for neighbours at a rounding midpoint.
+
+    A differing code is accepted only when the oracle's value lies within the
+    matrix-core accumulation error of linear1 (see _mfma_error_bound) from the
+    midpoint between the two codes, propagated through silu(gate) * up, in the
+    block's scaled units.
+    """
+    n_same = n_all = 0
+    x_deq = None
+    n = {k: synth.to_numpy(g[k]) for k in ("x", "x_sf", "w1", "w1_sf")}
+    I = g["I"]
+    for e, (codes, ex) in kern.items():
+        if codes.shape[0] == 0:
+            continue
+        want, wex = info["codes"][e], info["exps"][e]
+        assert np.array_equal(ex, wex), f"expert {e}: requant scale exponents differ"
+        same = _RANK[codes] == _RANK[want]                # +0 and -0 are the same value
+        n_same += same.sum()
+        n_all += same.size
+        if same.all():
+            continue
+        r, c = np.nonzero(~same)
+        if x_deq is None:
+            x_deq = R.dequant_x_ue8m0(n["x"], n["x_sf"])
+        tok = info["pairs"][e][0][r]
+        W1 = R.dequant_w_fp4(n["w1"][e], n["w1_sf"][e])
+        h = x_deq[tok]
+        gate = np.einsum("ik,ik->i", h, W1[c])
+        up = np.einsum("ik,ik->i", h, W1[I + c])
+        d_gate = _mfma_error_bound(h, W1[c])
+        d_up = _mfma_error_bound(h, W1[I + c])
+        sig = 1.0 / (1.0 + np.exp(-gate))
+        silu = gate * sig
+        dsilu = sig * (1.0 + gate * (1.0 - sig))
+        s = silu * up
+        d_s = np.abs(dsilu * up) * d_gate + np.abs(silu) * d_up + 2.0 ** -21 * np.abs(s)
+        scale = np.ldexp(1.0, wex[r, c // 128])
+        x = s / scale
+        delta = d_s / scale
+        # the kernel's code must round some value in [x - delta, x + delta]:
+        # its rounding interval (midpoints to its value neighbours) must meet it
+        rk = _RANK[codes[r, c]]
+        lo = np.where(rk > 0, (_DISTINCT[np.maximum(rk - 1, 0)] + _DISTINCT[rk]) / 2, -np.inf)
+        hi = np.where(rk < _DISTINCT.size - 1,
+                      (_DISTINCT[np.minimum(rk + 1, _DISTINCT.size - 1)] + _DISTINCT[rk]) / 2, np.inf)
+        assert np.all((x + delta >= lo) & (x - delta <= hi)), \
+            f"expert {e}: a differing code is not a rounding of any value within the accumulation error bound"
+    assert n_same >= 0.999 * n_all, f"only {n_same / n_all:.5f} of intermediate codes agree"
+
+
+@pytest.mark.parametrize("T,H,I,E,n_exp,topk,offset", [
+    (64, 512, 256, 4, 16, 4, 0),
+    (100, 1024, 384, 6, 12, 3, 6),
+    (1, 512, 128, 1, 1, 1, 0),
+    (300, 512, 512, 8, 8, 8, 0),      # every expert local: all T*k pairs computed
+])
+def test_ffn_small_parity(dg, T, H, I, E, n_exp, topk, offset):
+    g = _to_dev(synth.gen_ffn(T=T, H=H, I=I, num_local=E, num_experts=n_exp, topk=topk,
+                              seed=T + H + I, expert_offset=offset))
+    y, ws = _run(dg, g)
+    hit = _check_ffn(g, y, ws, f"ffn T{T} H{H} I{I}")
+    assert np.all(y[~hit] == 0), "tokens without a local expert must be exactly zero"
+    assert not np.any(y == 0xFFFF), "every row of y must be written"
+
+
+def test_ffn_weight_doubling_is_bit_exact(dg):
+    g = _to_dev(synth.gen_ffn(T=80, H=512, I=256, num_local=4, num_experts=8, topk=4, seed=5))
+    y1, _ = _run(dg, g)
+    y2, _ = _run(dg, g, topk_w=(g["topk_w"] * 2).contiguous())
+    v1 = torch.from_numpy(y1.view(np.int16)).view(torch.bfloat16).float()
+    v2 = torch.from_numpy(y2.view(np.int16)).view(torch.bfloat16).float()
+    assert torch.equal(v2, 2 * v1)
+
+
+def test_ffn_no_local_expert_gives_zero(dg):
+    g = _to_dev(synth.gen_ffn(T=50, H=512, I=128, num_local=4, num_experts=16, topk=2, seed=6))
+    y, _ = _run(dg, g, offset=1000)
+    assert np.all(y == 0)
+
+
+def test_ffn_repeat_calls_are_deterministic(dg):
+    g = _to_dev(synth.gen_ffn(T=120, H=1024, I=256, num_local=4, num_experts=8, topk=4, seed=7))
+    y1, _ = _run(dg, g)
+    y2, _ = _run(dg, g, ws_extra=4096)
+    assert np.array_equal(y1, y2)
+
+
+def test_ffn_full_size_sampled_tokens(dg):
+    """4096 tokens, hidden 7168, intermediate 2048, 32 local experts of 256, top-8;
+    generated on the device.  The oracle evaluates 24 tokens that hit local experts."""
+    g = synth.gen_ffn(T=4096, H=7168, I=2048, num_local=32, num_experts=256, topk=8, seed=synth.seed_for(4, 0),
+                      backend="torch", device="cuda")
+    y, ws = _run(dg, g)
+    idx = synth.to_numpy(g["topk_idx"])
+    hit = (idx < 32).any(1)
+    assert np.all(y[~hit] == 0)
+    assert not np.any(y == 0xFFFF)
+    rng = np.random.default_rng(4)
+    toks = np.sort(rng.choice(np.nonzero(hit)[0], 24, replace=False))
+    sub = {k: (g[k][toks] if k in ("x", "x_sf", "topk_idx", "topk_w") else g[k]) for k in g}
+    ref, info = _oracle(sub)
+    # the kernel's codes for the sampled tokens' pairs, in the oracle's pair order
+    full_info = {"pairs": []}
+    idx_s = synth.to_numpy(sub["topk_idx"])
+    for e in range(32):
+        tok, slot = np.nonzero(idx_s == e)
+        full_info["pairs"].append((toks[tok], slot))
+    kern = _kernel_intermediate(g, ws, full_info)
+    _check_codes(kern, info, sub)
+    ref_k, _ = _oracle(sub, codes_override=kern)
+    check_parity(y[toks], ref_k, ELEM_TOL, FRO_TOL, what="ffn full size (oracle on kernel codes)")
+    check_parity(y[toks], ref, np.inf, FRO_TOL, what="ffn full size (plain oracle, Frobenius)")
