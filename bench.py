@@ -1,29 +1,40 @@
 #!/usr/bin/env python3
-"""Benchmark of the fine-grained-scaled FP8 GEMM path on one MI355X.
+"""Benchmark of the fine-grained-scaled FP8 / FP8xFP4 GEMM path on one MI355X.
 
-Default workload (one "step"): the dense NT sweep -- M in {64, 4096} x the six
-(N, K) shapes (2112,7168) (24576,1536) (32768,512) (7168,16384) (4096,7168)
-(7168,2048), e4m3 A/B with 1x128 / 128x128 fp32 scales, C bf16 -- twelve
-dg_fp8_gemm_nt calls, each on its own resident inputs.  Value = algorithmic
-flops of the step / step time, in TFLOPS.
+Default workload (--config 1), one "step": the dense NT sweep -- M in {64, 4096}
+x the six (N, K) shapes (2112,7168) (24576,1536) (32768,512) (7168,16384)
+(4096,7168) (7168,2048); e4m3 A/B with 1x128 / 128x128 fp32 scales; C bf16 --
+twelve dg_fp8_gemm_nt calls, each on its own resident inputs.
+value = algorithmic flops of the step / step time (TFLOPS).
 
-Other workloads (--config): 0 the single M=128 N=2112 K=7168 GEMM, 2 the
-contiguous grouped GEMM (8 groups), 3 the masked grouped GEMM (32 groups),
-4 the FP8xFP4 expert FFN.
+Other workloads:
+  --config 0  dense M=128 N=2112 K=7168, C = 0
+  --config 2  M-grouped contiguous, 8 groups from 32768 routed rows, (N,K) in
+              {(4096,7168), (7168,2048)}
+  --config 3  M-grouped masked, 32 groups x 256 rows, masked_m ~ U{0..256},
+              same (N,K) pairs
+  --config 4  FP8xFP4 expert FFN, 4096 tokens, hidden 7168, intermediate 2048,
+              32 local experts of 256, top-8
 
-Caches: one step touches more than 1 GB of distinct inputs and outputs, so no
-shape's operands survive in the 4 MB L2s or the 256 MB Infinity Cache until
-that shape runs again; --flush additionally writes a 512 MB buffer before
-every step (outside the timed region is impossible per call, so it is only
-used with --per-call timing).
+Caches: one dense-sweep step touches more than 1 GB of distinct inputs and
+outputs, so no shape's operands survive in the 4 MB L2s or the 256 MB
+Infinity Cache until the shape runs again.  Configs 2-4 read 0.6-1 GB of
+weights per step, well beyond the Infinity Cache.
 
-Prints ONE JSON line (rank 0, N=1).
+Algorithmic work: flops = 2 * (valid rows) * N * K (the FFN counts linear1 and
+linear2 over routed pairs); bytes = every distinct operand and scale byte read
+once plus valid outputs written once (re-reads, padding rows and workspace
+traffic excluded).  Timing: HIP events on the launch stream around each call,
+inside one timed region of K steps bracketed by device synchronisation.
+
+Prints ONE JSON line.
 """
 
 import argparse
 import hashlib
 import json
 import os
+import platform
 import statistics
 import sys
 import time
@@ -35,6 +46,8 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense FP4/FP6 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
+METRIC = "block-scaled FP8 GEMM TFLOPS + % MFMA peak (dense, grouped, masked)"
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -43,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--shape", type=str, default=None,
                     help="M,N,K: time only this dense shape (C bf16), for profiling")
     ap.add_argument("--copy-calib", action="store_true",
@@ -60,97 +73,218 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def nb(n):
+    return (n + 127) // 128
+
+
 # ----------------------------------------------------------------------------
-# workloads
+# workloads: each item = one library call with its algorithmic flops / bytes
 # ----------------------------------------------------------------------------
 
-def dense_shapes(config):
-    import synth
-    if config == 0:
-        return [(128, 2112, 7168, False, synth.seed_for(0, 0))]
-    out = []
-    for mi, M in enumerate(synth.DENSE_M):
-        for j, (N, K) in enumerate(synth.DENSE_NK):
-            out.append((M, N, K, True, synth.seed_for(1, mi * 6 + j)))
-    return out
-
-
-def build_dense(config, only=None):
+def items_dense(config, only=None):
     import torch
     import synth
-    items = []
-    shapes = dense_shapes(config)
+    import fp4_gemm_dense_amd as dg
     if only is not None:
         M, N, K = (int(v) for v in only.split(","))
         shapes = [(M, N, K, True, 12345)]
+    elif config == 0:
+        shapes = [(128, 2112, 7168, False, synth.seed_for(0, 0))]
+    else:
+        shapes = [(M, N, K, True, synth.seed_for(1, mi * 6 + j))
+                  for mi, M in enumerate(synth.DENSE_M) for j, (N, K) in enumerate(synth.DENSE_NK)]
+    items = []
     for (M, N, K, with_c, seed) in shapes:
         g = synth.gen_dense(M, N, K, seed, with_c=with_c, backend="torch", device="cuda")
-        g["d"] = torch.empty(M, N, dtype=torch.int16, device="cuda")
-        flops = 2.0 * M * N * K
-        nbytes = M * K + N * K + 4 * (K // 128) * M + 4 * ((N + 127) // 128) * (K // 128) + 2 * M * N * (2 if with_c else 1)
-        items.append(dict(g=g, flops=flops, bytes=nbytes, label=f"M{M}_N{N}_K{K}", shape=(M, N, K)))
+        d = torch.empty(M, N, dtype=torch.int16, device="cuda")
+        nbytes = M * K + N * K + 4 * (K // 128) * M + 4 * nb(N) * (K // 128) + 2 * M * N * (2 if with_c else 1)
+
+        def run(g=g, d=d):
+            dg.dg_fp8_gemm_nt(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
+        items.append(dict(run=run, g=g, flops=2.0 * M * N * K, bytes=nbytes, label=f"M{M}_N{N}_K{K}",
+                          shape=(M, N, K), plan=dg.dg_query_plan(M, N, K)))
     return items
 
 
-def run_dense_item(dg, it):
-    g = it["g"]
-    dg.dg_fp8_gemm_nt(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], g["d"])
+def items_contiguous():
+    import torch
+    import synth
+    import fp4_gemm_dense_amd as dg
+    items = []
+    for j, (N, K) in enumerate(synth.GROUPED_NK):
+        g = synth.gen_contiguous(8, 32768, N, K, synth.seed_for(2, j), backend="torch", device="cuda")
+        M = g["M"]
+        d = torch.empty(M, N, dtype=torch.int16, device="cuda")
+        valid = sum(g["counts"])
+        groups_hit = sum(1 for c in g["counts"] if c > 0)
+        nbytes = valid * K + groups_hit * (N * K + 4 * nb(N) * (K // 128)) + 4 * (K // 128) * valid + 4 * M + 2 * valid * N
+
+        def run(g=g, d=d):
+            dg.dg_m_grouped_fp8_gemm_nt_contiguous(g["a"], g["sfa"], g["b"], g["sfb"], g["m_indices"], d)
+        items.append(dict(run=run, g=g, flops=2.0 * valid * N * K, bytes=nbytes, label=f"G8_contig_N{N}_K{K}",
+                          shape=(M, N, K)))
+    return items
+
+
+def items_masked():
+    import torch
+    import synth
+    import fp4_gemm_dense_amd as dg
+    items = []
+    for j, (N, K) in enumerate(synth.GROUPED_NK):
+        g = synth.gen_masked(32, 256, N, K, synth.seed_for(3, j), backend="torch", device="cuda")
+        mm = [int(v) for v in g["masked_m"].cpu()]
+        d = torch.empty(32, 256, N, dtype=torch.int16, device="cuda")
+        valid = sum(mm)
+        groups_hit = sum(1 for v in mm if v > 0)
+        nbytes = valid * K + groups_hit * (N * K + 4 * nb(N) * (K // 128)) + 4 * (K // 128) * valid + 4 * 32 + 2 * valid * N
+
+        def run(g=g, d=d):
+            dg.dg_m_grouped_fp8_gemm_nt_masked(g["a"], g["sfa"], g["b"], g["sfb"], g["masked_m"], d, 128)
+        items.append(dict(run=run, g=g, flops=2.0 * valid * N * K, bytes=nbytes, label=f"G32_masked_N{N}_K{K}",
+                          shape=(256, N, K), masked_m=mm))
+    return items
+
+
+def items_ffn():
+    import torch
+    import synth
+    import fp4_gemm_dense_amd as dg
+    T, H, I, E = 4096, 7168, 2048, 32
+    g = synth.gen_ffn(T=T, H=H, I=I, num_local=E, num_experts=256, topk=8, seed=synth.seed_for(4, 0),
+                      backend="torch", device="cuda")
+    idx = g["topk_idx"]
+    local = (idx >= 0) & (idx < E)
+    P = int(local.sum())
+    hit = torch.bincount(idx[local].long(), minlength=E)
+    experts_hit = int((hit > 0).sum())
+    k = idx.shape[1]
+    ws = torch.empty(dg.dg_fp8_fp4_expert_ffn_workspace_bytes(T, k, E, H, I), dtype=torch.uint8, device="cuda")
+    y = torch.empty(T, H, dtype=torch.int16, device="cuda")
+    w_bytes = experts_hit * (2 * I * H // 2 + 2 * I * (H // 32) + H * I // 2 + H * (I // 32))
+    nbytes = w_bytes + T * H + T * (H // 128) + T * k * 8 + T * H * 2
+
+    def run():
+        dg.dg_fp8_fp4_expert_ffn(g["x"], g["x_sf"], g["topk_idx"], g["topk_w"], g["w1"], g["w1_sf"], g["w2"],
+                                 g["w2_sf"], y, 0, ws)
+    return [dict(run=run, g=g, flops=2.0 * P * (2 * I * H + H * I), bytes=nbytes,
+                 label=f"ffn_T{T}_H{H}_I{I}_E{E}_pairs{P}", shape=(T, H, I), pairs=P)]
 
 
 # ----------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the same workload)
 # ----------------------------------------------------------------------------
 
-def cpu_baseline_dense(items, budget_s):
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        return 1
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def cpu_baseline(config, items, budget_s):
+    """Time the oracle, as it stands, on a bounded sample of the same inputs."""
     import numpy as np
     import synth
     from oracle import ref as R
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
-    rows_per_shape = 64
-    host = []
-    for it in items:
-        g = it["g"]
-        M, N, K = it["shape"]
-        r = min(M, rows_per_shape)
-        host.append(dict(a=synth.to_numpy(g["a"][:r]), sfa=synth.to_numpy(g["sfa"][:, :r]),
-                         b=synth.to_numpy(g["b"]), sfb=synth.to_numpy(g["sfb"]),
-                         c=None if g["c"] is None else synth.to_numpy(g["c"][:r]),
-                         flops=2.0 * r * N * K))
+    t_total = 0.0
     flops = 0.0
-    t0 = time.perf_counter()
-    done = 0
-    for h in host:
-        R.fp8_gemm_nt(h["a"], h["sfa"], h["b"], h["sfb"], h["c"])
-        flops += h["flops"]
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
+    desc = []
+    t_start = time.perf_counter()
+    for it in items:
+        if time.perf_counter() - t_start > budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
-            "sample": f"numpy fp64 oracle (dequantise + matmul) on the first {rows_per_shape} rows of "
-                      f"{done} of the {len(items)} sweep shapes, full N and K; {dt:.1f} s",
-            "seconds": dt}
+        g = it["g"]
+        if config in (0, 1):
+            M, N, K = it["shape"]
+            r = min(M, 64)
+            a, sfa, b, sfb = (synth.to_numpy(g["a"][:r]), synth.to_numpy(g["sfa"][:, :r]),
+                              synth.to_numpy(g["b"]), synth.to_numpy(g["sfb"]))
+            c = None if g["c"] is None else synth.to_numpy(g["c"][:r])
+            t0 = time.perf_counter()
+            R.fp8_gemm_nt(a, sfa, b, sfb, c)
+            t_total += time.perf_counter() - t0
+            flops += 2.0 * r * N * K
+            desc.append(f"{r} rows of {it['label']}")
+        elif config in (2, 3):
+            M, N, K = it["shape"]
+            G = 8 if config == 2 else 32
+            for grp in range(G):
+                if time.perf_counter() - t_start > budget_s:
+                    break
+                if config == 2:
+                    rows = np.nonzero(synth.to_numpy(g["m_indices"]) == grp)[0][:16]
+                    a, sfa = synth.to_numpy(g["a"][rows]), synth.to_numpy(g["sfa"][:, rows])
+                else:
+                    r = min(16, it["masked_m"][grp])
+                    rows = np.arange(r)
+                    a, sfa = synth.to_numpy(g["a"][grp, :r]), synth.to_numpy(g["sfa"][grp][:, :r])
+                if len(rows) == 0:
+                    continue
+                b, sfb = synth.to_numpy(g["b"][grp]), synth.to_numpy(g["sfb"][grp])
+                t0 = time.perf_counter()
+                R.fp8_gemm_nt(a, sfa, b, sfb)
+                t_total += time.perf_counter() - t0
+                flops += 2.0 * len(rows) * N * K
+            desc.append(f"up to 16 valid rows per group of {it['label']}")
+        else:
+            T, H, I = it["shape"]
+            idx = synth.to_numpy(g["topk_idx"])
+            toks = np.nonzero((idx < 32).any(1))[0][:12]
+            sub = {k: synth.to_numpy(g[k][toks]) for k in ("x", "x_sf", "topk_idx", "topk_w")}
+            w = {k: synth.to_numpy(g[k]) for k in ("w1", "w1_sf", "w2", "w2_sf")}
+            pairs = int((sub["topk_idx"] < 32).sum())
+            t0 = time.perf_counter()
+            R.expert_ffn(sub["x"], sub["x_sf"], sub["topk_idx"], sub["topk_w"], w["w1"], w["w1_sf"], w["w2"],
+                         w["w2_sf"], 0, 32)
+            t_total += time.perf_counter() - t0
+            flops += 2.0 * pairs * (2 * I * H + H * I)
+            desc.append(f"{len(toks)} tokens ({pairs} local pairs) of {it['label']}")
+    return {"value": flops / max(t_total, 1e-9) / 1e12, "unit": "TFLOPS", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": "numpy fp64 oracle (dequantise + matmul) on " + "; ".join(desc) +
+                      f"; {t_total:.1f} s of oracle time; input generation and host copies excluded",
+            "cpu": cpu_model(), "seconds": round(t_total, 2)}
 
 
 # ----------------------------------------------------------------------------
 # main
 # ----------------------------------------------------------------------------
 
+WORKLOADS = {
+    0: "dense NT M128 N2112 K7168, e4m3 1x128 / 128x128 fp32 scales, C=0",
+    1: "dense NT sweep M{64,4096} x (N,K){(2112,7168),(24576,1536),(32768,512),(7168,16384),(4096,7168),"
+       "(7168,2048)}, e4m3 1x128 / 128x128 fp32 scales, C bf16",
+    2: "M-grouped contiguous, 8 groups from 32768 routed rows (multinomial, padded to 128), "
+       "(N,K){(4096,7168),(7168,2048)}, e4m3 1x128 / 128x128 fp32 scales",
+    3: "M-grouped masked, 32 groups x 256 rows, masked_m ~ U{0..256}, (N,K){(4096,7168),(7168,2048)}, "
+       "e4m3 1x128 / 128x128 fp32 scales",
+    4: "FP8xFP4 expert FFN, 4096 tokens, hidden 7168, intermediate 2048, 32 local experts of 256, top-8, "
+       "e4m3 activations (UE8M0/128), E2M1 weights (UE8M0/32)",
+}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this build runs on one GPU only (no multi-GPU path); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
     import fp4_gemm_dense_amd as dg
     dg.load_library()
-    torch.cuda.init()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -161,22 +295,24 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calib_bytes": n}))
+        print(json.dumps({"copy_calib_bytes": n, "dispatches": 3}))
         return
 
-    if args.config not in (0, 1):
-        raise SystemExit("configs 2-4 are benchmarked by their own scripts in this version")
-
-    items = build_dense(args.config, args.shape)
+    cfg = args.config
+    if cfg in (0, 1):
+        items = items_dense(cfg, args.shape)
+    elif cfg == 2:
+        items = items_contiguous()
+    elif cfg == 3:
+        items = items_masked()
+    else:
+        items = items_ffn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step():
-        for it in items:
-            run_dense_item(dg, it)
-
     for _ in range(args.warmup):
-        step()
+        for it in items:
+            it["run"]()
     torch.cuda.synchronize()
 
     n = len(items)
@@ -189,56 +325,71 @@ def main():
     for s in range(args.steps):
         ev[s][0].record(stream)
         for i, it in enumerate(items):
-            run_dense_item(dg, it)
+            it["run"]()
             ev[s][i + 1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
     per = []
     for i, it in enumerate(items):
         durs = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+        it["mean_ms"] = statistics.mean(durs)
         med = statistics.median(durs)
-        per.append(dict(shape=it["label"], ms=med, tflops=it["flops"] / med / 1e9,
-                        gbs=it["bytes"] / med / 1e6,
-                        roofline_frac=max(it["flops"] / 1e12 / PEAK_FP8_TFLOPS, it["bytes"] / 1e9 / PEAK_HBM_GBS)
+        peak = PEAK_FP8_TFLOPS
+        per.append(dict(shape=it["label"], ms=med, tflops=it["flops"] / med / 1e9, gbs=it["bytes"] / med / 1e6,
+                        mfma_frac=it["flops"] / med / 1e9 / peak, hbm_frac=it["bytes"] / med / 1e6 / PEAK_HBM_GBS,
+                        roofline_frac=max(it["flops"] / 1e12 / peak, it["bytes"] / 1e9 / PEAK_HBM_GBS)
                         / (med / 1e3)))
     step_flops = sum(it["flops"] for it in items)
     value = step_flops / (ms_per_step / 1e3) / 1e12
 
-    # dominant kernel: the launches that use the largest tile (the M=4096 shapes)
-    plans = [dg.dg_query_plan(*it["shape"]) for it in items]
-    dom_kid = max(set(p["kernel_id"] for p in plans),
-                  key=lambda k: sum(per[i]["ms"] for i, p in enumerate(plans) if p["kernel_id"] == k))
-    dom = [i for i, p in enumerate(plans) if p["kernel_id"] == dom_kid]
-    dom_flops = sum(items[i]["flops"] for i in dom) / len(dom)
-    dom_ms = sum(statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) for i in dom) / len(dom)
-    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    # roofline of the dominant kernel
+    if cfg in (0, 1):
+        # launches of the largest-tile dense kernel (the one most of the step's time is in)
+        kid = max(set(it["plan"]["kernel_id"] for it in items),
+                  key=lambda k: sum(it["mean_ms"] for it in items if it["plan"]["kernel_id"] == k))
+        dom = [it for it in items if it["plan"]["kernel_id"] == kid]
+        bm, bn = dom[0]["plan"]["block_m"], dom[0]["plan"]["block_n"]
+        kname = f"fp8_gemm_kernel {bm}x{bn} tile, dense (kernel id {kid})"
+        bound = "mfma"
+    elif cfg == 2:
+        dom, kname, bound = items, "fp8_gemm_kernel, contiguous grouped", "mfma"
+    elif cfg == 3:
+        dom, kname, bound = items, "fp8_gemm_kernel, masked grouped", "hbm"
+    else:
+        dom, kname, bound = items, "expert FFN call (route + linear1 + linear2 + combine)", "hbm"
+    avg_ms = sum(it["mean_ms"] for it in dom) / len(dom)
+    if bound == "mfma":
+        per_launch = sum(it["flops"] for it in dom) / len(dom)
+        achieved = per_launch / (avg_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP8_TFLOPS, 4)}
+    else:
+        per_launch = sum(it["bytes"] for it in dom) / len(dom)
+        achieved = per_launch / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         try:
             tj = json.load(open(tfile))
-            if tj.get("kernel_source_hash") == kernel_source_hash() and tj.get("config") == args.config:
-                traffic = tj.get("bytes_per_launch")
-        except Exception:
+            entry = tj.get(str(cfg))
+            if entry and entry.get("kernel_source_hash") == kernel_source_hash():
+                traffic = entry.get("bytes_per_launch")
+        except (ValueError, OSError):
             traffic = None
-    bm, bn = plans[dom[0]]["block_m"], plans[dom[0]]["block_n"]
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
-                "kernel": f"fp8_gemm_kernel tile {bm}x{bn} (dense)", "launches_per_step": len(dom)}
+    roof.update({"traffic": traffic, "kernel": kname, "launches_per_step": len(dom),
+                 "avg_launch_ms": round(avg_ms, 5), "algorithmic_per_launch": per_launch})
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_dense(items, args.cpu_budget_s)
+        cpu = cpu_baseline(cfg, items, args.cpu_budget_s)
 
-    workload = ("dense NT sweep M{64,4096} x (N,K){(2112,7168),(24576,1536),(32768,512),(7168,16384),"
-                "(4096,7168),(7168,2048)}, e4m3 1x128/128x128 fp32 scales, C bf16"
-                if args.config == 1 else "dense NT M128 N2112 K7168, e4m3 1x128/128x128 fp32 scales, C=0")
     out = {
-        "metric": "block-scaled FP8 GEMM TFLOPS + % MFMA peak (dense, grouped, masked)",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -248,14 +399,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 x fp8e4m3 -> f32 acc, bf16 out",
-        "data": "synthetic (seeded N(0,1), quantised per 1x128 / 128x128)",
-        "config": {"workload": workload, "gemms_per_step": len(items), "parallelism": "none (1 GPU)"},
-        "roofline": roofline,
+        "dtype": "fp8e4m3 x fp4e2m1 -> f32" if cfg == 4 else "fp8e4m3 x fp8e4m3 -> f32",
+        "data": "synthetic (seeded N(0,1), quantised as the workload states)",
+        "config": {"workload": WORKLOADS[cfg] if args.shape is None else f"dense NT {args.shape}",
+                   "calls_per_step": n, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
         "cpu_baseline": cpu,
         "mfma_peak_frac": round(value / PEAK_FP8_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
-        "per_shape": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()} for p in per],
+        "per_call": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()} for p in per],
     }
     print(json.dumps(out))
 
