@@ -65,12 +65,29 @@ static bool log_enabled() {
 
 static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The kernels address A, B, C and D (one group's share of them) through buffer
+// resources with 32-bit offsets and park masked-off stores at offset 2^31, so
+// each of these operands must span at most 2 GiB.
+static bool fits_buffer(long long rows, long long cols, long long elem_bytes) {
+  return rows * cols * elem_bytes <= (1LL << 31);
+}
+static bool operands_fit(int m, int n, int k) {
+  return fits_buffer(m, k, 1) && fits_buffer(n, k, 1) && fits_buffer(m, n, 2);
+}
+
 static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream, const char* name) {
   DeviceInfo di = current_device_info();
   if (!di.ok) return DG_ERR_NO_DEVICE;
   int cus = effective_cus(di);
   GemmPlan plan = plan_fp8_gemm(p.m, p.n, p.k, p.num_groups, mode, cus, expected_m);
   if (plan.kernel_id < 0) return DG_ERR_UNSUPPORTED;
+  // DG_FORCE_KERNEL=<id>: override the heuristic's tile choice (for tuning)
+  if (const char* fk = std::getenv("DG_FORCE_KERNEL")) {
+    int id = std::atoi(fk);
+    if (id >= 0 && id < num_tile_configs() &&
+        !(mode == MODE_CONTIG && (128 % tile_config(id).block_m) != 0))
+      plan = plan_with_kernel(p.m, p.n, p.num_groups, mode, cus, id);
+  }
   p.tiles_m = plan.tiles_m;
   p.tiles_n = plan.tiles_n;
   p.total_tiles = plan.num_tiles;
@@ -97,7 +114,7 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sfa, 4) || !aligned(sfb, 4) ||
         (c && !aligned(c, 2)))
       return DG_ERR_INVALID_ARG;
-    if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
+    if (k % 128 != 0 || n % 16 != 0 || !operands_fit(m, n, k)) return DG_ERR_UNSUPPORTED;
     Fp8GemmParams p{};
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = c; p.d = d;
     p.m = m; p.n = n; p.k = k; p.num_groups = 1;
@@ -116,7 +133,7 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sfa, 4) || !aligned(sfb, 4) ||
         !aligned(m_indices, 4))
       return DG_ERR_INVALID_ARG;
-    if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
+    if (k % 128 != 0 || n % 16 != 0 || !operands_fit(m, n, k)) return DG_ERR_UNSUPPORTED;
     Fp8GemmParams p{};
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
     p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
@@ -136,7 +153,7 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sfa, 4) || !aligned(sfb, 4) ||
         !aligned(masked_m, 4))
       return DG_ERR_INVALID_ARG;
-    if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
+    if (k % 128 != 0 || n % 16 != 0 || !operands_fit(max_m, n, k)) return DG_ERR_UNSUPPORTED;
     // the whole tile grid must be addressable with 32-bit tile ids
     long long tiles = (long long)num_groups * ((max_m + 15) / 16) * ((n + 15) / 16);
     if (tiles > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;

@@ -7,6 +7,7 @@
 
 namespace dg {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -56,6 +57,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Waits until every LDS access of this wave has completed (lgkmcnt 0; vmcnt
+// and expcnt left at max).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Workgroup barrier without the memory fence __syncthreads() implies: the
 // fence would wait for every outstanding load, including the LDS-DMA loads of
 // later pipeline stages.  The empty asm keeps the compiler from moving LDS
@@ -66,6 +71,39 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource for raw (stride 0) buffer accesses: base address, size in
+// bytes (accesses at or beyond it read 0), and the gfx9 format word.
+__device__ __forceinline__ v4i make_buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// LLVM's raw buffer load into LDS: lane l's `size` bytes from
+// base + voffset(l) + soffset + offset land at lds + l * size (lds wave-uniform).
+extern "C" __device__ void dg_raw_buffer_load_lds(v4i rsrc, __attribute__((address_space(3))) uint32_t* lds,
+                                                  int size, int voffset, int soffset, int offset,
+                                                  int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+__device__ __forceinline__ void buf16_to_lds(const v4i& rsrc, uint32_t voff, uint32_t soff, void* lds_base) {
+  dg_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)lds_base, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void buf4_to_lds(const v4i& rsrc, uint32_t voff, uint32_t soff, void* lds_base) {
+  dg_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)lds_base, 4, (int)voff, (int)soff, 0, 0);
+}
+
+// LLVM's raw buffer store of 8 bytes per lane at base + voffset(l) + soffset.
+// A lane whose offset lies at or beyond the resource's size stores nothing, so
+// a masked-off lane passes an out-of-range offset instead of branching, and
+// every lane of the wave always issues exactly one store instruction.
+extern "C" __device__ void dg_raw_buffer_store_v2i32(v2i data, v4i rsrc, int voffset, int soffset,
+                                                     int aux) __asm("llvm.amdgcn.raw.buffer.store.v2i32");
+constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // valid with resources below 2 GiB
 
 // Direct global -> LDS copies: lane l's 16 (or 4) bytes land at
 // lds_base + 16*l (or 4*l).  lds_base must be the same for the whole wave.

@@ -55,6 +55,7 @@ struct GemmPlan {
   int num_workgroups;
 };
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m);
+GemmPlan plan_with_kernel(int m, int n, int num_groups, int mode, int num_cus, int kernel_id);
 
 // Launches the kernel chosen by plan on stream; returns a hipError_t.
 hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mode, hipStream_t stream);

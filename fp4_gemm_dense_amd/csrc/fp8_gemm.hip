@@ -11,13 +11,20 @@
 // scheduler for all of them).
 //
 // gfx950 design (not the pages' Hopper design):
-//   * 256 threads = 4 wave64s laid out WM x WN; each wave owns an
-//     (MT*16) x (NT*16) sub-tile of 16x16 accumulator blocks.
-//   * Per 128-wide K block: A and B tiles (BM x 128 and BN x 128 bytes) are
-//     staged through a double-buffered, XOR-swizzled LDS ring with 16-byte
-//     coalesced global loads prefetched one block ahead into registers.
+//   * WM x WN wave64s per workgroup; each wave owns an (MT*16) x (NT*16)
+//     sub-tile of 16x16 accumulator blocks, computed transposed (B_nt . A_mt^T)
+//     so that a lane's four results lie in one row of D and share one A scale.
+//   * Per 128-wide K block, A, B and the A scales are copied by buffer loads
+//     straight into a STAGES-deep LDS ring (no registers in between), XOR-
+//     swizzled so that fragment reads are free of bank conflicts.  Waits count
+//     outstanding memory operations (s_waitcnt vmcnt) instead of draining them.
 //   * Each 16x16 block does ONE v_mfma_f32_16x16x128_f8f6f4 per K block into a
-//     fresh fp32 partial, promoted by one FMA per element with sa[row]*sb.
+//     fresh fp32 partial; the partial is promoted by one FMA per element with
+//     sa[row]*sb a few matrix instructions later, so the vector ALU never waits
+//     on the matrix core.
+//   * Epilogue: C is copied into the ring slots the last two K blocks leave
+//     free; the next tile's first loads are issued before this tile's stores,
+//     which then drain while the next tile computes.
 //   * Persistent workgroups walk a group-M raster of tiles; block ids are
 //     remapped so that each XCD (workgroups are dealt round-robin to the 8
 //     XCDs) works on a contiguous stretch of the raster and shares its L2.
@@ -42,9 +49,25 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   constexpr int SPW = BM / NW;
   static_assert(SPW <= 64, "scale copy must fit one instruction per wave");
   constexpr int LPS = RA + RB + 1;            // DMA instructions per wave per stage
-  // the 16 columns of every accumulator block lie in one 128-wide B-scale block;
-  // when all of a wave's columns do, one sb serves the whole wave
-  constexpr bool ONE_SB = (128 % (NT * 16) == 0) && (BN % 128 == 0 || 128 % BN == 0);
+  // all of a wave's columns lie in one 128-wide B-scale block, so one sb per
+  // K block serves the whole wave
+  static_assert(128 % (NT * 16) == 0 && (BN % 128 == 0 || 128 % BN == 0), "one B scale per wave");
+  static_assert(MT == 4, "a lane reads its four row scales with one 16-byte LDS load");
+  constexpr int NBLK = MT * NT;   // 16x16 accumulator blocks per wave
+  constexpr int LAG = NT;         // matrix instructions between a partial's issue and its promotion
+  // Epilogue traffic.  The C tile (BM x BN bf16) is copied into two ring slots
+  // that the last two K blocks leave free, in halves of BM/2 rows; each wave
+  // copies CPW 1-KB pieces of a half.  A C row holds CPR 16-byte chunks, chunk c
+  // of row r sits at position c ^ (r % 16).  Every wave then issues exactly NST
+  // 8-byte stores of D.
+  constexpr int CPR = BN / 8;
+  constexpr int C_HALF = BM / 2 * BN * 2;
+  static_assert(CPR >= 16 && 1024 % (BN * 2) == 0, "C rows must be 256 or 512 bytes");
+  static_assert(C_HALF % (NW * 1024) == 0 && C_HALF <= STAGE, "C halves must fit a slot");
+  static_assert((BM / 2) % 16 == 0, "a 16-row block must not straddle the C halves");
+  constexpr int CPW = C_HALF / (NW * 1024);
+  constexpr int NST = MT * NT;
+  static_assert((STAGES - 2) * LPS + NST + CPW < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   typedef const __attribute__((address_space(4))) float cfloat;
@@ -68,10 +91,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   const uint32_t a_hi = (wave_m * MT * 16 + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
   const uint32_t b_lo = A_BYTES + (wave_n * NT * 16 + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
   const uint32_t b_hi = A_BYTES + (wave_n * NT * 16 + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
-  const uint32_t sa_rd = A_BYTES + B_BYTES + (wave_m * MT * 16 + 4 * lgrp) * 4;
-  // Per-lane DMA row inside an 8-row region; the swizzled chunk depends on the
-  // tile row's bit 3 as well, i.e. on the region's parity.
-  const int dma_row = lane >> 3;
+  const uint32_t sa_rd = A_BYTES + B_BYTES + (wave_m * MT * 16 + lrow * MT) * 4;
+  const int dma_row = lane >> 3;              // DMA row inside an 8-row region
+  const uint32_t a_dst = wave * RA * 1024;
+  const uint32_t b_dst = A_BYTES + wave * RB * 1024;
+  const uint32_t sa_dst = A_BYTES + B_BYTES + wave * SPW * 4;
 
   // XCD-aware remap of the persistent block id: workgroups are dealt to the
   // 8 XCDs round-robin, so give XCD x a contiguous stretch of the raster.
@@ -79,8 +103,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   int vb = blockIdx.x;
   if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
-  for (int t = vb; t < p.total_tiles; t += G) {
-    // ---------------- tile -> (group, tm, tn) ----------------
+  // ---------------- tile decode: tile id -> (group, m0, n0, valid rows) ----------------
+  struct Tile {
+    int g, m0, n0, rows_valid;
+  };
+  auto decode = [&](int t, Tile& tile) -> bool {
     int g = 0, tl = t;
     if (MODE == MODE_MASKED) {
       const int per = p.tiles_m * p.tiles_n;
@@ -92,113 +119,178 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     const int first_m = gi * p.group_m;
     const int gm = min(p.tiles_m - first_m, p.group_m);
     const int r = tl - gi * per_group;
-    const int tm = first_m + r % gm;
-    const int tn = r / gm;
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-
-    int rows_valid = M;      // rows that may be stored
+    tile.m0 = (first_m + r % gm) * BM;
+    tile.n0 = (r / gm) * BN;
+    tile.rows_valid = M;
     if (MODE == MODE_MASKED) {
-      int mm = p.masked_m[g];
-      rows_valid = mm < 0 ? 0 : (mm > M ? M : mm);
-      if (m0 >= rows_valid) continue;           // empty tile: the whole workgroup skips it
+      const int mm = p.masked_m[g];
+      tile.rows_valid = mm < 0 ? 0 : (mm > M ? M : mm);
+      if (tile.m0 >= tile.rows_valid) return false;  // empty tile
     }
     if (MODE == MODE_CONTIG) {
-      g = p.m_indices[m0];
-      if (g < 0 || g >= p.num_groups) continue; // padding block
+      g = p.m_indices[tile.m0];
+      if (g < 0 || g >= p.num_groups) return false;  // padding block
     }
+    tile.g = g;
+    return true;
+  };
+  // first tile at or after t with work (all lanes agree: every input is uniform)
+  auto next_tile = [&](int& t, Tile& tile) -> bool {
+    for (; t < p.total_tiles; t += G)
+      if (decode(t, tile)) return true;
+    return false;
+  };
 
+  // ---------------- per-tile DMA state ----------------
+  // Buffer resources (SGPRs) for A, B and the A scales of the tile's group; each
+  // lane keeps one 32-bit offset per DMA region and the K block advances the
+  // scalar offset, so the loop needs no 64-bit address arithmetic.
+  v4i rsA, rsB, rsSA;
+  cfloat* const SBc = (cfloat*)(uintptr_t)p.sfb;   // constant address space: scalar loads
+  uint32_t a_off[RA], b_off[RB], sa_off = 0;
+  int sb_idx = 0;
+  auto setup = [&](const Tile& tile) {
     const uint8_t* A = p.a;
     const float* SA = p.sfa;
     const uint8_t* B = p.b;
     const float* SB = p.sfb;
     if (MODE == MODE_MASKED) {
-      A += (size_t)g * M * K;
-      SA += (size_t)g * KB * M;
+      A += (size_t)tile.g * M * K;
+      SA += (size_t)tile.g * KB * M;
     }
     if (MODE != MODE_DENSE) {
-      B += (size_t)g * N * K;
-      SB += (size_t)g * NB * KB;
+      B += (size_t)tile.g * N * K;
+      SB += (size_t)tile.g * NB * KB;
     }
-
-    // ---------------- DMA sources of this wave ----------------
-    // A region (wave*RA + j) covers tile rows 8*(wave*RA+j) .. +7; lane l fills
-    // LDS bytes [16l, 16l+16) of it: row + l/8, position l%8, which holds
-    // logical chunk (l%8) ^ swz(row).  Offsets are 32-bit, relative to A / B.
-    uint32_t a_off[RA], b_off[RB];
+    rsA = make_buffer_rsrc(A, (uint32_t)M * (uint32_t)K);
+    rsB = make_buffer_rsrc(B, (uint32_t)N * (uint32_t)K);
+    rsSA = make_buffer_rsrc(SA, (uint32_t)KB * (uint32_t)M * 4u);
+    (void)SB;
+    // Region r covers tile rows 8r..8r+7; lane l fills LDS bytes [16l, 16l+16)
+    // of it: row 8r + l/8, position l%8, which holds chunk (l%8) ^ swz(row).
 #pragma unroll
     for (int j = 0; j < RA; ++j) {
       const int row = (wave * RA + j) * 8 + dma_row;
-      a_off[j] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4);
+      a_off[j] = (uint32_t)min(tile.m0 + row, M - 1) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4);
     }
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const int row = (wave * RB + j) * 8 + dma_row;
-      b_off[j] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4);
+      b_off[j] = (uint32_t)min(tile.n0 + row, N - 1) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4);
     }
-    const uint32_t sa_off = (uint32_t)min(m0 + wave * SPW + (lane < SPW ? lane : 0), M - 1) * 4;
-    const uint32_t a_dst = wave * RA * 1024;
-    const uint32_t b_dst = A_BYTES + wave * RB * 1024;
-    const uint32_t sa_dst = A_BYTES + B_BYTES + wave * SPW * 4;
-
-    auto issue = [&](int kb, uint32_t slot_off) {
-      const uint8_t* ak = A + (size_t)kb * 128;
-      const uint8_t* bk = B + (size_t)kb * 128;
-      const uint8_t* sk = reinterpret_cast<const uint8_t*>(SA + (size_t)kb * M);
+    {
+      // LDS position q of a tile's A scales holds row g*MT*16 + mt*16 + r for
+      // q = g*MT*16 + r*MT + mt, so the MT scales a lane needs are adjacent
+      const int q = wave * SPW + (lane < SPW ? lane : 0);
+      const int g = q / (MT * 16), rem = q % (MT * 16);
+      const int row = g * (MT * 16) + (rem % MT) * 16 + rem / MT;
+      sa_off = (uint32_t)min(tile.m0 + row, M - 1) * 4;
+    }
+    // B-scale element offsets from the kernel argument p.sfb, kept in SGPRs so the
+    // per-K-block reads are scalar loads (which vmcnt does not count)
+    const int sb_group = MODE != MODE_DENSE ? tile.g * NB * KB : 0;
+    sb_idx = __builtin_amdgcn_readfirstlane(sb_group + (min(tile.n0 + wave_n * NT * 16, N - 1) >> 7) * KB);
+  };
+  auto issue = [&](int kb, uint32_t slot_off) {
+    const uint32_t kofs = (uint32_t)kb * 128u;
+    const uint32_t sofs = (uint32_t)kb * (uint32_t)M * 4u;
 #pragma unroll
-      for (int j = 0; j < RA; ++j) dma16_to_lds(ak + a_off[j], smem + slot_off + a_dst + j * 1024);
+    for (int j = 0; j < RA; ++j) buf16_to_lds(rsA, a_off[j], kofs, smem + slot_off + a_dst + j * 1024);
 #pragma unroll
-      for (int j = 0; j < RB; ++j) dma16_to_lds(bk + b_off[j], smem + slot_off + b_dst + j * 1024);
-      if (SPW == 64 || lane < SPW) dma4_to_lds(sk + sa_off, smem + slot_off + sa_dst);
-    };
-
-    // B-scale indices are wave-uniform; reading them through the constant
-    // address space makes the per-K-block reads scalar loads (not counted by vmcnt)
-    cfloat* SBc = (cfloat*)(uintptr_t)(SB);
-    int sb_idx[NT];
+    for (int j = 0; j < RB; ++j) buf16_to_lds(rsB, b_off[j], kofs, smem + slot_off + b_dst + j * 1024);
+    if (SPW == 64 || lane < SPW) buf4_to_lds(rsSA, sa_off, sofs, smem + slot_off + sa_dst);
+  };
+  // DMA of half h of the C tile into the slot at slot_off (dense form only).
+  const bool has_c = MODE == MODE_DENSE && p.c != nullptr;
+  const v4i rsC = make_buffer_rsrc(p.c, (uint32_t)M * (uint32_t)N * 2u);
+  auto issue_c = [&](const Tile& tile, int h, uint32_t slot_off) {
+    constexpr int RPI = 1024 / (BN * 2);             // C rows per 1-KB piece
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      sb_idx[nt] = __builtin_amdgcn_readfirstlane((min(n0 + wave_n * NT * 16 + nt * 16, N - 1) >> 7) * KB);
+    for (int j = 0; j < CPW; ++j) {
+      const int q = wave * CPW + j;
+      const int rr = h * (BM / 2) + q * RPI + lane / CPR;   // tile row
+      const int c = (lane % CPR) ^ (rr & 15);                // C chunk this lane fetches
+      const uint32_t off = ((uint32_t)min(tile.m0 + rr, M - 1) * (uint32_t)N +
+                            (uint32_t)min(tile.n0 + c * 8, N - 8)) * 2u;
+      buf16_to_lds(rsC, off, 0u, smem + slot_off + q * 1024);
+    }
+  };
+  // Waits until stage kb of the ring has landed.  Operations of one wave retire
+  // in issue order (loads and stores alike), so stage kb is complete once no
+  // more remain than were issued after it: the stages kb+1.. already in flight,
+  // the previous tile's NST stores while kb was a prologue stage, and the first
+  // C half before the last block.
+  auto wait_stage = [&](int kb, bool stores_after) {
+    const int after = min(STAGES - 2, KB - 1 - kb);
+    const bool st = stores_after && kb <= STAGES - 2;
+    const bool ch = has_c && KB >= 2 && kb == KB - 1;
+    if (STAGES >= 4 && after == 2) {
+      if (st) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS + NST>();
+      else wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS>();
+    } else if (after == 1) {
+      if (st) wait_vmcnt<LPS + NST>();
+      else wait_vmcnt<LPS>();
+    } else {
+      if (st && ch) wait_vmcnt<NST + CPW>();
+      else if (st) wait_vmcnt<NST>();
+      else if (ch) wait_vmcnt<CPW>();
+      else wait_vmcnt<0>();
+    }
+  };
+  auto prologue = [&]() {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KB) issue(s, s * STAGE);
+  };
 
-    v4f acc[MT][NT];
+  int t = vb;
+  Tile cur;
+  bool stores_after = false;   // the previous tile's stores were issued after this tile's prologue
+  bool have = next_tile(t, cur);
+  if (have) {
+    setup(cur);
+    prologue();
+  }
+  while (have) {
+    v4f acc[MT][NT];       // fp32 accumulators
+    v4f part[LAG];         // fresh partials, promoted LAG matrix instructions late
+    float sprev = 0.f;     // sa * sb of the previous K block for the last row block
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // prologue: stages 0 .. STAGES-2 in flight
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < KB) issue(s, s * STAGE);
+    for (int r = 0; r < LAG; ++r) part[r] = v4f{0.f, 0.f, 0.f, 0.f};
 
     uint32_t rd_slot = 0;                          // slot of stage kb
     uint32_t wr_slot = (STAGES - 1) * STAGE;       // slot of stage kb + STAGES - 1
+#pragma clang loop unroll(disable)
     for (int kb = 0; kb < KB; ++kb) {
-      // stage kb has landed once at most (#stages issued after it) DMA ops remain
-      const int after = min(STAGES - 2, KB - 1 - kb);
-      if (STAGES >= 4 && after >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS>();
-      else if (STAGES >= 3 && after >= 1) wait_vmcnt<(STAGES >= 3 ? 1 : 0) * LPS>();
-      else wait_vmcnt<0>();
+      wait_stage(kb, stores_after);
       block_barrier();
-      if (kb + STAGES - 1 < KB) issue(kb + STAGES - 1, wr_slot);
-
-      float sbv[NT];
-      if (ONE_SB) {
-        const float s0 = SBc[sb_idx[0] + kb];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sbv[nt] = s0;
-      } else {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sbv[nt] = SBc[sb_idx[nt] + kb];
+      if (kb + STAGES - 1 < KB) {
+        issue(kb + STAGES - 1, wr_slot);
+      } else if (has_c) {
+        // slots (KB + h) % STAGES are free from block KB - 2 + h on
+        if (kb == KB - 1) {
+          if (KB == 1) issue_c(cur, 0, (uint32_t)(KB % STAGES) * STAGE);
+          issue_c(cur, 1, (uint32_t)((KB + 1) % STAGES) * STAGE);
+        } else if (kb == KB - 2) {
+          issue_c(cur, 0, (uint32_t)(KB % STAGES) * STAGE);
+        }
       }
+
+      // B scale of this block (one per wave: its columns share a 128-wide block)
+      const float sbv = SBc[sb_idx + kb];
       const uint8_t* ra_lo = smem + rd_slot + a_lo;
       const uint8_t* ra_hi = smem + rd_slot + a_hi;
       const uint8_t* rb_lo = smem + rd_slot + b_lo;
       const uint8_t* rb_hi = smem + rd_slot + b_hi;
       const uint8_t* rsa = smem + rd_slot + sa_rd;
-      v4f sa[MT];
+      const v4f sav = *reinterpret_cast<const v4f*>(rsa);
+      float scur[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) sa[mt] = *reinterpret_cast<const v4f*>(rsa + mt * 64);
+      for (int mt = 0; mt < MT; ++mt) scur[mt] = sav[mt] * sbv;
       v8i af[MT], bf[NT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -212,46 +304,99 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
         v4i hi = *reinterpret_cast<const v4i*>(rb_hi + nt * 2048);
         bf[nt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
-      if (ONE_SB) {
+      // The wave computes its tile transposed: block (mt, nt) is B_nt . A_mt^T,
+      // so a lane's four results share one row of D (column lrow of the block)
+      // and one A scale.  Block j = mt*NT + nt goes into partial register j % LAG;
+      // the register's previous partial is promoted first: for j < LAG the one
+      // of block j + NBLK - LAG of the previous K block (scale sprev), else the
+      // one of block j - LAG of this K block.  A partial is thus read LAG
+      // matrix instructions after its issue, so the FMAs never wait on it.
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) sa[mt] *= sbv[0];
-      }
+      for (int j = 0; j < NBLK; ++j) {
+        const int mt = j / NT, nt = j % NT;
+        const int r = j % LAG;
+        if (j < LAG) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+          for (int i = 0; i < 4; ++i) acc[MT - 1][j][i] = fmaf(part[r][i], sprev, acc[MT - 1][j][i]);
+        } else {
+          const int pm = (j - LAG) / NT, pn = (j - LAG) % NT;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          v4f part = mfma_e4m3_16x16x128(af[mt], bf[nt], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sc = ONE_SB ? sa[mt][i] : sa[mt][i] * sbv[nt];
-            acc[mt][nt][i] = fmaf(part[i], sc, acc[mt][nt][i]);
-          }
+          for (int i = 0; i < 4; ++i) acc[pm][pn][i] = fmaf(part[r][i], scur[pm], acc[pm][pn][i]);
         }
+        part[r] = mfma_e4m3_16x16x128(bf[nt], af[mt], v4f{0.f, 0.f, 0.f, 0.f});
       }
+      sprev = scur[MT - 1];
       rd_slot = (rd_slot + STAGE == STAGES * STAGE) ? 0u : rd_slot + STAGE;
       wr_slot = (wr_slot + STAGE == STAGES * STAGE) ? 0u : wr_slot + STAGE;
     }
-    block_barrier();   // every wave is done with the LDS ring before the next tile refills it
+    // promote the last LAG partials
+#pragma unroll
+    for (int j = 0; j < LAG; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[MT - 1][j][i] = fmaf(part[j][i], sprev, acc[MT - 1][j][i]);
+    const Tile done = cur;
 
-    // ---------------- epilogue: + C, bf16 RNE, predicated stores ----------------
-    uint16_t* D = p.d;
-    if (MODE == MODE_MASKED) D += (size_t)g * M * N;
+    // Epilogue, part 1: D = acc (+ C) rounded to bf16, still in registers.  Lane
+    // (lgrp, lrow) holds, for block (mt, nt), row mt*16 + lrow and the four
+    // columns nt*16 + 4*lgrp .. +3 of the wave's sub-tile: 8 bytes of one row.
+    v2i o[MT][NT];
+    if (has_c) {
+      wait_vmcnt<0>();   // this wave's C pieces have landed
+      block_barrier();   // ... and every other wave's
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      const int rr0 = wave_m * MT * 16 + mt * 16;       // first tile row of the block
+      const int h = rr0 >= BM / 2 ? 1 : 0;
+      const uint32_t c_row = (uint32_t)((KB + h) % STAGES) * STAGE + (uint32_t)(rr0 - h * (BM / 2) + lrow) * (BN * 2) +
+                             (uint32_t)((lgrp & 1) << 3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int grow = m0 + wave_m * MT * 16 + mt * 16 + 4 * lgrp + i;
-        bool row_ok = grow < rows_valid;
-        if (MODE == MODE_CONTIG && row_ok) row_ok = p.m_indices[grow] == g;
-        if (!row_ok) continue;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = n0 + wave_n * NT * 16 + nt * 16 + lrow;
-          if (col >= N) continue;
-          float v = acc[mt][nt][i];
-          if (MODE == MODE_DENSE && p.c != nullptr) v += bf16_to_f32(p.c[(size_t)grow * N + col]);
-          D[(size_t)grow * N + col] = f32_to_bf16_rne(v);
+      for (int nt = 0; nt < NT; ++nt) {
+        const v4f v = acc[mt][nt];
+        float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+        if (has_c) {
+          const int c = (wave_n * NT * 16 + nt * 16 + 4 * lgrp) >> 3;   // C chunk; tile row % 16 is lrow
+          const uint2 cv = *reinterpret_cast<const uint2*>(smem + c_row + ((c ^ lrow) << 4));
+          v0 += __uint_as_float(cv.x << 16);
+          v1 += __uint_as_float(cv.x & 0xffff0000u);
+          v2 += __uint_as_float(cv.y << 16);
+          v3 += __uint_as_float(cv.y & 0xffff0000u);
         }
+        o[mt][nt].x = (int)((uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16));
+        o[mt][nt].y = (int)((uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
+      }
+    }
+    wait_lgkmcnt0();
+    block_barrier();   // every wave is done with the LDS ring (and C)
+
+    // Start the next tile's loads before this tile's stores: the stores then
+    // drain while the next tile computes its first blocks.
+    t += G;
+    have = next_tile(t, cur);
+    if (have) {
+      setup(cur);
+      prologue();
+    }
+    stores_after = true;
+
+    // Epilogue, part 2: exactly NST stores per wave; masked-off pieces go to an
+    // out-of-range offset.
+    const uint16_t* D = p.d;
+    if (MODE == MODE_MASKED) D += (size_t)done.g * M * N;
+    const v4i rsD = make_buffer_rsrc(D, (uint32_t)M * (uint32_t)N * 2u);
+    const int grow0 = done.m0 + wave_m * MT * 16 + lrow;
+    const int gcol0 = done.n0 + wave_n * NT * 16 + 4 * lgrp;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int grow = grow0 + mt * 16;
+      bool row_ok = grow < done.rows_valid;
+      if (MODE == MODE_CONTIG) row_ok = row_ok && p.m_indices[min(grow, M - 1)] == done.g;
+      const uint32_t row_off = ((uint32_t)grow * (uint32_t)N + (uint32_t)gcol0) * 2u;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bool ok = row_ok && done.n0 + wave_n * NT * 16 + nt * 16 < N;
+        const uint32_t off = ok ? row_off + nt * 32 : kBufferOutOfRange;
+        dg_raw_buffer_store_v2i32(o[mt][nt], rsD, (int)off, 0, 0);
       }
     }
   }

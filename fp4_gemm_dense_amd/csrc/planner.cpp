@@ -24,6 +24,21 @@ static int blocks_per_cu_for(int kernel_id) {
   return std::max(1, std::min(tc.blocks_per_cu, by_lds));
 }
 
+GemmPlan plan_with_kernel(int m, int n, int num_groups, int mode, int num_cus, int kernel_id) {
+  GemmPlan plan{};
+  TileConfig tc = tile_config(kernel_id);
+  plan.kernel_id = kernel_id;
+  plan.block_m = tc.block_m;
+  plan.block_n = tc.block_n;
+  plan.tiles_m = cdiv(m, tc.block_m);
+  plan.tiles_n = cdiv(n, tc.block_n);
+  long long total = (long long)plan.tiles_m * plan.tiles_n * (mode == MODE_MASKED ? num_groups : 1);
+  plan.num_tiles = (int)std::min<long long>(total, 0x7fffffff);
+  long long slots = (long long)num_cus * blocks_per_cu_for(kernel_id);
+  plan.num_workgroups = (int)std::min<long long>(total, slots);
+  return plan;
+}
+
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m) {
   (void)k;
   GemmPlan best{};
@@ -53,16 +68,7 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
       best.kernel_id = id;
     }
   }
-  TileConfig tc = tile_config(best.kernel_id);
-  best.block_m = tc.block_m;
-  best.block_n = tc.block_n;
-  best.tiles_m = cdiv(m, tc.block_m);
-  best.tiles_n = cdiv(n, tc.block_n);
-  long long total = (long long)best.tiles_m * best.tiles_n * (mode == MODE_MASKED ? num_groups : 1);
-  best.num_tiles = (int)std::min<long long>(total, 0x7fffffff);
-  long long slots = (long long)num_cus * blocks_per_cu_for(best.kernel_id);
-  best.num_workgroups = (int)std::min<long long>(total, slots);
-  return best;
+  return plan_with_kernel(m, n, num_groups, mode, num_cus, best.kernel_id);
 }
 
 }  // namespace dg

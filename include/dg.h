@@ -69,7 +69,8 @@ typedef enum dg_status {
  *   sfb  [ceil(n/128), k/128] fp32, one scale per 128x128 block
  *   c    [m, n]               bf16, or NULL for C = 0
  *   d    [m, n]               bf16 output (may alias c only if identical)
- * Requirements: m, n, k > 0; k % 128 == 0; n % 16 == 0.
+ * Requirements: m, n, k > 0; k % 128 == 0; n % 16 == 0; m*k, n*k and 2*m*n
+ *   (the bytes of A, B and D) at most 2^31, else DG_ERR_UNSUPPORTED.
  */
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
@@ -90,7 +91,8 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
  *   sfb       [num_groups, ceil(n/128), k/128]  fp32
  *   m_indices [m]                               int32, device memory
  *   d         [m, n]                            bf16
- * Requirements: m, n, k, num_groups > 0; k % 128 == 0; n % 16 == 0.
+ * Requirements: m, n, k, num_groups > 0; k % 128 == 0; n % 16 == 0; m*k, n*k and
+ *   2*m*n at most 2^31 (B: one group), else DG_ERR_UNSUPPORTED.
  */
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
                                         const float* sfb, const int32_t* m_indices, uint16_t* d,
@@ -110,7 +112,8 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
  *   sfb      [num_groups, ceil(n/128), k/128]  fp32
  *   masked_m [num_groups]                      int32, device memory
  *   d        [num_groups, max_m, n]            bf16
- * Requirements: num_groups, max_m, n, k > 0; k % 128 == 0; n % 16 == 0.
+ * Requirements: num_groups, max_m, n, k > 0; k % 128 == 0; n % 16 == 0; per group,
+ *   max_m*k, n*k and 2*max_m*n at most 2^31, else DG_ERR_UNSUPPORTED.
  */
 int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
                                     const float* sfb, const int32_t* masked_m, uint16_t* d,
