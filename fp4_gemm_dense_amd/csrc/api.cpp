@@ -3,6 +3,7 @@
 // any HIP call; no exception crosses the boundary.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -92,6 +93,9 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
   p.tiles_n = plan.tiles_n;
   p.total_tiles = plan.num_tiles;
   p.group_m = 8;
+  // DG_KROT=<s>: K-block rotation step between neighbouring tiles (tuning)
+  p.k_rot = 0;
+  if (const char* kr = std::getenv("DG_KROT")) p.k_rot = std::max(0, std::atoi(kr));
   if (log_enabled())
     std::fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %dx%d (kernel %d), %d tiles, %d workgroups\n",
                  name, p.m, p.n, p.k, p.num_groups, plan.block_m, plan.block_n, plan.kernel_id,

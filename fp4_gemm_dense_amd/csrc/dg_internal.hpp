@@ -26,6 +26,7 @@ struct Fp8GemmParams {
   int tiles_m, tiles_n;       // tile grid of one group (masked: over max_m)
   int total_tiles;            // all groups
   int group_m;                // raster: tiles along M visited before moving along N
+  int k_rot;                  // K-block rotation step between neighbouring tiles (0: none)
 };
 
 // Tile shapes compiled into the library (kernel_id indexes this table).
@@ -34,6 +35,7 @@ struct TileConfig {
   int blocks_per_cu;    // resident workgroups per CU of the compiled kernel
   int threads;          // workgroup size
   int lds_bytes;        // dynamic LDS per workgroup
+  int min_k;            // shortest K the planner picks this shape for
 };
 int num_tile_configs();
 TileConfig tile_config(int kernel_id);

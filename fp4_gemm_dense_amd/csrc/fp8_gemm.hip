@@ -52,14 +52,17 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // all of a wave's columns lie in one 128-wide B-scale block, so one sb per
   // K block serves the whole wave
   static_assert(128 % (NT * 16) == 0 && (BN % 128 == 0 || 128 % BN == 0), "one B scale per wave");
-  static_assert(MT == 4, "a lane reads its four row scales with one 16-byte LDS load");
+  static_assert(MT % 4 == 0, "a lane reads its row scales with 16-byte LDS loads");
   constexpr int NBLK = MT * NT;   // 16x16 accumulator blocks per wave
   constexpr int LAG = NT;         // matrix instructions between a partial's issue and its promotion
+  constexpr bool STREAM_A = MT > 4;   // read A fragments A_AHEAD row blocks ahead instead of all at once
+  constexpr int A_AHEAD = 2;
   // Epilogue traffic.  The C tile (BM x BN bf16) is copied into two ring slots
   // that the last two K blocks leave free, in halves of BM/2 rows; each wave
   // copies CPW 1-KB pieces of a half.  A C row holds CPR 16-byte chunks, chunk c
   // of row r sits at position c ^ (r % 16).  Every wave then issues exactly NST
   // 8-byte stores of D.
+  // (With a two-slot ring the second half can only follow the last K block.)
   constexpr int CPR = BN / 8;
   constexpr int C_HALF = BM / 2 * BN * 2;
   static_assert(CPR >= 16 && 1024 % (BN * 2) == 0, "C rows must be 256 or 512 bytes");
@@ -106,6 +109,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // ---------------- tile decode: tile id -> (group, m0, n0, valid rows) ----------------
   struct Tile {
     int g, m0, n0, rows_valid;
+    int rot;   // first K block: tiles that share A rows or B rows start at different K
   };
   auto decode = [&](int t, Tile& tile) -> bool {
     int g = 0, tl = t;
@@ -121,6 +125,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     const int r = tl - gi * per_group;
     tile.m0 = (first_m + r % gm) * BM;
     tile.n0 = (r / gm) * BN;
+    tile.rot = (p.k_rot * (((first_m + r % gm) + r / gm) & 7)) % KB;
     tile.rows_valid = M;
     if (MODE == MODE_MASKED) {
       const int mm = p.masked_m[g];
@@ -148,6 +153,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   v4i rsA, rsB, rsSA;
   cfloat* const SBc = (cfloat*)(uintptr_t)p.sfb;   // constant address space: scalar loads
   uint32_t a_off[RA], b_off[RB], sa_off = 0;
+  int rot = 0;   // K-block rotation of the tile whose loads are being issued
   int sb_idx = 0;
   auto setup = [&](const Tile& tile) {
     const uint8_t* A = p.a;
@@ -162,6 +168,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       B += (size_t)tile.g * N * K;
       SB += (size_t)tile.g * NB * KB;
     }
+    rot = tile.rot;
     rsA = make_buffer_rsrc(A, (uint32_t)M * (uint32_t)K);
     rsB = make_buffer_rsrc(B, (uint32_t)N * (uint32_t)K);
     rsSA = make_buffer_rsrc(SA, (uint32_t)KB * (uint32_t)M * 4u);
@@ -192,8 +199,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     sb_idx = __builtin_amdgcn_readfirstlane(sb_group + (min(tile.n0 + wave_n * NT * 16, N - 1) >> 7) * KB);
   };
   auto issue = [&](int kb, uint32_t slot_off) {
-    const uint32_t kofs = (uint32_t)kb * 128u;
-    const uint32_t sofs = (uint32_t)kb * (uint32_t)M * 4u;
+    const int kp = kb + rot < KB ? kb + rot : kb + rot - KB;   // K block in memory
+    const uint32_t kofs = (uint32_t)kp * 128u;
+    const uint32_t sofs = (uint32_t)kp * (uint32_t)M * 4u;
 #pragma unroll
     for (int j = 0; j < RA; ++j) buf16_to_lds(rsA, a_off[j], kofs, smem + slot_off + a_dst + j * 1024);
 #pragma unroll
@@ -202,9 +210,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   };
   // DMA of half h of the C tile into the slot at slot_off (dense form only).
   const bool has_c = MODE == MODE_DENSE && p.c != nullptr;
-  const v4i rsC = make_buffer_rsrc(p.c, (uint32_t)M * (uint32_t)N * 2u);
   auto issue_c = [&](const Tile& tile, int h, uint32_t slot_off) {
     constexpr int RPI = 1024 / (BN * 2);             // C rows per 1-KB piece
+    const v4i rsC = make_buffer_rsrc(p.c, (uint32_t)M * (uint32_t)N * 2u);
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
       const int q = wave * CPW + j;
@@ -223,7 +231,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   auto wait_stage = [&](int kb, bool stores_after) {
     const int after = min(STAGES - 2, KB - 1 - kb);
     const bool st = stores_after && kb <= STAGES - 2;
-    const bool ch = has_c && KB >= 2 && kb == KB - 1;
+    const bool ch = STAGES >= 3 && has_c && KB >= 2 && kb == KB - 1;
     if (STAGES >= 4 && after == 2) {
       if (st) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS + NST>();
       else wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS>();
@@ -271,8 +279,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       if (kb + STAGES - 1 < KB) {
         issue(kb + STAGES - 1, wr_slot);
       } else if (has_c) {
-        // slots (KB + h) % STAGES are free from block KB - 2 + h on
-        if (kb == KB - 1) {
+        // slot (KB + h) % STAGES takes half h: free from block KB - 2 + h on with
+        // three or more slots; with two, half 0 goes in during the last block and
+        // half 1 after it
+        if (STAGES == 2) {
+          if (kb == KB - 1) issue_c(cur, 0, (uint32_t)(KB % STAGES) * STAGE);
+        } else if (kb == KB - 1) {
           if (KB == 1) issue_c(cur, 0, (uint32_t)(KB % STAGES) * STAGE);
           issue_c(cur, 1, (uint32_t)((KB + 1) % STAGES) * STAGE);
         } else if (kb == KB - 2) {
@@ -281,29 +293,33 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       }
 
       // B scale of this block (one per wave: its columns share a 128-wide block)
-      const float sbv = SBc[sb_idx + kb];
+      const float sbv = SBc[sb_idx + (kb + rot < KB ? kb + rot : kb + rot - KB)];
       const uint8_t* ra_lo = smem + rd_slot + a_lo;
       const uint8_t* ra_hi = smem + rd_slot + a_hi;
       const uint8_t* rb_lo = smem + rd_slot + b_lo;
       const uint8_t* rb_hi = smem + rd_slot + b_hi;
       const uint8_t* rsa = smem + rd_slot + sa_rd;
-      const v4f sav = *reinterpret_cast<const v4f*>(rsa);
       float scur[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) scur[mt] = sav[mt] * sbv;
-      v8i af[MT], bf[NT];
+      for (int q = 0; q < MT / 4; ++q) {
+        const v4f sav = *reinterpret_cast<const v4f*>(rsa + 16 * q);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        v4i lo = *reinterpret_cast<const v4i*>(ra_lo + mt * 2048);
-        v4i hi = *reinterpret_cast<const v4i*>(ra_hi + mt * 2048);
-        af[mt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        for (int i = 0; i < 4; ++i) scur[4 * q + i] = sav[i] * sbv;
       }
+      auto load_a = [&](int mt) -> v8i {
+        const v4i lo = *reinterpret_cast<const v4i*>(ra_lo + mt * 2048);
+        const v4i hi = *reinterpret_cast<const v4i*>(ra_hi + mt * 2048);
+        return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      };
+      v8i af[MT], bf[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         v4i lo = *reinterpret_cast<const v4i*>(rb_lo + nt * 2048);
         v4i hi = *reinterpret_cast<const v4i*>(rb_hi + nt * 2048);
         bf[nt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
+#pragma unroll
+      for (int mt = 0; mt < (STREAM_A ? A_AHEAD : MT); ++mt) af[mt] = load_a(mt);
       // The wave computes its tile transposed: block (mt, nt) is B_nt . A_mt^T,
       // so a lane's four results share one row of D (column lrow of the block)
       // and one A scale.  Block j = mt*NT + nt goes into partial register j % LAG;
@@ -311,19 +327,27 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       // of block j + NBLK - LAG of the previous K block (scale sprev), else the
       // one of block j - LAG of this K block.  A partial is thus read LAG
       // matrix instructions after its issue, so the FMAs never wait on it.
+      // With STREAM_A the A fragment of row block mt+A_AHEAD is read while row
+      // block mt computes (scheduling fences keep the reads from being hoisted),
+      // so only A_AHEAD+1 A fragments are live at a time.
 #pragma unroll
-      for (int j = 0; j < NBLK; ++j) {
-        const int mt = j / NT, nt = j % NT;
-        const int r = j % LAG;
-        if (j < LAG) {
+      for (int mt = 0; mt < MT; ++mt) {
+        if (STREAM_A && mt + A_AHEAD < MT) af[mt + A_AHEAD] = load_a(mt + A_AHEAD);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[MT - 1][j][i] = fmaf(part[r][i], sprev, acc[MT - 1][j][i]);
-        } else {
-          const int pm = (j - LAG) / NT, pn = (j - LAG) % NT;
+        for (int nt = 0; nt < NT; ++nt) {
+          const int j = mt * NT + nt;
+          const int r = j % LAG;
+          if (j < LAG) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[pm][pn][i] = fmaf(part[r][i], scur[pm], acc[pm][pn][i]);
+            for (int i = 0; i < 4; ++i) acc[MT - 1][j][i] = fmaf(part[r][i], sprev, acc[MT - 1][j][i]);
+          } else {
+            const int pm = (j - LAG) / NT, pn = (j - LAG) % NT;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[pm][pn][i] = fmaf(part[r][i], scur[pm], acc[pm][pn][i]);
+          }
+          part[r] = mfma_e4m3_16x16x128(bf[nt], af[mt], v4f{0.f, 0.f, 0.f, 0.f});
         }
-        part[r] = mfma_e4m3_16x16x128(bf[nt], af[mt], v4f{0.f, 0.f, 0.f, 0.f});
+        if (STREAM_A) __builtin_amdgcn_sched_barrier(0);
       }
       sprev = scur[MT - 1];
       rd_slot = (rd_slot + STAGE == STAGES * STAGE) ? 0u : rd_slot + STAGE;
@@ -341,6 +365,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     // columns nt*16 + 4*lgrp .. +3 of the wave's sub-tile: 8 bytes of one row.
     v2i o[MT][NT];
     if (has_c) {
+      if (STAGES == 2) {
+        block_barrier();   // every wave is done with the last block's slot
+        issue_c(done, 1, (uint32_t)((KB + 1) % STAGES) * STAGE);
+      }
       wait_vmcnt<0>();   // this wave's C pieces have landed
       block_barrier();   // ... and every other wave's
     }
@@ -411,11 +439,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   X(0, 4, 4, 4, 2, 3, 1)      \
   X(1, 4, 4, 2, 4, 3, 1)      \
   X(2, 4, 4, 2, 2, 3, 1)      \
-  X(3, 4, 2, 1, 4, 4, 1)
+  X(3, 4, 2, 1, 4, 4, 1)      \
+  X(4, 8, 4, 2, 4, 2, 1)
 
 static const TileConfig kTileConfigs[] = {
-#define X(id, MT, NT, WM, WN, ST, OCC) {WM * MT * 16, WN * NT * 16, OCC, WM * WN * 64, \
-                                        ST * ((WM * MT * 16 + WN * NT * 16) * 128 + WM * MT * 16 * 4)},
+#define X(id, MT, NT, WM, WN, ST, OCC) {WM * MT * 16, WN * NT * 16, OCC, WM * WN * 64,                     \
+                                        ST * ((WM * MT * 16 + WN * NT * 16) * 128 + WM * MT * 16 * 4), \
+                                        ST == 2 ? 4096 : 0},
     DG_TILE_CONFIGS(X)
 #undef X
 };

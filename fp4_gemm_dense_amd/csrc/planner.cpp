@@ -40,7 +40,6 @@ GemmPlan plan_with_kernel(int m, int n, int num_groups, int mode, int num_cus, i
 }
 
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m) {
-  (void)k;
   GemmPlan best{};
   best.kernel_id = -1;
   // rows each group contributes (masked: the expected count if given, else capacity)
@@ -51,6 +50,7 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
   for (int id = 0; id < num_tile_configs(); ++id) {
     TileConfig tc = tile_config(id);
     if (mode == MODE_CONTIG && (128 % tc.block_m) != 0) continue;   // blocks must be group-pure
+    if (k < tc.min_k) continue;   // two-slot rings only pay off over long K loops
     int tm = cdiv(rows, tc.block_m);
     int tn = cdiv(n, tc.block_n);
     long long tiles = (long long)tm * tn * (mode == MODE_DENSE ? 1 : (mode == MODE_MASKED ? num_groups : 1));
@@ -63,6 +63,8 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     // bigger tiles re-read less from L2/HBM: weight by tile area (arithmetic intensity)
     double intensity = (double)tc.block_m * tc.block_n / (tc.block_m + tc.block_n);
     double score = util * fill * intensity;
+    // short K loops are bound by the epilogue: wide tiles write longer rows of D
+    if (k <= 1024 && tc.block_n > tc.block_m) score *= 1.05;
     if (score > best_score + 1e-9) {
       best_score = score;
       best.kernel_id = id;
