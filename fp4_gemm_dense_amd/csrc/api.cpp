@@ -8,7 +8,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/dg.h"
 #include "dg_internal.hpp"
@@ -76,6 +78,36 @@ static bool operands_fit(int m, int n, int k) {
   return fits_buffer(m, k, 1) && fits_buffer(n, k, 1) && fits_buffer(m, n, 2);
 }
 
+// Split-K workspace: one fp32 buffer per (device, stream), grown on demand and
+// kept until the process ends, so calls on one stream reuse it in stream order.
+static std::mutex g_ws_mu;
+static std::map<std::pair<int, void*>, std::pair<void*, size_t>> g_ws;
+
+static float* split_workspace(int dev, hipStream_t stream, size_t bytes, hipError_t* err) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto& e = g_ws[{dev, reinterpret_cast<void*>(stream)}];
+  if (e.second < bytes) {
+    if (e.first) {
+      // earlier calls on this stream may still read the old buffer
+      hipError_t r = hipStreamSynchronize(stream);
+      if (r == hipSuccess) r = hipFree(e.first);
+      e = {nullptr, 0};
+      if (r != hipSuccess) {
+        *err = r;
+        return nullptr;
+      }
+    }
+    void* ptr = nullptr;
+    hipError_t r = hipMalloc(&ptr, bytes);
+    if (r != hipSuccess) {
+      *err = r;
+      return nullptr;
+    }
+    e = {ptr, bytes};
+  }
+  return static_cast<float*>(e.first);
+}
+
 static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream, const char* name) {
   DeviceInfo di = current_device_info();
   if (!di.ok) return DG_ERR_NO_DEVICE;
@@ -87,20 +119,36 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
     int id = std::atoi(fk);
     if (id >= 0 && id < num_tile_configs() &&
         !(mode == MODE_CONTIG && (128 % tile_config(id).block_m) != 0))
-      plan = plan_with_kernel(p.m, p.n, p.num_groups, mode, cus, id);
+      plan = plan_with_kernel(p.m, p.n, p.k, p.num_groups, mode, cus, id);
+  }
+  // split K needs one fp32 slice of m x n per K slice, addressed with 32-bit offsets
+  const size_t slice_bytes = (size_t)p.m * p.n * 4;
+  if (plan.splits > 1 && (slice_bytes > (size_t(1) << 31) || slice_bytes * plan.splits > (size_t(1) << 32))) {
+    plan.splits = 1;
+    plan.kb_per_split = p.k / 128;
+    plan.num_workgroups = std::min(plan.num_tiles, cus * std::max(1, tile_config(plan.kernel_id).blocks_per_cu));
   }
   p.tiles_m = plan.tiles_m;
   p.tiles_n = plan.tiles_n;
-  p.total_tiles = plan.num_tiles;
+  p.splits = plan.splits;
+  p.kb_per_split = plan.kb_per_split;
+  p.total_tiles = (int)std::min<long long>((long long)plan.num_tiles * plan.splits, 0x7fffffff);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (plan.splits > 1) {
+    hipError_t werr = hipSuccess;
+    p.ws = split_workspace(di.device, hs, slice_bytes * plan.splits, &werr);
+    if (!p.ws) return DG_ERR_HIP;
+  }
   p.group_m = 8;
   // DG_KROT=<s>: K-block rotation step between neighbouring tiles (tuning)
   p.k_rot = 0;
   if (const char* kr = std::getenv("DG_KROT")) p.k_rot = std::max(0, std::atoi(kr));
   if (log_enabled())
-    std::fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %dx%d (kernel %d), %d tiles, %d workgroups\n",
-                 name, p.m, p.n, p.k, p.num_groups, plan.block_m, plan.block_n, plan.kernel_id,
-                 plan.num_tiles, plan.num_workgroups);
-  hipError_t e = launch_fp8_gemm(p, plan, mode, reinterpret_cast<hipStream_t>(stream));
+    std::fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %dx%d (kernel %d), %d tiles x %d K slices, "
+                 "%d workgroups\n", name, p.m, p.n, p.k, p.num_groups, plan.block_m, plan.block_n, plan.kernel_id,
+                 plan.num_tiles, plan.splits, plan.num_workgroups);
+  hipError_t e = launch_fp8_gemm(p, plan, mode, hs);
+  if (e == hipSuccess && plan.splits > 1) e = launch_splitk_reduce(p.ws, p.c, p.d, p.m, p.n, plan.splits, cus, hs);
   return e == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
@@ -116,7 +164,7 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
     if (!a || !sfa || !b || !sfb || !d) return DG_ERR_INVALID_ARG;
     if (m <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sfa, 4) || !aligned(sfb, 4) ||
-        (c && !aligned(c, 2)))
+        (c && !aligned(c, 16)))
       return DG_ERR_INVALID_ARG;
     if (k % 128 != 0 || n % 16 != 0 || !operands_fit(m, n, k)) return DG_ERR_UNSUPPORTED;
     Fp8GemmParams p{};
@@ -208,6 +256,7 @@ int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out
   out->num_tiles = p.num_tiles;
   out->num_workgroups = p.num_workgroups;
   out->kernel_id = p.kernel_id;
+  out->splits = p.splits;
   return DG_OK;
 }
 

@@ -103,6 +103,8 @@ __device__ __forceinline__ void buf4_to_lds(const v4i& rsrc, uint32_t voff, uint
 // every lane of the wave always issues exactly one store instruction.
 extern "C" __device__ void dg_raw_buffer_store_v2i32(v2i data, v4i rsrc, int voffset, int soffset,
                                                      int aux) __asm("llvm.amdgcn.raw.buffer.store.v2i32");
+extern "C" __device__ void dg_raw_buffer_store_v4i32(v4i data, v4i rsrc, int voffset, int soffset,
+                                                     int aux) __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // valid with resources below 2 GiB
 
 // Direct global -> LDS copies: lane l's 16 (or 4) bytes land at

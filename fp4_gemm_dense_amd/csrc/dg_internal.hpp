@@ -27,6 +27,9 @@ struct Fp8GemmParams {
   int total_tiles;            // all groups
   int group_m;                // raster: tiles along M visited before moving along N
   int k_rot;                  // K-block rotation step between neighbouring tiles (0: none)
+  int splits;                 // K slices per output tile (1: no split)
+  int kb_per_split;           // K blocks per slice (the last one may hold fewer)
+  float* ws;                  // split K: fp32 partial sums [splits][m][n]
 };
 
 // Tile shapes compiled into the library (kernel_id indexes this table).
@@ -53,11 +56,17 @@ struct GemmPlan {
   int kernel_id;
   int block_m, block_n;
   int tiles_m, tiles_n;
-  int num_tiles;
+  int num_tiles;              // output tiles (all groups)
+  int splits;                 // K slices per output tile (dense only; 1: none)
+  int kb_per_split;
   int num_workgroups;
 };
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m);
-GemmPlan plan_with_kernel(int m, int n, int num_groups, int mode, int num_cus, int kernel_id);
+GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id);
+
+// Split K: D = bf16(sum of the ws slices + C); returns a hipError_t.
+hipError_t launch_splitk_reduce(const float* ws, const uint16_t* c, uint16_t* d, int m, int n, int splits,
+                                int num_cus, hipStream_t stream);
 
 // Launches the kernel chosen by plan on stream; returns a hipError_t.
 hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mode, hipStream_t stream);

@@ -28,6 +28,8 @@
 //   * Persistent workgroups walk a group-M raster of tiles; block ids are
 //     remapped so that each XCD (workgroups are dealt round-robin to the 8
 //     XCDs) works on a contiguous stretch of the raster and shares its L2.
+#include <algorithm>
+
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
 
@@ -109,9 +111,21 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // ---------------- tile decode: tile id -> (group, m0, n0, valid rows) ----------------
   struct Tile {
     int g, m0, n0, rows_valid;
-    int rot;   // first K block: tiles that share A rows or B rows start at different K
+    int kb0, nkb;   // K blocks [kb0, kb0 + nkb) of this work unit (split K: a slice)
+    int rot;        // first K block: tiles that share A rows or B rows start at different K
   };
+  const bool split = p.splits > 1;
   auto decode = [&](int t, Tile& tile) -> bool {
+    if (split) {
+      // work unit t = output tile t / splits, K slice t % splits
+      const int sl = t % p.splits;
+      t /= p.splits;
+      tile.kb0 = sl * p.kb_per_split;
+      tile.nkb = min(p.kb_per_split, KB - tile.kb0);
+    } else {
+      tile.kb0 = 0;
+      tile.nkb = KB;
+    }
     int g = 0, tl = t;
     if (MODE == MODE_MASKED) {
       const int per = p.tiles_m * p.tiles_n;
@@ -125,7 +139,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     const int r = tl - gi * per_group;
     tile.m0 = (first_m + r % gm) * BM;
     tile.n0 = (r / gm) * BN;
-    tile.rot = (p.k_rot * (((first_m + r % gm) + r / gm) & 7)) % KB;
+    tile.rot = split ? 0 : (p.k_rot * (((first_m + r % gm) + r / gm) & 7)) % KB;
     tile.rows_valid = M;
     if (MODE == MODE_MASKED) {
       const int mm = p.masked_m[g];
@@ -153,7 +167,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   v4i rsA, rsB, rsSA;
   cfloat* const SBc = (cfloat*)(uintptr_t)p.sfb;   // constant address space: scalar loads
   uint32_t a_off[RA], b_off[RB], sa_off = 0;
-  int rot = 0;   // K-block rotation of the tile whose loads are being issued
+  int rot = 0, kb0_d = 0, nkb_d = 1;   // K range and rotation of the tile whose loads are issued
   int sb_idx = 0;
   auto setup = [&](const Tile& tile) {
     const uint8_t* A = p.a;
@@ -169,6 +183,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       SB += (size_t)tile.g * NB * KB;
     }
     rot = tile.rot;
+    kb0_d = tile.kb0;
+    nkb_d = tile.nkb;
     rsA = make_buffer_rsrc(A, (uint32_t)M * (uint32_t)K);
     rsB = make_buffer_rsrc(B, (uint32_t)N * (uint32_t)K);
     rsSA = make_buffer_rsrc(SA, (uint32_t)KB * (uint32_t)M * 4u);
@@ -199,7 +215,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     sb_idx = __builtin_amdgcn_readfirstlane(sb_group + (min(tile.n0 + wave_n * NT * 16, N - 1) >> 7) * KB);
   };
   auto issue = [&](int kb, uint32_t slot_off) {
-    const int kp = kb + rot < KB ? kb + rot : kb + rot - KB;   // K block in memory
+    const int kp = kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d);   // K block in memory
     const uint32_t kofs = (uint32_t)kp * 128u;
     const uint32_t sofs = (uint32_t)kp * (uint32_t)M * 4u;
 #pragma unroll
@@ -209,7 +225,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     if (SPW == 64 || lane < SPW) buf4_to_lds(rsSA, sa_off, sofs, smem + slot_off + sa_dst);
   };
   // DMA of half h of the C tile into the slot at slot_off (dense form only).
-  const bool has_c = MODE == MODE_DENSE && p.c != nullptr;
+  const bool has_c = MODE == MODE_DENSE && p.c != nullptr && !split;
   auto issue_c = [&](const Tile& tile, int h, uint32_t slot_off) {
     constexpr int RPI = 1024 / (BN * 2);             // C rows per 1-KB piece
     const v4i rsC = make_buffer_rsrc(p.c, (uint32_t)M * (uint32_t)N * 2u);
@@ -228,10 +244,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // more remain than were issued after it: the stages kb+1.. already in flight,
   // the previous tile's NST stores while kb was a prologue stage, and the first
   // C half before the last block.
-  auto wait_stage = [&](int kb, bool stores_after) {
-    const int after = min(STAGES - 2, KB - 1 - kb);
+  auto wait_stage = [&](int kb, int KT, bool stores_after) {
+    const int after = min(STAGES - 2, KT - 1 - kb);
     const bool st = stores_after && kb <= STAGES - 2;
-    const bool ch = STAGES >= 3 && has_c && KB >= 2 && kb == KB - 1;
+    const bool ch = STAGES >= 3 && has_c && KT >= 2 && kb == KT - 1;
     if (STAGES >= 4 && after == 2) {
       if (st) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS + NST>();
       else wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS>();
@@ -248,7 +264,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   auto prologue = [&]() {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-      if (s < KB) issue(s, s * STAGE);
+      if (s < nkb_d) issue(s, s * STAGE);
   };
 
   int t = vb;
@@ -270,30 +286,32 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
 #pragma unroll
     for (int r = 0; r < LAG; ++r) part[r] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    const int KT = cur.nkb;                        // K blocks of this work unit
+    const int kb0 = cur.kb0;
     uint32_t rd_slot = 0;                          // slot of stage kb
     uint32_t wr_slot = (STAGES - 1) * STAGE;       // slot of stage kb + STAGES - 1
 #pragma clang loop unroll(disable)
-    for (int kb = 0; kb < KB; ++kb) {
-      wait_stage(kb, stores_after);
+    for (int kb = 0; kb < KT; ++kb) {
+      wait_stage(kb, KT, stores_after);
       block_barrier();
-      if (kb + STAGES - 1 < KB) {
+      if (kb + STAGES - 1 < KT) {
         issue(kb + STAGES - 1, wr_slot);
       } else if (has_c) {
-        // slot (KB + h) % STAGES takes half h: free from block KB - 2 + h on with
+        // slot (KT + h) % STAGES takes half h: free from block KT - 2 + h on with
         // three or more slots; with two, half 0 goes in during the last block and
         // half 1 after it
         if (STAGES == 2) {
-          if (kb == KB - 1) issue_c(cur, 0, (uint32_t)(KB % STAGES) * STAGE);
-        } else if (kb == KB - 1) {
-          if (KB == 1) issue_c(cur, 0, (uint32_t)(KB % STAGES) * STAGE);
-          issue_c(cur, 1, (uint32_t)((KB + 1) % STAGES) * STAGE);
-        } else if (kb == KB - 2) {
-          issue_c(cur, 0, (uint32_t)(KB % STAGES) * STAGE);
+          if (kb == KT - 1) issue_c(cur, 0, (uint32_t)(KT % STAGES) * STAGE);
+        } else if (kb == KT - 1) {
+          if (KT == 1) issue_c(cur, 0, (uint32_t)(KT % STAGES) * STAGE);
+          issue_c(cur, 1, (uint32_t)((KT + 1) % STAGES) * STAGE);
+        } else if (kb == KT - 2) {
+          issue_c(cur, 0, (uint32_t)(KT % STAGES) * STAGE);
         }
       }
 
       // B scale of this block (one per wave: its columns share a 128-wide block)
-      const float sbv = SBc[sb_idx + (kb + rot < KB ? kb + rot : kb + rot - KB)];
+      const float sbv = SBc[sb_idx + kb0 + (kb + rot < KT ? kb + rot : kb + rot - KT)];
       const uint8_t* ra_lo = smem + rd_slot + a_lo;
       const uint8_t* ra_hi = smem + rd_slot + a_hi;
       const uint8_t* rb_lo = smem + rd_slot + b_lo;
@@ -367,16 +385,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     if (has_c) {
       if (STAGES == 2) {
         block_barrier();   // every wave is done with the last block's slot
-        issue_c(done, 1, (uint32_t)((KB + 1) % STAGES) * STAGE);
+        issue_c(done, 1, (uint32_t)((KT + 1) % STAGES) * STAGE);
       }
       wait_vmcnt<0>();   // this wave's C pieces have landed
       block_barrier();   // ... and every other wave's
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = 0; mt < (split ? 0 : MT); ++mt) {
       const int rr0 = wave_m * MT * 16 + mt * 16;       // first tile row of the block
       const int h = rr0 >= BM / 2 ? 1 : 0;
-      const uint32_t c_row = (uint32_t)((KB + h) % STAGES) * STAGE + (uint32_t)(rr0 - h * (BM / 2) + lrow) * (BN * 2) +
+      const uint32_t c_row = (uint32_t)((KT + h) % STAGES) * STAGE + (uint32_t)(rr0 - h * (BM / 2) + lrow) * (BN * 2) +
                              (uint32_t)((lgrp & 1) << 3);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -394,6 +412,27 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
         o[mt][nt].y = (int)((uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
       }
     }
+    if (split) {
+      // split K: this slice's fp32 partial sums go to workspace slice kb0 / kb_per_split
+      // (4 consecutive columns = 16 bytes per lane and block); C is added when
+      // the slices are summed
+      const int sl = done.kb0 / p.kb_per_split;
+      const v4i rsW = make_buffer_rsrc(p.ws + (size_t)sl * M * N, (uint32_t)M * (uint32_t)N * 4u);
+      const int grow0 = done.m0 + wave_m * MT * 16 + lrow;
+      const int gcol0 = done.n0 + wave_n * NT * 16 + 4 * lgrp;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int grow = grow0 + mt * 16;
+        const uint32_t row_off = ((uint32_t)grow * (uint32_t)N + (uint32_t)gcol0) * 4u;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bool ok = grow < done.rows_valid && done.n0 + wave_n * NT * 16 + nt * 16 < N;
+          const v4i w = {__float_as_int(acc[mt][nt][0]), __float_as_int(acc[mt][nt][1]),
+                         __float_as_int(acc[mt][nt][2]), __float_as_int(acc[mt][nt][3])};
+          dg_raw_buffer_store_v4i32(w, rsW, (int)(ok ? row_off + nt * 64 : kBufferOutOfRange), 0, 0);
+        }
+      }
+    }
     wait_lgkmcnt0();
     block_barrier();   // every wave is done with the LDS ring (and C)
 
@@ -405,7 +444,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       setup(cur);
       prologue();
     }
-    stores_after = true;
+    // (split K: the partial stores precede the next tile's loads)
+    stores_after = !split;
+    if (split) continue;
 
     // Epilogue, part 2: exactly NST stores per wave; masked-off pieces go to an
     // out-of-range offset.
@@ -428,6 +469,48 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// split K: sum of the slices' fp32 partials (in slice order), plus C, to bf16
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ ws,
+                                                            const uint16_t* __restrict__ c, uint16_t* d,
+                                                            int m, int n, int splits) {
+  const size_t slice8 = (size_t)m * n / 8;   // 8-column groups per slice (n % 16 == 0)
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < slice8; i += (size_t)gridDim.x * 256) {
+    const float4* w = reinterpret_cast<const float4*>(ws) + 2 * i;
+    float4 lo = w[0], hi = w[1];
+    for (int s = 1; s < splits; ++s) {
+      const float4* ws_s = w + 2 * slice8 * s;
+      const float4 a = ws_s[0], b = ws_s[1];
+      lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+      hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+    }
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    if (c) {
+      const uint4 cv = reinterpret_cast<const uint4*>(c)[i];
+      const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] += __uint_as_float(cw[j] << 16);
+        v[2 * j + 1] += __uint_as_float(cw[j] & 0xffff0000u);
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = (uint32_t)f32_to_bf16_rne(v[2 * j]) | ((uint32_t)f32_to_bf16_rne(v[2 * j + 1]) << 16);
+    reinterpret_cast<uint4*>(d)[i] = uint4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+hipError_t launch_splitk_reduce(const float* ws, const uint16_t* c, uint16_t* d, int m, int n, int splits,
+                                int num_cus, hipStream_t stream) {
+  const size_t groups = (size_t)m * n / 8;
+  const int grid = (int)std::min<size_t>((groups + 255) / 256, (size_t)num_cus * 8);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, ws, c, d, m, n, splits);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

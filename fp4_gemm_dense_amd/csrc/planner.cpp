@@ -24,7 +24,20 @@ static int blocks_per_cu_for(int kernel_id) {
   return std::max(1, std::min(tc.blocks_per_cu, by_lds));
 }
 
-GemmPlan plan_with_kernel(int m, int n, int num_groups, int mode, int num_cus, int kernel_id) {
+// Split K for problems whose output tiles cannot fill the chip (skinny M):
+// enough K slices to occupy every workgroup slot once, at least four K blocks
+// per slice and at most 16 slices.  Returns 1 when splitting does not apply.
+static int choose_splits(long long tiles, int slots, int kb) {
+  if (tiles <= 0 || tiles * 2 > slots || kb < 8) return 1;
+  long long s = slots / tiles;
+  s = std::min<long long>(s, kb / 4);
+  s = std::min<long long>(s, 16);
+  if (s < 2) return 1;
+  const int per = cdiv(kb, (int)s);
+  return cdiv(kb, per);
+}
+
+GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id) {
   GemmPlan plan{};
   TileConfig tc = tile_config(kernel_id);
   plan.kernel_id = kernel_id;
@@ -35,13 +48,19 @@ GemmPlan plan_with_kernel(int m, int n, int num_groups, int mode, int num_cus, i
   long long total = (long long)plan.tiles_m * plan.tiles_n * (mode == MODE_MASKED ? num_groups : 1);
   plan.num_tiles = (int)std::min<long long>(total, 0x7fffffff);
   long long slots = (long long)num_cus * blocks_per_cu_for(kernel_id);
-  plan.num_workgroups = (int)std::min<long long>(total, slots);
+  plan.splits = 1;
+  plan.kb_per_split = k / 128;
+  if (mode == MODE_DENSE) {
+    plan.splits = choose_splits(total, (int)std::min<long long>(slots, 1 << 20), k / 128);
+    plan.kb_per_split = cdiv(k / 128, plan.splits);
+  }
+  const long long units = total * plan.splits;
+  plan.num_workgroups = (int)std::min<long long>(units, slots);
   return plan;
 }
 
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m) {
-  GemmPlan best{};
-  best.kernel_id = -1;
+  int best_id = -1;
   // rows each group contributes (masked: the expected count if given, else capacity)
   int rows = m;
   if (mode == MODE_MASKED) rows = expected_m > 0 ? std::min(expected_m, m) : m;
@@ -56,21 +75,30 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     long long tiles = (long long)tm * tn * (mode == MODE_DENSE ? 1 : (mode == MODE_MASKED ? num_groups : 1));
     // useful fraction of the MFMA work (padding in M and N is wasted)
     double util = (double)rows / (tm * tc.block_m) * (double)n / (tn * tc.block_n);
-    // wave quantisation: fraction of the last wave of tiles that is busy
+    // wave quantisation: fraction of the last wave of work units that is busy
     int slots = num_cus * blocks_per_cu_for(id);
-    long long waves = (tiles + slots - 1) / slots;
-    double fill = (double)tiles / (double)(waves * slots);
+    const int splits = mode == MODE_DENSE ? choose_splits(tiles, slots, k / 128) : 1;
+    long long units = tiles * splits;
+    long long waves = (units + slots - 1) / slots;
+    double fill = (double)units / (double)(waves * slots);
     // bigger tiles re-read less from L2/HBM: weight by tile area (arithmetic intensity)
     double intensity = (double)tc.block_m * tc.block_n / (tc.block_m + tc.block_n);
     double score = util * fill * intensity;
+    // split K writes and re-reads fp32 partials
+    if (splits > 1) score *= 0.8;
     // short K loops are bound by the epilogue: wide tiles write longer rows of D
     if (k <= 1024 && tc.block_n > tc.block_m) score *= 1.05;
     if (score > best_score + 1e-9) {
       best_score = score;
-      best.kernel_id = id;
+      best_id = id;
     }
   }
-  return plan_with_kernel(m, n, num_groups, mode, num_cus, best.kernel_id);
+  if (best_id < 0) {
+    GemmPlan none{};
+    none.kernel_id = -1;
+    return none;
+  }
+  return plan_with_kernel(m, n, k, num_groups, mode, num_cus, best_id);
 }
 
 }  // namespace dg

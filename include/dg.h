@@ -67,7 +67,7 @@ typedef enum dg_status {
  *   sfa  [k/128, m]           fp32, one scale per row per 128-wide K block
  *   b    [n, k]               e4m3 codes (B is stored N x K: the "T" of NT)
  *   sfb  [ceil(n/128), k/128] fp32, one scale per 128x128 block
- *   c    [m, n]               bf16, or NULL for C = 0
+ *   c    [m, n]               bf16, or NULL for C = 0 (16-byte aligned)
  *   d    [m, n]               bf16 output (may alias c only if identical)
  * Requirements: m, n, k > 0; k % 128 == 0; n % 16 == 0; m*k, n*k and 2*m*n
  *   (the bytes of A, B and D) at most 2^31, else DG_ERR_UNSUPPORTED.
@@ -177,15 +177,21 @@ int dg_get_num_cus(void);
  * The tile plan the heuristic picks for an M x N x K problem split over
  * num_groups groups (1 for dense), on num_cus compute units (<= 0: current cap).
  * Host-only: no HIP call is made when num_cus > 0.  Fills block_m, block_n,
- * the number of output tiles and the number of workgroups launched.
+ * the number of output tiles, the K slices per tile and the number of
+ * workgroups launched.  A dense problem whose tiles cannot fill the chip (skinny
+ * M) is split along K: each workgroup sums a range of 128-wide K blocks into an
+ * fp32 slice of an internal workspace, and a second kernel adds the slices (in
+ * slice order) and C and rounds to bf16.  The workspace is allocated by the
+ * library, one per (device, stream), on first need.
  * Exposed so callers can log the choice (DG_LOG=1 prints it on every call).
  */
 typedef struct dg_plan {
   int block_m;
   int block_n;
-  int num_tiles;
+  int num_tiles;        /* output tiles */
   int num_workgroups;
   int kernel_id;
+  int splits;           /* K slices per output tile (dense only; 1: no split) */
 } dg_plan;
 int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out);
 

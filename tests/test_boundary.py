@@ -105,5 +105,13 @@ def test_planner_is_host_only_and_fills_the_chip():
     for (m, n, k) in [(4096, 7168, 2048), (4096, 2112, 7168), (64, 32768, 512), (128, 2112, 7168)]:
         p = dgm.dg_query_plan(m, n, k, 1, 256)
         assert p["num_tiles"] == dgm.dg_num_tiles(m, n, p["block_m"], p["block_n"])
-        assert 0 < p["num_workgroups"] <= max(p["num_tiles"], 1)
+        assert p["splits"] >= 1
+        assert 0 < p["num_workgroups"] <= max(p["num_tiles"] * p["splits"], 1)
         assert p["num_workgroups"] <= 256 * 4
+    # skinny M: the 17 output tiles of a 128 x 2112 x 7168 problem are split along
+    # K so that the work units fill the chip; K slices hold whole 128-wide blocks
+    p = dgm.dg_query_plan(128, 2112, 7168, 1, 256)
+    assert p["splits"] > 1 and p["num_tiles"] * p["splits"] > 128
+    assert p["splits"] <= 7168 // 128 // 4
+    # a problem that already fills the chip is not split
+    assert dgm.dg_query_plan(4096, 7168, 2048, 1, 256)["splits"] == 1
