@@ -32,6 +32,13 @@ __device__ __forceinline__ v4f mfma_scaled_e4m3_e2m1_16x16x128(const v8i& a, int
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_E4M3, FMT_E2M1, 0, sa, 0, sb);
 }
 
+// The same instruction with the operands the other way round: A e2m1 (FP4,
+// low 4 dwords), B e4m3; scale bytes as above.
+__device__ __forceinline__ v4f mfma_scaled_e2m1_e4m3_16x16x128(const v8i& a, int sa, const v8i& b,
+                                                               int sb, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_E2M1, FMT_E4M3, 0, sa, 0, sb);
+}
+
 // fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -32,10 +32,6 @@
 namespace dg {
 
 constexpr int FFN_MAX_EXPERTS = 256;
-constexpr int FFN_BM = 64;          // pair rows per tile
-constexpr int FFN_BROWS = 256;      // weight rows per tile (128 gate + 128 up, or 256 outputs)
-constexpr int FFN_STAGES = 3;
-constexpr int FFN_THREADS = 256;
 
 struct FfnParams {
   const uint8_t* x;
@@ -156,32 +152,54 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
   return sign | code;
 }
 
+// Tile of the grouped GEMM: 128 pair rows x 256 weight rows, 8 waves as 4 x 2,
+// each wave 32 rows x 128 weight rows (2 x 8 blocks of 16 x 16).  Each block is
+// computed transposed (W_nt . X_mt^T, the FP4 weights as the instruction's first
+// operand), so a lane's four results are four consecutive weight rows (output
+// columns) of one pair row.  Operand tiles and their scale words go through a
+// 4-slot LDS ring by buffer loads; the K block advances the scalar offset only.
+constexpr int FFN_WM = 4, FFN_WN = 2, FFN_MT = 2, FFN_NT = 8;
+constexpr int FFN_BM = FFN_WM * FFN_MT * 16;      // 128 pair rows per tile
+constexpr int FFN_BN = FFN_WN * FFN_NT * 16;      // 256 weight rows per tile
+constexpr int FFN_STAGES = 4;
+constexpr int FFN_THREADS = 512;
+constexpr int FFN_A_BYTES = FFN_BM * 128;         // e4m3, 128 K per row
+constexpr int FFN_B_BYTES = FFN_BN * 64;          // e2m1, 128 K per row
+constexpr int FFN_SA_BYTES = FFN_BM * 4;          // one scale word per row
+constexpr int FFN_SB_BYTES = FFN_BN * 4;
+constexpr int FFN_STAGE = FFN_A_BYTES + FFN_B_BYTES + FFN_SA_BYTES + FFN_SB_BYTES;
+constexpr int FFN_LDS = FFN_STAGES * FFN_STAGE;
+
 template <int MODE>   // 1: linear1 (+ SwiGLU + requant), 2: linear2 (fp32 out)
-__global__ void __launch_bounds__(FFN_THREADS, 2) ffn_gemm_kernel(FfnParams p) {
-  constexpr int A_BYTES = FFN_BM * 128;            // e4m3, 128 K per row
-  constexpr int B_BYTES = FFN_BROWS * 64;          // e2m1, 128 K per row
-  constexpr int SA_BYTES = FFN_BM * 4;             // one scale word per row
-  constexpr int SB_BYTES = FFN_BROWS * 4;
-  constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-  constexpr int OFF_B = A_BYTES, OFF_SA = A_BYTES + B_BYTES, OFF_SB = OFF_SA + SA_BYTES;
-  constexpr int LPS = 2 + 4 + 1 + 1;               // DMA instructions per wave per stage
-  __shared__ __attribute__((aligned(16))) uint8_t smem[FFN_STAGES * STAGE];
+__global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
+  constexpr int NW = FFN_WM * FFN_WN;
+  constexpr int MT = FFN_MT, NT = FFN_NT, STAGES = FFN_STAGES, STAGE = FFN_STAGE;
+  constexpr int OFF_B = FFN_A_BYTES, OFF_SA = OFF_B + FFN_B_BYTES, OFF_SB = OFF_SA + FFN_SA_BYTES;
+  constexpr int RA = FFN_BM / 8 / NW;              // A regions (8 rows x 128 B) per wave
+  constexpr int RB = FFN_BN / 16 / NW;             // B regions (16 rows x 64 B) per wave
+  constexpr int SAW = FFN_BM / NW;                 // A scale words per wave
+  constexpr int SBW = FFN_BN / NW;                 // B scale words per wave
+  static_assert(SAW <= 64 && SBW <= 64, "one scale copy per wave");
+  constexpr int LPS = RA + RB + 2;                 // copy instructions per wave per stage
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int tile_base[FFN_MAX_EXPERTS + 1];
-  __shared__ float red[4][FFN_BM];
+  __shared__ float red[FFN_WN][FFN_BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave / FFN_WN;
+  const int wave_n = wave % FFN_WN;
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
 
   const int H = p.H, I = p.I, E = p.E;
   const int K = MODE == 1 ? H : I;
   const int KB = K >> 7;
-  const int tiles_n = MODE == 1 ? I / 128 : (H + FFN_BROWS - 1) / FFN_BROWS;
+  const int tiles_n = MODE == 1 ? I / 128 : H / FFN_BN;   // H % 512 == 0
 
   // device-side tile enumeration: expert e owns tiles_m(e) * tiles_n tiles,
-  // ordered (n-tile, m-tile) so consecutive tiles share a weight tile
+  // ordered (n-tile, m-tile) so that consecutive tiles share a weight tile
   if (tid == 0) {
     int s = 0;
     for (int e = 0; e < E; ++e) {
@@ -197,25 +215,33 @@ __global__ void __launch_bounds__(FFN_THREADS, 2) ffn_gemm_kernel(FfnParams p) {
   int vb = blockIdx.x;
   if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
-  // Per-lane LDS read offsets.  In the F8F6F4 instruction an e4m3 operand lane
-  // (row, g) holds K [16g, 16g+16) in its first 16 bytes and K [64+16g, 64+16g+16)
-  // in the next 16, while an e2m1 operand lane (col, g) holds K [32g, 32g+32)
-  // contiguously (low nibble first); so the e4m3 lane reads 16-byte chunks g and
-  // g + 4 of its 128-byte row.
+  // Per-lane LDS read offsets.  An e4m3 operand lane (row, g) of the F8F6F4
+  // instruction holds K [16g, 16g+16) and [64+16g, 64+16g+16), so it reads the
+  // 16-byte chunks g and g+4 of its 128-byte row; an e2m1 lane (row, g) holds
+  // K [32g, 32g+32): chunk g of its 64-byte row.
   const int sw = swz(lrow);
-  const uint32_t a_lo = lrow * 128 + ((lgrp ^ sw) << 4);
-  const uint32_t a_hi = lrow * 128 + (((lgrp + 4) ^ sw) << 4);
-  // weight rows read by this wave: linear1 gate rows 32w..32w+31 (nt 0,1) and
-  // up rows 128+32w.. (nt 2,3); linear2 rows 64w + 16nt
-  uint32_t b_rd[4], sb_rd[4];
+  const uint32_t a_lo = (wave_m * MT * 16 + lrow) * 128 + ((lgrp ^ sw) << 4);
+  const uint32_t a_hi = (wave_m * MT * 16 + lrow) * 128 + (((lgrp + 4) ^ sw) << 4);
+  const uint32_t sa_rd = OFF_SA + (wave_m * MT * 16 + lrow) * 4;
+  // weight rows of block nt: linear1 gate rows 64*wn + 16nt (nt < 4) and the
+  // matching up rows 128 + 64*wn + 16(nt-4); linear2 output rows 128*wn + 16nt
+  uint32_t b_rd[NT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int row = MODE == 1 ? ((nt < 2 ? 0 : 128) + wave * 32 + (nt & 1) * 16 + lrow) : (wave * 64 + nt * 16 + lrow);
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = MODE == 1 ? ((nt < 4 ? 0 : 128) + wave_n * 64 + (nt & 3) * 16 + lrow)
+                              : (wave_n * 128 + nt * 16 + lrow);
     b_rd[nt] = OFF_B + row * 64 + ((lgrp ^ swzb(row)) << 4);
-    sb_rd[nt] = OFF_SB + row * 4;
   }
-  const int dma_arow = lane >> 3;   // A: 8 rows x 128 B per 1 KB region
-  const int dma_brow = lane >> 2;   // B: 16 rows x 64 B per 1 KB region
+  const uint32_t sb_rd0 = OFF_SB + (MODE == 1 ? wave_n * 64 + lrow : wave_n * 128 + lrow) * 4;
+
+  const uint8_t* a_base = MODE == 1 ? p.x : p.q;
+  const size_t a_rows = MODE == 1 ? (size_t)p.T : (size_t)p.T * p.k;
+  const v4i rsA = make_buffer_rsrc(a_base, (uint32_t)(a_rows * (size_t)K));
+  const v4i rsSA = MODE == 1 ? make_buffer_rsrc(p.x_sf, (uint32_t)((size_t)p.T * (H / 512) * 4))
+                             : make_buffer_rsrc(p.sq, (uint32_t)((size_t)p.T * p.k * p.sq_stride));
+  const uint32_t wrow_bytes = (uint32_t)K / 2;
+  const uint32_t wsf_bytes = (uint32_t)(K / 128) * 4;
+  const uint32_t e_rows = MODE == 1 ? 2u * I : (uint32_t)H;
 
   for (int t = vb; t < total; t += G) {
     // ---------------- tile -> (expert, m-tile, n-tile) ----------------
@@ -234,167 +260,150 @@ __global__ void __launch_bounds__(FFN_THREADS, 2) ffn_gemm_kernel(FfnParams p) {
     const int rows = min(FFN_BM, cnt_e - tm * FFN_BM); // valid pairs in the tile
     const int last_pair = p.start[e] + cnt_e - 1;
 
-    // ---------------- DMA sources ----------------
-    const uint8_t* a_src[2];
-    const uint8_t* sa_src;
+    // ---------------- copy sources (per-lane offsets, scalar K offsets) ----------------
+    const uint8_t* wb = MODE == 1 ? p.w1 : p.w2;
+    const int32_t* wsf = MODE == 1 ? p.w1_sf : p.w2_sf;
+    const v4i rsB = make_buffer_rsrc(wb + (size_t)e * e_rows * wrow_bytes, e_rows * wrow_bytes);
+    const v4i rsSB = make_buffer_rsrc(wsf + (size_t)e * e_rows * (K / 128), e_rows * wsf_bytes);
+    uint32_t a_off[RA], b_off[RB], sa_off, sb_off;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = (wave * 2 + j) * 8 + dma_arow;
+    for (int j = 0; j < RA; ++j) {
+      const int r = (wave * RA + j) * 8 + (lane >> 3);
       const int pr = min(row0 + r, last_pair);
-      const int chunk = ((lane & 7) ^ swz(r)) << 4;
-      if (MODE == 1) a_src[j] = p.x + (size_t)p.pair_token[pr] * H + chunk;
-      else a_src[j] = p.q + (size_t)pr * I + chunk;
+      const uint32_t src_row = MODE == 1 ? (uint32_t)p.pair_token[pr] : (uint32_t)pr;
+      a_off[j] = src_row * (uint32_t)K + (((lane & 7) ^ swz(r)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int r = (wave * RB + j) * 16 + (lane >> 2);            // tile weight row
+      const uint32_t wr = MODE == 1 ? (uint32_t)((r < 128 ? 0 : I) + tn * 128 + (r & 127))
+                                    : (uint32_t)(tn * FFN_BN + r);
+      b_off[j] = wr * wrow_bytes + (((lane & 3) ^ swzb(r)) << 4);
     }
     {
-      const int r = wave * 16 + (lane & 15);
+      const int r = wave * SAW + (lane < SAW ? lane : 0);
       const int pr = min(row0 + r, last_pair);
-      if (MODE == 1) sa_src = reinterpret_cast<const uint8_t*>(p.x_sf + (size_t)p.pair_token[pr] * (H / 512));
-      else sa_src = p.sq + (size_t)pr * p.sq_stride;
-    }
-    const uint8_t* b_src[4];
-    const uint8_t* sb_src;
-    const size_t wrow_bytes = MODE == 1 ? (size_t)(H / 2) : (size_t)(I / 2);
-    const size_t wsf_words = MODE == 1 ? (size_t)(H / 128) : (size_t)(I / 128);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = (wave * 4 + j) * 16 + dma_brow;                // tile weight row
-      size_t wr;                                                    // expert-local weight row
-      if (MODE == 1) wr = (r < 128 ? 0 : I) + tn * 128 + (r & 127);
-      else wr = min(tn * FFN_BROWS + r, H - 1);
-      const size_t erows = MODE == 1 ? (size_t)2 * I : (size_t)H;
-      const uint8_t* wb = MODE == 1 ? p.w1 : p.w2;
-      b_src[j] = wb + ((size_t)e * erows + wr) * wrow_bytes + (((lane & 3) ^ swzb(r)) << 4);
+      sa_off = MODE == 1 ? (uint32_t)p.pair_token[pr] * (uint32_t)(H / 512) * 4u
+                         : (uint32_t)pr * (uint32_t)p.sq_stride;
     }
     {
-      const int r = wave * 64 + lane;
-      size_t wr;
-      if (MODE == 1) wr = (r < 128 ? 0 : I) + tn * 128 + (r & 127);
-      else wr = min(tn * FFN_BROWS + r, H - 1);
-      const size_t erows = MODE == 1 ? (size_t)2 * I : (size_t)H;
-      const int32_t* ws = MODE == 1 ? p.w1_sf : p.w2_sf;
-      sb_src = reinterpret_cast<const uint8_t*>(ws + ((size_t)e * erows + wr) * wsf_words);
+      const int r = wave * SBW + (lane < SBW ? lane : 0);
+      const uint32_t wr = MODE == 1 ? (uint32_t)((r < 128 ? 0 : I) + tn * 128 + (r & 127))
+                                    : (uint32_t)(tn * FFN_BN + r);
+      sb_off = wr * wsf_bytes;
     }
-
     auto issue = [&](int kb, uint32_t slot) {
       uint8_t* base = smem + slot;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dma16_to_lds(a_src[j] + kb * 128, base + (wave * 2 + j) * 1024);
+      for (int j = 0; j < RA; ++j) buf16_to_lds(rsA, a_off[j], (uint32_t)kb * 128u, base + (wave * RA + j) * 1024);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16_to_lds(b_src[j] + kb * 64, base + OFF_B + (wave * 4 + j) * 1024);
-      // A scale word: four 128-blocks per word for x_sf / sq; lanes 16..63 idle
-      if (lane < 16) dma4_to_lds(sa_src + (kb >> 2) * 4, base + OFF_SA + wave * 64);
-      dma4_to_lds(sb_src + kb * 4, base + OFF_SB + wave * 256);
+      for (int j = 0; j < RB; ++j)
+        buf16_to_lds(rsB, b_off[j], (uint32_t)kb * 64u, base + OFF_B + (wave * RB + j) * 1024);
+      // the A scale word holds four 128-wide K blocks (x_sf, and sq in groups of four)
+      if (SAW == 64 || lane < SAW) buf4_to_lds(rsSA, sa_off, (uint32_t)(kb >> 2) * 4u, base + OFF_SA + wave * SAW * 4);
+      if (SBW == 64 || lane < SBW) buf4_to_lds(rsSB, sb_off, (uint32_t)kb * 4u, base + OFF_SB + wave * SBW * 4);
     };
 
-    v4f acc[4][4];
+    v4f acc[MT][NT];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-    for (int s = 0; s < FFN_STAGES - 1; ++s)
+    for (int s = 0; s < STAGES - 1; ++s)
       if (s < KB) issue(s, s * STAGE);
 
-    uint32_t rd = 0, wr = (FFN_STAGES - 1) * STAGE;
+    uint32_t rd = 0, wr = (STAGES - 1) * STAGE;
+#pragma clang loop unroll(disable)
     for (int kb = 0; kb < KB; ++kb) {
-      if (kb + 1 < KB) wait_vmcnt<LPS>();
+      // stage kb has landed once at most (#stages issued after it) copies remain
+      const int after = min(STAGES - 2, KB - 1 - kb);
+      if (after >= 2) wait_vmcnt<2 * LPS>();
+      else if (after == 1) wait_vmcnt<LPS>();
       else wait_vmcnt<0>();
       block_barrier();
-      if (kb + FFN_STAGES - 1 < KB) issue(kb + FFN_STAGES - 1, wr);
+      if (kb + STAGES - 1 < KB) issue(kb + STAGES - 1, wr);
 
       const uint8_t* sbase = smem + rd;
       const int byte_sel = (kb & 3) * 8;
-      int sa_s[4];
-      v8i af[4];
+      int sa_s[MT];
+      v8i af[MT];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(sbase + OFF_SA + (mt * 16 + lrow) * 4);
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(sbase + sa_rd + mt * 64);
         sa_s[mt] = (int)((w >> byte_sel) & 0xffu);
-        v4i l4 = *reinterpret_cast<const v4i*>(sbase + a_lo + mt * 2048);
-        v4i h4 = *reinterpret_cast<const v4i*>(sbase + a_hi + mt * 2048);
+        const v4i l4 = *reinterpret_cast<const v4i*>(sbase + a_lo + mt * 2048);
+        const v4i h4 = *reinterpret_cast<const v4i*>(sbase + a_hi + mt * 2048);
         af[mt] = v8i{l4.x, l4.y, l4.z, l4.w, h4.x, h4.y, h4.z, h4.w};
       }
-      int sb_s[4];
-      v8i bfr[4];
+      int sb_s[NT];
+      v8i bfr[NT];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(sbase + sb_rd[nt]);
+      for (int nt = 0; nt < NT; ++nt) {
+        const int row_off = MODE == 1 ? ((nt < 4 ? 0 : 128) + (nt & 3) * 16) : nt * 16;
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(sbase + sb_rd0 + row_off * 4);
         sb_s[nt] = (int)((w >> (8 * lgrp)) & 0xffu);
-        v4i b4 = *reinterpret_cast<const v4i*>(sbase + b_rd[nt]);
+        const v4i b4 = *reinterpret_cast<const v4i*>(sbase + b_rd[nt]);
         bfr[nt] = v8i{b4.x, b4.y, b4.z, b4.w, 0, 0, 0, 0};
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = mfma_scaled_e4m3_e2m1_16x16x128(af[mt], sa_s[mt], bfr[nt], sb_s[nt], acc[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = mfma_scaled_e2m1_e4m3_16x16x128(bfr[nt], sb_s[nt], af[mt], sa_s[mt], acc[mt][nt]);
 
-      rd = (rd + STAGE == FFN_STAGES * STAGE) ? 0u : rd + STAGE;
-      wr = (wr + STAGE == FFN_STAGES * STAGE) ? 0u : wr + STAGE;
+      rd = (rd + STAGE == STAGES * STAGE) ? 0u : rd + STAGE;
+      wr = (wr + STAGE == STAGES * STAGE) ? 0u : wr + STAGE;
     }
     block_barrier();   // the ring is free before the next tile's prologue
 
     if (MODE == 2) {
-      // fp32 output rows of the pairs
+      // fp32 output rows of the pairs: 4 consecutive columns (16 bytes) per lane and block
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = wave_m * MT * 16 + mt * 16 + lrow;
+        if (r >= rows) continue;
+        float* orow = p.o + (size_t)(row0 + r) * H + tn * FFN_BN + wave_n * 128 + 4 * lgrp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = mt * 16 + 4 * lgrp + i;
-          if (r >= rows) continue;
-          float* orow = p.o + (size_t)(row0 + r) * H;
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const int col = tn * FFN_BROWS + wave * 64 + nt * 16 + lrow;
-            if (col < H) orow[col] = acc[mt][nt][i];
-          }
-        }
+        for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<v4f*>(orow + nt * 16) = acc[mt][nt];
+      }
     } else {
-      // SwiGLU in registers: gate blocks nt = 0,1 pair with up blocks nt = 2,3
-      float s[4][2][4];
-      float rmax[4][4];
+      // SwiGLU in registers: gate block nt pairs with up block nt + 4 (same columns)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = wave_m * MT * 16 + mt * 16 + lrow;
+        float sv[4][4];
+        float m = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float m = 0.f;
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float v = silu_f32(acc[mt][h][i]) * acc[mt][h + 2][i];
-            s[mt][h][i] = v;
+          for (int i = 0; i < 4; ++i) {
+            const float v = silu_f32(acc[mt][nt][i]) * acc[mt][nt + 4][i];
+            sv[nt][i] = v;
             m = fmaxf(m, fabsf(v));
           }
-          // max over the 16 lanes holding this row's columns (lanes differ in lrow)
-#pragma unroll
-          for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-          rmax[mt][i] = m;
-        }
-      if (lrow == 0) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) red[wave][mt * 16 + 4 * lgrp + i] = rmax[mt][i];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = mt * 16 + 4 * lgrp + i;
-          const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
-          const int ex = pow2_exponent_448(amax);
-          if (r >= rows) continue;
+        // this wave's 64 columns of the row sit in the four lanes lrow + 16g
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (lgrp == 0) red[wave_n][r] = m;
+        __syncthreads();
+        const float amax = fmaxf(red[0][r], red[1][r]);
+        const int ex = pow2_exponent_448(amax);
+        if (r < rows) {
           const size_t pr = (size_t)(row0 + r);
-          uint8_t* qrow = p.q + pr * I + tn * 128;
+          uint8_t* qrow = p.q + pr * I + tn * 128 + wave_n * 64 + 4 * lgrp;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int col = wave * 32 + h * 16 + lrow;
-            qrow[col] = (uint8_t)e4m3_rne(ldexpf(s[mt][h][i], -ex));
+          for (int nt = 0; nt < 4; ++nt) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w |= e4m3_rne(ldexpf(sv[nt][i], -ex)) << (8 * i);
+            *reinterpret_cast<uint32_t*>(qrow + nt * 16) = w;
           }
-          if (wave == 0 && lrow == 0) p.sq[pr * p.sq_stride + tn] = (uint8_t)(ex + 127);
+          if (wave_n == 0 && lgrp == 0) p.sq[pr * p.sq_stride + tn] = (uint8_t)(ex + 127);
         }
-      __syncthreads();   // red[] is reused by the next tile
+        __syncthreads();   // red[] is rewritten by the next row block
+      }
     }
   }
 }
@@ -431,10 +440,16 @@ static hipError_t launch_ffn(FfnParams& p, int num_cus, hipStream_t stream) {
   hipLaunchKernelGGL(ffn_route_kernel, dim3(1), dim3(1024), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = num_cus * 2;
-  hipLaunchKernelGGL(ffn_gemm_kernel<1>, dim3(grid), dim3(FFN_THREADS), 0, stream, p);
+  static const hipError_t attr1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_gemm_kernel<1>),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, FFN_LDS);
+  static const hipError_t attr2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_gemm_kernel<2>),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, FFN_LDS);
+  if (attr1 != hipSuccess) return attr1;
+  if (attr2 != hipSuccess) return attr2;
+  const int grid = num_cus;
+  hipLaunchKernelGGL(ffn_gemm_kernel<1>, dim3(grid), dim3(FFN_THREADS), FFN_LDS, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(ffn_gemm_kernel<2>, dim3(grid), dim3(FFN_THREADS), 0, stream, p);
+  hipLaunchKernelGGL(ffn_gemm_kernel<2>, dim3(grid), dim3(FFN_THREADS), FFN_LDS, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 cgrid((p.H / 8 + 255) / 256, p.T);
   hipLaunchKernelGGL(ffn_combine_kernel, cgrid, dim3(256), 0, stream, p);
@@ -464,6 +479,12 @@ int dg_fp8_fp4_expert_ffn(const uint8_t* x, const int32_t* x_sf, const int32_t* 
     if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || I <= 0) return DG_ERR_INVALID_ARG;
     if (H % 512 != 0 || I % 128 != 0 || E > FFN_MAX_EXPERTS) return DG_ERR_UNSUPPORTED;
     if ((long long)T * k > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
+    // the GEMM kernels address x, the intermediate and one expert's weights
+    // through buffer resources with 32-bit offsets
+    const long long lim = 1LL << 31;
+    if ((long long)T * H > lim || (long long)T * k * I > lim || (long long)T * k * ((I / 128 + 3) & ~3) > lim ||
+        (long long)I * H > lim)
+      return DG_ERR_UNSUPPORTED;
     uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w1) |
                    reinterpret_cast<uintptr_t>(w2) | reinterpret_cast<uintptr_t>(y);
     if ((al & 15) || (reinterpret_cast<uintptr_t>(x_sf) & 3) || (reinterpret_cast<uintptr_t>(topk_idx) & 3) ||

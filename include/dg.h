@@ -152,7 +152,8 @@ size_t dg_fp8_fp4_expert_ffn_workspace_bytes(int num_tokens, int num_topk, int n
  *   y         [T, H]            bf16 output
  *   workspace device buffer of at least dg_fp8_fp4_expert_ffn_workspace_bytes(...) bytes,
  *             256-byte aligned; its contents on entry are ignored
- * Requirements: T, num_topk, E > 0; H % 512 == 0; I % 128 == 0.
+ * Requirements: T, num_topk, E > 0; E <= 256; H % 512 == 0; I % 128 == 0; T*H,
+ *   T*num_topk*I and I*H at most 2^31 (else DG_ERR_UNSUPPORTED).
  */
 int dg_fp8_fp4_expert_ffn(const uint8_t* x, const int32_t* x_sf, const int32_t* topk_idx,
                           const float* topk_w, const uint8_t* w1, const int32_t* w1_sf,
