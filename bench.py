@@ -64,9 +64,11 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+def kernel_source_hash(cfg):
+    """Hash of the sources that decide the kernels (and their plans) a config runs."""
     h = hashlib.sha256()
-    for f in ("fp8_gemm.hip", "dg_device.hpp", "ffn.hip"):
+    files = ("ffn.hip", "dg_device.hpp") if cfg == 4 else ("fp8_gemm.hip", "planner.cpp", "dg_device.hpp")
+    for f in files:
         p = os.path.join(ROOT, "fp4_gemm_dense_amd", "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
@@ -377,7 +379,7 @@ def main():
         try:
             tj = json.load(open(tfile))
             entry = tj.get(str(cfg))
-            if entry and entry.get("kernel_source_hash") == kernel_source_hash():
+            if entry and entry.get("kernel_source_hash") == kernel_source_hash(cfg):
                 traffic = entry.get("bytes_per_launch")
         except (ValueError, OSError):
             traffic = None

@@ -79,6 +79,9 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     int slots = num_cus * blocks_per_cu_for(id);
     const int splits = mode == MODE_DENSE ? choose_splits(tiles, slots, k / 128) : 1;
     long long units = tiles * splits;
+    // a two-slot (long K) shape must at least fill the chip once: in a single
+    // partial wave its large tiles leave compute units idle for the whole call
+    if (tc.min_k > 0 && units < slots) continue;
     long long waves = (units + slots - 1) / slots;
     double fill = (double)units / (double)(waves * slots);
     // bigger tiles re-read less from L2/HBM: weight by tile area (arithmetic intensity)
