@@ -140,6 +140,7 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
     if (!p.ws) return DG_ERR_HIP;
   }
   p.group_m = 8;
+  if (const char* gm = std::getenv("DG_GROUP_M")) p.group_m = std::max(1, std::atoi(gm));   // raster band (tuning)
   // DG_KROT=<s>: K-block rotation step between neighbouring tiles (tuning)
   p.k_rot = 0;
   if (const char* kr = std::getenv("DG_KROT")) p.k_rot = std::max(0, std::atoi(kr));

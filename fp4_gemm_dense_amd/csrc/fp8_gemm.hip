@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     int kb0, nkb;   // K blocks [kb0, kb0 + nkb) of this work unit (split K: a slice)
     int rot;        // first K block: tiles that share A rows or B rows start at different K
   };
-  const bool split = p.splits > 1;
+  const bool split = STAGES >= 3 && p.splits > 1;   // (the planner never splits two-slot shapes)
   auto decode = [&](int t, Tile& tile) -> bool {
     if (split) {
       // work unit t = output tile t / splits, K slice t % splits

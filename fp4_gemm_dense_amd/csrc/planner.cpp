@@ -50,7 +50,7 @@ GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num
   long long slots = (long long)num_cus * blocks_per_cu_for(kernel_id);
   plan.splits = 1;
   plan.kb_per_split = k / 128;
-  if (mode == MODE_DENSE) {
+  if (mode == MODE_DENSE && tc.min_k == 0) {   // two-slot (long K) shapes never split
     plan.splits = choose_splits(total, (int)std::min<long long>(slots, 1 << 20), k / 128);
     plan.kb_per_split = cdiv(k / 128, plan.splits);
   }
@@ -77,7 +77,7 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     double util = (double)rows / (tm * tc.block_m) * (double)n / (tn * tc.block_n);
     // wave quantisation: fraction of the last wave of work units that is busy
     int slots = num_cus * blocks_per_cu_for(id);
-    const int splits = mode == MODE_DENSE ? choose_splits(tiles, slots, k / 128) : 1;
+    const int splits = mode == MODE_DENSE && tc.min_k == 0 ? choose_splits(tiles, slots, k / 128) : 1;
     long long units = tiles * splits;
     // a two-slot (long K) shape must at least fill the chip once: in a single
     // partial wave its large tiles leave compute units idle for the whole call
