@@ -29,6 +29,7 @@
 //     remapped so that each XCD (workgroups are dealt round-robin to the 8
 //     XCDs) works on a contiguous stretch of the raster and shares its L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
@@ -224,6 +225,24 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     for (int j = 0; j < RB; ++j) buf16_to_lds(rsB, b_off[j], kofs, smem + slot_off + b_dst + j * 1024);
     if (SPW == 64 || lane < SPW) buf4_to_lds(rsSA, sa_off, sofs, smem + slot_off + sa_dst);
   };
+  // The same copies one instruction at a time (idx < RA: A region idx, then the
+  // B regions), so that a K block's copies can be spread between its matrix
+  // instructions; the row-scale copy (issue_sa) goes first.
+  auto issue_ab = [&](int idx, int kb, uint32_t slot_off) {
+    const int kp = kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d);
+    const uint32_t kofs = (uint32_t)kp * 128u;
+#pragma unroll
+    for (int j = 0; j < RA; ++j)
+      if (idx == j) buf16_to_lds(rsA, a_off[j], kofs, smem + slot_off + a_dst + j * 1024);
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+      if (idx == RA + j) buf16_to_lds(rsB, b_off[j], kofs, smem + slot_off + b_dst + j * 1024);
+  };
+  auto issue_sa = [&](int kb, uint32_t slot_off) {
+    const int kp = kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d);
+    const uint32_t sofs = (uint32_t)kp * (uint32_t)M * 4u;
+    if (SPW == 64 || lane < SPW) buf4_to_lds(rsSA, sa_off, sofs, smem + slot_off + sa_dst);
+  };
   // DMA of half h of the C tile into the slot at slot_off (dense form only).
   const bool has_c = MODE == MODE_DENSE && p.c != nullptr && !split;
   auto issue_c = [&](const Tile& tile, int h, uint32_t slot_off) {
@@ -290,12 +309,24 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     const int kb0 = cur.kb0;
     uint32_t rd_slot = 0;                          // slot of stage kb
     uint32_t wr_slot = (STAGES - 1) * STAGE;       // slot of stage kb + STAGES - 1
-#pragma clang loop unroll(disable)
-    for (int kb = 0; kb < KT; ++kb) {
+    // One K block.  STEADY: a later stage is copied in this block, its copy
+    // instructions spread between the matrix instructions (a copy that finds
+    // the memory pipeline full then stalls the wave while matrix work is
+    // queued, instead of before any is); otherwise the C tile may be copied.
+    auto kstep = [&](int kb, auto steady_tag) {
+      constexpr bool STEADY = decltype(steady_tag)::value;
+      // copies spread over the block (not with streamed A fragments, whose
+      // scheduling fences would split the pattern)
+      constexpr int ILV = RA + RB;
+      constexpr int ILV_STEP = (!STREAM_A && NBLK / ILV > 0) ? NBLK / ILV : NBLK + 1;
       wait_stage(kb, KT, stores_after);
       block_barrier();
-      if (kb + STAGES - 1 < KT) {
-        issue(kb + STAGES - 1, wr_slot);
+      if (STEADY) {
+        issue_sa(kb + STAGES - 1, wr_slot);
+        if (ILV_STEP * ILV > NBLK) {
+#pragma unroll
+          for (int idx = 0; idx < ILV; ++idx) issue_ab(idx, kb + STAGES - 1, wr_slot);
+        }
       } else if (has_c) {
         // slot (KT + h) % STAGES takes half h: free from block KT - 2 + h on with
         // three or more slots; with two, half 0 goes in during the last block and
@@ -364,13 +395,27 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
             for (int i = 0; i < 4; ++i) acc[pm][pn][i] = fmaf(part[r][i], scur[pm], acc[pm][pn][i]);
           }
           part[r] = mfma_e4m3_16x16x128(bf[nt], af[mt], v4f{0.f, 0.f, 0.f, 0.f});
+          const bool copy_here = STEADY && ILV_STEP * ILV <= NBLK && j % ILV_STEP == ILV_STEP - 1 && j / ILV_STEP < ILV;
+          if (copy_here) issue_ab(j / ILV_STEP, kb + STAGES - 1, wr_slot);
+          if (!STREAM_A) {
+            // keep the schedule: the promotion FMAs of block j ride with its matrix
+            // instruction, and a copy follows every ILV_STEP-th one
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (promotion)
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            if (copy_here) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM read (copy)
+          }
         }
         if (STREAM_A) __builtin_amdgcn_sched_barrier(0);
       }
       sprev = scur[MT - 1];
       rd_slot = (rd_slot + STAGE == STAGES * STAGE) ? 0u : rd_slot + STAGE;
       wr_slot = (wr_slot + STAGE == STAGES * STAGE) ? 0u : wr_slot + STAGE;
-    }
+    };
+    int kb = 0;
+#pragma clang loop unroll(disable)
+    for (; kb + STAGES - 1 < KT; ++kb) kstep(kb, std::true_type{});
+#pragma clang loop unroll(disable)
+    for (; kb < KT; ++kb) kstep(kb, std::false_type{});
     // promote the last LAG partials
 #pragma unroll
     for (int j = 0; j < LAG; ++j)
@@ -528,7 +573,7 @@ hipError_t launch_splitk_reduce(const float* ws, const uint16_t* c, uint16_t* d,
 static const TileConfig kTileConfigs[] = {
 #define X(id, MT, NT, WM, WN, ST, OCC) {WM * MT * 16, WN * NT * 16, OCC, WM * WN * 64,                     \
                                         ST * ((WM * MT * 16 + WN * NT * 16) * 128 + WM * MT * 16 * 4), \
-                                        ST == 2 ? 4096 : 0},
+                                        ST == 2 ? (1 << 30) : 0},
     DG_TILE_CONFIGS(X)
 #undef X
 };
