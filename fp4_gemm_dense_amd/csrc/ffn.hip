@@ -25,6 +25,8 @@
 //   4. combine: y[t] = sum over slots j (in order) of w[t,j] * o[pair(t,j)], bf16.
 // Operand tiles and their scale words are staged through a 3-stage LDS ring with
 // global_load_lds (the token gather happens in the DMA addresses).
+#include <type_traits>
+
 #include "../../include/dg.h"
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
@@ -303,6 +305,22 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
       if (SAW == 64 || lane < SAW) buf4_to_lds(rsSA, sa_off, (uint32_t)(kb >> 2) * 4u, base + OFF_SA + wave * SAW * 4);
       if (SBW == 64 || lane < SBW) buf4_to_lds(rsSB, sb_off, (uint32_t)kb * 4u, base + OFF_SB + wave * SBW * 4);
     };
+    // the same copies split up: the two scale words first, then A/B region idx
+    // (A regions, then B regions) one instruction at a time
+    auto issue_scales = [&](int kb, uint32_t slot) {
+      uint8_t* base = smem + slot;
+      if (SAW == 64 || lane < SAW) buf4_to_lds(rsSA, sa_off, (uint32_t)(kb >> 2) * 4u, base + OFF_SA + wave * SAW * 4);
+      if (SBW == 64 || lane < SBW) buf4_to_lds(rsSB, sb_off, (uint32_t)kb * 4u, base + OFF_SB + wave * SBW * 4);
+    };
+    auto issue_ab = [&](int idx, int kb, uint32_t slot) {
+      uint8_t* base = smem + slot;
+#pragma unroll
+      for (int j = 0; j < RA; ++j)
+        if (idx == j) buf16_to_lds(rsA, a_off[j], (uint32_t)kb * 128u, base + (wave * RA + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+        if (idx == RA + j) buf16_to_lds(rsB, b_off[j], (uint32_t)kb * 64u, base + OFF_B + (wave * RB + j) * 1024);
+    };
 
     v4f acc[MT][NT];
 #pragma unroll
@@ -315,15 +333,21 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
       if (s < KB) issue(s, s * STAGE);
 
     uint32_t rd = 0, wr = (STAGES - 1) * STAGE;
-#pragma clang loop unroll(disable)
-    for (int kb = 0; kb < KB; ++kb) {
+    // One K block.  STEADY: a later stage is copied in this block, its A/B copy
+    // instructions spread between the matrix instructions (a copy that finds the
+    // memory pipeline full stalls the wave; spread out, matrix work is queued
+    // meanwhile), pinned with scheduling group barriers.
+    auto kstep = [&](int kb, auto steady_tag) {
+      constexpr bool STEADY = decltype(steady_tag)::value;
+      constexpr int ILV = RA + RB;
+      constexpr int ILV_STEP = (MT * NT) / ILV;
       // stage kb has landed once at most (#stages issued after it) copies remain
       const int after = min(STAGES - 2, KB - 1 - kb);
       if (after >= 2) wait_vmcnt<2 * LPS>();
       else if (after == 1) wait_vmcnt<LPS>();
       else wait_vmcnt<0>();
       block_barrier();
-      if (kb + STAGES - 1 < KB) issue(kb + STAGES - 1, wr);
+      if (STEADY) issue_scales(kb + STAGES - 1, wr);
 
       const uint8_t* sbase = smem + rd;
       const int byte_sel = (kb & 3) * 8;
@@ -350,12 +374,23 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NT; ++nt) {
+          const int j = mt * NT + nt;
           acc[mt][nt] = mfma_scaled_e2m1_e4m3_16x16x128(bfr[nt], sb_s[nt], af[mt], sa_s[mt], acc[mt][nt]);
+          const bool copy_here = STEADY && j % ILV_STEP == ILV_STEP - 1 && j / ILV_STEP < ILV;
+          if (copy_here) issue_ab(j / ILV_STEP, kb + STAGES - 1, wr);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
+          if (copy_here) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // then 1 copy
+        }
 
       rd = (rd + STAGE == STAGES * STAGE) ? 0u : rd + STAGE;
       wr = (wr + STAGE == STAGES * STAGE) ? 0u : wr + STAGE;
-    }
+    };
+    int kb = 0;
+#pragma clang loop unroll(disable)
+    for (; kb + STAGES - 1 < KB; ++kb) kstep(kb, std::true_type{});
+#pragma clang loop unroll(disable)
+    for (; kb < KB; ++kb) kstep(kb, std::false_type{});
     block_barrier();   // the ring is free before the next tile's prologue
 
     if (MODE == 2) {
