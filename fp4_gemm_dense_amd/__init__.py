@@ -45,7 +45,7 @@ _SIGNATURES = {
 
 class DgPlan(ctypes.Structure):
     _fields_ = [("block_m", _I), ("block_n", _I), ("num_tiles", _I), ("num_workgroups", _I),
-                ("kernel_id", _I), ("splits", _I)]
+                ("kernel_id", _I), ("splits", _I), ("full_tiles", _I)]
 
 
 class DgError(RuntimeError):

@@ -121,22 +121,20 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
         !(mode == MODE_CONTIG && (128 % tile_config(id).block_m) != 0))
       plan = plan_with_kernel(p.m, p.n, p.k, p.num_groups, mode, cus, id);
   }
-  // split K needs one fp32 slice of m x n per K slice, addressed with 32-bit offsets
-  const size_t slice_bytes = (size_t)p.m * p.n * 4;
-  if (plan.splits > 1 && (slice_bytes > (size_t(1) << 31) || slice_bytes * plan.splits > (size_t(1) << 32))) {
-    plan.splits = 1;
-    plan.kb_per_split = p.k / 128;
-    plan.num_workgroups = std::min(plan.num_tiles, cus * std::max(1, tile_config(plan.kernel_id).blocks_per_cu));
-  }
   p.tiles_m = plan.tiles_m;
   p.tiles_n = plan.tiles_n;
   p.splits = plan.splits;
   p.kb_per_split = plan.kb_per_split;
-  p.total_tiles = (int)std::min<long long>((long long)plan.num_tiles * plan.splits, 0x7fffffff);
+  p.full_tiles = plan.full_tiles;
+  p.total_tiles = (int)std::min<long long>(
+      (long long)plan.full_tiles + (long long)(plan.num_tiles - plan.full_tiles) * plan.splits, 0x7fffffff);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (plan.splits > 1) {
+    // one fp32 block_m x block_n partial per slice of every split tile (at most
+    // one per workgroup slot, so a few tens of MB at most)
+    const size_t ws_bytes = (size_t)(plan.num_tiles - plan.full_tiles) * plan.splits * plan.block_m * plan.block_n * 4;
     hipError_t werr = hipSuccess;
-    p.ws = split_workspace(di.device, hs, slice_bytes * plan.splits, &werr);
+    p.ws = split_workspace(di.device, hs, ws_bytes, &werr);
     if (!p.ws) return DG_ERR_HIP;
   }
   p.group_m = 8;
@@ -145,11 +143,11 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
   p.k_rot = 0;
   if (const char* kr = std::getenv("DG_KROT")) p.k_rot = std::max(0, std::atoi(kr));
   if (log_enabled())
-    std::fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %dx%d (kernel %d), %d tiles x %d K slices, "
-                 "%d workgroups\n", name, p.m, p.n, p.k, p.num_groups, plan.block_m, plan.block_n, plan.kernel_id,
-                 plan.num_tiles, plan.splits, plan.num_workgroups);
+    std::fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %dx%d (kernel %d), %d tiles (%d whole, the rest "
+                 "x %d K slices), %d workgroups\n", name, p.m, p.n, p.k, p.num_groups, plan.block_m, plan.block_n,
+                 plan.kernel_id, plan.num_tiles, plan.full_tiles, plan.splits, plan.num_workgroups);
   hipError_t e = launch_fp8_gemm(p, plan, mode, hs);
-  if (e == hipSuccess && plan.splits > 1) e = launch_splitk_reduce(p.ws, p.c, p.d, p.m, p.n, plan.splits, cus, hs);
+  if (e == hipSuccess && plan.splits > 1) e = launch_splitk_reduce(p, plan, cus, hs);
   return e == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
@@ -258,6 +256,7 @@ int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out
   out->num_workgroups = p.num_workgroups;
   out->kernel_id = p.kernel_id;
   out->splits = p.splits;
+  out->full_tiles = p.full_tiles;
   return DG_OK;
 }
 

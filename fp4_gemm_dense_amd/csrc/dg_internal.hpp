@@ -27,9 +27,10 @@ struct Fp8GemmParams {
   int total_tiles;            // all groups
   int group_m;                // raster: tiles along M visited before moving along N
   int k_rot;                  // K-block rotation step between neighbouring tiles (0: none)
-  int splits;                 // K slices per output tile (1: no split)
+  int splits;                 // K slices per split tile (1: no split)
   int kb_per_split;           // K blocks per slice (the last one may hold fewer)
-  float* ws;                  // split K: fp32 partial sums [splits][m][n]
+  int full_tiles;             // tiles [0, full_tiles) of the raster run whole; the rest are split
+  float* ws;                  // split K: fp32 partial tiles [(tile - full_tiles) * splits + slice][BM][BN]
 };
 
 // Tile shapes compiled into the library (kernel_id indexes this table).
@@ -57,16 +58,29 @@ struct GemmPlan {
   int block_m, block_n;
   int tiles_m, tiles_n;
   int num_tiles;              // output tiles (all groups)
-  int splits;                 // K slices per output tile (dense only; 1: none)
+  int splits;                 // K slices per split tile (dense only; 1: none)
   int kb_per_split;
+  int full_tiles;             // tiles computed whole; tiles [full_tiles, num_tiles) are split
   int num_workgroups;
 };
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m);
 GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id);
 
-// Split K: D = bf16(sum of the ws slices + C); returns a hipError_t.
-hipError_t launch_splitk_reduce(const float* ws, const uint16_t* c, uint16_t* d, int m, int n, int splits,
-                                int num_cus, hipStream_t stream);
+// Split K: for every split tile, D = bf16(sum of its ws slices in slice order + C);
+// returns a hipError_t.
+hipError_t launch_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& plan, int num_cus, hipStream_t stream);
+
+// Raster order of the output tiles (one group): bands of group_m tile rows, walked
+// column by column inside a band, tile rows fastest.  Tile index tl -> (tile row, tile column).
+__host__ __device__ inline void raster_tile(int tl, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {
+  const int per_group = group_m * tiles_n;
+  const int gi = tl / per_group;
+  const int first_m = gi * group_m;
+  const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+  const int r = tl - gi * per_group;
+  *tm = first_m + r % gm;
+  *tn = r / gm;
+}
 
 // Launches the kernel chosen by plan on stream; returns a hipError_t.
 hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mode, hipStream_t stream);

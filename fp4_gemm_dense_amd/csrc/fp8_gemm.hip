@@ -114,18 +114,23 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     int g, m0, n0, rows_valid;
     int kb0, nkb;   // K blocks [kb0, kb0 + nkb) of this work unit (split K: a slice)
     int rot;        // first K block: tiles that share A rows or B rows start at different K
+    int part;       // split K: index of this slice's fp32 partial tile in the workspace; -1: whole tile
   };
-  const bool split = STAGES >= 3 && p.splits > 1;   // (the planner never splits two-slot shapes)
+  // Work units: units [0, full_tiles) are the tiles of the same index, computed
+  // whole; unit full_tiles + u is K slice u % splits of tile full_tiles + u / splits.
+  // (The planner never splits two-slot shapes.)
+  const bool can_split = STAGES >= 3 && p.splits > 1;
   auto decode = [&](int t, Tile& tile) -> bool {
-    if (split) {
-      // work unit t = output tile t / splits, K slice t % splits
-      const int sl = t % p.splits;
-      t /= p.splits;
+    tile.kb0 = 0;
+    tile.nkb = KB;
+    tile.part = -1;
+    if (can_split && t >= p.full_tiles) {
+      const int u = t - p.full_tiles;
+      const int sl = u % p.splits;
+      t = p.full_tiles + u / p.splits;
       tile.kb0 = sl * p.kb_per_split;
       tile.nkb = min(p.kb_per_split, KB - tile.kb0);
-    } else {
-      tile.kb0 = 0;
-      tile.nkb = KB;
+      tile.part = u;
     }
     int g = 0, tl = t;
     if (MODE == MODE_MASKED) {
@@ -133,14 +138,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       g = t / per;
       tl = t - g * per;
     }
-    const int per_group = p.group_m * p.tiles_n;
-    const int gi = tl / per_group;
-    const int first_m = gi * p.group_m;
-    const int gm = min(p.tiles_m - first_m, p.group_m);
-    const int r = tl - gi * per_group;
-    tile.m0 = (first_m + r % gm) * BM;
-    tile.n0 = (r / gm) * BN;
-    tile.rot = split ? 0 : (p.k_rot * (((first_m + r % gm) + r / gm) & 7)) % KB;
+    int tm, tn;
+    raster_tile(tl, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    tile.m0 = tm * BM;
+    tile.n0 = tn * BN;
+    tile.rot = tile.part >= 0 ? 0 : (p.k_rot * ((tm + tn) & 7)) % KB;
     tile.rows_valid = M;
     if (MODE == MODE_MASKED) {
       const int mm = p.masked_m[g];
@@ -243,8 +245,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     const uint32_t sofs = (uint32_t)kp * (uint32_t)M * 4u;
     if (SPW == 64 || lane < SPW) buf4_to_lds(rsSA, sa_off, sofs, smem + slot_off + sa_dst);
   };
-  // DMA of half h of the C tile into the slot at slot_off (dense form only).
-  const bool has_c = MODE == MODE_DENSE && p.c != nullptr && !split;
+  // DMA of half h of the C tile into the slot at slot_off (dense form, whole
+  // tiles only: a split tile's C is added when its slices are summed).
+  const bool dense_c = MODE == MODE_DENSE && p.c != nullptr;
+  bool has_c = false;   // the current tile copies C
   auto issue_c = [&](const Tile& tile, int h, uint32_t slot_off) {
     constexpr int RPI = 1024 / (BN * 2);             // C rows per 1-KB piece
     const v4i rsC = make_buffer_rsrc(p.c, (uint32_t)M * (uint32_t)N * 2u);
@@ -295,6 +299,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     prologue();
   }
   while (have) {
+    has_c = dense_c && cur.part < 0;
     v4f acc[MT][NT];       // fp32 accumulators
     v4f part[LAG];         // fresh partials, promoted LAG matrix instructions late
     float sprev = 0.f;     // sa * sb of the previous K block for the last row block
@@ -435,8 +440,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       wait_vmcnt<0>();   // this wave's C pieces have landed
       block_barrier();   // ... and every other wave's
     }
+    // (a split tile's slice stores its fp32 partial instead, below)
 #pragma unroll
-    for (int mt = 0; mt < (split ? 0 : MT); ++mt) {
+    for (int mt = 0; mt < (done.part >= 0 ? 0 : MT); ++mt) {
       const int rr0 = wave_m * MT * 16 + mt * 16;       // first tile row of the block
       const int h = rr0 >= BM / 2 ? 1 : 0;
       const uint32_t c_row = (uint32_t)((KT + h) % STAGES) * STAGE + (uint32_t)(rr0 - h * (BM / 2) + lrow) * (BN * 2) +
@@ -457,24 +463,19 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
         o[mt][nt].y = (int)((uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
       }
     }
-    if (split) {
-      // split K: this slice's fp32 partial sums go to workspace slice kb0 / kb_per_split
-      // (4 consecutive columns = 16 bytes per lane and block); C is added when
-      // the slices are summed
-      const int sl = done.kb0 / p.kb_per_split;
-      const v4i rsW = make_buffer_rsrc(p.ws + (size_t)sl * M * N, (uint32_t)M * (uint32_t)N * 4u);
-      const int grow0 = done.m0 + wave_m * MT * 16 + lrow;
-      const int gcol0 = done.n0 + wave_n * NT * 16 + 4 * lgrp;
+    if (done.part >= 0) {
+      // split K: this slice's fp32 partial tile (BM x BN, row-major) goes to
+      // workspace tile `part`, 4 consecutive columns = 16 bytes per lane and
+      // block.  Rows and columns beyond D are stored too and never read.
+      const v4i rsW = make_buffer_rsrc(p.ws + (size_t)done.part * (BM * BN), (uint32_t)(BM * BN * 4));
+      const uint32_t off0 = (uint32_t)((wave_m * MT * 16 + lrow) * BN + wave_n * NT * 16 + 4 * lgrp) * 4u;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int grow = grow0 + mt * 16;
-        const uint32_t row_off = ((uint32_t)grow * (uint32_t)N + (uint32_t)gcol0) * 4u;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const bool ok = grow < done.rows_valid && done.n0 + wave_n * NT * 16 + nt * 16 < N;
           const v4i w = {__float_as_int(acc[mt][nt][0]), __float_as_int(acc[mt][nt][1]),
                          __float_as_int(acc[mt][nt][2]), __float_as_int(acc[mt][nt][3])};
-          dg_raw_buffer_store_v4i32(w, rsW, (int)(ok ? row_off + nt * 64 : kBufferOutOfRange), 0, 0);
+          dg_raw_buffer_store_v4i32(w, rsW, (int)(off0 + (uint32_t)(mt * 16 * BN + nt * 16) * 4u), 0, 0);
         }
       }
     }
@@ -490,8 +491,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       prologue();
     }
     // (split K: the partial stores precede the next tile's loads)
-    stores_after = !split;
-    if (split) continue;
+    stores_after = done.part < 0;
+    if (done.part >= 0) continue;
 
     // Epilogue, part 2: exactly NST stores per wave; masked-off pieces go to an
     // out-of-range offset.
@@ -517,24 +518,40 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
 }
 
 // ---------------------------------------------------------------------------
-// split K: sum of the slices' fp32 partials (in slice order), plus C, to bf16
+// split K: for every split tile, the sum of its slices' fp32 partials (in slice
+// order), plus C, rounded to bf16
 // ---------------------------------------------------------------------------
+// One thread per 8 consecutive columns of one row of a split tile.  Split tile
+// i (raster tile full_tiles + i) keeps slice s at workspace tile i * splits + s,
+// each bm x bn fp32, row-major.
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ ws,
-                                                            const uint16_t* __restrict__ c, uint16_t* d,
-                                                            int m, int n, int splits) {
-  const size_t slice8 = (size_t)m * n / 8;   // 8-column groups per slice (n % 16 == 0)
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < slice8; i += (size_t)gridDim.x * 256) {
-    const float4* w = reinterpret_cast<const float4*>(ws) + 2 * i;
+                                                            const uint16_t* __restrict__ c, uint16_t* d, int m,
+                                                            int n, int splits, int full_tiles, int split_tiles,
+                                                            int bm, int bn, int tiles_m, int tiles_n, int group_m) {
+  const int per_row = bn / 8;
+  const long long per_tile = (long long)bm * per_row;
+  const long long total = per_tile * split_tiles;
+  const size_t tile_elems = (size_t)bm * bn;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+    const int st = (int)(i / per_tile);
+    const int q = (int)(i - (long long)st * per_tile);
+    const int r = q / per_row, c8 = q - r * per_row;
+    int tm, tn;
+    raster_tile(full_tiles + st, tiles_m, tiles_n, group_m, &tm, &tn);
+    const int row = tm * bm + r, col = tn * bn + c8 * 8;
+    if (row >= m || col >= n) continue;
+    const float4* w = reinterpret_cast<const float4*>(ws + (size_t)st * splits * tile_elems + (size_t)r * bn + c8 * 8);
     float4 lo = w[0], hi = w[1];
     for (int s = 1; s < splits; ++s) {
-      const float4* ws_s = w + 2 * slice8 * s;
+      const float4* ws_s = w + s * (tile_elems / 4);
       const float4 a = ws_s[0], b = ws_s[1];
       lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
       hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
     }
     float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const size_t o8 = ((size_t)row * n + col) / 8;   // n % 16 == 0: 16-byte aligned
     if (c) {
-      const uint4 cv = reinterpret_cast<const uint4*>(c)[i];
+      const uint4 cv = reinterpret_cast<const uint4*>(c)[o8];
       const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -545,16 +562,17 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = (uint32_t)f32_to_bf16_rne(v[2 * j]) | ((uint32_t)f32_to_bf16_rne(v[2 * j + 1]) << 16);
-    reinterpret_cast<uint4*>(d)[i] = uint4{o[0], o[1], o[2], o[3]};
+    reinterpret_cast<uint4*>(d)[o8] = uint4{o[0], o[1], o[2], o[3]};
   }
 }
 
-hipError_t launch_splitk_reduce(const float* ws, const uint16_t* c, uint16_t* d, int m, int n, int splits,
-                                int num_cus, hipStream_t stream) {
-  const size_t groups = (size_t)m * n / 8;
-  const int grid = (int)std::min<size_t>((groups + 255) / 256, (size_t)num_cus * 8);
+hipError_t launch_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& plan, int num_cus, hipStream_t stream) {
+  const int split_tiles = plan.num_tiles - plan.full_tiles;
+  const long long threads = (long long)plan.block_m * (plan.block_n / 8) * split_tiles;
+  const int grid = (int)std::min<long long>((threads + 255) / 256, (long long)num_cus * 8);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, ws, c, d, m, n, splits);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, p.ws, p.c, p.d, p.m, p.n, plan.splits,
+                     plan.full_tiles, split_tiles, plan.block_m, plan.block_n, p.tiles_m, p.tiles_n, p.group_m);
   return hipGetLastError();
 }
 

@@ -24,17 +24,32 @@ static int blocks_per_cu_for(int kernel_id) {
   return std::max(1, std::min(tc.blocks_per_cu, by_lds));
 }
 
-// Split K for problems whose output tiles cannot fill the chip (skinny M):
-// enough K slices to occupy every workgroup slot once, at least four K blocks
-// per slice and at most 16 slices.  Returns 1 when splitting does not apply.
-static int choose_splits(long long tiles, int slots, int kb) {
-  if (tiles <= 0 || tiles * 2 > slots || kb < 8) return 1;
-  long long s = slots / tiles;
-  s = std::min<long long>(s, kb / 4);
+// K splitting (dense only).  Returns the K slices per split tile (1: none) and
+// sets *full to the number of tiles computed whole:
+//  * skinny M, where the tiles cannot fill the chip (tiles * 2 <= slots): every
+//    tile is split, into enough slices to occupy every workgroup slot once;
+//  * a partial last round (the tile count is not a multiple of the slots, and
+//    the remainder is at most half of them): the whole rounds run unsplit and
+//    only the remainder is split, so the last round takes a slice's time
+//    instead of a whole tile's.  Taken only when that saves at least
+//    kTailMinGain K blocks per workgroup (the partials' round trip and the
+//    second launch cost about that much).
+// Slices hold at least four K blocks; at most 16 slices.
+constexpr int kTailMinGain = 24;
+static int choose_splits(long long tiles, long long slots, int kb, long long* full) {
+  *full = tiles;
+  if (tiles <= 0 || kb < 8) return 1;
+  const bool all = tiles * 2 <= slots;
+  const long long rem = all ? tiles : tiles % slots;
+  if (rem == 0 || rem * 2 > slots) return 1;
+  long long s = std::min<long long>(slots / rem, kb / 4);
   s = std::min<long long>(s, 16);
   if (s < 2) return 1;
   const int per = cdiv(kb, (int)s);
-  return cdiv(kb, per);
+  s = cdiv(kb, per);
+  if (!all && kb - per < kTailMinGain) return 1;
+  *full = tiles - rem;
+  return (int)s;
 }
 
 GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id) {
@@ -50,11 +65,14 @@ GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num
   long long slots = (long long)num_cus * blocks_per_cu_for(kernel_id);
   plan.splits = 1;
   plan.kb_per_split = k / 128;
+  plan.full_tiles = plan.num_tiles;
   if (mode == MODE_DENSE && tc.min_k == 0) {   // two-slot (long K) shapes never split
-    plan.splits = choose_splits(total, (int)std::min<long long>(slots, 1 << 20), k / 128);
+    long long full = total;
+    plan.splits = choose_splits(total, slots, k / 128, &full);
     plan.kb_per_split = cdiv(k / 128, plan.splits);
+    plan.full_tiles = (int)full;
   }
-  const long long units = total * plan.splits;
+  const long long units = plan.full_tiles + (total - plan.full_tiles) * plan.splits;
   plan.num_workgroups = (int)std::min<long long>(units, slots);
   return plan;
 }
@@ -75,20 +93,29 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     long long tiles = (long long)tm * tn * (mode == MODE_DENSE ? 1 : (mode == MODE_MASKED ? num_groups : 1));
     // useful fraction of the MFMA work (padding in M and N is wasted)
     double util = (double)rows / (tm * tc.block_m) * (double)n / (tn * tc.block_n);
-    // wave quantisation: fraction of the last wave of work units that is busy
+    // wave quantisation: busy fraction of the workgroup slots over the call, in
+    // K-block steps (a split tail costs its slice plus about kTailMinGain / 3
+    // steps for the partials' round trip)
     int slots = num_cus * blocks_per_cu_for(id);
-    const int splits = mode == MODE_DENSE && tc.min_k == 0 ? choose_splits(tiles, slots, k / 128) : 1;
-    long long units = tiles * splits;
+    const int kb = k / 128;
+    long long full = tiles;
+    const int splits = mode == MODE_DENSE && tc.min_k == 0 ? choose_splits(tiles, slots, kb, &full) : 1;
+    const long long units = full + (tiles - full) * splits;
     // a two-slot (long K) shape must at least fill the chip once: in a single
     // partial wave its large tiles leave compute units idle for the whole call
     if (tc.min_k > 0 && units < slots) continue;
-    long long waves = (units + slots - 1) / slots;
-    double fill = (double)units / (double)(waves * slots);
+    double fill;
+    if (splits > 1 && full > 0) {
+      const double steps = (double)(full / slots) * kb + cdiv(kb, splits) + kTailMinGain / 3.0;
+      fill = (double)tiles * kb / ((double)slots * steps);
+    } else {
+      const long long waves = (units + slots - 1) / slots;
+      fill = (double)units / (double)(waves * slots);
+      if (splits > 1) fill *= 0.8;   // split K writes and re-reads fp32 partials
+    }
     // bigger tiles re-read less from L2/HBM: weight by tile area (arithmetic intensity)
     double intensity = (double)tc.block_m * tc.block_n / (tc.block_m + tc.block_n);
     double score = util * fill * intensity;
-    // split K writes and re-reads fp32 partials
-    if (splits > 1) score *= 0.8;
     // short K loops are bound by the epilogue: wide tiles write longer rows of D
     if (k <= 1024 && tc.block_n > tc.block_m) score *= 1.05;
     if (score > best_score + 1e-9) {

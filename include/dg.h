@@ -178,12 +178,16 @@ int dg_get_num_cus(void);
  * The tile plan the heuristic picks for an M x N x K problem split over
  * num_groups groups (1 for dense), on num_cus compute units (<= 0: current cap).
  * Host-only: no HIP call is made when num_cus > 0.  Fills block_m, block_n,
- * the number of output tiles, the K slices per tile and the number of
- * workgroups launched.  A dense problem whose tiles cannot fill the chip (skinny
- * M) is split along K: each workgroup sums a range of 128-wide K blocks into an
- * fp32 slice of an internal workspace, and a second kernel adds the slices (in
- * slice order) and C and rounds to bf16.  The workspace is allocated by the
- * library, one per (device, stream), on first need.
+ * the number of output tiles, the K slices per split tile, the tiles computed
+ * whole and the number of workgroups launched.  Dense problems may be split
+ * along K: when the tiles cannot fill the chip (skinny M) every tile is split,
+ * and when the last round of tiles would leave at least half of the workgroup
+ * slots idle over a long K loop, only that round's tiles are.  Each slice of a
+ * split tile sums a range of 128-wide K blocks into an fp32 partial tile of an
+ * internal workspace, and a second kernel adds a tile's partials (in slice
+ * order) and C and rounds to bf16.  The workspace is allocated by the library,
+ * one per (device, stream), on first need, and grows to at most one partial
+ * tile per workgroup slot.
  * Exposed so callers can log the choice (DG_LOG=1 prints it on every call).
  */
 typedef struct dg_plan {
@@ -192,7 +196,8 @@ typedef struct dg_plan {
   int num_tiles;        /* output tiles */
   int num_workgroups;
   int kernel_id;
-  int splits;           /* K slices per output tile (dense only; 1: no split) */
+  int splits;           /* K slices per split tile (dense only; 1: no split) */
+  int full_tiles;       /* tiles computed whole; the other num_tiles - full_tiles are split */
 } dg_plan;
 int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out);
 

@@ -113,5 +113,36 @@ def test_planner_is_host_only_and_fills_the_chip():
     p = dgm.dg_query_plan(128, 2112, 7168, 1, 256)
     assert p["splits"] > 1 and p["num_tiles"] * p["splits"] > 128
     assert p["splits"] <= 7168 // 128 // 4
-    # a problem that already fills the chip is not split
-    assert dgm.dg_query_plan(4096, 7168, 2048, 1, 256)["splits"] == 1
+    assert p["full_tiles"] == 0, "skinny M splits every tile"
+    # a problem that already fills the chip is not split: 4096 x 7168 x 2048 has a
+    # half-empty last round, but 16 K blocks are too few to gain from splitting it
+    p = dgm.dg_query_plan(4096, 7168, 2048, 1, 256)
+    assert p["splits"] == 1 and p["full_tiles"] == p["num_tiles"]
+    # whole rounds need no split either
+    p = dgm.dg_query_plan(4096, 4096, 7168, 1, 256)
+    assert p["num_tiles"] % 256 == 0 and p["splits"] == 1
+
+
+@pytest.mark.parametrize("m,n,k", [(4096, 7168, 16384), (4096, 2112, 7168), (2304, 3840, 4096)])
+def test_planner_splits_only_the_last_partial_round(m, n, k):
+    """Long K with a partial last round: the whole rounds run unsplit and only the
+    remainder is split, into slices that together fit in one round."""
+    slots = 256
+    p = dgm.dg_query_plan(m, n, k, 1, slots)
+    tiles, full, s = p["num_tiles"], p["full_tiles"], p["splits"]
+    assert s > 1, p
+    assert full % slots == 0 and 0 < tiles - full <= slots // 2
+    assert (tiles - full) * s <= slots
+    assert p["num_workgroups"] == slots
+    kb = k // 128
+    per = -(-kb // s)
+    assert per >= 4 and kb - per >= 24   # slices of >= 4 K blocks; the tail gains >= 24 blocks
+
+
+def test_planner_split_tail_with_a_cu_cap():
+    # the same rule on a capped part: 40 tiles of 256 x 128 on 32 CUs leave a
+    # remainder of 8, split 4 ways over K = 128 * 32
+    p = dgm.dg_query_plan(1280, 1024, 128 * 32, 1, 32)
+    if p["block_m"] == 256 and p["block_n"] == 128:
+        assert p["full_tiles"] == 32 and p["splits"] == 4
+    assert p["full_tiles"] % 32 == 0 or p["full_tiles"] == p["num_tiles"]

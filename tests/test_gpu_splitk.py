@@ -86,3 +86,92 @@ def test_splitk_workspace_grows_on_one_stream(dg):
             dg.dg_fp8_gemm_nt(*ins, d)
         torch.cuda.synchronize()
         check_parity(bits(d), R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"split ws {M}x{N}x{K}")
+
+
+# ---------------------------------------------------------------------------
+# split tail: whole rounds of tiles run unsplit, only the last partial round is
+# split along K (a CU cap makes small problems take this path)
+# ---------------------------------------------------------------------------
+class _cu_cap:
+    def __init__(self, n):
+        self.n = n
+
+    def __enter__(self):
+        dgm.dg_set_num_cus(self.n)
+
+    def __exit__(self, *exc):
+        dgm.dg_set_num_cus(0)
+
+
+def _tail_plan(M, N, K, cus):
+    p = dgm.dg_query_plan(M, N, K, 1, cus)
+    assert p["splits"] > 1 and 0 < p["full_tiles"] < p["num_tiles"], f"no split tail: {p}"
+    return p
+
+
+@pytest.mark.parametrize("M,N,K,cus,with_c", [(1280, 1024, 128 * 32, 32, True),
+                                              (1100, 1040, 128 * 60, 32, True),
+                                              (1300, 1040, 128 * 36, 48, False)])
+def test_split_tail_random_parity(dg, M, N, K, cus, with_c):
+    _tail_plan(M, N, K, cus)
+    g = synth.gen_dense(M, N, K, seed=M + N + K + cus, with_c=with_c)
+    a, sfa, b, sfb = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb"))
+    c = synth.to_numpy(g["c"]) if with_c else None
+    d = sentinel_like((M, N))
+    with _cu_cap(cus):
+        dg.dg_fp8_gemm_nt(_dev(a), _dev(sfa), _dev(b), _dev(sfb), _dev(c), d)
+        torch.cuda.synchronize()
+    db = bits(d)
+    assert not (db == 0xFFFF).any(), "every output element must be written"
+    check_parity(db, R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"split tail {M}x{N}x{K} on {cus} CUs")
+
+
+def test_split_tail_exact_integer_case_bit_exact(dg):
+    M, N, K, cus = 512, 640, 128 * 32, 8
+    _tail_plan(M, N, K, cus)
+    rng = np.random.default_rng(77)
+    a, sfa, b, sfb, c, exact = make_exact_case(rng, M, N, K, True)
+    d = sentinel_like((M, N))
+    with _cu_cap(cus):
+        dg.dg_fp8_gemm_nt(_dev(a), _dev(sfa), _dev(b), _dev(sfb), _dev(c), d)
+        torch.cuda.synchronize()
+    check_bit_exact(bits(d), exact, f"split tail exact {M}x{N}x{K}")
+
+
+def test_split_tail_full_size_sampled_rows(dg):
+    """4096 x 2112 x 7168 on the whole chip: 272 tiles of 256 x 128, of which 256
+    run whole and 16 (in the lower half of the rows, last two tile columns) are
+    split.  Sampled rows from both halves are checked against the oracle."""
+    M, N, K = 4096, 2112, 7168
+    ncu = dgm.dg_get_num_cus()
+    p = dgm.dg_query_plan(M, N, K, 1, ncu)
+    if not (p["splits"] > 1 and 0 < p["full_tiles"] < p["num_tiles"]):
+        pytest.skip(f"no split tail on {ncu} CUs: {p}")
+    g = synth.gen_dense(M, N, K, seed=4242, with_c=True, backend="torch", device="cuda")
+    d = sentinel_like((M, N))
+    dg.dg_fp8_gemm_nt(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.sort(np.concatenate([rng.choice(M // 2, 24, replace=False),
+                                   M // 2 + rng.choice(M // 2, 40, replace=False)]))
+    db = bits(d)
+    assert not (db == 0xFFFF).any(), "every output element must be written"
+    t_rows = torch.from_numpy(rows).cuda()
+    a = synth.to_numpy(g["a"][t_rows])
+    sfa = synth.to_numpy(g["sfa"][:, t_rows])
+    c = synth.to_numpy(g["c"][t_rows])
+    b, sfb = synth.to_numpy(g["b"]), synth.to_numpy(g["sfb"])
+    check_parity(db[rows], R.fp8_gemm_nt(a, sfa, b, sfb, c), what="split tail 4096x2112x7168 sampled rows")
+
+
+def test_split_tail_then_pure_split_then_whole_on_one_stream(dg):
+    """The workspace serves both split forms in turn; results stay correct."""
+    cases = [(1280, 1024, 128 * 32, 32), (48, 528, 128 * 20, 0), (1024, 1024, 128 * 8, 0)]
+    for i, (M, N, K, cus) in enumerate(cases):
+        g = synth.gen_dense(M, N, K, seed=900 + i, with_c=True)
+        a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+        d = sentinel_like((M, N))
+        with _cu_cap(cus):
+            dg.dg_fp8_gemm_nt(_dev(a), _dev(sfa), _dev(b), _dev(sfb), _dev(c), d)
+            torch.cuda.synchronize()
+        check_parity(bits(d), R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"sequence {M}x{N}x{K}")
