@@ -49,6 +49,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
+// Two fp32 -> two bf16 (lo in bits 15:0), one v_cvt_pk_bf16_f32.  Round to nearest
+// even; for every non-NaN input the result equals f32_to_bf16_rne bit for bit
+// (denormals and overflow to infinity included).  A NaN stays a quiet NaN with
+// its payload's top bits (not the canonical 0x7fc0).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // LDS layout of a K-block tile: each row is 128 bytes = 8 chunks of 16 bytes;
 // chunk c of row r lives at position c ^ swz(r).  swz spreads any 8 (and any 16)
 // consecutive rows that read the same logical chunk over distinct bank groups,

@@ -464,10 +464,10 @@ __global__ void __launch_bounds__(256) ffn_combine_kernel(FfnParams p) {
     }
   }
   v4i out;
-  out.x = (int)f32_to_bf16_rne(acc[0]) | ((int)f32_to_bf16_rne(acc[1]) << 16);
-  out.y = (int)f32_to_bf16_rne(acc[2]) | ((int)f32_to_bf16_rne(acc[3]) << 16);
-  out.z = (int)f32_to_bf16_rne(acc[4]) | ((int)f32_to_bf16_rne(acc[5]) << 16);
-  out.w = (int)f32_to_bf16_rne(acc[6]) | ((int)f32_to_bf16_rne(acc[7]) << 16);
+  out.x = (int)pack_bf16x2_rne(acc[0], acc[1]);
+  out.y = (int)pack_bf16x2_rne(acc[2], acc[3]);
+  out.z = (int)pack_bf16x2_rne(acc[4], acc[5]);
+  out.w = (int)pack_bf16x2_rne(acc[6], acc[7]);
   *reinterpret_cast<v4i*>(p.y + (size_t)t * p.H + c8) = out;
 }
 

@@ -459,8 +459,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
           v2 += __uint_as_float(cv.y << 16);
           v3 += __uint_as_float(cv.y & 0xffff0000u);
         }
-        o[mt][nt].x = (int)((uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16));
-        o[mt][nt].y = (int)((uint32_t)f32_to_bf16_rne(v2) | ((uint32_t)f32_to_bf16_rne(v3) << 16));
+        o[mt][nt].x = (int)pack_bf16x2_rne(v0, v1);
+        o[mt][nt].y = (int)pack_bf16x2_rne(v2, v3);
       }
     }
     if (done.part >= 0) {
@@ -561,7 +561,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     }
     uint32_t o[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = (uint32_t)f32_to_bf16_rne(v[2 * j]) | ((uint32_t)f32_to_bf16_rne(v[2 * j + 1]) << 16);
+    for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2_rne(v[2 * j], v[2 * j + 1]);
     reinterpret_cast<uint4*>(d)[o8] = uint4{o[0], o[1], o[2], o[3]};
   }
 }

@@ -18,14 +18,18 @@
  *     contiguous).  Sizes are element counts.  Operand and output pointers must
  *     be 16-byte aligned; scale pointers 4-byte aligned.
  *   - The caller owns every buffer, including outputs and workspaces.  The
- *     library never allocates or frees device memory on these calls and keeps
- *     only host-side state (a device-property cache and the CU cap).
+ *     library keeps only host-side state (a device-property cache and the CU
+ *     cap) and allocates no device memory, with one exception: the dense
+ *     GEMM's split-K workspace (see dg_query_plan), which the first split call
+ *     on a (device, stream) allocates and a later call needing more grows.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
- *     There is no host synchronisation and no host read of device data, so the
- *     calls may be captured in a HIP graph.
+ *     There is no host read of device data and no host synchronisation, except
+ *     that growing the split-K workspace first synchronises its stream.  Calls
+ *     may be captured in a HIP graph once that stream's workspace is as large
+ *     as the captured calls need (run them once before capturing).
  *   - e4m3 means OCP e4m3fn (bias 7, max 448, NaN = 0x7F/0xFF).  bf16 values
  *     are passed as their uint16 bit patterns.  Outputs are rounded from fp32
- *     to bf16 with round-to-nearest-even.
+ *     to bf16 with round-to-nearest-even (a NaN result stays a quiet NaN).
  *   - Every function returns a dg_status.  Arguments are validated on the host
  *     before any HIP call; on an error nothing is enqueued and nothing is
  *     written.  No C++ exception crosses this boundary and the library never
