@@ -137,7 +137,10 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
     p.ws = split_workspace(di.device, hs, ws_bytes, &werr);
     if (!p.ws) return DG_ERR_HIP;
   }
-  p.group_m = 8;
+  // raster band: the 32 tiles an XCD runs at once share the fewest A and B rows
+  // as a 4 x 8 block of 256 x 128 tiles (1024 + 1024 rows) or an 8 x 4 block of
+  // 128 x 256 ones; long K loops gain most from the L2 reuse
+  p.group_m = (plan.block_m == 256 && plan.block_n == 128 && p.k >= 4096) ? 4 : 8;
   if (const char* gm = std::getenv("DG_GROUP_M")) p.group_m = std::max(1, std::atoi(gm));   // raster band (tuning)
   // DG_KROT=<s>: K-block rotation step between neighbouring tiles (tuning)
   p.k_rot = 0;

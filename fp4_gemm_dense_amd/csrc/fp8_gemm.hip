@@ -57,9 +57,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   static_assert(128 % (NT * 16) == 0 && (BN % 128 == 0 || 128 % BN == 0), "one B scale per wave");
   static_assert(MT % 4 == 0, "a lane reads its row scales with 16-byte LDS loads");
   constexpr int NBLK = MT * NT;   // 16x16 accumulator blocks per wave
-  constexpr int LAG = NT;         // matrix instructions between a partial's issue and its promotion
   constexpr bool STREAM_A = MT > 4;   // read A fragments A_AHEAD row blocks ahead instead of all at once
-  constexpr int A_AHEAD = 2;
+#ifndef DG_STREAM_LAG
+#define DG_STREAM_LAG 4
+#endif
+#ifndef DG_A_AHEAD
+#define DG_A_AHEAD 2
+#endif
+  // matrix instructions between a partial's issue and its promotion (at most NT)
+  constexpr int LAG = STREAM_A ? (DG_STREAM_LAG < NT ? DG_STREAM_LAG : NT) : NT;
+  constexpr int A_AHEAD = DG_A_AHEAD;
   // Epilogue traffic.  The C tile (BM x BN bf16) is copied into two ring slots
   // that the last two K blocks leave free, in halves of BM/2 rows; each wave
   // copies CPW 1-KB pieces of a half.  A C row holds CPR 16-byte chunks, chunk c
@@ -194,15 +201,21 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     (void)SB;
     // Region r covers tile rows 8r..8r+7; lane l fills LDS bytes [16l, 16l+16)
     // of it: row 8r + l/8, position l%8, which holds chunk (l%8) ^ swz(row).
+    // Rows past the valid ones (ragged edges, masked-off rows) take an
+    // out-of-range offset: the copy then reads zeros without a memory request,
+    // and their results are never stored.
 #pragma unroll
     for (int j = 0; j < RA; ++j) {
       const int row = (wave * RA + j) * 8 + dma_row;
-      a_off[j] = (uint32_t)min(tile.m0 + row, M - 1) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4);
+      a_off[j] = tile.m0 + row < tile.rows_valid
+                     ? (uint32_t)(tile.m0 + row) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4)
+                     : kBufferOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const int row = (wave * RB + j) * 8 + dma_row;
-      b_off[j] = (uint32_t)min(tile.n0 + row, N - 1) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4);
+      b_off[j] = tile.n0 + row < N ? (uint32_t)(tile.n0 + row) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4)
+                                   : kBufferOutOfRange;
     }
     {
       // LDS position q of a tile's A scales holds row g*MT*16 + mt*16 + r for
@@ -210,7 +223,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       const int q = wave * SPW + (lane < SPW ? lane : 0);
       const int g = q / (MT * 16), rem = q % (MT * 16);
       const int row = g * (MT * 16) + (rem % MT) * 16 + rem / MT;
-      sa_off = (uint32_t)min(tile.m0 + row, M - 1) * 4;
+      sa_off = tile.m0 + row < tile.rows_valid ? (uint32_t)(tile.m0 + row) * 4 : kBufferOutOfRange;
     }
     // B-scale element offsets from the kernel argument p.sfb, kept in SGPRs so the
     // per-K-block reads are scalar loads (which vmcnt does not count)
@@ -257,8 +270,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       const int q = wave * CPW + j;
       const int rr = h * (BM / 2) + q * RPI + lane / CPR;   // tile row
       const int c = (lane % CPR) ^ (rr & 15);                // C chunk this lane fetches
-      const uint32_t off = ((uint32_t)min(tile.m0 + rr, M - 1) * (uint32_t)N +
-                            (uint32_t)min(tile.n0 + c * 8, N - 8)) * 2u;
+      const uint32_t off = tile.m0 + rr < M && tile.n0 + c * 8 < N
+                               ? ((uint32_t)(tile.m0 + rr) * (uint32_t)N + (uint32_t)(tile.n0 + c * 8)) * 2u
+                               : kBufferOutOfRange;
       buf16_to_lds(rsC, off, 0u, smem + slot_off + q * 1024);
     }
   };
@@ -323,7 +337,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       // copies spread over the block (not with streamed A fragments, whose
       // scheduling fences would split the pattern)
       constexpr int ILV = RA + RB;
-      constexpr int ILV_STEP = (!STREAM_A && NBLK / ILV > 0) ? NBLK / ILV : NBLK + 1;
+#ifndef DG_STREAM_ILV
+#define DG_STREAM_ILV 0
+#endif
+      constexpr int ILV_STEP = ((!STREAM_A || DG_STREAM_ILV) && NBLK / ILV > 0) ? NBLK / ILV : NBLK + 1;
       wait_stage(kb, KT, stores_after);
       block_barrier();
       if (STEADY) {
@@ -393,7 +410,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
           const int r = j % LAG;
           if (j < LAG) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[MT - 1][j][i] = fmaf(part[r][i], sprev, acc[MT - 1][j][i]);
+            for (int i = 0; i < 4; ++i)
+              acc[MT - 1][j + NT - LAG][i] = fmaf(part[r][i], sprev, acc[MT - 1][j + NT - LAG][i]);
           } else {
             const int pm = (j - LAG) / NT, pn = (j - LAG) % NT;
 #pragma unroll
@@ -421,11 +439,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     for (; kb + STAGES - 1 < KT; ++kb) kstep(kb, std::true_type{});
 #pragma clang loop unroll(disable)
     for (; kb < KT; ++kb) kstep(kb, std::false_type{});
-    // promote the last LAG partials
+    // promote the last LAG partials (blocks NBLK - LAG .. NBLK - 1: row MT - 1)
 #pragma unroll
     for (int j = 0; j < LAG; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[MT - 1][j][i] = fmaf(part[j][i], sprev, acc[MT - 1][j][i]);
+      for (int i = 0; i < 4; ++i)
+        acc[MT - 1][NT - LAG + j][i] = fmaf(part[(NBLK - LAG + j) % LAG][i], sprev, acc[MT - 1][NT - LAG + j][i]);
     const Tile done = cur;
 
     // Epilogue, part 1: D = acc (+ C) rounded to bf16, still in registers.  Lane
