@@ -129,6 +129,24 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
   p.total_tiles = (int)std::min<long long>(
       (long long)plan.full_tiles + (long long)(plan.num_tiles - plan.full_tiles) * plan.splits, 0x7fffffff);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  // Masked form: the kernel walks only the tiles holding valid rows, spread
+  // evenly over one full set of workgroup slots, and over long K splits a small
+  // last round along K (decided on the device from masked_m; the reduce kernel
+  // re-derives the same plan and does nothing when there is no split).
+  int masked_slots = 0;
+  p.device_split = 0;
+  if (mode == MODE_MASKED && tile_config(plan.kernel_id).min_k == 0) {
+    masked_slots = plan_slots(plan.kernel_id, cus);
+    plan.num_workgroups = masked_slots;
+    p.device_split = p.k / 128 >= 4 + kTailMinGain ? 1 : 2;
+  }
+  if (p.device_split == 1) {
+    // at most one partial tile per workgroup slot
+    const size_t ws_bytes = (size_t)masked_slots * plan.block_m * plan.block_n * 4;
+    hipError_t werr = hipSuccess;
+    p.ws = split_workspace(di.device, hs, ws_bytes, &werr);
+    if (!p.ws) return DG_ERR_HIP;
+  }
   if (plan.splits > 1) {
     // one fp32 block_m x block_n partial per slice of every split tile (at most
     // one per workgroup slot, so a few tens of MB at most)
@@ -151,6 +169,7 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
                  plan.kernel_id, plan.num_tiles, plan.full_tiles, plan.splits, plan.num_workgroups);
   hipError_t e = launch_fp8_gemm(p, plan, mode, hs);
   if (e == hipSuccess && plan.splits > 1) e = launch_splitk_reduce(p, plan, cus, hs);
+  if (e == hipSuccess && p.device_split == 1) e = launch_masked_splitk_reduce(p, plan, masked_slots, hs);
   return e == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 

@@ -31,6 +31,8 @@ struct Fp8GemmParams {
   int kb_per_split;           // K blocks per slice (the last one may hold fewer)
   int full_tiles;             // tiles [0, full_tiles) of the raster run whole; the rest are split
   float* ws;                  // split K: fp32 partial tiles [(tile - full_tiles) * splits + slice][BM][BN]
+  int device_split;           // masked: 0 static tile walk; 1 valid tiles only, split rule applied on the
+                              // device (launch the masked reduce after); 2 valid tiles only, no split
 };
 
 // Tile shapes compiled into the library (kernel_id indexes this table).
@@ -65,10 +67,50 @@ struct GemmPlan {
 };
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m);
 GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id);
+// Resident workgroup slots of a compiled tile shape on num_cus CUs.
+int plan_slots(int kernel_id, int num_cus);
 
 // Split K: for every split tile, D = bf16(sum of its ws slices in slice order + C);
 // returns a hipError_t.
 hipError_t launch_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& plan, int num_cus, hipStream_t stream);
+// The same for the device-planned masked form, on the plan the GEMM kernel
+// derived from masked_m with `slots` workgroups.
+hipError_t launch_masked_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& plan, int slots, hipStream_t stream);
+
+// K splitting rule, shared by the host planner and (for the masked form, whose
+// tile count only the device knows) the kernels.  Returns the K slices per
+// split tile (1: none) and sets *full to the number of tiles computed whole:
+//  * when the tiles cannot fill the workgroup slots (tiles * 2 <= slots) every
+//    tile is split, into enough slices to occupy every slot once;
+//  * when the last round is partial and at most half full, the whole rounds run
+//    unsplit and only the remainder is split, so the last round takes a slice's
+//    time instead of a whole tile's; taken only when that saves at least
+//    kTailMinGain K blocks per workgroup (the partials' round trip and the
+//    second launch cost about that much).
+// Slices hold at least four K blocks; at most 16 slices.
+constexpr int kTailMinGain = 24;
+__host__ __device__ inline int split_rule(long long tiles, long long slots, int kb, long long* full) {
+  *full = tiles;
+  if (tiles <= 0 || kb < 8) return 1;
+  const bool all = tiles * 2 <= slots;
+  const long long rem = all ? tiles : tiles % slots;
+  if (rem == 0 || rem * 2 > slots) return 1;
+  long long s = slots / rem < kb / 4 ? slots / rem : kb / 4;
+  s = s < 16 ? s : 16;
+  if (s < 2) return 1;
+  const int per = (kb + (int)s - 1) / (int)s;
+  s = (kb + per - 1) / per;
+  if (!all && kb - per < kTailMinGain) return 1;
+  *full = tiles - rem;
+  return (int)s;
+}
+
+// Masked form: output tiles of group g (valid rows rounded up to whole tiles).
+__device__ inline int masked_group_tiles(const int32_t* masked_m, int g, int max_m, int bm, int tiles_n) {
+  int mm = masked_m[g];
+  mm = mm < 0 ? 0 : (mm > max_m ? max_m : mm);
+  return (mm + bm - 1) / bm * tiles_n;
+}
 
 // Raster order of the output tiles (one group): bands of group_m tile rows, walked
 // column by column inside a band, tile rows fastest.  Tile index tl -> (tile row, tile column).

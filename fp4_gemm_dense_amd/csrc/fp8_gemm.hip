@@ -125,28 +125,53 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   };
   // Work units: units [0, full_tiles) are the tiles of the same index, computed
   // whole; unit full_tiles + u is K slice u % splits of tile full_tiles + u / splits.
-  // (The planner never splits two-slot shapes.)
-  const bool can_split = STAGES >= 3 && p.splits > 1;
+  // (Two-slot shapes are never split.)
+  int full_tiles = p.full_tiles, splits = p.splits, kb_per_split = p.kb_per_split, total_units = p.total_tiles;
+  // Masked form, device-planned: the tiles are those holding valid rows, group
+  // after group (group g has ceil(masked_m[g] / BM) tile rows), and the split
+  // rule is applied to their count, which only the device knows.  Every
+  // workgroup (and the reduce kernel) derives the same plan.
+  const bool dev_plan = MODE == MODE_MASKED && p.device_split;
+  int mg = 0, mg_base = 0, mg_cnt = 0;   // group cursor of the decode (tile ids only grow)
+  if (dev_plan) {
+    int tiles = 0;
+    for (int g = 0; g < p.num_groups; ++g) tiles += masked_group_tiles(p.masked_m, g, M, BM, p.tiles_n);
+    long long full = tiles;
+    splits = STAGES >= 3 && p.device_split == 1 ? split_rule(tiles, G, KB, &full) : 1;
+    full_tiles = (int)full;
+    kb_per_split = (KB + splits - 1) / splits;
+    total_units = full_tiles + (tiles - full_tiles) * splits;
+    mg_cnt = masked_group_tiles(p.masked_m, 0, M, BM, p.tiles_n);
+  }
+  const bool can_split = STAGES >= 3 && splits > 1;
   auto decode = [&](int t, Tile& tile) -> bool {
     tile.kb0 = 0;
     tile.nkb = KB;
     tile.part = -1;
-    if (can_split && t >= p.full_tiles) {
-      const int u = t - p.full_tiles;
-      const int sl = u % p.splits;
-      t = p.full_tiles + u / p.splits;
-      tile.kb0 = sl * p.kb_per_split;
-      tile.nkb = min(p.kb_per_split, KB - tile.kb0);
+    if (can_split && t >= full_tiles) {
+      const int u = t - full_tiles;
+      const int sl = u % splits;
+      t = full_tiles + u / splits;
+      tile.kb0 = sl * kb_per_split;
+      tile.nkb = min(kb_per_split, KB - tile.kb0);
       tile.part = u;
     }
-    int g = 0, tl = t;
-    if (MODE == MODE_MASKED) {
+    int g = 0, tl = t, tiles_m = p.tiles_m;
+    if (dev_plan) {
+      while (t >= mg_base + mg_cnt) {
+        mg_base += mg_cnt;
+        mg_cnt = masked_group_tiles(p.masked_m, ++mg, M, BM, p.tiles_n);
+      }
+      g = mg;
+      tl = t - mg_base;
+      tiles_m = mg_cnt / p.tiles_n;
+    } else if (MODE == MODE_MASKED) {
       const int per = p.tiles_m * p.tiles_n;
       g = t / per;
       tl = t - g * per;
     }
     int tm, tn;
-    raster_tile(tl, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    raster_tile(tl, tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     tile.m0 = tm * BM;
     tile.n0 = tn * BN;
     tile.rot = tile.part >= 0 ? 0 : (p.k_rot * ((tm + tn) & 7)) % KB;
@@ -165,7 +190,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   };
   // first tile at or after t with work (all lanes agree: every input is uniform)
   auto next_tile = [&](int& t, Tile& tile) -> bool {
-    for (; t < p.total_tiles; t += G)
+    for (; t < total_units; t += G)
       if (decode(t, tile)) return true;
     return false;
   };
@@ -592,6 +617,59 @@ hipError_t launch_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& plan, in
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, p.ws, p.c, p.d, p.m, p.n, plan.splits,
                      plan.full_tiles, split_tiles, plan.block_m, plan.block_n, p.tiles_m, p.tiles_n, p.group_m);
+  return hipGetLastError();
+}
+
+// Masked form, device-planned: the same plan as the GEMM kernel (valid tiles
+// of all groups in group order, split rule over their count on `slots`
+// workgroups); one workgroup per split tile at a time.
+__global__ void __launch_bounds__(256) masked_splitk_reduce_kernel(const float* __restrict__ ws, uint16_t* d,
+                                                                   const int32_t* __restrict__ masked_m,
+                                                                   int groups, int max_m, int n, int kb, int bm,
+                                                                   int bn, int tiles_n, int group_m, int slots) {
+  int tiles = 0;
+  for (int g = 0; g < groups; ++g) tiles += masked_group_tiles(masked_m, g, max_m, bm, tiles_n);
+  long long full = tiles;
+  const int splits = split_rule(tiles, slots, kb, &full);
+  if (splits <= 1) return;
+  const int split_tiles = tiles - (int)full;
+  const int per_row = bn / 8;
+  const size_t tile_elems = (size_t)bm * bn;
+  int mg = 0, base = 0, cnt = masked_group_tiles(masked_m, 0, max_m, bm, tiles_n);
+  for (int st = blockIdx.x; st < split_tiles; st += gridDim.x) {
+    const int t = (int)full + st;
+    while (t >= base + cnt) {
+      base += cnt;
+      cnt = masked_group_tiles(masked_m, ++mg, max_m, bm, tiles_n);
+    }
+    int tm, tn;
+    raster_tile(t - base, cnt / tiles_n, tiles_n, group_m, &tm, &tn);
+    int mm = masked_m[mg];
+    mm = mm < 0 ? 0 : (mm > max_m ? max_m : mm);
+    uint16_t* dg = d + (size_t)mg * max_m * n;
+    const float* wt = ws + (size_t)st * splits * tile_elems;
+    for (int q = threadIdx.x; q < bm * per_row; q += 256) {
+      const int r = q / per_row, c8 = q - r * per_row;
+      const int row = tm * bm + r, col = tn * bn + c8 * 8;
+      if (row >= mm || col >= n) continue;
+      const float4* w = reinterpret_cast<const float4*>(wt + (size_t)r * bn + c8 * 8);
+      float4 lo = w[0], hi = w[1];
+      for (int sl = 1; sl < splits; ++sl) {
+        const float4* ws_s = w + sl * (tile_elems / 4);
+        const float4 a = ws_s[0], b = ws_s[1];
+        lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+        hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+      }
+      const uint4 o = {pack_bf16x2_rne(lo.x, lo.y), pack_bf16x2_rne(lo.z, lo.w), pack_bf16x2_rne(hi.x, hi.y),
+                       pack_bf16x2_rne(hi.z, hi.w)};
+      reinterpret_cast<uint4*>(dg)[((size_t)row * n + col) / 8] = o;
+    }
+  }
+}
+
+hipError_t launch_masked_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& plan, int slots, hipStream_t stream) {
+  hipLaunchKernelGGL(masked_splitk_reduce_kernel, dim3(slots), dim3(256), 0, stream, p.ws, p.d, p.masked_m,
+                     p.num_groups, p.m, p.n, p.k / 128, plan.block_m, plan.block_n, p.tiles_n, p.group_m, slots);
   return hipGetLastError();
 }
 

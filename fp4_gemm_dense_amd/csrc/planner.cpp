@@ -24,32 +24,11 @@ static int blocks_per_cu_for(int kernel_id) {
   return std::max(1, std::min(tc.blocks_per_cu, by_lds));
 }
 
-// K splitting (dense only).  Returns the K slices per split tile (1: none) and
-// sets *full to the number of tiles computed whole:
-//  * skinny M, where the tiles cannot fill the chip (tiles * 2 <= slots): every
-//    tile is split, into enough slices to occupy every workgroup slot once;
-//  * a partial last round (the tile count is not a multiple of the slots, and
-//    the remainder is at most half of them): the whole rounds run unsplit and
-//    only the remainder is split, so the last round takes a slice's time
-//    instead of a whole tile's.  Taken only when that saves at least
-//    kTailMinGain K blocks per workgroup (the partials' round trip and the
-//    second launch cost about that much).
-// Slices hold at least four K blocks; at most 16 slices.
-constexpr int kTailMinGain = 24;
+int plan_slots(int kernel_id, int num_cus) { return num_cus * blocks_per_cu_for(kernel_id); }
+
+// K splitting (dense only here; see split_rule).
 static int choose_splits(long long tiles, long long slots, int kb, long long* full) {
-  *full = tiles;
-  if (tiles <= 0 || kb < 8) return 1;
-  const bool all = tiles * 2 <= slots;
-  const long long rem = all ? tiles : tiles % slots;
-  if (rem == 0 || rem * 2 > slots) return 1;
-  long long s = std::min<long long>(slots / rem, kb / 4);
-  s = std::min<long long>(s, 16);
-  if (s < 2) return 1;
-  const int per = cdiv(kb, (int)s);
-  s = cdiv(kb, per);
-  if (!all && kb - per < kTailMinGain) return 1;
-  *full = tiles - rem;
-  return (int)s;
+  return split_rule(tiles, slots, kb, full);
 }
 
 GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id) {

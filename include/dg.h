@@ -192,6 +192,11 @@ int dg_get_num_cus(void);
  * order) and C and rounds to bf16.  The workspace is allocated by the library,
  * one per (device, stream), on first need, and grows to at most one partial
  * tile per workgroup slot.
+ * The masked form's tile list depends on masked_m, which only the device
+ * reads: its kernel walks just the tiles that hold valid rows, spread evenly
+ * over the workgroups, and for K >= 3584 applies the same split rule to their
+ * count on the device (a second kernel then sums the split tiles).  For it this
+ * function reports the tile shape and splits = 1.
  * Exposed so callers can log the choice (DG_LOG=1 prints it on every call).
  */
 typedef struct dg_plan {

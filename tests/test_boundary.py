@@ -146,3 +146,15 @@ def test_planner_split_tail_with_a_cu_cap():
     if p["block_m"] == 256 and p["block_n"] == 128:
         assert p["full_tiles"] == 32 and p["splits"] == 4
     assert p["full_tiles"] % 32 == 0 or p["full_tiles"] == p["num_tiles"]
+
+
+def test_split_rule_mirror_matches_the_planner():
+    """The host mirror of the split rule used by the masked-form GPU tests agrees
+    with the library's dense plans (same rule, whole-tile count known on the host)."""
+    from tests.test_gpu_splitk import _split_rule
+    for (m, n, k, cus) in [(4096, 7168, 16384, 256), (4096, 2112, 7168, 256), (2304, 3840, 4096, 256),
+                           (4096, 7168, 2048, 256), (128, 2112, 7168, 256), (1280, 1024, 4096, 32),
+                           (64, 7168, 16384, 256), (1100, 1040, 7680, 32), (1300, 1040, 4608, 48)]:
+        p = dgm.dg_query_plan(m, n, k, 1, cus)
+        s, full = _split_rule(p["num_tiles"], cus, k // 128)
+        assert (s, full) == (p["splits"], p["full_tiles"]), (m, n, k, cus, p)

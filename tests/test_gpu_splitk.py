@@ -175,3 +175,82 @@ def test_split_tail_then_pure_split_then_whole_on_one_stream(dg):
             dg.dg_fp8_gemm_nt(_dev(a), _dev(sfa), _dev(b), _dev(sfb), _dev(c), d)
             torch.cuda.synchronize()
         check_parity(bits(d), R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"sequence {M}x{N}x{K}")
+
+
+# ---------------------------------------------------------------------------
+# masked form: the kernel walks only the tiles holding valid rows and, over long
+# K, applies the split rule to their count on the device
+# ---------------------------------------------------------------------------
+def _split_rule(tiles, slots, kb, min_gain=24):
+    """Host mirror of the library's split rule (checked against dg_query_plan in
+    test_boundary): returns (splits, whole tiles)."""
+    if tiles <= 0 or kb < 8:
+        return 1, tiles
+    every = tiles * 2 <= slots
+    rem = tiles if every else tiles % slots
+    if rem == 0 or rem * 2 > slots:
+        return 1, tiles
+    s = min(slots // rem, kb // 4, 16)
+    if s < 2:
+        return 1, tiles
+    per = -(-kb // s)
+    s = -(-kb // per)
+    if not every and kb - per < min_gain:
+        return 1, tiles
+    return s, tiles - rem
+
+
+def _masked_device_plan(mm, max_m, N, K, cus):
+    p = dgm.dg_query_plan(max_m, N, K, len(mm), cus)
+    bm, bn = p["block_m"], p["block_n"]
+    tiles = sum(-(-min(max(m, 0), max_m) // bm) for m in mm) * (-(-N // bn))
+    return _split_rule(tiles, cus, K // 128)
+
+
+@pytest.mark.parametrize("mm,max_m,N,K,cus", [
+    ([256, 200, 3, 0], 256, 512, 128 * 48, 8),       # a partial last round, split
+    ([256, 200, 3, 0], 256, 512, 128 * 40, 10),
+    ([256, 3, 0], 256, 256, 128 * 32, 32),            # too few tiles to fill 32 CUs: every tile split
+    ([100, 0, 256, 130, 7, 255], 256, 784, 128 * 40, 16),
+    ([0, 0, 0], 128, 256, 128 * 32, 8),               # no valid rows at all
+])
+def test_masked_device_split_parity(dg, mm, max_m, N, K, cus):
+    s, full = _masked_device_plan(mm, max_m, N, K, cus)
+    if sum(mm) > 0:
+        assert s > 1, f"the case must take the device-side split (plan {s}, {full})"
+    g = synth.gen_masked(len(mm), max_m, N, K, seed=sum(mm) + N + cus, masked_m=mm)
+    a, sfa, b, sfb = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb"))
+    d = sentinel_like((len(mm), max_m, N))
+    with _cu_cap(cus):
+        dg.dg_m_grouped_fp8_gemm_nt_masked(_dev(a), _dev(sfa), _dev(b), _dev(sfb),
+                                           _dev(np.asarray(mm, np.int32)), d, 0)
+        torch.cuda.synchronize()
+    db = bits(d)
+    ref, written = R.m_grouped_masked(a, sfa, b, sfb, mm)
+    assert np.all(db[~written] == 0xFFFF), "rows >= masked_m were written"
+    assert not np.any(db[written] == 0xFFFF), "valid rows left unwritten"
+    if written.any():
+        check_parity(db[written], ref[written], what=f"masked device split {mm} on {cus} CUs")
+
+
+def test_masked_device_split_exact_integer_bit_exact(dg):
+    rng = np.random.default_rng(31)
+    G, max_m, N, K, cus = 3, 256, 384, 128 * 48, 8
+    mm = [256, 129, 40]
+    s, _ = _masked_device_plan(mm, max_m, N, K, cus)
+    assert s > 1
+    a = np.zeros((G, max_m, K), np.uint8)
+    sfa = np.zeros((G, K // 128, max_m), np.float32)
+    b = np.zeros((G, N, K), np.uint8)
+    sfb = np.zeros((G, -(-N // 128), K // 128), np.float32)
+    for i in range(G):
+        a[i], sfa[i], b[i], sfb[i], _, _ = make_exact_case(rng, max_m, N, K, with_c=False)
+    d = sentinel_like((G, max_m, N))
+    with _cu_cap(cus):
+        dg.dg_m_grouped_fp8_gemm_nt_masked(_dev(a), _dev(sfa), _dev(b), _dev(sfb),
+                                           _dev(np.asarray(mm, np.int32)), d, 0)
+        torch.cuda.synchronize()
+    db = bits(d)
+    ref, written = R.m_grouped_masked(a, sfa, b, sfb, mm)
+    assert np.all(db[~written] == 0xFFFF)
+    check_bit_exact(db[written], ref[written], "masked device split exact")
