@@ -135,7 +135,7 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
   // re-derives the same plan and does nothing when there is no split).
   int masked_slots = 0;
   p.device_split = 0;
-  if (mode == MODE_MASKED && tile_config(plan.kernel_id).min_k == 0) {
+  if (mode == MODE_MASKED) {
     masked_slots = plan_slots(plan.kernel_id, cus);
     plan.num_workgroups = masked_slots;
     p.device_split = p.k / 128 >= 4 + kTailMinGain ? 1 : 2;

@@ -41,7 +41,6 @@ struct TileConfig {
   int blocks_per_cu;    // resident workgroups per CU of the compiled kernel
   int threads;          // workgroup size
   int lds_bytes;        // dynamic LDS per workgroup
-  int min_k;            // shortest K the planner picks this shape for
 };
 int num_tile_configs();
 TileConfig tile_config(int kernel_id);

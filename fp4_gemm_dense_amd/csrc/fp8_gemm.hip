@@ -57,22 +57,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   static_assert(128 % (NT * 16) == 0 && (BN % 128 == 0 || 128 % BN == 0), "one B scale per wave");
   static_assert(MT % 4 == 0, "a lane reads its row scales with 16-byte LDS loads");
   constexpr int NBLK = MT * NT;   // 16x16 accumulator blocks per wave
-  constexpr bool STREAM_A = MT > 4;   // read A fragments A_AHEAD row blocks ahead instead of all at once
-#ifndef DG_STREAM_LAG
-#define DG_STREAM_LAG 4
-#endif
-#ifndef DG_A_AHEAD
-#define DG_A_AHEAD 2
-#endif
-  // matrix instructions between a partial's issue and its promotion (at most NT)
-  constexpr int LAG = STREAM_A ? (DG_STREAM_LAG < NT ? DG_STREAM_LAG : NT) : NT;
-  constexpr int A_AHEAD = DG_A_AHEAD;
+  static_assert(MT <= 4 && STAGES >= 3, "all A fragments of a K block live at once; three or more slots");
+  constexpr int LAG = NT;         // matrix instructions between a partial's issue and its promotion (<= NT)
   // Epilogue traffic.  The C tile (BM x BN bf16) is copied into two ring slots
   // that the last two K blocks leave free, in halves of BM/2 rows; each wave
   // copies CPW 1-KB pieces of a half.  A C row holds CPR 16-byte chunks, chunk c
   // of row r sits at position c ^ (r % 16).  Every wave then issues exactly NST
   // 8-byte stores of D.
-  // (With a two-slot ring the second half can only follow the last K block.)
   constexpr int CPR = BN / 8;
   constexpr int C_HALF = BM / 2 * BN * 2;
   static_assert(CPR >= 16 && 1024 % (BN * 2) == 0, "C rows must be 256 or 512 bytes");
@@ -125,7 +116,6 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   };
   // Work units: units [0, full_tiles) are the tiles of the same index, computed
   // whole; unit full_tiles + u is K slice u % splits of tile full_tiles + u / splits.
-  // (Two-slot shapes are never split.)
   int full_tiles = p.full_tiles, splits = p.splits, kb_per_split = p.kb_per_split, total_units = p.total_tiles;
   // Masked form, device-planned: the tiles are those holding valid rows, group
   // after group (group g has ceil(masked_m[g] / BM) tile rows), and the split
@@ -137,13 +127,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     int tiles = 0;
     for (int g = 0; g < p.num_groups; ++g) tiles += masked_group_tiles(p.masked_m, g, M, BM, p.tiles_n);
     long long full = tiles;
-    splits = STAGES >= 3 && p.device_split == 1 ? split_rule(tiles, G, KB, &full) : 1;
+    splits = p.device_split == 1 ? split_rule(tiles, G, KB, &full) : 1;
     full_tiles = (int)full;
     kb_per_split = (KB + splits - 1) / splits;
     total_units = full_tiles + (tiles - full_tiles) * splits;
     mg_cnt = masked_group_tiles(p.masked_m, 0, M, BM, p.tiles_n);
   }
-  const bool can_split = STAGES >= 3 && splits > 1;
+  const bool can_split = splits > 1;
   auto decode = [&](int t, Tile& tile) -> bool {
     tile.kb0 = 0;
     tile.nkb = KB;
@@ -362,10 +352,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       // copies spread over the block (not with streamed A fragments, whose
       // scheduling fences would split the pattern)
       constexpr int ILV = RA + RB;
-#ifndef DG_STREAM_ILV
-#define DG_STREAM_ILV 0
-#endif
-      constexpr int ILV_STEP = ((!STREAM_A || DG_STREAM_ILV) && NBLK / ILV > 0) ? NBLK / ILV : NBLK + 1;
+      constexpr int ILV_STEP = NBLK / ILV > 0 ? NBLK / ILV : NBLK + 1;
       wait_stage(kb, KT, stores_after);
       block_barrier();
       if (STEADY) {
@@ -375,12 +362,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
           for (int idx = 0; idx < ILV; ++idx) issue_ab(idx, kb + STAGES - 1, wr_slot);
         }
       } else if (has_c) {
-        // slot (KT + h) % STAGES takes half h: free from block KT - 2 + h on with
-        // three or more slots; with two, half 0 goes in during the last block and
-        // half 1 after it
-        if (STAGES == 2) {
-          if (kb == KT - 1) issue_c(cur, 0, (uint32_t)(KT % STAGES) * STAGE);
-        } else if (kb == KT - 1) {
+        // slot (KT + h) % STAGES takes half h: free from block KT - 2 + h on
+        if (kb == KT - 1) {
           if (KT == 1) issue_c(cur, 0, (uint32_t)(KT % STAGES) * STAGE);
           issue_c(cur, 1, (uint32_t)((KT + 1) % STAGES) * STAGE);
         } else if (kb == KT - 2) {
@@ -415,7 +398,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
         bf[nt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
 #pragma unroll
-      for (int mt = 0; mt < (STREAM_A ? A_AHEAD : MT); ++mt) af[mt] = load_a(mt);
+      for (int mt = 0; mt < MT; ++mt) af[mt] = load_a(mt);
       // The wave computes its tile transposed: block (mt, nt) is B_nt . A_mt^T,
       // so a lane's four results share one row of D (column lrow of the block)
       // and one A scale.  Block j = mt*NT + nt goes into partial register j % LAG;
@@ -423,12 +406,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       // of block j + NBLK - LAG of the previous K block (scale sprev), else the
       // one of block j - LAG of this K block.  A partial is thus read LAG
       // matrix instructions after its issue, so the FMAs never wait on it.
-      // With STREAM_A the A fragment of row block mt+A_AHEAD is read while row
-      // block mt computes (scheduling fences keep the reads from being hoisted),
-      // so only A_AHEAD+1 A fragments are live at a time.
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if (STREAM_A && mt + A_AHEAD < MT) af[mt + A_AHEAD] = load_a(mt + A_AHEAD);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int j = mt * NT + nt;
@@ -445,15 +424,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
           part[r] = mfma_e4m3_16x16x128(bf[nt], af[mt], v4f{0.f, 0.f, 0.f, 0.f});
           const bool copy_here = STEADY && ILV_STEP * ILV <= NBLK && j % ILV_STEP == ILV_STEP - 1 && j / ILV_STEP < ILV;
           if (copy_here) issue_ab(j / ILV_STEP, kb + STAGES - 1, wr_slot);
-          if (!STREAM_A) {
-            // keep the schedule: the promotion FMAs of block j ride with its matrix
-            // instruction, and a copy follows every ILV_STEP-th one
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (promotion)
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-            if (copy_here) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM read (copy)
-          }
+          // keep the schedule: the promotion FMAs of block j ride with its matrix
+          // instruction, and a copy follows every ILV_STEP-th one
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (promotion)
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+          if (copy_here) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM read (copy)
         }
-        if (STREAM_A) __builtin_amdgcn_sched_barrier(0);
       }
       sprev = scur[MT - 1];
       rd_slot = (rd_slot + STAGE == STAGES * STAGE) ? 0u : rd_slot + STAGE;
@@ -477,10 +453,6 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     // columns nt*16 + 4*lgrp .. +3 of the wave's sub-tile: 8 bytes of one row.
     v2i o[MT][NT];
     if (has_c) {
-      if (STAGES == 2) {
-        block_barrier();   // every wave is done with the last block's slot
-        issue_c(done, 1, (uint32_t)((KT + 1) % STAGES) * STAGE);
-      }
       wait_vmcnt<0>();   // this wave's C pieces have landed
       block_barrier();   // ... and every other wave's
     }
@@ -682,13 +654,11 @@ hipError_t launch_masked_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& p
   X(0, 4, 4, 4, 2, 3, 1)      \
   X(1, 4, 4, 2, 4, 3, 1)      \
   X(2, 4, 4, 2, 2, 3, 1)      \
-  X(3, 4, 2, 1, 4, 4, 1)      \
-  X(4, 8, 4, 2, 4, 2, 1)
+  X(3, 4, 2, 1, 4, 4, 1)
 
 static const TileConfig kTileConfigs[] = {
 #define X(id, MT, NT, WM, WN, ST, OCC) {WM * MT * 16, WN * NT * 16, OCC, WM * WN * 64,                     \
-                                        ST * ((WM * MT * 16 + WN * NT * 16) * 128 + WM * MT * 16 * 4), \
-                                        ST == 2 ? (1 << 30) : 0},
+                                        ST * ((WM * MT * 16 + WN * NT * 16) * 128 + WM * MT * 16 * 4)},
     DG_TILE_CONFIGS(X)
 #undef X
 };

@@ -45,7 +45,7 @@ GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num
   plan.splits = 1;
   plan.kb_per_split = k / 128;
   plan.full_tiles = plan.num_tiles;
-  if (mode == MODE_DENSE && tc.min_k == 0) {   // two-slot (long K) shapes never split
+  if (mode == MODE_DENSE) {
     long long full = total;
     plan.splits = choose_splits(total, slots, k / 128, &full);
     plan.kb_per_split = cdiv(k / 128, plan.splits);
@@ -66,7 +66,6 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
   for (int id = 0; id < num_tile_configs(); ++id) {
     TileConfig tc = tile_config(id);
     if (mode == MODE_CONTIG && (128 % tc.block_m) != 0) continue;   // blocks must be group-pure
-    if (k < tc.min_k) continue;   // two-slot rings only pay off over long K loops
     int tm = cdiv(rows, tc.block_m);
     int tn = cdiv(n, tc.block_n);
     long long tiles = (long long)tm * tn * (mode == MODE_DENSE ? 1 : (mode == MODE_MASKED ? num_groups : 1));
@@ -78,11 +77,8 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     int slots = num_cus * blocks_per_cu_for(id);
     const int kb = k / 128;
     long long full = tiles;
-    const int splits = mode == MODE_DENSE && tc.min_k == 0 ? choose_splits(tiles, slots, kb, &full) : 1;
+    const int splits = mode == MODE_DENSE ? choose_splits(tiles, slots, kb, &full) : 1;
     const long long units = full + (tiles - full) * splits;
-    // a two-slot (long K) shape must at least fill the chip once: in a single
-    // partial wave its large tiles leave compute units idle for the whole call
-    if (tc.min_k > 0 && units < slots) continue;
     double fill;
     if (splits > 1 && full > 0) {
       const double steps = (double)(full / slots) * kb + cdiv(kb, splits) + kTailMinGain / 3.0;
