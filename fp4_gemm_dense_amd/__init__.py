@@ -38,6 +38,7 @@ _SIGNATURES = {
     "dg_set_num_cus": (_I, [_I]),
     "dg_get_num_cus": (_I, []),
     "dg_query_plan": (_I, [_I, _I, _I, _I, _I, _P]),
+    "dg_query_plan_contiguous": (_I, [_I, _I, _I, _I, _I, _P]),
     "dg_num_tiles": (_I, [_I, _I, _I, _I]),
     "dg_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -210,6 +211,13 @@ def dg_get_num_cus():
 def dg_query_plan(m, n, k, num_groups=1, num_cus=0):
     p = DgPlan()
     _check("dg_query_plan", lib().dg_query_plan(m, n, k, num_groups, num_cus, ctypes.byref(p)))
+    return {f: getattr(p, f) for f, _ in DgPlan._fields_}
+
+
+def dg_query_plan_contiguous(m, n, k, num_groups, num_cus=0):
+    p = DgPlan()
+    _check("dg_query_plan_contiguous",
+           lib().dg_query_plan_contiguous(m, n, k, num_groups, num_cus, ctypes.byref(p)))
     return {f: getattr(p, f) for f, _ in DgPlan._fields_}
 
 

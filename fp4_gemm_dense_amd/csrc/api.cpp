@@ -262,7 +262,7 @@ int dg_num_tiles(int m, int n, int block_m, int block_n) {
   return ((m + block_m - 1) / block_m) * ((n + block_n - 1) / block_n);
 }
 
-int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out) {
+static int query_plan(int m, int n, int k, int num_groups, int mode, int num_cus, dg_plan* out) {
   if (!out || m <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERR_INVALID_ARG;
   if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
   if (num_cus <= 0) {
@@ -270,7 +270,6 @@ int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out
     if (!di.ok) return DG_ERR_NO_DEVICE;
     num_cus = effective_cus(di);
   }
-  int mode = num_groups > 1 ? MODE_MASKED : MODE_DENSE;
   GemmPlan p = plan_fp8_gemm(m, n, k, num_groups, mode, num_cus, 0);
   out->block_m = p.block_m;
   out->block_n = p.block_n;
@@ -280,6 +279,14 @@ int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out
   out->splits = p.splits;
   out->full_tiles = p.full_tiles;
   return DG_OK;
+}
+
+int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out) {
+  return query_plan(m, n, k, num_groups, num_groups > 1 ? MODE_MASKED : MODE_DENSE, num_cus, out);
+}
+
+int dg_query_plan_contiguous(int m, int n, int k, int num_groups, int num_cus, dg_plan* out) {
+  return query_plan(m, n, k, num_groups, MODE_CONTIG, num_cus, out);
 }
 
 const char* dg_status_string(int status) {

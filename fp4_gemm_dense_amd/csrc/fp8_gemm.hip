@@ -539,11 +539,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
 // ---------------------------------------------------------------------------
 // One thread per 8 consecutive columns of one row of a split tile.  Split tile
 // i (raster tile full_tiles + i) keeps slice s at workspace tile i * splits + s,
-// each bm x bn fp32, row-major.
+// each bm x bn fp32, row-major.  Contiguous form (m_indices given): a padding
+// block's tile was never computed and rows of other groups are not written.
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ ws,
                                                             const uint16_t* __restrict__ c, uint16_t* d, int m,
                                                             int n, int splits, int full_tiles, int split_tiles,
-                                                            int bm, int bn, int tiles_m, int tiles_n, int group_m) {
+                                                            int bm, int bn, int tiles_m, int tiles_n, int group_m,
+                                                            const int32_t* __restrict__ m_indices, int groups) {
   const int per_row = bn / 8;
   const long long per_tile = (long long)bm * per_row;
   const long long total = per_tile * split_tiles;
@@ -556,6 +558,10 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     raster_tile(full_tiles + st, tiles_m, tiles_n, group_m, &tm, &tn);
     const int row = tm * bm + r, col = tn * bn + c8 * 8;
     if (row >= m || col >= n) continue;
+    if (m_indices) {
+      const int g = m_indices[tm * bm];
+      if (g < 0 || g >= groups || m_indices[row] != g) continue;
+    }
     const float4* w = reinterpret_cast<const float4*>(ws + (size_t)st * splits * tile_elems + (size_t)r * bn + c8 * 8);
     float4 lo = w[0], hi = w[1];
     for (int s = 1; s < splits; ++s) {
@@ -588,7 +594,8 @@ hipError_t launch_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& plan, in
   const int grid = (int)std::min<long long>((threads + 255) / 256, (long long)num_cus * 8);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, p.ws, p.c, p.d, p.m, p.n, plan.splits,
-                     plan.full_tiles, split_tiles, plan.block_m, plan.block_n, p.tiles_m, p.tiles_n, p.group_m);
+                     plan.full_tiles, split_tiles, plan.block_m, plan.block_n, p.tiles_m, p.tiles_n, p.group_m,
+                     p.m_indices, p.num_groups);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ static int blocks_per_cu_for(int kernel_id) {
 
 int plan_slots(int kernel_id, int num_cus) { return num_cus * blocks_per_cu_for(kernel_id); }
 
-// K splitting (dense only here; see split_rule).
+// K splitting for the dense and contiguous forms (see split_rule).
 static int choose_splits(long long tiles, long long slots, int kb, long long* full) {
   return split_rule(tiles, slots, kb, full);
 }
@@ -45,7 +45,7 @@ GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num
   plan.splits = 1;
   plan.kb_per_split = k / 128;
   plan.full_tiles = plan.num_tiles;
-  if (mode == MODE_DENSE) {
+  if (mode != MODE_MASKED) {   // (the masked form's split is planned on the device)
     long long full = total;
     plan.splits = choose_splits(total, slots, k / 128, &full);
     plan.kb_per_split = cdiv(k / 128, plan.splits);
@@ -77,7 +77,7 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     int slots = num_cus * blocks_per_cu_for(id);
     const int kb = k / 128;
     long long full = tiles;
-    const int splits = mode == MODE_DENSE ? choose_splits(tiles, slots, kb, &full) : 1;
+    const int splits = mode != MODE_MASKED ? choose_splits(tiles, slots, kb, &full) : 1;
     const long long units = full + (tiles - full) * splits;
     double fill;
     if (splits > 1 && full > 0) {

@@ -210,6 +210,12 @@ typedef struct dg_plan {
 } dg_plan;
 int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out);
 
+/* The same for the M-grouped contiguous form (dg_m_grouped_fp8_gemm_nt_contiguous):
+ * m is the total row count of the layout, num_groups the groups.  Its tiles may
+ * be split along K by the same rule (padding blocks are skipped).  Host-only
+ * when num_cus > 0. */
+int dg_query_plan_contiguous(int m, int n, int k, int num_groups, int num_cus, dg_plan* out);
+
 /* Number of output tiles for a tile shape: ceil(m/block_m) * ceil(n/block_n). Host-only. */
 int dg_num_tiles(int m, int n, int block_m, int block_n);
 

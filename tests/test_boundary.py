@@ -158,3 +158,14 @@ def test_split_rule_mirror_matches_the_planner():
         p = dgm.dg_query_plan(m, n, k, 1, cus)
         s, full = _split_rule(p["num_tiles"], cus, k // 128)
         assert (s, full) == (p["splits"], p["full_tiles"]), (m, n, k, cus, p)
+
+
+def test_contiguous_plan_query_is_host_only_and_may_split():
+    # 33280 rows (8 groups padded to 128) x 4096 x 7168 on 256 CUs: 4160 tiles of
+    # 128 x 256, the last 64 split along K
+    p = dgm.dg_query_plan_contiguous(33280, 4096, 7168, 8, 256)
+    assert p["block_m"] <= 128 and 128 % p["block_m"] == 0   # blocks stay group-pure
+    assert p["num_tiles"] == dgm.dg_num_tiles(33280, 4096, p["block_m"], p["block_n"])
+    assert p["splits"] > 1 and p["full_tiles"] % 256 == 0 and p["full_tiles"] < p["num_tiles"]
+    p = dgm.dg_query_plan_contiguous(33280, 7168, 2048, 8, 256)
+    assert p["splits"] == 1 and p["full_tiles"] == p["num_tiles"]

@@ -254,3 +254,52 @@ def test_masked_device_split_exact_integer_bit_exact(dg):
     ref, written = R.m_grouped_masked(a, sfa, b, sfb, mm)
     assert np.all(db[~written] == 0xFFFF)
     check_bit_exact(db[written], ref[written], "masked device split exact")
+
+
+# ---------------------------------------------------------------------------
+# contiguous form: the same split rule over its tiles (padding blocks skipped)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("counts,N,K,cus", [
+    ([256, 384, 128, 512], 1024, 128 * 32, 32),       # whole blocks only
+    ([300, 0, 100, 500, 380], 768, 128 * 48, 16),     # padding rows inside split tiles
+])
+def test_contiguous_split_tail_parity(dg, counts, N, K, cus):
+    g = synth.gen_contiguous(len(counts), sum(counts), N, K, seed=sum(counts) + N, counts=counts)
+    a, sfa, b, sfb, mi = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "m_indices"))
+    M = mi.size
+    p = dgm.dg_query_plan_contiguous(M, N, K, len(counts), cus)
+    assert p["splits"] > 1 and 0 < p["full_tiles"] < p["num_tiles"], f"no split tail: {p}"
+    d = sentinel_like((M, N))
+    with _cu_cap(cus):
+        dg.dg_m_grouped_fp8_gemm_nt_contiguous(_dev(a), _dev(sfa), _dev(b), _dev(sfb), _dev(mi), d)
+        torch.cuda.synchronize()
+    db = bits(d)
+    ref, written = R.m_grouped_contiguous(a, sfa, b, sfb, mi)
+    assert np.all(db[~written] == 0xFFFF), "padding rows were written"
+    assert not np.any(db[written] == 0xFFFF), "group rows left unwritten"
+    check_parity(db[written], ref[written], what=f"contig split tail {counts} on {cus} CUs")
+
+
+def test_contiguous_split_tail_exact_integer_bit_exact(dg):
+    rng = np.random.default_rng(17)
+    counts, N, K, cus = [300, 0, 100, 500, 380], 768, 128 * 48, 16
+    mi, _ = synth.padded_group_layout(counts)
+    mi = np.array(mi, np.int32)
+    M = mi.size
+    p = dgm.dg_query_plan_contiguous(M, N, K, len(counts), cus)
+    assert p["splits"] > 1 and 0 < p["full_tiles"] < p["num_tiles"]
+    a, sfa, _, _, _, _ = make_exact_case(rng, M, N, K, with_c=False)
+    bs, sbs = [], []
+    for _ in counts:
+        _, _, b1, sfb1, _, _ = make_exact_case(rng, 1, N, K, with_c=False)
+        bs.append(b1)
+        sbs.append(sfb1)
+    b, sfb = np.stack(bs), np.stack(sbs)
+    d = sentinel_like((M, N))
+    with _cu_cap(cus):
+        dg.dg_m_grouped_fp8_gemm_nt_contiguous(_dev(a), _dev(sfa), _dev(b), _dev(sfb), _dev(mi), d)
+        torch.cuda.synchronize()
+    db = bits(d)
+    ref, written = R.m_grouped_contiguous(a, sfa, b, sfb, mi)
+    assert np.all(db[~written] == 0xFFFF)
+    check_bit_exact(db[written], ref[written], "contig split tail exact")
