@@ -111,6 +111,15 @@ __device__ inline int masked_group_tiles(const int32_t* masked_m, int g, int max
   return (mm + bm - 1) / bm * tiles_n;
 }
 
+// Masked form: output tiles of all groups, summed by the 64 lanes of a wave
+// in parallel (every lane returns the total).
+__device__ inline int masked_total_tiles(const int32_t* masked_m, int groups, int max_m, int bm, int tiles_n) {
+  int part = 0;
+  for (int g = (int)(threadIdx.x & 63); g < groups; g += 64) part += masked_group_tiles(masked_m, g, max_m, bm, tiles_n);
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+  return __builtin_amdgcn_readfirstlane(part);
+}
+
 // Raster order of the output tiles (one group): bands of group_m tile rows, walked
 // column by column inside a band, tile rows fastest.  Tile index tl -> (tile row, tile column).
 __host__ __device__ inline void raster_tile(int tl, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {

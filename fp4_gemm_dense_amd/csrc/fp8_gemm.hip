@@ -124,8 +124,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   const bool dev_plan = MODE == MODE_MASKED && p.device_split;
   int mg = 0, mg_base = 0, mg_cnt = 0;   // group cursor of the decode (tile ids only grow)
   if (dev_plan) {
-    int tiles = 0;
-    for (int g = 0; g < p.num_groups; ++g) tiles += masked_group_tiles(p.masked_m, g, M, BM, p.tiles_n);
+    const int tiles = masked_total_tiles(p.masked_m, p.num_groups, M, BM, p.tiles_n);
     long long full = tiles;
     splits = p.device_split == 1 ? split_rule(tiles, G, KB, &full) : 1;
     full_tiles = (int)full;
@@ -601,21 +600,25 @@ hipError_t launch_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& plan, in
 
 // Masked form, device-planned: the same plan as the GEMM kernel (valid tiles
 // of all groups in group order, split rule over their count on `slots`
-// workgroups); one workgroup per split tile at a time.
+// workgroups).  Work item = 8 rows of one split tile (one thread per 8
+// columns for bn = 256), so a split tile's partials are summed by many
+// workgroups at once.
 __global__ void __launch_bounds__(256) masked_splitk_reduce_kernel(const float* __restrict__ ws, uint16_t* d,
                                                                    const int32_t* __restrict__ masked_m,
                                                                    int groups, int max_m, int n, int kb, int bm,
                                                                    int bn, int tiles_n, int group_m, int slots) {
-  int tiles = 0;
-  for (int g = 0; g < groups; ++g) tiles += masked_group_tiles(masked_m, g, max_m, bm, tiles_n);
+  const int tiles = masked_total_tiles(masked_m, groups, max_m, bm, tiles_n);
   long long full = tiles;
   const int splits = split_rule(tiles, slots, kb, &full);
   if (splits <= 1) return;
   const int split_tiles = tiles - (int)full;
   const int per_row = bn / 8;
+  const int rows_per_item = 256 / per_row;
+  const int items_per_tile = bm / rows_per_item;
   const size_t tile_elems = (size_t)bm * bn;
   int mg = 0, base = 0, cnt = masked_group_tiles(masked_m, 0, max_m, bm, tiles_n);
-  for (int st = blockIdx.x; st < split_tiles; st += gridDim.x) {
+  for (int it = blockIdx.x; it < split_tiles * items_per_tile; it += gridDim.x) {
+    const int st = it / items_per_tile;
     const int t = (int)full + st;
     while (t >= base + cnt) {
       base += cnt;
@@ -625,24 +628,22 @@ __global__ void __launch_bounds__(256) masked_splitk_reduce_kernel(const float* 
     raster_tile(t - base, cnt / tiles_n, tiles_n, group_m, &tm, &tn);
     int mm = masked_m[mg];
     mm = mm < 0 ? 0 : (mm > max_m ? max_m : mm);
-    uint16_t* dg = d + (size_t)mg * max_m * n;
-    const float* wt = ws + (size_t)st * splits * tile_elems;
-    for (int q = threadIdx.x; q < bm * per_row; q += 256) {
-      const int r = q / per_row, c8 = q - r * per_row;
-      const int row = tm * bm + r, col = tn * bn + c8 * 8;
-      if (row >= mm || col >= n) continue;
-      const float4* w = reinterpret_cast<const float4*>(wt + (size_t)r * bn + c8 * 8);
-      float4 lo = w[0], hi = w[1];
-      for (int sl = 1; sl < splits; ++sl) {
-        const float4* ws_s = w + sl * (tile_elems / 4);
-        const float4 a = ws_s[0], b = ws_s[1];
-        lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
-        hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
-      }
-      const uint4 o = {pack_bf16x2_rne(lo.x, lo.y), pack_bf16x2_rne(lo.z, lo.w), pack_bf16x2_rne(hi.x, hi.y),
-                       pack_bf16x2_rne(hi.z, hi.w)};
-      reinterpret_cast<uint4*>(dg)[((size_t)row * n + col) / 8] = o;
+    const int r = (it - st * items_per_tile) * rows_per_item + (int)threadIdx.x / per_row;
+    const int c8 = (int)threadIdx.x % per_row;
+    const int row = tm * bm + r, col = tn * bn + c8 * 8;
+    if (r >= bm || row >= mm || col >= n) continue;
+    const float4* w = reinterpret_cast<const float4*>(ws + (size_t)st * splits * tile_elems + (size_t)r * bn + c8 * 8);
+    float4 lo = w[0], hi = w[1];
+    for (int sl = 1; sl < splits; ++sl) {
+      const float4* ws_s = w + sl * (tile_elems / 4);
+      const float4 a = ws_s[0], b = ws_s[1];
+      lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+      hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
     }
+    const uint4 o = {pack_bf16x2_rne(lo.x, lo.y), pack_bf16x2_rne(lo.z, lo.w), pack_bf16x2_rne(hi.x, hi.y),
+                     pack_bf16x2_rne(hi.z, hi.w)};
+    uint16_t* dg = d + (size_t)mg * max_m * n;
+    reinterpret_cast<uint4*>(dg)[((size_t)row * n + col) / 8] = o;
   }
 }
 
