@@ -124,10 +124,6 @@ __global__ void __launch_bounds__(1024) ffn_route_kernel(FfnParams p) {
 // 2./3. grouped FP8 x FP4 GEMM (linear1 with SwiGLU + requant, or linear2)
 // ---------------------------------------------------------------------------
 
-// 64-byte rows of FP4 weights: 4 chunks of 16 bytes; chunk c of row r sits at
-// position c ^ swzb(r) (conflict-free for 16 consecutive rows; depends on r % 16).
-__device__ __forceinline__ int swzb(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
-
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 // Smallest e with 448 * 2^e >= amax (amax > 0): with amax = f * 2^x, f in [0.5, 1),
@@ -158,31 +154,43 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
 // each wave 32 rows x 128 weight rows (2 x 8 blocks of 16 x 16).  Each block is
 // computed transposed (W_nt . X_mt^T, the FP4 weights as the instruction's first
 // operand), so a lane's four results are four consecutive weight rows (output
-// columns) of one pair row.  Operand tiles and their scale words go through a
-// 4-slot LDS ring by buffer loads; the K block advances the scalar offset only.
+// columns) of one pair row.  Operand tiles and their scale words go through LDS
+// rings by buffer loads; the K position advances the scalar offset only:
+//  * per 128-wide K block (4-slot ring): the activation tile and the scale
+//    words of both operands;
+//  * per pair of K blocks (2-slot ring): the FP4 weight tile.  A weight row
+//    holds 64 bytes per K block, so copying two blocks at once makes every copy
+//    request a whole 128-byte line (half-line requests move about a third fewer
+//    bytes per CU and cycle).
 constexpr int FFN_WM = 4, FFN_WN = 2, FFN_MT = 2, FFN_NT = 8;
 constexpr int FFN_BM = FFN_WM * FFN_MT * 16;      // 128 pair rows per tile
 constexpr int FFN_BN = FFN_WN * FFN_NT * 16;      // 256 weight rows per tile
-constexpr int FFN_STAGES = 4;
+constexpr int FFN_STAGES = 4;                     // K-block slots (activations, scales)
+constexpr int FFN_BSTAGES = 2;                    // K-block-pair slots (weights)
 constexpr int FFN_THREADS = 512;
 constexpr int FFN_A_BYTES = FFN_BM * 128;         // e4m3, 128 K per row
-constexpr int FFN_B_BYTES = FFN_BN * 64;          // e2m1, 128 K per row
 constexpr int FFN_SA_BYTES = FFN_BM * 4;          // one scale word per row
 constexpr int FFN_SB_BYTES = FFN_BN * 4;
-constexpr int FFN_STAGE = FFN_A_BYTES + FFN_B_BYTES + FFN_SA_BYTES + FFN_SB_BYTES;
-constexpr int FFN_LDS = FFN_STAGES * FFN_STAGE;
+constexpr int FFN_STAGE = FFN_A_BYTES + FFN_SA_BYTES + FFN_SB_BYTES;
+constexpr int FFN_BPAIR = FFN_BN * 128;           // e2m1, 256 K per row
+constexpr int FFN_LDS = FFN_STAGES * FFN_STAGE + FFN_BSTAGES * FFN_BPAIR;
 
 template <int MODE>   // 1: linear1 (+ SwiGLU + requant), 2: linear2 (fp32 out)
 __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
   constexpr int NW = FFN_WM * FFN_WN;
   constexpr int MT = FFN_MT, NT = FFN_NT, STAGES = FFN_STAGES, STAGE = FFN_STAGE;
-  constexpr int OFF_B = FFN_A_BYTES, OFF_SA = OFF_B + FFN_B_BYTES, OFF_SB = OFF_SA + FFN_SA_BYTES;
-  constexpr int RA = FFN_BM / 8 / NW;              // A regions (8 rows x 128 B) per wave
-  constexpr int RB = FFN_BN / 16 / NW;             // B regions (16 rows x 64 B) per wave
+  constexpr int OFF_SA = FFN_A_BYTES, OFF_SB = OFF_SA + FFN_SA_BYTES;
+  constexpr int BRING = FFN_STAGES * FFN_STAGE;    // start of the weight-pair ring
+  constexpr int RA = FFN_BM / 8 / NW;              // A regions (8 rows x 128 B) per wave per K block
+  constexpr int RB = FFN_BN / 8 / NW;              // B regions (8 rows x 128 B) per wave per K-block pair
   constexpr int SAW = FFN_BM / NW;                 // A scale words per wave
   constexpr int SBW = FFN_BN / NW;                 // B scale words per wave
   static_assert(SAW <= 64 && SBW <= 64, "one scale copy per wave");
-  constexpr int LPS = RA + RB + 2;                 // copy instructions per wave per stage
+  // Copy instructions per wave: LA per K block (two scale words, A regions),
+  // LB more per K-block pair (B regions).  Past the end of a tile's K range the
+  // same instructions are issued with out-of-range offsets (they read nothing),
+  // so the counts, and the waits below, never change.
+  constexpr int LA = RA + 2, LB = RB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int tile_base[FFN_MAX_EXPERTS + 1];
   __shared__ float red[FFN_WN][FFN_BM];
@@ -226,14 +234,18 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
   const uint32_t a_hi = (wave_m * MT * 16 + lrow) * 128 + (((lgrp + 4) ^ sw) << 4);
   const uint32_t sa_rd = OFF_SA + (wave_m * MT * 16 + lrow) * 4;
   // weight rows of block nt: linear1 gate rows 64*wn + 16nt (nt < 4) and the
-  // matching up rows 128 + 64*wn + 16(nt-4); linear2 output rows 128*wn + 16nt
+  // matching up rows 128 + 64*wn + 16(nt-4); linear2 output rows 128*wn + 16nt.
+  // A weight row in the pair ring holds 8 chunks of 16 bytes (chunks 0-3: the
+  // even K block, 4-7: the odd one), chunk c at position c ^ swz(row); an e2m1
+  // lane (row, g) reads chunk g of its K block.
   uint32_t b_rd[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = MODE == 1 ? ((nt < 4 ? 0 : 128) + wave_n * 64 + (nt & 3) * 16 + lrow)
                               : (wave_n * 128 + nt * 16 + lrow);
-    b_rd[nt] = OFF_B + row * 64 + ((lgrp ^ swzb(row)) << 4);
+    b_rd[nt] = row * 128;
   }
+  const uint32_t b_ch[2] = {(uint32_t)((lgrp ^ sw) << 4), (uint32_t)(((4 + lgrp) ^ sw) << 4)};
   const uint32_t sb_rd0 = OFF_SB + (MODE == 1 ? wave_n * 64 + lrow : wave_n * 128 + lrow) * 4;
 
   const uint8_t* a_base = MODE == 1 ? p.x : p.q;
@@ -277,10 +289,10 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
     }
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
-      const int r = (wave * RB + j) * 16 + (lane >> 2);            // tile weight row
+      const int r = (wave * RB + j) * 8 + (lane >> 3);             // tile weight row
       const uint32_t wr = MODE == 1 ? (uint32_t)((r < 128 ? 0 : I) + tn * 128 + (r & 127))
                                     : (uint32_t)(tn * FFN_BN + r);
-      b_off[j] = wr * wrow_bytes + (((lane & 3) ^ swzb(r)) << 4);
+      b_off[j] = wr * wrow_bytes + (((lane & 7) ^ swz(r)) << 4);
     }
     {
       const int r = wave * SAW + (lane < SAW ? lane : 0);
@@ -294,32 +306,27 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
                                     : (uint32_t)(tn * FFN_BN + r);
       sb_off = wr * wsf_bytes;
     }
-    auto issue = [&](int kb, uint32_t slot) {
-      uint8_t* base = smem + slot;
-#pragma unroll
-      for (int j = 0; j < RA; ++j) buf16_to_lds(rsA, a_off[j], (uint32_t)kb * 128u, base + (wave * RA + j) * 1024);
-#pragma unroll
-      for (int j = 0; j < RB; ++j)
-        buf16_to_lds(rsB, b_off[j], (uint32_t)kb * 64u, base + OFF_B + (wave * RB + j) * 1024);
-      // the A scale word holds four 128-wide K blocks (x_sf, and sq in groups of four)
-      if (SAW == 64 || lane < SAW) buf4_to_lds(rsSA, sa_off, (uint32_t)(kb >> 2) * 4u, base + OFF_SA + wave * SAW * 4);
-      if (SBW == 64 || lane < SBW) buf4_to_lds(rsSB, sb_off, (uint32_t)kb * 4u, base + OFF_SB + wave * SBW * 4);
-    };
-    // the same copies split up: the two scale words first, then A/B region idx
-    // (A regions, then B regions) one instruction at a time
+    const int NPAIR = (KB + 1) >> 1;
+    // copies of K block kb into A-ring slot `slot` (kb >= KB: read nothing)
     auto issue_scales = [&](int kb, uint32_t slot) {
       uint8_t* base = smem + slot;
-      if (SAW == 64 || lane < SAW) buf4_to_lds(rsSA, sa_off, (uint32_t)(kb >> 2) * 4u, base + OFF_SA + wave * SAW * 4);
-      if (SBW == 64 || lane < SBW) buf4_to_lds(rsSB, sb_off, (uint32_t)kb * 4u, base + OFF_SB + wave * SBW * 4);
+      const bool live = kb < KB;
+      const uint32_t sa = live ? sa_off : kBufferOutOfRange, sb = live ? sb_off : kBufferOutOfRange;
+      const int kc = live ? kb : 0;
+      // the A scale word holds four 128-wide K blocks (x_sf, and sq in groups of four)
+      if (SAW == 64 || lane < SAW) buf4_to_lds(rsSA, sa, (uint32_t)(kc >> 2) * 4u, base + OFF_SA + wave * SAW * 4);
+      if (SBW == 64 || lane < SBW) buf4_to_lds(rsSB, sb, (uint32_t)kc * 4u, base + OFF_SB + wave * SBW * 4);
     };
-    auto issue_ab = [&](int idx, int kb, uint32_t slot) {
-      uint8_t* base = smem + slot;
-#pragma unroll
-      for (int j = 0; j < RA; ++j)
-        if (idx == j) buf16_to_lds(rsA, a_off[j], (uint32_t)kb * 128u, base + (wave * RA + j) * 1024);
-#pragma unroll
-      for (int j = 0; j < RB; ++j)
-        if (idx == RA + j) buf16_to_lds(rsB, b_off[j], (uint32_t)kb * 64u, base + OFF_B + (wave * RB + j) * 1024);
+    auto issue_a = [&](int j, int kb, uint32_t slot) {
+      const bool live = kb < KB;
+      buf16_to_lds(rsA, live ? a_off[j] : kBufferOutOfRange, (uint32_t)(live ? kb : 0) * 128u,
+                   smem + slot + (wave * RA + j) * 1024);
+    };
+    // copies of K-block pair pp into pair slot `bslot` (pp >= NPAIR: read nothing)
+    auto issue_b = [&](int j, int pp, uint32_t bslot) {
+      const bool live = pp < NPAIR;
+      buf16_to_lds(rsB, live ? b_off[j] : kBufferOutOfRange, (uint32_t)(live ? pp : 0) * 128u,
+                   smem + BRING + bslot + (wave * RB + j) * 1024);
     };
 
     v4f acc[MT][NT];
@@ -328,28 +335,50 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Prologue: weight pair 0, then K blocks 0 .. STAGES-2.  Block i then copies
+    // K block i + STAGES - 1 and, when i is even, weight pair i/2 + 1.
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < KB) issue(s, s * STAGE);
+    for (int j = 0; j < RB; ++j) issue_b(j, 0, 0);
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) {
+      issue_scales(s, s * STAGE);
+#pragma unroll
+      for (int j = 0; j < RA; ++j) issue_a(j, s, s * STAGE);
+    }
 
     uint32_t rd = 0, wr = (STAGES - 1) * STAGE;
-    // One K block.  STEADY: a later stage is copied in this block, its A/B copy
-    // instructions spread between the matrix instructions (a copy that finds the
-    // memory pipeline full stalls the wave; spread out, matrix work is queued
-    // meanwhile), pinned with scheduling group barriers.
-    auto kstep = [&](int kb, auto steady_tag) {
-      constexpr bool STEADY = decltype(steady_tag)::value;
-      constexpr int ILV = RA + RB;
+    // One K block; ODD: kb is odd (no weight pair is copied in it).  The copy
+    // instructions are spread between the matrix instructions (a copy that finds
+    // the memory pipeline full stalls the wave; spread out, matrix work is
+    // queued meanwhile), pinned with scheduling group barriers: the scale words
+    // first, then the A regions, then (even blocks) the B regions.
+    auto kstep = [&](int kb, auto odd_tag) {
+      constexpr bool ODD = decltype(odd_tag)::value;
+      constexpr int ILV = RA + (ODD ? 0 : RB);
       constexpr int ILV_STEP = (MT * NT) / ILV;
-      // stage kb has landed once at most (#stages issued after it) copies remain
-      const int after = min(STAGES - 2, KB - 1 - kb);
-      if (after >= 2) wait_vmcnt<2 * LPS>();
-      else if (after == 1) wait_vmcnt<LPS>();
-      else wait_vmcnt<0>();
+      // Stage kb (and its weight pair) has landed once at most this many copies
+      // remain (a wave's loads retire in issue order):
+      //  * even kb >= 2: the weight pair was the last copy of block kb - 2; only
+      //    block kb - 1's LA copies are younger;
+      //  * odd kb >= 3: K block kb was copied in block kb - 3, before that
+      //    block's LB weight copies, then blocks kb - 2 (LA) and kb - 1 (LA + LB);
+      //  * kb = 0: the prologue's two later K blocks; kb = 1: K block 2 and block
+      //    0's K block and weight pair.
+      if (ODD) {
+        if (kb == 1) wait_vmcnt<2 * LA + LB>();
+        else wait_vmcnt<2 * LA + 2 * LB>();
+      } else {
+        if (kb == 0) wait_vmcnt<2 * LA>();
+        else wait_vmcnt<LA>();
+      }
       block_barrier();
-      if (STEADY) issue_scales(kb + STAGES - 1, wr);
+      const int kn = kb + STAGES - 1;              // K block copied in this block
+      const int pn = (kb >> 1) + 1;                // weight pair copied in this block (even kb)
+      const uint32_t bwr = (uint32_t)(pn & 1) * FFN_BPAIR;
+      issue_scales(kn, wr);
 
       const uint8_t* sbase = smem + rd;
+      const uint8_t* bbase = smem + BRING + (uint32_t)((kb >> 1) & 1) * FFN_BPAIR + b_ch[ODD ? 1 : 0];
       const int byte_sel = (kb & 3) * 8;
       int sa_s[MT];
       v8i af[MT];
@@ -368,7 +397,7 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
         const int row_off = MODE == 1 ? ((nt < 4 ? 0 : 128) + (nt & 3) * 16) : nt * 16;
         const uint32_t w = *reinterpret_cast<const uint32_t*>(sbase + sb_rd0 + row_off * 4);
         sb_s[nt] = (int)((w >> (8 * lgrp)) & 0xffu);
-        const v4i b4 = *reinterpret_cast<const v4i*>(sbase + b_rd[nt]);
+        const v4i b4 = *reinterpret_cast<const v4i*>(bbase + b_rd[nt]);
         bfr[nt] = v8i{b4.x, b4.y, b4.z, b4.w, 0, 0, 0, 0};
       }
 #pragma unroll
@@ -377,8 +406,12 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
         for (int nt = 0; nt < NT; ++nt) {
           const int j = mt * NT + nt;
           acc[mt][nt] = mfma_scaled_e2m1_e4m3_16x16x128(bfr[nt], sb_s[nt], af[mt], sa_s[mt], acc[mt][nt]);
-          const bool copy_here = STEADY && j % ILV_STEP == ILV_STEP - 1 && j / ILV_STEP < ILV;
-          if (copy_here) issue_ab(j / ILV_STEP, kb + STAGES - 1, wr);
+          const bool copy_here = j % ILV_STEP == ILV_STEP - 1 && j / ILV_STEP < ILV;
+          if (copy_here) {
+            const int idx = j / ILV_STEP;
+            if (idx < RA) issue_a(idx, kn, wr);
+            else issue_b(idx - RA, pn, bwr);
+          }
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
           if (copy_here) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // then 1 copy
         }
@@ -386,11 +419,12 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
       rd = (rd + STAGE == STAGES * STAGE) ? 0u : rd + STAGE;
       wr = (wr + STAGE == STAGES * STAGE) ? 0u : wr + STAGE;
     };
-    int kb = 0;
 #pragma clang loop unroll(disable)
-    for (; kb + STAGES - 1 < KB; ++kb) kstep(kb, std::true_type{});
-#pragma clang loop unroll(disable)
-    for (; kb < KB; ++kb) kstep(kb, std::false_type{});
+    for (int kb = 0; kb < KB; kb += 2) {
+      kstep(kb, std::false_type{});
+      if (kb + 1 < KB) kstep(kb + 1, std::true_type{});
+    }
+    wait_vmcnt<0>();   // the trailing copies (of nothing) have retired
     block_barrier();   // the ring is free before the next tile's prologue
 
     if (MODE == 2) {
