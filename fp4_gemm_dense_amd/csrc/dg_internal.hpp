@@ -41,6 +41,7 @@ struct TileConfig {
   int blocks_per_cu;    // resident workgroups per CU of the compiled kernel
   int threads;          // workgroup size
   int lds_bytes;        // dynamic LDS per workgroup
+  int stages;           // LDS ring slots
 };
 int num_tile_configs();
 TileConfig tile_config(int kernel_id);

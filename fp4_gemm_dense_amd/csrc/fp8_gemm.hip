@@ -666,7 +666,7 @@ hipError_t launch_masked_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& p
 
 static const TileConfig kTileConfigs[] = {
 #define X(id, MT, NT, WM, WN, ST, OCC) {WM * MT * 16, WN * NT * 16, OCC, WM * WN * 64,                     \
-                                        ST * ((WM * MT * 16 + WN * NT * 16) * 128 + WM * MT * 16 * 4)},
+                                        ST * ((WM * MT * 16 + WN * NT * 16) * 128 + WM * MT * 16 * 4), ST},
     DG_TILE_CONFIGS(X)
 #undef X
 };

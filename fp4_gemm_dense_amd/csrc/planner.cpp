@@ -90,6 +90,10 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     }
     // bigger tiles re-read less from L2/HBM: weight by tile area (arithmetic intensity)
     double intensity = (double)tc.block_m * tc.block_n / (tc.block_m + tc.block_n);
+    // ... except when every tile is split (skinny M): such calls stream B from
+    // HBM, and a deeper copy ring keeps more of it in flight (measured: the
+    // 4-slot 64x128 shape beats the 3-slot ones at M = 64 and 128)
+    if (splits > 1 && full == 0) intensity = tc.stages;
     double score = util * fill * intensity;
     // short K loops are bound by the epilogue: wide tiles write longer rows of D
     if (k <= 1024 && tc.block_n > tc.block_m) score *= 1.05;
