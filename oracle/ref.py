@@ -155,6 +155,66 @@ def dequant_w_fp4(w, w_sf) -> np.ndarray:
     return vals * np.repeat(s, 32, axis=1)
 
 
+# ----------------------------------------------------------------------------
+# FP8 x FP4 M-grouped GEMM (the FFN's GEMM form, exported on its own)
+# ----------------------------------------------------------------------------
+
+def fp8_fp4_gemm_nt(a, a_sf, b, b_sf) -> np.ndarray:
+    """D = A . B^T with block scales applied per block (Mega-MoE explainer: FP8
+    activations times FP4 weights; usage guide NT layout), unrounded, float64 [M, N].
+
+    a     uint8 [M, K]          e4m3fn codes
+    a_sf  int32 [M, ceil(K/512)] UE8M0 exponent bytes, one per 1x128 block, 4 per word
+    b     uint8 [N, K/2]        E2M1 pairs (low nibble = even K index)
+    b_sf  int32 [N, K/128]      UE8M0 exponent bytes, one per 1x32 block, 4 per word
+    """
+    return dequant_x_ue8m0(a, a_sf) @ dequant_w_fp4(b, b_sf).T
+
+
+def m_grouped_fp8_fp4_contiguous(a, a_sf, b, b_sf, m_indices):
+    """Contiguous M-grouped FP8 x FP4 GEMM: row r with g = m_indices[r] >= 0 gets
+    A[r] . B[g]^T; rows with -1 are padding and not part of the result.
+
+    a [M, K], a_sf [M, ceil(K/512)], b [G, N, K/2], b_sf [G, N, K/128], m_indices [M].
+    Returns (ref float64 [M, N], NaN in padding rows; written bool [M]).
+    """
+    a = np.asarray(a)
+    a_sf = np.asarray(a_sf)
+    m_idx = np.asarray(m_indices).astype(np.int64)
+    G, N = np.asarray(b).shape[:2]
+    M = a.shape[0]
+    ref = np.full((M, N), np.nan)
+    written = np.zeros(M, dtype=bool)
+    for g in range(G):
+        rows = np.nonzero(m_idx == g)[0]
+        if rows.size == 0:
+            continue
+        ref[rows] = fp8_fp4_gemm_nt(a[rows], a_sf[rows], b[g], b_sf[g])
+        written[rows] = True
+    return ref, written
+
+
+def m_grouped_fp8_fp4_masked(a, a_sf, b, b_sf, masked_m):
+    """Masked M-grouped FP8 x FP4 GEMM: for r < masked_m[g], D[g, r] = A[g, r] . B[g]^T.
+
+    a [G, max_m, K], a_sf [G, max_m, ceil(K/512)], b [G, N, K/2], b_sf [G, N, K/128].
+    Returns (ref float64 [G, max_m, N], NaN outside; written bool [G, max_m]).
+    """
+    a = np.asarray(a)
+    a_sf = np.asarray(a_sf)
+    G, max_m, _ = a.shape
+    N = np.asarray(b).shape[1]
+    ref = np.full((G, max_m, N), np.nan)
+    written = np.zeros((G, max_m), dtype=bool)
+    for g in range(G):
+        mg = min(max(int(masked_m[g]), 0), max_m)
+        if mg == 0:
+            continue
+        ref[g, :mg] = fp8_fp4_gemm_nt(a[g, :mg], a_sf[g, :mg], b[g], b_sf[g])
+        written[g, :mg] = True
+    return ref, written
+
+
 def silu(x):
     """silu(x) = x * sigmoid(x) = x / (1 + exp(-x))."""
     return x / (1.0 + np.exp(-x))

@@ -221,6 +221,41 @@ def gen_contiguous(G, total_rows, N, K, seed, align=128, counts=None, backend="n
                 counts=counts, M=M, N=N, K=K, G=G)
 
 
+def gen_fp4_contiguous(G, total_rows, N, K, seed, align=128, counts=None, backend="numpy", device="cpu"):
+    """Contiguous-layout FP8 x FP4 grouped GEMM inputs: A e4m3 with UE8M0 1x128 scales
+    (packed 4 per int32), B E2M1 with UE8M0 1x32 scales per group."""
+    d = _Draw(seed, backend, device)
+    if counts is None:
+        counts = d.multinomial_counts(total_rows, G)
+    m_idx, _ = padded_group_layout(counts, align)
+    M = len(m_idx)
+    m_indices = torch.tensor(m_idx, dtype=torch.int32, device=device)
+    a, a_sf = quant_rows_pow2_1x128(d.normal(M, K))
+    pad_rows = m_indices < 0
+    a[pad_rows] = E4M3_NAN
+    a_sf[pad_rows] = -1                      # exponent bytes 0xFF: NaN scales
+    bs, sbs = zip(*[quant_fp4_1x32(d.normal(N, K)) for _ in range(G)])
+    return dict(a=a, a_sf=a_sf, b=torch.stack(bs), b_sf=torch.stack(sbs), m_indices=m_indices,
+                counts=counts, M=M, N=N, K=K, G=G)
+
+
+def gen_fp4_masked(G, max_m, N, K, seed, masked_m=None, backend="numpy", device="cpu"):
+    """Masked-layout FP8 x FP4 grouped GEMM inputs; rows past masked_m hold NaN codes."""
+    d = _Draw(seed, backend, device)
+    as_, sas = zip(*[quant_rows_pow2_1x128(d.normal(max_m, K)) for _ in range(G)])
+    a = torch.stack(as_)
+    a_sf = torch.stack(sas)                                         # [G, max_m, ceil(K/512)]
+    bs, sbs = zip(*[quant_fp4_1x32(d.normal(N, K)) for _ in range(G)])
+    if masked_m is None:
+        masked_m = d.integers(0, max_m, G)
+    for g, mg in enumerate(masked_m):
+        a[g, max(mg, 0):] = E4M3_NAN
+        a_sf[g, max(mg, 0):] = -1
+    return dict(a=a, a_sf=a_sf, b=torch.stack(bs), b_sf=torch.stack(sbs),
+                masked_m=torch.tensor(masked_m, dtype=torch.int32, device=device),
+                G=G, max_m=max_m, N=N, K=K)
+
+
 def gen_masked(G, max_m, N, K, seed, masked_m=None, backend="numpy", device="cpu"):
     d = _Draw(seed, backend, device)
     as_, sas = zip(*[quant_rows_1x128(d.normal(max_m, K)) for _ in range(G)])

@@ -500,6 +500,91 @@ def _pins_dense(fn):
         return False
 
 
+# ----------------------------------------------------------------------------
+# FP8 x FP4 M-grouped GEMM
+# ----------------------------------------------------------------------------
+
+_FP4_MAGS = [0, .5, 1, 1.5, 2, 3, 4, 6]
+
+
+def _fp4_frac(byte, hi):
+    n = (int(byte) >> 4) if hi else (int(byte) & 15)
+    return Fraction(_FP4_MAGS[n & 7]) * (-1 if n & 8 else 1)
+
+
+def _ue8m0_frac(words, j):
+    return Fraction(2) ** (((int(np.uint32(words[j // 4].view(np.uint32))) >> (8 * (j % 4))) & 0xFF) - 127)
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 5, 128), (2, 3, 384), (4, 2, 640)])
+def test_fp8_fp4_gemm_matches_exact_rational_brute_force(M, N, K):
+    """Every entry as an exact rational: e4m3 through torch's float8 cast, E2M1 from
+    its closed-form magnitudes, UE8M0 as powers of two; 640 = 1.25 scale words."""
+    g = synth.gen_fp4_contiguous(1, M, N, K, seed=M * 100 + N + K, align=1, counts=[M])
+    a, a_sf, b, b_sf = (synth.to_numpy(g[k]) for k in ("a", "a_sf", "b", "b_sf"))
+    got = R.fp8_fp4_gemm_nt(a, a_sf, b[0], b_sf[0])
+    av = torch.from_numpy(a.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += (Fraction(float(av[m, k])) * _ue8m0_frac(a_sf[m], k // 128) *
+                        _fp4_frac(b[0, n, k // 2], k % 2) * _ue8m0_frac(b_sf[0, n], k // 32))
+            assert got[m, n] == float(acc), (m, n, got[m, n], float(acc))
+
+
+def test_fp8_fp4_gemm_scale_exponents_shift_exactly():
+    """Raising every B exponent byte by one doubles D exactly; raising the A
+    exponent of one 1x128 block changes only that block's contribution."""
+    g = synth.gen_fp4_contiguous(1, 6, 16, 512, seed=7, align=1, counts=[6])
+    a, a_sf, b, b_sf = (synth.to_numpy(g[k]) for k in ("a", "a_sf", "b", "b_sf"))
+    base = R.fp8_fp4_gemm_nt(a, a_sf, b[0], b_sf[0])
+    bsf2 = (b_sf[0].view(np.uint32) + np.uint32(0x01010101)).view(np.int32)
+    assert np.array_equal(R.fp8_fp4_gemm_nt(a, a_sf, b[0], bsf2), 2 * base)
+    # A block 2 of every row: one more in byte 2 of word 0
+    asf2 = (a_sf.view(np.uint32) + np.uint32(0x00010000) * np.array([1, 0], np.uint32)).view(np.int32)
+    part = R.fp8_fp4_gemm_nt(a[:, 256:384], a_sf[:, :1] * 0 + np.int32(0x7F7F7F7F), b[0][:, 128:192],
+                             b_sf[0][:, 2:3])
+    scale2 = np.ldexp(1.0, ((a_sf[:, 0].view(np.uint32) >> 16) & 0xFF).astype(np.int64) - 127)
+    want = base + part * scale2[:, None]
+    assert np.allclose(R.fp8_fp4_gemm_nt(a, asf2, b[0], b_sf[0]), want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_fp8_fp4_contiguous_groups_padding_and_relabelling():
+    """Each row uses its own group's B; padding rows (-1) are not written; relabelling
+    the groups together with B leaves the result unchanged."""
+    g = synth.gen_fp4_contiguous(3, 300, 32, 256, seed=3, counts=[100, 0, 200])
+    a, a_sf, b, b_sf, mi = (synth.to_numpy(g[k]) for k in ("a", "a_sf", "b", "b_sf", "m_indices"))
+    ref, written = R.m_grouped_fp8_fp4_contiguous(a, a_sf, b, b_sf, mi)
+    assert written.sum() == 300 and np.all(np.isnan(ref[~written])) and np.all(np.isfinite(ref[written]))
+    for r in (0, 99, 100, 128, 327, 383):
+        if mi[r] >= 0:
+            assert np.array_equal(ref[r], R.fp8_fp4_gemm_nt(a[r:r + 1], a_sf[r:r + 1], b[mi[r]], b_sf[mi[r]])[0])
+    perm = np.array([2, 0, 1])                       # new label of old group g: perm[g]
+    mi2 = np.where(mi >= 0, perm[np.maximum(mi, 0)], -1).astype(np.int32)
+    b2, bsf2 = np.empty_like(b), np.empty_like(b_sf)
+    b2[perm], bsf2[perm] = b, b_sf
+    ref2, written2 = R.m_grouped_fp8_fp4_contiguous(a, a_sf, b2, bsf2, mi2)
+    assert np.array_equal(written, written2) and np.array_equal(ref[written], ref2[written2])
+
+
+def test_fp8_fp4_masked_equals_contiguous_of_the_same_rows():
+    """Masked groups hold the same rows as a contiguous layout of the valid rows;
+    rows at or past masked_m (and counts outside [0, max_m]) are not written."""
+    mm = [130, 0, 7]
+    g = synth.gen_fp4_masked(3, 130, 48, 384, seed=9, masked_m=mm)
+    a, a_sf, b, b_sf = (synth.to_numpy(g[k]) for k in ("a", "a_sf", "b", "b_sf"))
+    ref, written = R.m_grouped_fp8_fp4_masked(a, a_sf, b, b_sf, mm)
+    assert written.sum() == 137
+    rows = np.concatenate([a[gi, :m] for gi, m in enumerate(mm)])
+    rsf = np.concatenate([a_sf[gi, :m] for gi, m in enumerate(mm)])
+    mi = np.concatenate([np.full(m, gi, np.int32) for gi, m in enumerate(mm)])
+    cref, _ = R.m_grouped_fp8_fp4_contiguous(rows, rsf, b, b_sf, mi)
+    assert np.array_equal(ref[written], cref)
+    ref_c, written_c = R.m_grouped_fp8_fp4_masked(a, a_sf, b, b_sf, [500, -3, 7])
+    assert np.array_equal(written_c[0], np.ones(130, bool)) and not written_c[1].any()
+
+
 def test_planted_mistakes_fail_dense_pins():
     assert _pins_dense(R.fp8_gemm_nt)
 
