@@ -32,6 +32,8 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "dg_m_grouped_fp8_fp4_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "dg_m_grouped_fp8_fp4_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "dg_fp8_fp4_expert_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "dg_fp8_fp4_expert_ffn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "dg_get_mk_alignment_for_contiguous_layout": (_I, []),
@@ -165,6 +167,38 @@ def dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked_m, d, expected_m=0):
     _check("dg_m_grouped_fp8_gemm_nt_masked",
            L.dg_m_grouped_fp8_gemm_nt_masked(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m), _ptr(d),
                                              G, max_m, N, K, int(expected_m), _stream(a)))
+    return d
+
+
+def dg_m_grouped_fp8_fp4_gemm_nt_contiguous(a, a_sf, b, b_sf, m_indices, d):
+    L = lib()
+    M, K = a.shape
+    G, N = b.shape[0], b.shape[1]
+    _req(a, _U8, (M, K), "a")
+    _req(a_sf, torch.int32, (M, (K // 128 + 3) // 4), "a_sf")
+    _req(b, _U8, (G, N, K // 2), "b")
+    _req(b_sf, torch.int32, (G, N, K // 128), "b_sf")
+    _req(m_indices, torch.int32, (M,), "m_indices")
+    _req_bf16(d, (M, N), "d")
+    _check("dg_m_grouped_fp8_fp4_gemm_nt_contiguous",
+           L.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(m_indices),
+                                                     _ptr(d), M, N, K, G, _stream(a)))
+    return d
+
+
+def dg_m_grouped_fp8_fp4_gemm_nt_masked(a, a_sf, b, b_sf, masked_m, d, expected_m=0):
+    L = lib()
+    G, max_m, K = a.shape
+    N = b.shape[1]
+    _req(a, _U8, (G, max_m, K), "a")
+    _req(a_sf, torch.int32, (G, max_m, (K // 128 + 3) // 4), "a_sf")
+    _req(b, _U8, (G, N, K // 2), "b")
+    _req(b_sf, torch.int32, (G, N, K // 128), "b_sf")
+    _req(masked_m, torch.int32, (G,), "masked_m")
+    _req_bf16(d, (G, max_m, N), "d")
+    _check("dg_m_grouped_fp8_fp4_gemm_nt_masked",
+           L.dg_m_grouped_fp8_fp4_gemm_nt_masked(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(masked_m),
+                                                 _ptr(d), G, max_m, N, K, int(expected_m), _stream(a)))
     return d
 
 

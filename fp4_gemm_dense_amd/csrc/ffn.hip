@@ -54,6 +54,13 @@ struct FfnParams {
   uint8_t* q;           // [T*k, I]
   uint8_t* sq;          // [T*k, sq_stride]
   float* o;             // [T*k, H]
+  // standalone M-grouped FP8 x FP4 GEMM (modes 3, 4): D = A_rows . B_g^T in bf16,
+  // A = x / x_sf, B = w2 / w2_sf
+  int gm, gn, gk;       // rows of A (masked: groups * max_m), N, K
+  int groups, max_m;
+  const int32_t* m_indices;   // contiguous: group of each row (-1: padding)
+  const int32_t* masked_m;    // masked: valid rows per group
+  uint16_t* d;
 };
 
 struct FfnLayout {
@@ -175,7 +182,9 @@ constexpr int FFN_STAGE = FFN_A_BYTES + FFN_SA_BYTES + FFN_SB_BYTES;
 constexpr int FFN_BPAIR = FFN_BN * 128;           // e2m1, 256 K per row
 constexpr int FFN_LDS = FFN_STAGES * FFN_STAGE + FFN_BSTAGES * FFN_BPAIR;
 
-template <int MODE>   // 1: linear1 (+ SwiGLU + requant), 2: linear2 (fp32 out)
+// MODE 1: linear1 (+ SwiGLU + requant); 2: linear2 (fp32 out); 3 / 4: the
+// standalone masked / contiguous M-grouped GEMM (bf16 out).
+template <int MODE>
 __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
   constexpr int NW = FFN_WM * FFN_WN;
   constexpr int MT = FFN_MT, NT = FFN_NT, STAGES = FFN_STAGES, STAGE = FFN_STAGE;
@@ -203,23 +212,37 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
 
-  const int H = p.H, I = p.I, E = p.E;
-  const int K = MODE == 1 ? H : I;
+  constexpr bool GEMM = MODE >= 3;
+  const int H = p.H, I = p.I;
+  const int E = MODE == 3 ? p.groups : p.E;         // row lists: experts, or masked groups
+  const int K = GEMM ? p.gk : (MODE == 1 ? H : I);
   const int KB = K >> 7;
-  const int tiles_n = MODE == 1 ? I / 128 : H / FFN_BN;   // H % 512 == 0
+  const int NOUT = GEMM ? p.gn : H;                 // output row length (modes 2-4)
+  const int tiles_n = MODE == 1 ? I / 128 : NOUT / FFN_BN;   // H % 512 == 0, N % 256 == 0
+  const int tiles_m4 = (p.gm + FFN_BM - 1) / FFN_BM;        // contiguous form: 128-row blocks
+  // rows of row list e (expert pairs, or a masked group's valid rows) and where they start
+  auto list_cnt = [&](int e) -> int {
+    if (MODE == 3) {
+      const int mm = p.masked_m[e];
+      return mm < 0 ? 0 : (mm > p.max_m ? p.max_m : mm);
+    }
+    return p.cnt[e];
+  };
+  auto list_start = [&](int e) -> int { return MODE == 3 ? e * p.max_m : p.start[e]; };
 
-  // device-side tile enumeration: expert e owns tiles_m(e) * tiles_n tiles,
-  // ordered (n-tile, m-tile) so that consecutive tiles share a weight tile
-  if (tid == 0) {
+  // device-side tile enumeration: row list e owns tiles_m(e) * tiles_n tiles,
+  // ordered (n-tile, m-tile) so that consecutive tiles share a weight tile; the
+  // contiguous form walks (n-tile, 128-row block) and skips padding blocks
+  if (MODE != 4 && tid == 0) {
     int s = 0;
     for (int e = 0; e < E; ++e) {
       tile_base[e] = s;
-      s += ((p.cnt[e] + FFN_BM - 1) / FFN_BM) * tiles_n;
+      s += ((list_cnt(e) + FFN_BM - 1) / FFN_BM) * tiles_n;
     }
     tile_base[E] = s;
   }
   __syncthreads();
-  const int total = tile_base[E];
+  const int total = MODE == 4 ? tiles_m4 * tiles_n : tile_base[E];
 
   const int G = gridDim.x;
   int vb = blockIdx.x;
@@ -248,31 +271,44 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
   const uint32_t b_ch[2] = {(uint32_t)((lgrp ^ sw) << 4), (uint32_t)(((4 + lgrp) ^ sw) << 4)};
   const uint32_t sb_rd0 = OFF_SB + (MODE == 1 ? wave_n * 64 + lrow : wave_n * 128 + lrow) * 4;
 
-  const uint8_t* a_base = MODE == 1 ? p.x : p.q;
-  const size_t a_rows = MODE == 1 ? (size_t)p.T : (size_t)p.T * p.k;
+  const uint8_t* a_base = MODE == 2 ? p.q : p.x;
+  const size_t a_rows = MODE == 1 ? (size_t)p.T : (GEMM ? (size_t)p.gm : (size_t)p.T * p.k);
+  // bytes per A-scale row: one word per four K blocks
+  const uint32_t sa_stride = MODE == 1 ? (uint32_t)(H / 512) * 4u
+                                       : (MODE == 2 ? (uint32_t)p.sq_stride : (uint32_t)((KB + 3) / 4) * 4u);
   const v4i rsA = make_buffer_rsrc(a_base, (uint32_t)(a_rows * (size_t)K));
-  const v4i rsSA = MODE == 1 ? make_buffer_rsrc(p.x_sf, (uint32_t)((size_t)p.T * (H / 512) * 4))
-                             : make_buffer_rsrc(p.sq, (uint32_t)((size_t)p.T * p.k * p.sq_stride));
+  const v4i rsSA = make_buffer_rsrc(MODE == 2 ? (const void*)p.sq : (const void*)p.x_sf,
+                                    (uint32_t)(a_rows * sa_stride));
   const uint32_t wrow_bytes = (uint32_t)K / 2;
   const uint32_t wsf_bytes = (uint32_t)(K / 128) * 4;
-  const uint32_t e_rows = MODE == 1 ? 2u * I : (uint32_t)H;
+  const uint32_t e_rows = MODE == 1 ? 2u * I : (uint32_t)NOUT;
 
   for (int t = vb; t < total; t += G) {
-    // ---------------- tile -> (expert, m-tile, n-tile) ----------------
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {                            // last e with tile_base[e] <= t
-      const int mid = (lo + hi + 1) >> 1;
-      if (tile_base[mid] <= t) lo = mid; else hi = mid - 1;
+    // ---------------- tile -> (row list / group e, m-tile, n-tile) ----------------
+    int e, tn, row0, rows, last_pair;
+    if (MODE == 4) {
+      tn = t / tiles_m4;
+      row0 = (t - tn * tiles_m4) * FFN_BM;
+      e = p.m_indices[row0];
+      if (e < 0 || e >= p.groups) continue;       // padding block (uniform: skip the tile)
+      rows = min(FFN_BM, p.gm - row0);
+      last_pair = p.gm - 1;
+    } else {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {                          // last e with tile_base[e] <= t
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_base[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+      const int cnt_e = list_cnt(e);
+      const int tm_e = (cnt_e + FFN_BM - 1) / FFN_BM;
+      const int local = t - tile_base[e];
+      tn = local / tm_e;
+      const int tm = local - tn * tm_e;
+      row0 = list_start(e) + tm * FFN_BM;        // first row (pair) of the tile
+      rows = min(FFN_BM, cnt_e - tm * FFN_BM);   // valid rows in the tile
+      last_pair = list_start(e) + cnt_e - 1;
     }
-    const int e = lo;
-    const int cnt_e = p.cnt[e];
-    const int tm_e = (cnt_e + FFN_BM - 1) / FFN_BM;
-    const int local = t - tile_base[e];
-    const int tn = local / tm_e;
-    const int tm = local - tn * tm_e;
-    const int row0 = p.start[e] + tm * FFN_BM;        // first pair of the tile
-    const int rows = min(FFN_BM, cnt_e - tm * FFN_BM); // valid pairs in the tile
-    const int last_pair = p.start[e] + cnt_e - 1;
 
     // ---------------- copy sources (per-lane offsets, scalar K offsets) ----------------
     const uint8_t* wb = MODE == 1 ? p.w1 : p.w2;
@@ -297,8 +333,7 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
     {
       const int r = wave * SAW + (lane < SAW ? lane : 0);
       const int pr = min(row0 + r, last_pair);
-      sa_off = MODE == 1 ? (uint32_t)p.pair_token[pr] * (uint32_t)(H / 512) * 4u
-                         : (uint32_t)pr * (uint32_t)p.sq_stride;
+      sa_off = MODE == 1 ? (uint32_t)p.pair_token[pr] * sa_stride : (uint32_t)pr * sa_stride;
     }
     {
       const int r = wave * SBW + (lane < SBW ? lane : 0);
@@ -427,7 +462,22 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
     wait_vmcnt<0>();   // the trailing copies (of nothing) have retired
     block_barrier();   // the ring is free before the next tile's prologue
 
-    if (MODE == 2) {
+    if (GEMM) {
+      // bf16 D rows: 4 consecutive columns (8 bytes) per lane and block; contiguous
+      // form: only rows of this block's group (padding rows keep their contents)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = wave_m * MT * 16 + mt * 16 + lrow;
+        if (r >= rows) continue;
+        if (MODE == 4 && p.m_indices[row0 + r] != e) continue;
+        uint16_t* drow = p.d + (size_t)(row0 + r) * NOUT + tn * FFN_BN + wave_n * 128 + 4 * lgrp;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const v4f v = acc[mt][nt];
+          *reinterpret_cast<uint2*>(drow + nt * 16) = uint2{pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])};
+        }
+      }
+    } else if (MODE == 2) {
       // fp32 output rows of the pairs: 4 consecutive columns (16 bytes) per lane and block
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -529,7 +579,83 @@ static hipError_t launch_ffn(FfnParams& p, int num_cus, hipStream_t stream) {
 
 using namespace dg;
 
+static hipError_t launch_gemm4(FfnParams& p, bool masked, int num_cus, hipStream_t stream) {
+  static const hipError_t attr3 = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_gemm_kernel<3>),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, FFN_LDS);
+  static const hipError_t attr4 = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_gemm_kernel<4>),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, FFN_LDS);
+  if (attr3 != hipSuccess) return attr3;
+  if (attr4 != hipSuccess) return attr4;
+  if (masked)
+    hipLaunchKernelGGL(ffn_gemm_kernel<3>, dim3(num_cus), dim3(FFN_THREADS), FFN_LDS, stream, p);
+  else
+    hipLaunchKernelGGL(ffn_gemm_kernel<4>, dim3(num_cus), dim3(FFN_THREADS), FFN_LDS, stream, p);
+  return hipGetLastError();
+}
+
+// Checks shared by the two exported forms; rows = rows of A (and D).
+static int gemm4_check(const uint8_t* a, const int32_t* a_sf, const uint8_t* b, const int32_t* b_sf,
+                       const int32_t* meta, uint16_t* d, long long rows, int n, int k, int groups) {
+  if (!a || !a_sf || !b || !b_sf || !meta || !d) return DG_ERR_INVALID_ARG;
+  if (rows <= 0 || n <= 0 || k <= 0 || groups <= 0) return DG_ERR_INVALID_ARG;
+  if (k % 128 != 0 || n % 256 != 0) return DG_ERR_UNSUPPORTED;
+  const long long lim = 1LL << 31;
+  if (rows * k > lim || (long long)n * (k / 2) > lim || rows * 4LL * ((k / 128 + 3) / 4) > lim ||
+      (long long)n * (k / 128) * 4 > lim)
+    return DG_ERR_UNSUPPORTED;
+  const uintptr_t al16 = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                         reinterpret_cast<uintptr_t>(d);
+  const uintptr_t al4 = reinterpret_cast<uintptr_t>(a_sf) | reinterpret_cast<uintptr_t>(b_sf) |
+                        reinterpret_cast<uintptr_t>(meta);
+  if ((al16 & 15) || (al4 & 3)) return DG_ERR_INVALID_ARG;
+  return DG_OK;
+}
+
 extern "C" {
+
+int dg_m_grouped_fp8_fp4_gemm_nt_contiguous(const uint8_t* a, const int32_t* a_sf, const uint8_t* b,
+                                            const int32_t* b_sf, const int32_t* m_indices, uint16_t* d,
+                                            int m, int n, int k, int num_groups, void* stream) {
+  try {
+    const int st = gemm4_check(a, a_sf, b, b_sf, m_indices, d, m, n, k, num_groups);
+    if (st != DG_OK) return st;
+    DeviceInfo di = current_device_info();
+    if (!di.ok) return DG_ERR_NO_DEVICE;
+    FfnParams p{};
+    p.x = a; p.x_sf = a_sf; p.w2 = b; p.w2_sf = b_sf; p.d = d; p.m_indices = m_indices;
+    p.gm = m; p.gn = n; p.gk = k; p.groups = num_groups;
+    int cus = dg_get_num_cus();
+    if (cus <= 0) cus = di.num_cus;
+    const hipError_t e = launch_gemm4(p, false, cus, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DG_OK : DG_ERR_HIP;
+  } catch (...) {
+    return DG_ERR_HIP;
+  }
+}
+
+int dg_m_grouped_fp8_fp4_gemm_nt_masked(const uint8_t* a, const int32_t* a_sf, const uint8_t* b,
+                                        const int32_t* b_sf, const int32_t* masked_m, uint16_t* d,
+                                        int num_groups, int max_m, int n, int k, int expected_m,
+                                        void* stream) {
+  (void)expected_m;
+  try {
+    if (max_m <= 0) return DG_ERR_INVALID_ARG;
+    const int st = gemm4_check(a, a_sf, b, b_sf, masked_m, d, (long long)num_groups * max_m, n, k, num_groups);
+    if (st != DG_OK) return st;
+    if (num_groups > FFN_MAX_EXPERTS) return DG_ERR_UNSUPPORTED;
+    DeviceInfo di = current_device_info();
+    if (!di.ok) return DG_ERR_NO_DEVICE;
+    FfnParams p{};
+    p.x = a; p.x_sf = a_sf; p.w2 = b; p.w2_sf = b_sf; p.d = d; p.masked_m = masked_m;
+    p.gm = num_groups * max_m; p.gn = n; p.gk = k; p.groups = num_groups; p.max_m = max_m;
+    int cus = dg_get_num_cus();
+    if (cus <= 0) cus = di.num_cus;
+    const hipError_t e = launch_gemm4(p, true, cus, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DG_OK : DG_ERR_HIP;
+  } catch (...) {
+    return DG_ERR_HIP;
+  }
+}
 
 size_t dg_fp8_fp4_expert_ffn_workspace_bytes(int num_tokens, int num_topk, int num_local_experts, int hidden,
                                              int intermediate) {

@@ -165,6 +165,43 @@ int dg_fp8_fp4_expert_ffn(const uint8_t* x, const int32_t* x_sf, const int32_t* 
                           int num_topk, int num_local_experts, int expert_offset, int hidden,
                           int intermediate, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * M-grouped FP8 x FP4 GEMM, the FFN's GEMM form exported on its own (news page
+ * "DeepSeek 发布 DeepGEMM 重大更新：Mega MoE 融合算子与 FP4 精度支持", section FP4
+ * 精度支持: FP8 activations times FP4 weights; usage guide, 分组 GEMM（MoE）, for the
+ * contiguous and masked layouts).  The block scales are applied by the matrix
+ * cores; there is no C input and no split along K.
+ *   D[r] = bf16( sum_k A[r,k] 2^(ea(r, k/128)) * B_g[n,k] 2^(eb(g, n, k/32)) )
+ * with g the group of row r.
+ *   a      e4m3 rows, 16-byte aligned
+ *   a_sf   int32, ceil(k/512) words per row, four UE8M0 exponents per word (1x128
+ *          blocks; byte i of word j is block 4j+i), 4-byte aligned
+ *   b      [num_groups, n, k/2] E2M1 pairs (element 2i in the low nibble of byte i), 16-byte aligned
+ *   b_sf   [num_groups, n, k/128] int32, four UE8M0 exponents per word (1x32 blocks)
+ *   d      bf16 rows of n, 16-byte aligned
+ * Requirements: n % 256 == 0; k % 128 == 0; (rows of A) * k, n * k / 2 and
+ *   (rows of A) * 4 * ceil(k/512) at most 2^31 (else DG_ERR_UNSUPPORTED).
+ *
+ * Contiguous: a [m, k], a_sf [m, ceil(k/512)], m_indices [m] (group of each row,
+ * -1 for padding; groups padded to 128 rows, so each 128-row block holds one
+ * group), d [m, n]; only rows of a group are written.
+ */
+int dg_m_grouped_fp8_fp4_gemm_nt_contiguous(const uint8_t* a, const int32_t* a_sf, const uint8_t* b,
+                                            const int32_t* b_sf, const int32_t* m_indices, uint16_t* d,
+                                            int m, int n, int k, int num_groups, void* stream);
+
+/*
+ * Masked: a [num_groups, max_m, k], a_sf [num_groups, max_m, ceil(k/512)],
+ * masked_m [num_groups] (valid rows per group, clamped to [0, max_m]),
+ * d [num_groups, max_m, n]; rows r < masked_m[g] of group g are written, no other.
+ * num_groups <= 256.  expected_m is accepted for symmetry with the FP8 form and
+ * unused: the kernel walks only the tiles that hold valid rows.
+ */
+int dg_m_grouped_fp8_fp4_gemm_nt_masked(const uint8_t* a, const int32_t* a_sf, const uint8_t* b,
+                                        const int32_t* b_sf, const int32_t* masked_m, uint16_t* d,
+                                        int num_groups, int max_m, int n, int k, int expected_m,
+                                        void* stream);
+
 /* Row alignment of each group in the contiguous layout (usage guide, 工具函数). Returns 128. */
 int dg_get_mk_alignment_for_contiguous_layout(void);
 

@@ -72,6 +72,24 @@ def test_dense_argument_validation(args, status):
         assert got == status
 
 
+def test_fp8_fp4_grouped_argument_validation():
+    lib = dgm.load_library()
+    f = lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous
+    assert f(A16, A16, A16, A16, 0, A16, 256, 256, 128, 4, None) == 1           # null m_indices
+    assert f(A16, A16, A16, A16, A16, A16, 256, 256, 128, 0, None) == 1         # no groups
+    assert f(A16 + 8, A16, A16, A16, A16, A16, 256, 256, 128, 4, None) == 1     # misaligned a
+    assert f(A16, A16 + 2, A16, A16, A16, A16, 256, 256, 128, 4, None) == 1     # misaligned a_sf
+    assert f(A16, A16, A16, A16, A16, A16, 256, 272, 128, 4, None) == 2         # N % 256
+    assert f(A16, A16, A16, A16, A16, A16, 256, 256, 200, 4, None) == 2         # K % 128
+    assert f(A16, A16, A16, A16, A16, A16, 1 << 21, 256, 1152, 4, None) == 2    # A above 2 GiB
+    assert f(A16, A16, A16, A16, A16, A16, 256, 256, 128, 4, None) in (0, 4)    # valid: device check
+    g = lib.dg_m_grouped_fp8_fp4_gemm_nt_masked
+    assert g(A16, A16, A16, A16, 0, A16, 4, 256, 256, 128, 0, None) == 1        # null masked_m
+    assert g(A16, A16, A16, A16, A16, A16, 4, 0, 256, 128, 0, None) == 1        # max_m = 0
+    assert g(A16, A16, A16, A16, A16, A16, 300, 64, 256, 128, 0, None) == 2     # more than 256 groups
+    assert g(A16, A16, A16, A16, A16, A16, 4, 256, 256, 128, 0, None) in (0, 4)
+
+
 def test_grouped_and_ffn_argument_validation():
     lib = dgm.load_library()
     f = lib.dg_m_grouped_fp8_gemm_nt_contiguous
