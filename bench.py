@@ -15,6 +15,9 @@ Other workloads:
               same (N,K) pairs
   --config 4  FP8xFP4 expert FFN, 4096 tokens, hidden 7168, intermediate 2048,
               32 local experts of 256, top-8
+  --config 5  M-grouped FP8xFP4 GEMM, contiguous, 8 groups from 32768 routed rows,
+              (N,K) in {(4096,7168), (7168,2048)}: config 2 with E2M1 weights
+              (UE8M0 per 1x32) and UE8M0 activation scales per 1x128
 
 Caches: one dense-sweep step touches more than 1 GB of distinct inputs and
 outputs, so no shape's operands survive in the 4 MB L2s or the 256 MB
@@ -54,7 +57,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--shape", type=str, default=None,
@@ -67,7 +70,7 @@ def parse():
 def kernel_source_hash(cfg):
     """Hash of the sources that decide the kernels (and their plans) a config runs."""
     h = hashlib.sha256()
-    files = ("ffn.hip", "dg_device.hpp") if cfg == 4 else ("fp8_gemm.hip", "planner.cpp", "dg_device.hpp")
+    files = ("ffn.hip", "dg_device.hpp") if cfg in (4, 5) else ("fp8_gemm.hip", "planner.cpp", "dg_device.hpp")
     for f in files:
         p = os.path.join(ROOT, "fp4_gemm_dense_amd", "csrc", f)
         if os.path.exists(p):
@@ -148,6 +151,29 @@ def items_masked():
     return items
 
 
+def items_fp4_contiguous():
+    import torch
+    import synth
+    import fp4_gemm_dense_amd as dg
+    items = []
+    for j, (N, K) in enumerate(synth.GROUPED_NK):
+        g = synth.gen_fp4_contiguous(8, 32768, N, K, synth.seed_for(5, j), backend="torch", device="cuda")
+        M = g["M"]
+        d = torch.empty(M, N, dtype=torch.int16, device="cuda")
+        valid = sum(g["counts"])
+        groups_hit = sum(1 for c in g["counts"] if c > 0)
+        nbytes = (valid * K + groups_hit * (N * K // 2 + N * (K // 32)) + valid * 4 * ((K // 128 + 3) // 4)
+                  + 4 * M + 2 * valid * N)
+
+        b_sf_t = dg.dg_transform_fp4_weight_sf(g["b_sf"])     # weight pre-transform, once per weight set
+
+        def run(g=g, d=d, b_sf_t=b_sf_t):
+            dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(g["a"], g["a_sf"], g["b"], b_sf_t, g["m_indices"], d)
+        items.append(dict(run=run, g=g, flops=2.0 * valid * N * K, bytes=nbytes, label=f"G8_fp4_contig_N{N}_K{K}",
+                          shape=(M, N, K)))
+    return items
+
+
 def items_ffn():
     import torch
     import synth
@@ -166,9 +192,11 @@ def items_ffn():
     w_bytes = experts_hit * (2 * I * H // 2 + 2 * I * (H // 32) + H * I // 2 + H * (I // 32))
     nbytes = w_bytes + T * H + T * (H // 128) + T * k * 8 + T * H * 2
 
+    # weight pre-transform, once per weight set (outside the timed step)
+    (w1, w1_sf), (w2, w2_sf) = dg.transform_weights_for_expert_ffn((g["w1"], g["w1_sf"]), (g["w2"], g["w2_sf"]))
+
     def run():
-        dg.dg_fp8_fp4_expert_ffn(g["x"], g["x_sf"], g["topk_idx"], g["topk_w"], g["w1"], g["w1_sf"], g["w2"],
-                                 g["w2_sf"], y, 0, ws)
+        dg.dg_fp8_fp4_expert_ffn(g["x"], g["x_sf"], g["topk_idx"], g["topk_w"], w1, w1_sf, w2, w2_sf, y, 0, ws)
     return [dict(run=run, g=g, flops=2.0 * P * (2 * I * H + H * I), bytes=nbytes,
                  label=f"ffn_T{T}_H{H}_I{I}_E{E}_pairs{P}", shape=(T, H, I), pairs=P)]
 
@@ -239,6 +267,23 @@ def _cpu_pass(config, items, budget_s, t_start, npass, t_total, flops, desc):
             flops += 2.0 * r * N * K
             if npass == 0:
                 desc.append(f"{r} rows of {it['label']}")
+        elif config == 5:
+            M, N, K = it["shape"]
+            mi = synth.to_numpy(g["m_indices"])
+            for grp in range(8):
+                if time.perf_counter() - t_start > budget_s:
+                    break
+                rows = np.nonzero(mi == grp)[0][16 * npass:16 * npass + 16]
+                if len(rows) == 0:
+                    continue
+                a, a_sf = synth.to_numpy(g["a"][rows]), synth.to_numpy(g["a_sf"][rows])
+                b, b_sf = synth.to_numpy(g["b"][grp]), synth.to_numpy(g["b_sf"][grp])
+                t0 = time.perf_counter()
+                R.fp8_fp4_gemm_nt(a, a_sf, b, b_sf)
+                t_total += time.perf_counter() - t0
+                flops += 2.0 * len(rows) * N * K
+            if npass == 0:
+                desc.append(f"up to 16 valid rows per group of {it['label']}")
         elif config in (2, 3):
             M, N, K = it["shape"]
             G = 8 if config == 2 else 32
@@ -294,6 +339,8 @@ WORKLOADS = {
        "e4m3 1x128 / 128x128 fp32 scales",
     4: "FP8xFP4 expert FFN, 4096 tokens, hidden 7168, intermediate 2048, 32 local experts of 256, top-8, "
        "e4m3 activations (UE8M0/128), E2M1 weights (UE8M0/32)",
+    5: "M-grouped FP8xFP4 GEMM, contiguous, 8 groups from 32768 routed rows (multinomial, padded to 128), "
+       "(N,K){(4096,7168),(7168,2048)}, e4m3 activations (UE8M0/128), E2M1 weights (UE8M0/32)",
 }
 
 
@@ -327,6 +374,8 @@ def main():
         items = items_contiguous()
     elif cfg == 3:
         items = items_masked()
+    elif cfg == 5:
+        items = items_fp4_contiguous()
     else:
         items = items_ffn()
     torch.cuda.synchronize()
@@ -380,6 +429,9 @@ def main():
         dom, kname, bound = items, "fp8_gemm_kernel, contiguous grouped", "mfma"
     elif cfg == 3:
         dom, kname, bound = items, "fp8_gemm_kernel, masked grouped", "hbm"
+    elif cfg == 5:
+        # the e2m1 x e4m3 matrix instruction runs at the e4m3 rate: FP8 peak
+        dom, kname, bound = items, "ffn_gemm_kernel (FP8xFP4), contiguous grouped", "mfma"
     else:
         dom, kname, bound = items, "expert FFN call (route + linear1 + linear2 + combine)", "hbm"
     avg_ms = sum(it["mean_ms"] for it in dom) / len(dom)
@@ -421,7 +473,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 x fp4e2m1 -> f32" if cfg == 4 else "fp8e4m3 x fp8e4m3 -> f32",
+        "dtype": "fp8e4m3 x fp4e2m1 -> f32" if cfg in (4, 5) else "fp8e4m3 x fp8e4m3 -> f32",
         "data": "synthetic (seeded N(0,1), quantised as the workload states)",
         "config": {"workload": WORKLOADS[cfg] if args.shape is None else f"dense NT {args.shape}",
                    "calls_per_step": n, "parallelism": "none (1 GPU)"},

@@ -34,6 +34,7 @@ _SIGNATURES = {
     "dg_m_grouped_fp8_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_fp4_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_fp4_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "dg_transform_fp4_weight_sf": (_I, [_P, _P, _I, _I, _I, _P]),
     "dg_fp8_fp4_expert_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "dg_fp8_fp4_expert_ffn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "dg_get_mk_alignment_for_contiguous_layout": (_I, []),
@@ -177,7 +178,7 @@ def dg_m_grouped_fp8_fp4_gemm_nt_contiguous(a, a_sf, b, b_sf, m_indices, d):
     _req(a, _U8, (M, K), "a")
     _req(a_sf, torch.int32, (M, (K // 128 + 3) // 4), "a_sf")
     _req(b, _U8, (G, N, K // 2), "b")
-    _req(b_sf, torch.int32, (G, N, K // 128), "b_sf")
+    _req(b_sf, torch.int32, (G, K // 128, N), "b_sf")
     _req(m_indices, torch.int32, (M,), "m_indices")
     _req_bf16(d, (M, N), "d")
     _check("dg_m_grouped_fp8_fp4_gemm_nt_contiguous",
@@ -193,13 +194,26 @@ def dg_m_grouped_fp8_fp4_gemm_nt_masked(a, a_sf, b, b_sf, masked_m, d, expected_
     _req(a, _U8, (G, max_m, K), "a")
     _req(a_sf, torch.int32, (G, max_m, (K // 128 + 3) // 4), "a_sf")
     _req(b, _U8, (G, N, K // 2), "b")
-    _req(b_sf, torch.int32, (G, N, K // 128), "b_sf")
+    _req(b_sf, torch.int32, (G, K // 128, N), "b_sf")
     _req(masked_m, torch.int32, (G,), "masked_m")
     _req_bf16(d, (G, max_m, N), "d")
     _check("dg_m_grouped_fp8_fp4_gemm_nt_masked",
            L.dg_m_grouped_fp8_fp4_gemm_nt_masked(_ptr(a), _ptr(a_sf), _ptr(b), _ptr(b_sf), _ptr(masked_m),
                                                  _ptr(d), G, max_m, N, K, int(expected_m), _stream(a)))
     return d
+
+
+def dg_transform_fp4_weight_sf(sf, sf_t=None):
+    """Packed UE8M0 weight-scale words [G, N, K/128] -> K-block-major [G, K/128, N] (new tensor
+    unless sf_t is given)."""
+    G, N, KB = sf.shape
+    _req(sf, torch.int32, (G, N, KB), "sf")
+    if sf_t is None:
+        sf_t = torch.empty(G, KB, N, dtype=torch.int32, device=sf.device)
+    _req(sf_t, torch.int32, (G, KB, N), "sf_t")
+    _check("dg_transform_fp4_weight_sf",
+           lib().dg_transform_fp4_weight_sf(_ptr(sf), _ptr(sf_t), G, N, KB * 128, _stream(sf)))
+    return sf_t
 
 
 def dg_fp8_fp4_expert_ffn_workspace_bytes(num_tokens, num_topk, num_local_experts, hidden, intermediate):
@@ -218,9 +232,9 @@ def dg_fp8_fp4_expert_ffn(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y, ex
     _req(topk_idx, torch.int32, (T, k), "topk_idx")
     _req(topk_w, torch.float32, (T, k), "topk_w")
     _req(w1, _U8, (E, 2 * I, H // 2), "w1")
-    _req(w1_sf, torch.int32, (E, 2 * I, H // 128), "w1_sf")
+    _req(w1_sf, torch.int32, (E, H // 128, 2 * I), "w1_sf")
     _req(w2, _U8, (E, H, I // 2), "w2")
-    _req(w2_sf, torch.int32, (E, H, I // 128), "w2_sf")
+    _req(w2_sf, torch.int32, (E, I // 128, H), "w2_sf")
     _req_bf16(y, (T, H), "y")
     _req(workspace, _U8, (workspace.numel(),), "workspace")
     _check("dg_fp8_fp4_expert_ffn",
@@ -280,6 +294,13 @@ def m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked_m, expected_m=0, out=Non
     d = out if out is not None else torch.empty(a.shape[0], a.shape[1], b.shape[1], dtype=torch.bfloat16,
                                                 device=a.device)
     return dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked_m, d, expected_m)
+
+
+def transform_weights_for_expert_ffn(l1_weights, l2_weights):
+    """(w1, w1_sf), (w2, w2_sf) with row-major scale words -> the same pairs with the scale
+    words K-block-major, the layout dg_fp8_fp4_expert_ffn reads; the E2M1 bytes are unchanged."""
+    (w1, w1_sf), (w2, w2_sf) = l1_weights, l2_weights
+    return (w1, dg_transform_fp4_weight_sf(w1_sf)), (w2, dg_transform_fp4_weight_sf(w2_sf))
 
 
 def fp8_fp4_expert_ffn(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, expert_offset=0, workspace=None):

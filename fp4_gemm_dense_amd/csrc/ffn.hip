@@ -172,15 +172,16 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
 constexpr int FFN_WM = 4, FFN_WN = 2, FFN_MT = 2, FFN_NT = 8;
 constexpr int FFN_BM = FFN_WM * FFN_MT * 16;      // 128 pair rows per tile
 constexpr int FFN_BN = FFN_WN * FFN_NT * 16;      // 256 weight rows per tile
-constexpr int FFN_STAGES = 4;                     // K-block slots (activations, scales)
+constexpr int FFN_STAGES = 4;                     // K-block slots (activations, weight scales)
 constexpr int FFN_BSTAGES = 2;                    // K-block-pair slots (weights)
+constexpr int FFN_SASLOTS = 4;                    // activation-scale slots (four K blocks each)
 constexpr int FFN_THREADS = 512;
 constexpr int FFN_A_BYTES = FFN_BM * 128;         // e4m3, 128 K per row
-constexpr int FFN_SA_BYTES = FFN_BM * 4;          // one scale word per row
-constexpr int FFN_SB_BYTES = FFN_BN * 4;
-constexpr int FFN_STAGE = FFN_A_BYTES + FFN_SA_BYTES + FFN_SB_BYTES;
+constexpr int FFN_SB_BYTES = FFN_BN * 4;          // one weight-scale word per row
+constexpr int FFN_STAGE = FFN_A_BYTES + FFN_SB_BYTES;
 constexpr int FFN_BPAIR = FFN_BN * 128;           // e2m1, 256 K per row
-constexpr int FFN_LDS = FFN_STAGES * FFN_STAGE + FFN_BSTAGES * FFN_BPAIR;
+constexpr int FFN_SASLOT = FFN_BM * 4;            // one activation-scale word per row
+constexpr int FFN_LDS = FFN_STAGES * FFN_STAGE + FFN_BSTAGES * FFN_BPAIR + FFN_SASLOTS * FFN_SASLOT;
 
 // MODE 1: linear1 (+ SwiGLU + requant); 2: linear2 (fp32 out); 3 / 4: the
 // standalone masked / contiguous M-grouped GEMM (bf16 out).
@@ -188,13 +189,20 @@ template <int MODE>
 __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
   constexpr int NW = FFN_WM * FFN_WN;
   constexpr int MT = FFN_MT, NT = FFN_NT, STAGES = FFN_STAGES, STAGE = FFN_STAGE;
-  constexpr int OFF_SA = FFN_A_BYTES, OFF_SB = OFF_SA + FFN_SA_BYTES;
+  constexpr int OFF_SB = FFN_A_BYTES;
   constexpr int BRING = FFN_STAGES * FFN_STAGE;    // start of the weight-pair ring
+  constexpr int SARING = BRING + FFN_BSTAGES * FFN_BPAIR;   // start of the activation-scale ring
   constexpr int RA = FFN_BM / 8 / NW;              // A regions (8 rows x 128 B) per wave per K block
   constexpr int RB = FFN_BN / 8 / NW;              // B regions (8 rows x 128 B) per wave per K-block pair
-  constexpr int SAW = FFN_BM / NW;                 // A scale words per wave
+  constexpr int SAQ = FFN_BM / 4 / NW;             // A scale words per wave per quarter slot
   constexpr int SBW = FFN_BN / NW;                 // B scale words per wave
-  static_assert(SAW <= 64 && SBW <= 64, "one scale copy per wave");
+  static_assert(SAQ >= 1 && SAQ <= 64 && SBW <= 64, "one scale copy per wave");
+  // An activation-scale word holds the exponents of four K blocks, so the words
+  // of K-block group q = kb / 4 (all tile rows) are copied once, into slot q % 4
+  // of their own ring, a quarter of the rows at a time: staging K block kn
+  // copies quarter kn % 4 of group kn / 4 + 1, so group q is complete once K
+  // block 4q is (group 0 is copied at the start of the tile).  Weight-scale
+  // words (one per row and K block, K-block-major) travel with their K block.
   // Copy instructions per wave: LA per K block (two scale words, A regions),
   // LB more per K-block pair (B regions).  Past the end of a tile's K range the
   // same instructions are issued with out-of-range offsets (they read nothing),
@@ -255,7 +263,7 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
   const int sw = swz(lrow);
   const uint32_t a_lo = (wave_m * MT * 16 + lrow) * 128 + ((lgrp ^ sw) << 4);
   const uint32_t a_hi = (wave_m * MT * 16 + lrow) * 128 + (((lgrp + 4) ^ sw) << 4);
-  const uint32_t sa_rd = OFF_SA + (wave_m * MT * 16 + lrow) * 4;
+  const uint32_t sa_rd = SARING + (wave_m * MT * 16 + lrow) * 4;
   // weight rows of block nt: linear1 gate rows 64*wn + 16nt (nt < 4) and the
   // matching up rows 128 + 64*wn + 16(nt-4); linear2 output rows 128*wn + 16nt.
   // A weight row in the pair ring holds 8 chunks of 16 bytes (chunks 0-3: the
@@ -280,15 +288,16 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
   const v4i rsSA = make_buffer_rsrc(MODE == 2 ? (const void*)p.sq : (const void*)p.x_sf,
                                     (uint32_t)(a_rows * sa_stride));
   const uint32_t wrow_bytes = (uint32_t)K / 2;
-  const uint32_t wsf_bytes = (uint32_t)(K / 128) * 4;
   const uint32_t e_rows = MODE == 1 ? 2u * I : (uint32_t)NOUT;
+  const uint32_t wsf_kb_bytes = e_rows * 4u;        // weight-scale words of one K block (K-block-major)
 
   for (int t = vb; t < total; t += G) {
     // ---------------- tile -> (row list / group e, m-tile, n-tile) ----------------
     int e, tn, row0, rows, last_pair;
     if (MODE == 4) {
-      tn = t / tiles_m4;
-      row0 = (t - tn * tiles_m4) * FFN_BM;
+      int tm;
+      raster_tile(t, tiles_m4, tiles_n, 8, &tm, &tn);
+      row0 = tm * FFN_BM;
       e = p.m_indices[row0];
       if (e < 0 || e >= p.groups) continue;       // padding block (uniform: skip the tile)
       rows = min(FFN_BM, p.gm - row0);
@@ -302,9 +311,8 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
       e = lo;
       const int cnt_e = list_cnt(e);
       const int tm_e = (cnt_e + FFN_BM - 1) / FFN_BM;
-      const int local = t - tile_base[e];
-      tn = local / tm_e;
-      const int tm = local - tn * tm_e;
+      int tm;
+      raster_tile(t - tile_base[e], tm_e, tiles_n, 8, &tm, &tn);
       row0 = list_start(e) + tm * FFN_BM;        // first row (pair) of the tile
       rows = min(FFN_BM, cnt_e - tm * FFN_BM);   // valid rows in the tile
       last_pair = list_start(e) + cnt_e - 1;
@@ -314,8 +322,8 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
     const uint8_t* wb = MODE == 1 ? p.w1 : p.w2;
     const int32_t* wsf = MODE == 1 ? p.w1_sf : p.w2_sf;
     const v4i rsB = make_buffer_rsrc(wb + (size_t)e * e_rows * wrow_bytes, e_rows * wrow_bytes);
-    const v4i rsSB = make_buffer_rsrc(wsf + (size_t)e * e_rows * (K / 128), e_rows * wsf_bytes);
-    uint32_t a_off[RA], b_off[RB], sa_off, sb_off;
+    const v4i rsSB = make_buffer_rsrc(wsf + (size_t)e * e_rows * (K / 128), e_rows * (uint32_t)(K / 128) * 4u);
+    uint32_t a_off[RA], b_off[RB], sa_off[4], sb_off;
 #pragma unroll
     for (int j = 0; j < RA; ++j) {
       const int r = (wave * RA + j) * 8 + (lane >> 3);
@@ -330,27 +338,36 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
                                     : (uint32_t)(tn * FFN_BN + r);
       b_off[j] = wr * wrow_bytes + (((lane & 7) ^ swz(r)) << 4);
     }
-    {
-      const int r = wave * SAW + (lane < SAW ? lane : 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {                 // scale-word quarter j: rows j*BM/4 + wave*SAQ + lane
+      const int r = j * (FFN_BM / 4) + wave * SAQ + (lane < SAQ ? lane : 0);
       const int pr = min(row0 + r, last_pair);
-      sa_off = MODE == 1 ? (uint32_t)p.pair_token[pr] * sa_stride : (uint32_t)pr * sa_stride;
+      sa_off[j] = MODE == 1 ? (uint32_t)p.pair_token[pr] * sa_stride : (uint32_t)pr * sa_stride;
     }
     {
       const int r = wave * SBW + (lane < SBW ? lane : 0);
       const uint32_t wr = MODE == 1 ? (uint32_t)((r < 128 ? 0 : I) + tn * 128 + (r & 127))
                                     : (uint32_t)(tn * FFN_BN + r);
-      sb_off = wr * wsf_bytes;
+      sb_off = wr * 4u;
     }
     const int NPAIR = (KB + 1) >> 1;
-    // copies of K block kb into A-ring slot `slot` (kb >= KB: read nothing)
-    auto issue_scales = [&](int kb, uint32_t slot) {
-      uint8_t* base = smem + slot;
+    // activation-scale quarter j of K-block group q into its slot (q beyond the K range: read nothing)
+    // (j is a compile-time quarter so that sa_off stays in registers)
+    auto issue_sa = [&](int q, auto j_tag) {
+      constexpr int j = decltype(j_tag)::value;
+      const bool live = q * 4 < KB;
+      if (SAQ == 64 || lane < SAQ)
+        buf4_to_lds(rsSA, live ? sa_off[j] : kBufferOutOfRange, (uint32_t)(live ? q : 0) * 4u,
+                    smem + SARING + (q & 3) * FFN_SASLOT + (j * (FFN_BM / 4) + wave * SAQ) * 4);
+    };
+    // scale copies that travel with K block kb (staged into A-ring slot `slot`;
+    // kb >= KB: read nothing); kb % 4 == decltype(j_tag)::value
+    auto issue_scales = [&](int kb, uint32_t slot, auto j_tag) {
+      issue_sa((kb >> 2) + 1, j_tag);
       const bool live = kb < KB;
-      const uint32_t sa = live ? sa_off : kBufferOutOfRange, sb = live ? sb_off : kBufferOutOfRange;
-      const int kc = live ? kb : 0;
-      // the A scale word holds four 128-wide K blocks (x_sf, and sq in groups of four)
-      if (SAW == 64 || lane < SAW) buf4_to_lds(rsSA, sa, (uint32_t)(kc >> 2) * 4u, base + OFF_SA + wave * SAW * 4);
-      if (SBW == 64 || lane < SBW) buf4_to_lds(rsSB, sb, (uint32_t)kc * 4u, base + OFF_SB + wave * SBW * 4);
+      if (SBW == 64 || lane < SBW)
+        buf4_to_lds(rsSB, live ? sb_off : kBufferOutOfRange, (uint32_t)(live ? kb : 0) * wsf_kb_bytes,
+                    smem + slot + OFF_SB + wave * SBW * 4);
     };
     auto issue_a = [&](int j, int kb, uint32_t slot) {
       const bool live = kb < KB;
@@ -370,25 +387,34 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: weight pair 0, then K blocks 0 .. STAGES-2.  Block i then copies
-    // K block i + STAGES - 1 and, when i is even, weight pair i/2 + 1.
+    // Prologue: activation-scale group 0, weight pair 0, then K blocks
+    // 0 .. STAGES-2.  Block i then copies K block i + STAGES - 1 and, when i is
+    // even, weight pair i/2 + 1.
+    issue_sa(0, std::integral_constant<int, 0>{});
+    issue_sa(0, std::integral_constant<int, 1>{});
+    issue_sa(0, std::integral_constant<int, 2>{});
+    issue_sa(0, std::integral_constant<int, 3>{});
 #pragma unroll
     for (int j = 0; j < RB; ++j) issue_b(j, 0, 0);
+    static_assert(STAGES == 4, "the prologue stages K blocks 0, 1, 2");
+    issue_scales(0, 0u, std::integral_constant<int, 0>{});
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-      issue_scales(s, s * STAGE);
+    for (int j = 0; j < RA; ++j) issue_a(j, 0, 0u);
+    issue_scales(1, (uint32_t)STAGE, std::integral_constant<int, 1>{});
 #pragma unroll
-      for (int j = 0; j < RA; ++j) issue_a(j, s, s * STAGE);
-    }
+    for (int j = 0; j < RA; ++j) issue_a(j, 1, (uint32_t)STAGE);
+    issue_scales(2, 2u * STAGE, std::integral_constant<int, 2>{});
+#pragma unroll
+    for (int j = 0; j < RA; ++j) issue_a(j, 2, 2u * STAGE);
 
-    uint32_t rd = 0, wr = (STAGES - 1) * STAGE;
-    // One K block; ODD: kb is odd (no weight pair is copied in it).  The copy
+    // One K block; PH = kb % 4, ODD: kb is odd (no weight pair is copied in it).  The copy
     // instructions are spread between the matrix instructions (a copy that finds
     // the memory pipeline full stalls the wave; spread out, matrix work is
     // queued meanwhile), pinned with scheduling group barriers: the scale words
     // first, then the A regions, then (even blocks) the B regions.
-    auto kstep = [&](int kb, auto odd_tag) {
-      constexpr bool ODD = decltype(odd_tag)::value;
+    auto kstep = [&](int kb, auto ph_tag) {
+      constexpr int PH = decltype(ph_tag)::value;
+      constexpr bool ODD = (PH & 1) != 0;
       constexpr int ILV = RA + (ODD ? 0 : RB);
       constexpr int ILV_STEP = (MT * NT) / ILV;
       // Stage kb (and its weight pair) has landed once at most this many copies
@@ -409,17 +435,21 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
       block_barrier();
       const int kn = kb + STAGES - 1;              // K block copied in this block
       const int pn = (kb >> 1) + 1;                // weight pair copied in this block (even kb)
-      const uint32_t bwr = (uint32_t)(pn & 1) * FFN_BPAIR;
-      issue_scales(kn, wr);
+      // ring slots follow from kb % 4 alone (four A-ring slots, two pair slots)
+      constexpr uint32_t rd = PH * STAGE, wr = ((PH + STAGES - 1) % STAGES) * STAGE;
+      constexpr uint32_t bwr = (uint32_t)(((PH >> 1) + 1) & 1) * FFN_BPAIR;
+      constexpr uint32_t brd = (uint32_t)((PH >> 1) & 1) * FFN_BPAIR;
+      issue_scales(kn, wr, std::integral_constant<int, (PH + STAGES - 1) & 3>{});
 
       const uint8_t* sbase = smem + rd;
-      const uint8_t* bbase = smem + BRING + (uint32_t)((kb >> 1) & 1) * FFN_BPAIR + b_ch[ODD ? 1 : 0];
-      const int byte_sel = (kb & 3) * 8;
+      const uint8_t* sabase = smem + (uint32_t)((kb >> 2) & 3) * FFN_SASLOT;
+      const uint8_t* bbase = smem + BRING + brd + b_ch[ODD ? 1 : 0];
+      constexpr int byte_sel = PH * 8;
       int sa_s[MT];
       v8i af[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(sbase + sa_rd + mt * 64);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(sabase + sa_rd + mt * 64);
         sa_s[mt] = (int)((w >> byte_sel) & 0xffu);
         const v4i l4 = *reinterpret_cast<const v4i*>(sbase + a_lo + mt * 2048);
         const v4i h4 = *reinterpret_cast<const v4i*>(sbase + a_hi + mt * 2048);
@@ -450,14 +480,13 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
           if (copy_here) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // then 1 copy
         }
-
-      rd = (rd + STAGE == STAGES * STAGE) ? 0u : rd + STAGE;
-      wr = (wr + STAGE == STAGES * STAGE) ? 0u : wr + STAGE;
     };
 #pragma clang loop unroll(disable)
-    for (int kb = 0; kb < KB; kb += 2) {
-      kstep(kb, std::false_type{});
-      if (kb + 1 < KB) kstep(kb + 1, std::true_type{});
+    for (int kb = 0; kb < KB; kb += 4) {
+      kstep(kb, std::integral_constant<int, 0>{});
+      if (kb + 1 < KB) kstep(kb + 1, std::integral_constant<int, 1>{});
+      if (kb + 2 < KB) kstep(kb + 2, std::integral_constant<int, 2>{});
+      if (kb + 3 < KB) kstep(kb + 3, std::integral_constant<int, 3>{});
     }
     wait_vmcnt<0>();   // the trailing copies (of nothing) have retired
     block_barrier();   // the ring is free before the next tile's prologue
@@ -575,6 +604,23 @@ static hipError_t launch_ffn(FfnParams& p, int num_cus, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// weight pre-transform: packed UE8M0 weight-scale words [G][N][KB] -> [G][KB][N]
+// (K-block-major), 64 x 64 words at a time through LDS so that both the reads
+// (along K) and the writes (along N) are contiguous
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) fp4_sf_transpose_kernel(const int32_t* in, int32_t* out, int n, int kb) {
+  __shared__ int32_t tile[64][65];
+  const size_t gbase = (size_t)blockIdx.z * n * kb;
+  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4)
+    if (n0 + r < n && k0 + tx < kb) tile[r][tx] = in[gbase + (size_t)(n0 + r) * kb + k0 + tx];
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4)
+    if (k0 + r < kb && n0 + tx < n) out[gbase + (size_t)(k0 + r) * n + n0 + tx] = tile[tx][r];
+}
+
 }  // namespace dg
 
 using namespace dg;
@@ -652,6 +698,25 @@ int dg_m_grouped_fp8_fp4_gemm_nt_masked(const uint8_t* a, const int32_t* a_sf, c
     if (cus <= 0) cus = di.num_cus;
     const hipError_t e = launch_gemm4(p, true, cus, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? DG_OK : DG_ERR_HIP;
+  } catch (...) {
+    return DG_ERR_HIP;
+  }
+}
+
+int dg_transform_fp4_weight_sf(const int32_t* sf, int32_t* sf_t, int num_groups, int n, int k, void* stream) {
+  try {
+    if (!sf || !sf_t || num_groups <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
+    if (k % 128 != 0) return DG_ERR_UNSUPPORTED;
+    if (num_groups > 65535) return DG_ERR_UNSUPPORTED;
+    const size_t bytes = (size_t)num_groups * n * (k / 128) * 4;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(sf), lo_t = reinterpret_cast<uintptr_t>(sf_t);
+    if (((lo | lo_t) & 3) || (lo < lo_t + bytes && lo_t < lo + bytes)) return DG_ERR_INVALID_ARG;
+    DeviceInfo di = current_device_info();
+    if (!di.ok) return DG_ERR_NO_DEVICE;
+    const int kb = k / 128;
+    hipLaunchKernelGGL(fp4_sf_transpose_kernel, dim3((n + 63) / 64, (kb + 63) / 64, num_groups), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), sf, sf_t, n, kb);
+    return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
   } catch (...) {
     return DG_ERR_HIP;
   }

@@ -125,6 +125,24 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
                                     void* stream);
 
 /*
+ * Weight pre-transform for the FP8 x FP4 entry points (news page "DeepSeek 发布
+ * DeepGEMM 重大更新：Mega MoE 融合算子与 FP4 精度支持": section FP4 精度支持, the
+ * weight pre-transform tool, and section Mega MoE, whose expert weights are
+ * converted once to the layout the fused kernel reads).  Here the E2M1 weight
+ * bytes keep their row-major layout and the packed UE8M0 scale words are made
+ * K-block-major:
+ *   sf_t[g][kb][r] = sf[g][r][kb]     sf [num_groups, n, k/128] -> sf_t [num_groups, k/128, n]
+ * so that the scale words of one K block of a weight tile are one contiguous run.
+ * dg_fp8_fp4_expert_ffn (w1_sf, w2_sf) and the M-grouped FP8 x FP4 GEMMs (b_sf)
+ * take the transformed words; the transform is meant to run once per weight set.
+ *   sf, sf_t  device buffers, 4-byte aligned, not overlapping (DG_ERR_INVALID_ARG)
+ * Requirements: k % 128 == 0, num_groups <= 65535 (else DG_ERR_UNSUPPORTED).
+ * Enqueued on stream; no host synchronisation.
+ */
+int dg_transform_fp4_weight_sf(const int32_t* sf, int32_t* sf_t, int num_groups, int n, int k,
+                               void* stream);
+
+/*
  * Bytes of device workspace dg_fp8_fp4_expert_ffn needs for these sizes
  * (routing lists, the requantised intermediate and per-pair outputs).
  * Returns 0 for invalid sizes.
@@ -150,9 +168,11 @@ size_t dg_fp8_fp4_expert_ffn_workspace_bytes(int num_tokens, int num_topk, int n
  *   topk_idx  [T, num_topk]     int32 global expert ids (any value; out-of-range ids ignored)
  *   topk_w    [T, num_topk]     fp32
  *   w1        [E, 2I, H/2]      E2M1 pairs; element 2i in the low nibble of byte i
- *   w1_sf     [E, 2I, H/128]    int32, four UE8M0 scales per word (1x32 blocks)
+ *   w1_sf     [E, H/128, 2I]    int32, four UE8M0 scales per word (1x32 blocks; byte i of
+ *                               word [e][kb][r] is K 128kb+32i..+32 of row r), K-block-major
+ *                               as dg_transform_fp4_weight_sf writes it
  *   w2        [E, H, I/2]       E2M1 pairs
- *   w2_sf     [E, H, I/128]     int32
+ *   w2_sf     [E, I/128, H]     int32, K-block-major likewise
  *   y         [T, H]            bf16 output
  *   workspace device buffer of at least dg_fp8_fp4_expert_ffn_workspace_bytes(...) bytes,
  *             256-byte aligned; its contents on entry are ignored
@@ -177,7 +197,8 @@ int dg_fp8_fp4_expert_ffn(const uint8_t* x, const int32_t* x_sf, const int32_t* 
  *   a_sf   int32, ceil(k/512) words per row, four UE8M0 exponents per word (1x128
  *          blocks; byte i of word j is block 4j+i), 4-byte aligned
  *   b      [num_groups, n, k/2] E2M1 pairs (element 2i in the low nibble of byte i), 16-byte aligned
- *   b_sf   [num_groups, n, k/128] int32, four UE8M0 exponents per word (1x32 blocks)
+ *   b_sf   [num_groups, k/128, n] int32, four UE8M0 exponents per word (1x32 blocks),
+ *          K-block-major as dg_transform_fp4_weight_sf writes it
  *   d      bf16 rows of n, 16-byte aligned
  * Requirements: n % 256 == 0; k % 128 == 0; (rows of A) * k, n * k / 2 and
  *   (rows of A) * 4 * ceil(k/512) at most 2^31 (else DG_ERR_UNSUPPORTED).

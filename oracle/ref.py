@@ -215,6 +215,21 @@ def m_grouped_fp8_fp4_masked(a, a_sf, b, b_sf, masked_m):
     return ref, written
 
 
+def fp4_weight_sf_k_major(sf) -> np.ndarray:
+    """Weight pre-transform of the packed UE8M0 scale words (news page on the DeepGEMM
+    update, section FP4 精度支持: a tool converts FP4 weights once to the layout the fused
+    MoE kernel reads).  A pure relayout, words unchanged: out[g, kb, r] = sf[g, r, kb].
+
+    sf [G, R, KB] int32 -> [G, KB, R] int32.
+    """
+    sf = np.asarray(sf)
+    G, R, KB = sf.shape
+    out = np.empty((G, KB, R), dtype=sf.dtype)
+    for kb in range(KB):
+        out[:, kb, :] = sf[:, :, kb]
+    return out
+
+
 def silu(x):
     """silu(x) = x * sigmoid(x) = x / (1 + exp(-x))."""
     return x / (1.0 + np.exp(-x))

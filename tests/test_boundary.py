@@ -90,6 +90,19 @@ def test_fp8_fp4_grouped_argument_validation():
     assert g(A16, A16, A16, A16, A16, A16, 4, 256, 256, 128, 0, None) in (0, 4)
 
 
+def test_transform_fp4_weight_sf_argument_validation():
+    lib = dgm.load_library()
+    t = lib.dg_transform_fp4_weight_sf
+    far = A16 + (1 << 24)
+    assert t(0, far, 2, 256, 512, None) == 1                                     # null input
+    assert t(A16, far, 0, 256, 512, None) == 1                                   # no groups
+    assert t(A16 + 2, far, 2, 256, 512, None) == 1                               # misaligned
+    assert t(A16, A16 + 64, 2, 256, 512, None) == 1                              # output overlaps input
+    assert t(A16, far, 2, 256, 500, None) == 2                                   # K % 128
+    assert t(A16, far, 70000, 1, 128, None) == 2                                 # grid z limit
+    assert t(A16, far, 2, 256, 512, None) in (0, 4)                              # valid: device check
+
+
 def test_grouped_and_ffn_argument_validation():
     lib = dgm.load_library()
     f = lib.dg_m_grouped_fp8_gemm_nt_contiguous

@@ -38,8 +38,9 @@ def _run(dg, g, topk_w=None, offset=None, ws_extra=0):
     nbytes = dg.dg_fp8_fp4_expert_ffn_workspace_bytes(T, k, E, H, I2 // 2)
     ws = torch.zeros(nbytes + ws_extra, dtype=torch.uint8, device="cuda")
     y = torch.full((T, H), -1, dtype=torch.int16, device="cuda")      # sentinel 0xFFFF
+    (w1, w1_sf), (w2, w2_sf) = dg.transform_weights_for_expert_ffn((g["w1"], g["w1_sf"]), (g["w2"], g["w2_sf"]))
     dg.dg_fp8_fp4_expert_ffn(g["x"], g["x_sf"], g["topk_idx"], g["topk_w"] if topk_w is None else topk_w,
-                             g["w1"], g["w1_sf"], g["w2"], g["w2_sf"], y,
+                             w1, w1_sf, w2, w2_sf, y,
                              g["expert_offset"] if offset is None else offset, ws)
     torch.cuda.synchronize()
     return bits(y), ws

@@ -31,7 +31,8 @@ def _dev(x):
 
 def _run_contig(dg, a, a_sf, b, b_sf, mi):
     d = sentinel_like((a.shape[0], b.shape[1]))
-    dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(_dev(a), _dev(a_sf), _dev(b), _dev(b_sf), _dev(mi), d)
+    dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(_dev(a), _dev(a_sf), _dev(b),
+                                               dg.dg_transform_fp4_weight_sf(_dev(b_sf)), _dev(mi), d)
     torch.cuda.synchronize()
     return bits(d)
 
@@ -39,7 +40,7 @@ def _run_contig(dg, a, a_sf, b, b_sf, mi):
 def _run_masked(dg, a, a_sf, b, b_sf, mm):
     G, max_m, _ = a.shape
     d = sentinel_like((G, max_m, b.shape[1]))
-    dg.dg_m_grouped_fp8_fp4_gemm_nt_masked(_dev(a), _dev(a_sf), _dev(b), _dev(b_sf),
+    dg.dg_m_grouped_fp8_fp4_gemm_nt_masked(_dev(a), _dev(a_sf), _dev(b), dg.dg_transform_fp4_weight_sf(_dev(b_sf)),
                                            _dev(np.asarray(mm, np.int32)), d, 0)
     torch.cuda.synchronize()
     return bits(d)
@@ -130,7 +131,8 @@ def test_fp4_contiguous_full_size_sampled(dg):
     g = synth.gen_fp4_contiguous(G, 32768, N, K, seed=515, backend="torch", device="cuda")
     M = int(g["M"])
     d = sentinel_like((M, N))
-    dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(g["a"], g["a_sf"], g["b"], g["b_sf"], g["m_indices"], d)
+    dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(g["a"], g["a_sf"], g["b"], dg.dg_transform_fp4_weight_sf(g["b_sf"]),
+                                               g["m_indices"], d)
     torch.cuda.synchronize()
     db = bits(d)
     mi = synth.to_numpy(g["m_indices"])
@@ -148,3 +150,15 @@ def test_fp4_contiguous_full_size_sampled(dg):
         want.append(R.fp8_fp4_gemm_nt(a, a_sf, b[grp], b_sf[grp]))
         got.append(db[rows])
     check_parity(np.concatenate(got), np.concatenate(want), what="fp4 contig full size")
+
+
+@pytest.mark.parametrize("G,N,K", [(1, 256, 128), (3, 200, 70 * 128), (2, 4096, 7168), (5, 65, 65 * 128)])
+def test_transform_fp4_weight_sf_bit_exact(dg, G, N, K):
+    """The weight-scale relayout against the oracle's, word for word (sizes straddle the
+    64 x 64 transpose tiles in both directions)."""
+    rng = np.random.default_rng(G * 1000 + N + K)
+    sf = rng.integers(-2**31, 2**31 - 1, size=(G, N, K // 128), dtype=np.int64).astype(np.int32)
+    out = torch.full((G, K // 128, N), -1, dtype=torch.int32, device="cuda")
+    dg.dg_transform_fp4_weight_sf(_dev(sf), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), R.fp4_weight_sf_k_major(sf))

@@ -585,6 +585,23 @@ def test_fp8_fp4_masked_equals_contiguous_of_the_same_rows():
     assert np.array_equal(written_c[0], np.ones(130, bool)) and not written_c[1].any()
 
 
+def test_fp4_weight_sf_k_major_fixture_and_labelled_words():
+    """The scale relayout on a hand-written case, and on words that carry their own
+    (group, row, K block) label, so a swapped index or group shows as a wrong label."""
+    sf = np.array([[[1, 2, 3], [4, 5, 6]]], np.int32)                   # G 1, rows 2, K blocks 3
+    assert R.fp4_weight_sf_k_major(sf).tolist() == [[[1, 4], [2, 5], [3, 6]]]
+    G, Rr, KB = 3, 70, 5
+    g_, r_, k_ = np.meshgrid(np.arange(G), np.arange(Rr), np.arange(KB), indexing="ij")
+    lab = ((g_ << 20) | (r_ << 8) | k_).astype(np.int32)
+    out = R.fp4_weight_sf_k_major(lab)
+    assert out.shape == (G, KB, Rr)
+    for g in range(G):
+        for kb in range(KB):
+            for r in range(Rr):
+                w = int(out[g, kb, r])
+                assert (w >> 20, (w >> 8) & 0xFFF, w & 0xFF) == (g, r, kb)
+
+
 def test_planted_mistakes_fail_dense_pins():
     assert _pins_dense(R.fp8_gemm_nt)
 
