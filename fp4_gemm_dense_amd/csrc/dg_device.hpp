@@ -3,6 +3,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
 #include <stdint.h>
 
 namespace dg {
@@ -66,6 +69,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
 // and depends only on r % 16, so rows r and r + 16k share one pattern (their
 // addresses differ by a constant that fits an instruction offset).
 __device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1, in order: a loop
+// whose index is a compile-time constant in the body (register arrays indexed by
+// it stay in registers, and `if constexpr` can select per iteration).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Waits until at most n vector-memory operations of this wave are outstanding.
 // (gfx9 encoding: vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at max.)

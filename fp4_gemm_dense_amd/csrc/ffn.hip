@@ -387,99 +387,130 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: activation-scale group 0, weight pair 0, then K blocks
-    // 0 .. STAGES-2.  Block i then copies K block i + STAGES - 1 and, when i is
-    // even, weight pair i/2 + 1.
+    // Operand fragments live in two register sets: block kb multiplies set
+    // kb % 2, read from LDS during block kb - 1, while it reads K block kb + 1
+    // into the other set.  The LDS reads thus never hold up the matrix
+    // instructions, and a block's barrier also certifies that every wave has
+    // read stage kb, whose A slot is then refilled (with K block kb + 4).
+    v8i af[2][MT], bfr[2][NT];
+    uint32_t saw[2][MT], sbw[2][NT];   // scale words; the exponent byte is taken at use
+    // Part `part` of the fragments of K block kb (kb % 4 == PH) into set PH % 2:
+    // parts 0 .. MT-1 the A fragments (two 16-byte reads each), MT .. MT+NT-1
+    // the B fragments, then the A scale words and the B scale words.
+    constexpr int NPARTS = MT + NT + 2;
+    auto read_part = [&](int kb, auto ph_tag, auto part_tag) {
+      constexpr int PH = decltype(ph_tag)::value, S = PH & 1, P = decltype(part_tag)::value;
+      const uint8_t* sbase = smem + PH * STAGE;
+      if constexpr (P < MT) {
+        const v4i l4 = *reinterpret_cast<const v4i*>(sbase + a_lo + P * 2048);
+        const v4i h4 = *reinterpret_cast<const v4i*>(sbase + a_hi + P * 2048);
+        af[S][P] = v8i{l4.x, l4.y, l4.z, l4.w, h4.x, h4.y, h4.z, h4.w};
+      } else if constexpr (P < MT + NT) {
+        const uint8_t* bbase = smem + BRING + (uint32_t)((PH >> 1) & 1) * FFN_BPAIR + b_ch[S];
+        const v4i b4 = *reinterpret_cast<const v4i*>(bbase + b_rd[P - MT]);
+        bfr[S][P - MT] = v8i{b4.x, b4.y, b4.z, b4.w, 0, 0, 0, 0};
+      } else if constexpr (P == MT + NT) {
+        const uint8_t* sabase = smem + (uint32_t)((kb >> 2) & 3) * FFN_SASLOT;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) saw[S][mt] = *reinterpret_cast<const uint32_t*>(sabase + sa_rd + mt * 64);
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int row_off = MODE == 1 ? ((nt < 4 ? 0 : 128) + (nt & 3) * 16) : nt * 16;
+          sbw[S][nt] = *reinterpret_cast<const uint32_t*>(sbase + sb_rd0 + row_off * 4);
+        }
+      }
+    };
+    auto read_frags = [&](int kb, auto ph_tag) {
+      static_for<NPARTS>([&](auto part_tag) { read_part(kb, ph_tag, part_tag); });
+    };
+
+    // Prologue: activation-scale group 0, weight pair 0, K blocks 0 and 1,
+    // weight pair 1, K blocks 2 and 3; then K block 0's fragments.  Block kb
+    // copies K block kb + 4 (into the slot of K block kb) and, when kb is odd,
+    // weight pair (kb + 3) / 2 (into the slot of pair (kb - 1) / 2, whose last
+    // K block was read in block kb - 1).
+    static_assert(STAGES == 4, "four A-ring slots: the slot of K block kb is kb % 4");
     issue_sa(0, std::integral_constant<int, 0>{});
     issue_sa(0, std::integral_constant<int, 1>{});
     issue_sa(0, std::integral_constant<int, 2>{});
     issue_sa(0, std::integral_constant<int, 3>{});
 #pragma unroll
     for (int j = 0; j < RB; ++j) issue_b(j, 0, 0);
-    static_assert(STAGES == 4, "the prologue stages K blocks 0, 1, 2");
     issue_scales(0, 0u, std::integral_constant<int, 0>{});
 #pragma unroll
     for (int j = 0; j < RA; ++j) issue_a(j, 0, 0u);
     issue_scales(1, (uint32_t)STAGE, std::integral_constant<int, 1>{});
 #pragma unroll
     for (int j = 0; j < RA; ++j) issue_a(j, 1, (uint32_t)STAGE);
+#pragma unroll
+    for (int j = 0; j < RB; ++j) issue_b(j, 1, (uint32_t)FFN_BPAIR);
     issue_scales(2, 2u * STAGE, std::integral_constant<int, 2>{});
 #pragma unroll
     for (int j = 0; j < RA; ++j) issue_a(j, 2, 2u * STAGE);
+    issue_scales(3, 3u * STAGE, std::integral_constant<int, 3>{});
+#pragma unroll
+    for (int j = 0; j < RA; ++j) issue_a(j, 3, 3u * STAGE);
+    wait_vmcnt<3 * LA + LB>();   // K block 0, pair 0 and scale group 0 have landed
+    block_barrier();
+    read_frags(0, std::integral_constant<int, 0>{});
 
-    // One K block; PH = kb % 4, ODD: kb is odd (no weight pair is copied in it).  The copy
-    // instructions are spread between the matrix instructions (a copy that finds
-    // the memory pipeline full stalls the wave; spread out, matrix work is
-    // queued meanwhile), pinned with scheduling group barriers: the scale words
-    // first, then the A regions, then (even blocks) the B regions.
+    // One K block; PH = kb % 4.  The copy instructions are spread between the
+    // matrix instructions (a copy that finds the memory pipeline full stalls the
+    // wave; spread out, matrix work is queued meanwhile), pinned with scheduling
+    // group barriers: the scale words first, then the A regions, then (odd
+    // blocks) the weight pair.
     auto kstep = [&](int kb, auto ph_tag) {
-      constexpr int PH = decltype(ph_tag)::value;
+      constexpr int PH = decltype(ph_tag)::value, S = PH & 1;
       constexpr bool ODD = (PH & 1) != 0;
-      constexpr int ILV = RA + (ODD ? 0 : RB);
+      constexpr int ILV = RA + (ODD ? RB : 0);
       constexpr int ILV_STEP = (MT * NT) / ILV;
-      // Stage kb (and its weight pair) has landed once at most this many copies
-      // remain (a wave's loads retire in issue order):
-      //  * even kb >= 2: the weight pair was the last copy of block kb - 2; only
-      //    block kb - 1's LA copies are younger;
-      //  * odd kb >= 3: K block kb was copied in block kb - 3, before that
-      //    block's LB weight copies, then blocks kb - 2 (LA) and kb - 1 (LA + LB);
-      //  * kb = 0: the prologue's two later K blocks; kb = 1: K block 2 and block
-      //    0's K block and weight pair.
+      // K block kb + 1 (and its weight pair) has landed once at most this many
+      // copies remain (a wave's loads retire in issue order):
+      //  * even kb: K block kb + 1 and its pair were copied in block kb - 3 (the
+      //    pair last); younger are blocks kb - 2 (LA) and kb - 1 (LA + LB);
+      //  * odd kb >= 3: the pair of K block kb + 1 was the last copy of block
+      //    kb - 2; younger is block kb - 1 (LA);
+      //  * kb = 1: pair 1 came before the prologue's K blocks 2 and 3 and block
+      //    0's copies (K block 2 is older than K block 3).
       if (ODD) {
-        if (kb == 1) wait_vmcnt<2 * LA + LB>();
-        else wait_vmcnt<2 * LA + 2 * LB>();
-      } else {
-        if (kb == 0) wait_vmcnt<2 * LA>();
+        if (kb == 1) wait_vmcnt<2 * LA>();
         else wait_vmcnt<LA>();
+      } else {
+        wait_vmcnt<2 * LA + LB>();
       }
-      block_barrier();
-      const int kn = kb + STAGES - 1;              // K block copied in this block
-      const int pn = (kb >> 1) + 1;                // weight pair copied in this block (even kb)
-      // ring slots follow from kb % 4 alone (four A-ring slots, two pair slots)
-      constexpr uint32_t rd = PH * STAGE, wr = ((PH + STAGES - 1) % STAGES) * STAGE;
-      constexpr uint32_t bwr = (uint32_t)(((PH >> 1) + 1) & 1) * FFN_BPAIR;
-      constexpr uint32_t brd = (uint32_t)((PH >> 1) & 1) * FFN_BPAIR;
-      issue_scales(kn, wr, std::integral_constant<int, (PH + STAGES - 1) & 3>{});
+      wait_lgkmcnt0();   // this wave's reads of K block kb are done ...
+      block_barrier();   // ... and every wave's: its slot can be refilled
+      const int kn = kb + 4;                       // K block copied in this block
+      const int pn = (kb + 3) >> 1;                // weight pair copied in this block (odd kb)
+      constexpr uint32_t wr = PH * STAGE;
+      constexpr uint32_t bwr = (uint32_t)(((PH + 3) >> 1) & 1) * FFN_BPAIR;
+      issue_scales(kn, wr, std::integral_constant<int, PH>{});
 
-      const uint8_t* sbase = smem + rd;
-      const uint8_t* sabase = smem + (uint32_t)((kb >> 2) & 3) * FFN_SASLOT;
-      const uint8_t* bbase = smem + BRING + brd + b_ch[ODD ? 1 : 0];
       constexpr int byte_sel = PH * 8;
-      int sa_s[MT];
-      v8i af[MT];
+      int sa_s[MT], sb_s[NT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(sabase + sa_rd + mt * 64);
-        sa_s[mt] = (int)((w >> byte_sel) & 0xffu);
-        const v4i l4 = *reinterpret_cast<const v4i*>(sbase + a_lo + mt * 2048);
-        const v4i h4 = *reinterpret_cast<const v4i*>(sbase + a_hi + mt * 2048);
-        af[mt] = v8i{l4.x, l4.y, l4.z, l4.w, h4.x, h4.y, h4.z, h4.w};
-      }
-      int sb_s[NT];
-      v8i bfr[NT];
+      for (int mt = 0; mt < MT; ++mt) sa_s[mt] = (int)((saw[S][mt] >> byte_sel) & 0xffu);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int row_off = MODE == 1 ? ((nt < 4 ? 0 : 128) + (nt & 3) * 16) : nt * 16;
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(sbase + sb_rd0 + row_off * 4);
-        sb_s[nt] = (int)((w >> (8 * lgrp)) & 0xffu);
-        const v4i b4 = *reinterpret_cast<const v4i*>(bbase + b_rd[nt]);
-        bfr[nt] = v8i{b4.x, b4.y, b4.z, b4.w, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int j = mt * NT + nt;
-          acc[mt][nt] = mfma_scaled_e2m1_e4m3_16x16x128(bfr[nt], sb_s[nt], af[mt], sa_s[mt], acc[mt][nt]);
-          const bool copy_here = j % ILV_STEP == ILV_STEP - 1 && j / ILV_STEP < ILV;
-          if (copy_here) {
-            const int idx = j / ILV_STEP;
-            if (idx < RA) issue_a(idx, kn, wr);
-            else issue_b(idx - RA, pn, bwr);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
-          if (copy_here) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // then 1 copy
+      for (int nt = 0; nt < NT; ++nt) sb_s[nt] = (int)((sbw[S][nt] >> (8 * lgrp)) & 0xffu);
+      // matrix instruction j is followed by read part j of K block kb + 1 (the
+      // LDS reads spread over the block keep them off the barrier's critical
+      // path) and, every ILV_STEP-th, by one copy
+      static_for<MT * NT>([&](auto j_tag) {
+        constexpr int j = decltype(j_tag)::value, mt = j / NT, nt = j % NT;
+        acc[mt][nt] = mfma_scaled_e2m1_e4m3_16x16x128(bfr[S][nt], sb_s[nt], af[S][mt], sa_s[mt], acc[mt][nt]);
+        constexpr bool copy_here = j % ILV_STEP == ILV_STEP - 1 && j / ILV_STEP < ILV;
+        if constexpr (j < NPARTS) read_part(kb + 1, std::integral_constant<int, (PH + 1) & 3>{}, j_tag);
+        if constexpr (copy_here) {
+          constexpr int idx = j / ILV_STEP;
+          if constexpr (idx < RA) issue_a(idx, kn, wr);
+          else issue_b(idx - RA, pn, bwr);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // 1 MFMA
+        if constexpr (j < NPARTS)
+          __builtin_amdgcn_sched_group_barrier(0x100, j < MT ? 2 : (j < MT + NT ? 1 : (j == MT + NT ? 1 : 4)), 0);
+        if constexpr (copy_here) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // then 1 copy
+      });
     };
 #pragma clang loop unroll(disable)
     for (int kb = 0; kb < KB; kb += 4) {
@@ -489,6 +520,7 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
       if (kb + 3 < KB) kstep(kb + 3, std::integral_constant<int, 3>{});
     }
     wait_vmcnt<0>();   // the trailing copies (of nothing) have retired
+    wait_lgkmcnt0();   // and the last block's reads (of K block KB)
     block_barrier();   // the ring is free before the next tile's prologue
 
     if (GEMM) {
