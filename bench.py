@@ -18,6 +18,8 @@ Other workloads:
   --config 5  M-grouped FP8xFP4 GEMM, contiguous, 8 groups from 32768 routed rows,
               (N,K) in {(4096,7168), (7168,2048)}: config 2 with E2M1 weights
               (UE8M0 per 1x32) and UE8M0 activation scales per 1x128
+  --config 6  the config-1 dense sweep with packed UE8M0 scales (power-of-two,
+              A per 1x128, B per 128x128), applied by the scaled matrix instruction
 
 Caches: one dense-sweep step touches more than 1 GB of distinct inputs and
 outputs, so no shape's operands survive in the 4 MB L2s or the 256 MB
@@ -57,7 +59,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--shape", type=str, default=None,
@@ -96,16 +98,21 @@ def items_dense(config, only=None):
     elif config == 0:
         shapes = [(128, 2112, 7168, False, synth.seed_for(0, 0))]
     else:
-        shapes = [(M, N, K, True, synth.seed_for(1, mi * 6 + j))
+        shapes = [(M, N, K, True, synth.seed_for(config, mi * 6 + j))
                   for mi, M in enumerate(synth.DENSE_M) for j, (N, K) in enumerate(synth.DENSE_NK)]
+    ue = config == 6          # packed UE8M0 scales
     items = []
     for (M, N, K, with_c, seed) in shapes:
-        g = synth.gen_dense(M, N, K, seed, with_c=with_c, backend="torch", device="cuda")
+        gen = synth.gen_dense_ue8m0 if ue else synth.gen_dense
+        g = gen(M, N, K, seed, with_c=with_c, backend="torch", device="cuda")
         d = torch.empty(M, N, dtype=torch.int16, device="cuda")
-        nbytes = M * K + N * K + 4 * (K // 128) * M + 4 * nb(N) * (K // 128) + 2 * M * N * (2 if with_c else 1)
+        kw = (K // 128 + 3) // 4
+        sf_bytes = 4 * kw * (M + nb(N)) if ue else 4 * (K // 128) * (M + nb(N))
+        nbytes = M * K + N * K + sf_bytes + 2 * M * N * (2 if with_c else 1)
+        gemm = dg.dg_fp8_gemm_nt_ue8m0 if ue else dg.dg_fp8_gemm_nt
 
-        def run(g=g, d=d):
-            dg.dg_fp8_gemm_nt(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
+        def run(g=g, d=d, gemm=gemm):
+            gemm(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
         items.append(dict(run=run, g=g, flops=2.0 * M * N * K, bytes=nbytes, label=f"M{M}_N{N}_K{K}",
                           shape=(M, N, K), plan=dg.dg_query_plan(M, N, K)))
     return items
@@ -251,7 +258,7 @@ def _cpu_pass(config, items, budget_s, t_start, npass, t_total, flops, desc):
         if time.perf_counter() - t_start > budget_s:
             break
         g = it["g"]
-        if config in (0, 1):
+        if config in (0, 1, 6):
             M, N, K = it["shape"]
             r = min(M, 64)
             r0 = (npass * r) % M
@@ -259,10 +266,11 @@ def _cpu_pass(config, items, budget_s, t_start, npass, t_total, flops, desc):
             if "_np_b" not in it:      # B is copied to the host once, not per pass
                 it["_np_b"] = (synth.to_numpy(g["b"]), synth.to_numpy(g["sfb"]))
             b, sfb = it["_np_b"]
-            a, sfa = synth.to_numpy(g["a"][r0:r0 + r]), synth.to_numpy(g["sfa"][:, r0:r0 + r])
+            a = synth.to_numpy(g["a"][r0:r0 + r])
+            sfa = synth.to_numpy(g["sfa"][r0:r0 + r] if config == 6 else g["sfa"][:, r0:r0 + r])
             c = None if g["c"] is None else synth.to_numpy(g["c"][r0:r0 + r])
             t0 = time.perf_counter()
-            R.fp8_gemm_nt(a, sfa, b, sfb, c)
+            (R.fp8_gemm_nt_ue8m0 if config == 6 else R.fp8_gemm_nt)(a, sfa, b, sfb, c)
             t_total += time.perf_counter() - t0
             flops += 2.0 * r * N * K
             if npass == 0:
@@ -339,6 +347,8 @@ WORKLOADS = {
        "e4m3 1x128 / 128x128 fp32 scales",
     4: "FP8xFP4 expert FFN, 4096 tokens, hidden 7168, intermediate 2048, 32 local experts of 256, top-8, "
        "e4m3 activations (UE8M0/128), E2M1 weights (UE8M0/32)",
+    6: "dense NT GEMM sweep, M{64,4096} x (N,K){(2112,7168),(24576,1536),(32768,512),(7168,16384),(4096,7168),"
+       "(7168,2048)}, C bf16, e4m3 with packed UE8M0 scales (A 1x128, B 128x128, power-of-two amax/448)",
     5: "M-grouped FP8xFP4 GEMM, contiguous, 8 groups from 32768 routed rows (multinomial, padded to 128), "
        "(N,K){(4096,7168),(7168,2048)}, e4m3 activations (UE8M0/128), E2M1 weights (UE8M0/32)",
 }
@@ -368,7 +378,7 @@ def main():
         return
 
     cfg = args.config
-    if cfg in (0, 1):
+    if cfg in (0, 1, 6):
         items = items_dense(cfg, args.shape)
     elif cfg == 2:
         items = items_contiguous()
@@ -417,13 +427,13 @@ def main():
     value = step_flops / (ms_per_step / 1e3) / 1e12
 
     # roofline of the dominant kernel
-    if cfg in (0, 1):
+    if cfg in (0, 1, 6):
         # launches of the largest-tile dense kernel (the one most of the step's time is in)
         kid = max(set(it["plan"]["kernel_id"] for it in items),
                   key=lambda k: sum(it["mean_ms"] for it in items if it["plan"]["kernel_id"] == k))
         dom = [it for it in items if it["plan"]["kernel_id"] == kid]
         bm, bn = dom[0]["plan"]["block_m"], dom[0]["plan"]["block_n"]
-        kname = f"fp8_gemm_kernel {bm}x{bn} tile, dense (kernel id {kid})"
+        kname = f"fp8_gemm_kernel {bm}x{bn} tile, dense{' UE8M0' if cfg == 6 else ''} (kernel id {kid})"
         bound = "mfma"
     elif cfg == 2:
         dom, kname, bound = items, "fp8_gemm_kernel, contiguous grouped", "mfma"

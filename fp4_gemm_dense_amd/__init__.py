@@ -32,6 +32,9 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "dg_fp8_gemm_nt_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "dg_m_grouped_fp8_gemm_nt_masked_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_fp4_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_fp4_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "dg_transform_fp4_weight_sf": (_I, [_P, _P, _I, _I, _I, _P]),
@@ -168,6 +171,59 @@ def dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked_m, d, expected_m=0):
     _check("dg_m_grouped_fp8_gemm_nt_masked",
            L.dg_m_grouped_fp8_gemm_nt_masked(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m), _ptr(d),
                                              G, max_m, N, K, int(expected_m), _stream(a)))
+    return d
+
+
+def _kw(K):
+    return (K // 128 + 3) // 4
+
+
+def dg_fp8_gemm_nt_ue8m0(a, sfa, b, sfb, c, d):
+    L = lib()
+    M, K = a.shape
+    N = b.shape[0]
+    _req(a, _U8, (M, K), "a")
+    _req(sfa, torch.int32, (M, _kw(K)), "sfa")
+    _req(b, _U8, (N, K), "b")
+    _req(sfb, torch.int32, (_nb(N), _kw(K)), "sfb")
+    if c is not None:
+        _req_bf16(c, (M, N), "c")
+    _req_bf16(d, (M, N), "d")
+    _check("dg_fp8_gemm_nt_ue8m0",
+           L.dg_fp8_gemm_nt_ue8m0(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c),
+                                  _ptr(d), M, N, K, _stream(a)))
+    return d
+
+
+def dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(a, sfa, b, sfb, m_indices, d):
+    L = lib()
+    M, K = a.shape
+    G, N = b.shape[0], b.shape[1]
+    _req(a, _U8, (M, K), "a")
+    _req(sfa, torch.int32, (M, _kw(K)), "sfa")
+    _req(b, _U8, (G, N, K), "b")
+    _req(sfb, torch.int32, (G, _nb(N), _kw(K)), "sfb")
+    _req(m_indices, torch.int32, (M,), "m_indices")
+    _req_bf16(d, (M, N), "d")
+    _check("dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
+           L.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(m_indices),
+                                                       _ptr(d), M, N, K, G, _stream(a)))
+    return d
+
+
+def dg_m_grouped_fp8_gemm_nt_masked_ue8m0(a, sfa, b, sfb, masked_m, d, expected_m=0):
+    L = lib()
+    G, max_m, K = a.shape
+    N = b.shape[1]
+    _req(a, _U8, (G, max_m, K), "a")
+    _req(sfa, torch.int32, (G, max_m, _kw(K)), "sfa")
+    _req(b, _U8, (G, N, K), "b")
+    _req(sfb, torch.int32, (G, _nb(N), _kw(K)), "sfb")
+    _req(masked_m, torch.int32, (G,), "masked_m")
+    _req_bf16(d, (G, max_m, N), "d")
+    _check("dg_m_grouped_fp8_gemm_nt_masked_ue8m0",
+           L.dg_m_grouped_fp8_gemm_nt_masked_ue8m0(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m),
+                                                   _ptr(d), G, max_m, N, K, int(expected_m), _stream(a)))
     return d
 
 

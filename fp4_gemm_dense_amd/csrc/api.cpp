@@ -108,7 +108,8 @@ static float* split_workspace(int dev, hipStream_t stream, size_t bytes, hipErro
   return static_cast<float*>(e.first);
 }
 
-static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream, const char* name) {
+static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream, const char* name,
+                        bool ue8m0 = false) {
   DeviceInfo di = current_device_info();
   if (!di.ok) return DG_ERR_NO_DEVICE;
   int cus = effective_cus(di);
@@ -167,7 +168,7 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
     std::fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %dx%d (kernel %d), %d tiles (%d whole, the rest "
                  "x %d K slices), %d workgroups\n", name, p.m, p.n, p.k, p.num_groups, plan.block_m, plan.block_n,
                  plan.kernel_id, plan.num_tiles, plan.full_tiles, plan.splits, plan.num_workgroups);
-  hipError_t e = launch_fp8_gemm(p, plan, mode, hs);
+  hipError_t e = launch_fp8_gemm(p, plan, mode | (ue8m0 ? MODE_UE8M0 : 0), hs);
   if (e == hipSuccess && plan.splits > 1) e = launch_splitk_reduce(p, plan, cus, hs);
   if (e == hipSuccess && p.device_split == 1) e = launch_masked_splitk_reduce(p, plan, masked_slots, hs);
   return e == hipSuccess ? DG_OK : DG_ERR_HIP;
@@ -177,10 +178,9 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
 
 using namespace dg;
 
-extern "C" {
-
-int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
+// The three forms; ue8m0 selects packed UE8M0 scale words instead of fp32 scales.
+static int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, const uint16_t* c,
+                       uint16_t* d, int m, int n, int k, void* stream, bool ue8m0) {
   try {
     if (!a || !sfa || !b || !sfb || !d) return DG_ERR_INVALID_ARG;
     if (m <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
@@ -191,15 +191,15 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
     Fp8GemmParams p{};
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = c; p.d = d;
     p.m = m; p.n = n; p.k = k; p.num_groups = 1;
-    return run_fp8_gemm(p, MODE_DENSE, 0, stream, "fp8_gemm_nt");
+    return run_fp8_gemm(p, MODE_DENSE, 0, stream, ue8m0 ? "fp8_gemm_nt_ue8m0" : "fp8_gemm_nt", ue8m0);
   } catch (...) {
     return DG_ERR_HIP;
   }
 }
 
-int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
-                                        const float* sfb, const int32_t* m_indices, uint16_t* d,
-                                        int m, int n, int k, int num_groups, void* stream) {
+static int contiguous_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb,
+                            const int32_t* m_indices, uint16_t* d, int m, int n, int k, int num_groups, void* stream,
+                            bool ue8m0) {
   try {
     if (!a || !sfa || !b || !sfb || !m_indices || !d) return DG_ERR_INVALID_ARG;
     if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERR_INVALID_ARG;
@@ -210,16 +210,16 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
     Fp8GemmParams p{};
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
     p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
-    return run_fp8_gemm(p, MODE_CONTIG, 0, stream, "m_grouped_fp8_gemm_nt_contiguous");
+    return run_fp8_gemm(p, MODE_CONTIG, 0, stream,
+                        ue8m0 ? "m_grouped_fp8_gemm_nt_contiguous_ue8m0" : "m_grouped_fp8_gemm_nt_contiguous", ue8m0);
   } catch (...) {
     return DG_ERR_HIP;
   }
 }
 
-int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
-                                    const float* sfb, const int32_t* masked_m, uint16_t* d,
-                                    int num_groups, int max_m, int n, int k, int expected_m,
-                                    void* stream) {
+static int masked_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb,
+                        const int32_t* masked_m, uint16_t* d, int num_groups, int max_m, int n, int k, int expected_m,
+                        void* stream, bool ue8m0) {
   try {
     if (!a || !sfa || !b || !sfb || !masked_m || !d) return DG_ERR_INVALID_ARG;
     if (num_groups <= 0 || max_m <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
@@ -233,10 +233,49 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
     Fp8GemmParams p{};
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
     p.m = max_m; p.n = n; p.k = k; p.num_groups = num_groups;
-    return run_fp8_gemm(p, MODE_MASKED, expected_m, stream, "m_grouped_fp8_gemm_nt_masked");
+    return run_fp8_gemm(p, MODE_MASKED, expected_m, stream,
+                        ue8m0 ? "m_grouped_fp8_gemm_nt_masked_ue8m0" : "m_grouped_fp8_gemm_nt_masked", ue8m0);
   } catch (...) {
     return DG_ERR_HIP;
   }
+}
+
+extern "C" {
+
+int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, false);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                        const float* sfb, const int32_t* m_indices, uint16_t* d,
+                                        int m, int n, int k, int num_groups, void* stream) {
+  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, false);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                    const float* sfb, const int32_t* masked_m, uint16_t* d,
+                                    int num_groups, int max_m, int n, int k, int expected_m,
+                                    void* stream) {
+  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, stream, false);
+}
+
+int dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b, const int32_t* sfb,
+                         const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, true);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
+                                              const int32_t* sfb, const int32_t* m_indices, uint16_t* d,
+                                              int m, int n, int k, int num_groups, void* stream) {
+  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, true);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
+                                          const int32_t* sfb, const int32_t* masked_m, uint16_t* d,
+                                          int num_groups, int max_m, int n, int k, int expected_m,
+                                          void* stream) {
+  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, stream, true);
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }

@@ -27,6 +27,13 @@ __device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b, c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_E4M3, FMT_E4M3, 0, 0, 0, 0);
 }
 
+// 16x16x128 e4m3 x e4m3 with hardware block scales: each lane supplies one
+// UE8M0 byte for its operand row's K chunk of A and one for B.
+__device__ __forceinline__ v4f mfma_scaled_e4m3_16x16x128(const v8i& a, int sa, const v8i& b, int sb,
+                                                          const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_E4M3, FMT_E4M3, 0, sa, 0, sb);
+}
+
 // 16x16x128 e4m3 (A) x e2m1 (B) with hardware block scales: each lane supplies
 // one UE8M0 byte for its 32-element K chunk of A and one for its chunk of B
 // (byte 0 of the given word).  B's 32 FP4 values occupy the low 4 dwords.

@@ -9,13 +9,16 @@
 namespace dg {
 
 enum GemmMode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
+// Flag or-ed into a mode: A and B scales are packed UE8M0 words (four K blocks
+// per int32) instead of fp32, applied by the scaled matrix instruction.
+constexpr int MODE_UE8M0 = 4;
 
 // Arguments of one FP8 block-scaled GEMM launch (dense or grouped).
 struct Fp8GemmParams {
   const uint8_t* a;
-  const float* sfa;
+  const void* sfa;            // fp32 scales, or packed UE8M0 words (MODE_UE8M0)
   const uint8_t* b;
-  const float* sfb;
+  const void* sfb;
   const uint16_t* c;          // dense only; may be null
   uint16_t* d;
   const int32_t* m_indices;   // contiguous only

@@ -36,8 +36,13 @@
 
 namespace dg {
 
-template <int MT, int NT, int WM, int WN, int STAGES, int MODE>
+// MODE_SF: the form (MODE_DENSE, MODE_CONTIG, MODE_MASKED), plus MODE_UE8M0 for
+// packed power-of-two scale factors, which the matrix instruction applies
+// itself (no fresh partials, no promotion on the vector ALUs).
+template <int MT, int NT, int WM, int WN, int STAGES, int MODE_SF>
 __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams p) {
+  constexpr int MODE = MODE_SF & 3;
+  constexpr bool UE = (MODE_SF & MODE_UE8M0) != 0;
   constexpr int NW = WM * WN;                 // waves per workgroup
   constexpr int BM = WM * MT * 16;
   constexpr int BN = WN * NT * 16;
@@ -87,6 +92,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   const int M = p.m, N = p.n, K = p.k;
   const int KB = K >> 7;
   const int NB = (N + 127) >> 7;
+  const int KW = (KB + 3) >> 2;   // packed UE8M0 words per row of scales (four K blocks each)
 
   // Per-lane LDS read offsets (slot 0); blocks mt / nt add mt*2048 / nt*2048
   // and the slot adds slot*STAGE.  The swizzle depends on row % 16 only.
@@ -190,29 +196,28 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // scalar offset, so the loop needs no 64-bit address arithmetic.
   v4i rsA, rsB, rsSA;
   cfloat* const SBc = (cfloat*)(uintptr_t)p.sfb;   // constant address space: scalar loads
+  typedef const __attribute__((address_space(4))) uint32_t cword;
+  cword* const SBw = (cword*)(uintptr_t)p.sfb;      // the same, packed UE8M0 words
   uint32_t a_off[RA], b_off[RB], sa_off = 0;
   int rot = 0, kb0_d = 0, nkb_d = 1;   // K range and rotation of the tile whose loads are issued
   int sb_idx = 0;
   auto setup = [&](const Tile& tile) {
     const uint8_t* A = p.a;
-    const float* SA = p.sfa;
+    // A scales: fp32 [groups][KB][M], or packed UE8M0 words [groups][M][KW]
+    const uint8_t* SA = static_cast<const uint8_t*>(p.sfa);
     const uint8_t* B = p.b;
-    const float* SB = p.sfb;
+    const uint32_t sa_bytes = UE ? (uint32_t)M * (uint32_t)KW * 4u : (uint32_t)KB * (uint32_t)M * 4u;
     if (MODE == MODE_MASKED) {
       A += (size_t)tile.g * M * K;
-      SA += (size_t)tile.g * KB * M;
+      SA += (size_t)tile.g * sa_bytes;
     }
-    if (MODE != MODE_DENSE) {
-      B += (size_t)tile.g * N * K;
-      SB += (size_t)tile.g * NB * KB;
-    }
+    if (MODE != MODE_DENSE) B += (size_t)tile.g * N * K;
     rot = tile.rot;
     kb0_d = tile.kb0;
     nkb_d = tile.nkb;
     rsA = make_buffer_rsrc(A, (uint32_t)M * (uint32_t)K);
     rsB = make_buffer_rsrc(B, (uint32_t)N * (uint32_t)K);
-    rsSA = make_buffer_rsrc(SA, (uint32_t)KB * (uint32_t)M * 4u);
-    (void)SB;
+    rsSA = make_buffer_rsrc(SA, sa_bytes);
     // Region r covers tile rows 8r..8r+7; lane l fills LDS bytes [16l, 16l+16)
     // of it: row 8r + l/8, position l%8, which holds chunk (l%8) ^ swz(row).
     // Rows past the valid ones (ragged edges, masked-off rows) take an
@@ -237,17 +242,19 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       const int q = wave * SPW + (lane < SPW ? lane : 0);
       const int g = q / (MT * 16), rem = q % (MT * 16);
       const int row = g * (MT * 16) + (rem % MT) * 16 + rem / MT;
-      sa_off = tile.m0 + row < tile.rows_valid ? (uint32_t)(tile.m0 + row) * 4 : kBufferOutOfRange;
+      sa_off = tile.m0 + row < tile.rows_valid ? (uint32_t)(tile.m0 + row) * (UE ? (uint32_t)KW * 4u : 4u)
+                                               : kBufferOutOfRange;
     }
     // B-scale element offsets from the kernel argument p.sfb, kept in SGPRs so the
     // per-K-block reads are scalar loads (which vmcnt does not count)
-    const int sb_group = MODE != MODE_DENSE ? tile.g * NB * KB : 0;
-    sb_idx = __builtin_amdgcn_readfirstlane(sb_group + (min(tile.n0 + wave_n * NT * 16, N - 1) >> 7) * KB);
+    const int sb_row = UE ? KW : KB;   // scale entries per 128-row block of B
+    const int sb_group = MODE != MODE_DENSE ? tile.g * NB * sb_row : 0;
+    sb_idx = __builtin_amdgcn_readfirstlane(sb_group + (min(tile.n0 + wave_n * NT * 16, N - 1) >> 7) * sb_row);
   };
   auto issue = [&](int kb, uint32_t slot_off) {
-    const int kp = kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d);   // K block in memory
+    const int kp = __builtin_amdgcn_readfirstlane(kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d));   // K block in memory
     const uint32_t kofs = (uint32_t)kp * 128u;
-    const uint32_t sofs = (uint32_t)kp * (uint32_t)M * 4u;
+    const uint32_t sofs = UE ? (uint32_t)(kp >> 2) * 4u : (uint32_t)kp * (uint32_t)M * 4u;
 #pragma unroll
     for (int j = 0; j < RA; ++j) buf16_to_lds(rsA, a_off[j], kofs, smem + slot_off + a_dst + j * 1024);
 #pragma unroll
@@ -258,7 +265,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // B regions), so that a K block's copies can be spread between its matrix
   // instructions; the row-scale copy (issue_sa) goes first.
   auto issue_ab = [&](int idx, int kb, uint32_t slot_off) {
-    const int kp = kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d);
+    const int kp = __builtin_amdgcn_readfirstlane(kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d));
     const uint32_t kofs = (uint32_t)kp * 128u;
 #pragma unroll
     for (int j = 0; j < RA; ++j)
@@ -268,8 +275,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       if (idx == RA + j) buf16_to_lds(rsB, b_off[j], kofs, smem + slot_off + b_dst + j * 1024);
   };
   auto issue_sa = [&](int kb, uint32_t slot_off) {
-    const int kp = kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d);
-    const uint32_t sofs = (uint32_t)kp * (uint32_t)M * 4u;
+    const int kp = __builtin_amdgcn_readfirstlane(kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d));
+    const uint32_t sofs = UE ? (uint32_t)(kp >> 2) * 4u : (uint32_t)kp * (uint32_t)M * 4u;
     if (SPW == 64 || lane < SPW) buf4_to_lds(rsSA, sa_off, sofs, smem + slot_off + sa_dst);
   };
   // DMA of half h of the C tile into the slot at slot_off (dense form, whole
@@ -370,19 +377,35 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
         }
       }
 
-      // B scale of this block (one per wave: its columns share a 128-wide block)
-      const float sbv = SBc[sb_idx + kb0 + (kb + rot < KT ? kb + rot : kb + rot - KT)];
+      // K block in memory; the B scale of this block is one per wave (its
+      // columns share a 128-wide block)
+      // (uniform: kept in an SGPR so that the scale load stays scalar and the
+      // copies' K offsets need no per-lane handling)
+      const int kp = __builtin_amdgcn_readfirstlane(kb0 + (kb + rot < KT ? kb + rot : kb + rot - KT));
       const uint8_t* ra_lo = smem + rd_slot + a_lo;
       const uint8_t* ra_hi = smem + rd_slot + a_hi;
       const uint8_t* rb_lo = smem + rd_slot + b_lo;
       const uint8_t* rb_hi = smem + rd_slot + b_hi;
       const uint8_t* rsa = smem + rd_slot + sa_rd;
-      float scur[MT];
+      float scur[MT];              // fp32 scales: sa * sb per row block
+      int sab[MT], sbb = 0;        // UE8M0: the exponent bytes of this K block
+      if constexpr (UE) {
+        const int sh = (kp & 3) * 8;
+        sbb = (int)((SBw[sb_idx + (kp >> 2)] >> sh) & 0xffu);
 #pragma unroll
-      for (int q = 0; q < MT / 4; ++q) {
-        const v4f sav = *reinterpret_cast<const v4f*>(rsa + 16 * q);
+        for (int q = 0; q < MT / 4; ++q) {
+          const v4i sav = *reinterpret_cast<const v4i*>(rsa + 16 * q);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) scur[4 * q + i] = sav[i] * sbv;
+          for (int i = 0; i < 4; ++i) sab[4 * q + i] = (int)(((uint32_t)sav[i] >> sh) & 0xffu);
+        }
+      } else {
+        const float sbv = SBc[sb_idx + kp];
+#pragma unroll
+        for (int q = 0; q < MT / 4; ++q) {
+          const v4f sav = *reinterpret_cast<const v4f*>(rsa + 16 * q);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) scur[4 * q + i] = sav[i] * sbv;
+        }
       }
       auto load_a = [&](int mt) -> v8i {
         const v4i lo = *reinterpret_cast<const v4i*>(ra_lo + mt * 2048);
@@ -410,27 +433,32 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int j = mt * NT + nt;
-          const int r = j % LAG;
-          if (j < LAG) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[MT - 1][j + NT - LAG][i] = fmaf(part[r][i], sprev, acc[MT - 1][j + NT - LAG][i]);
+          if constexpr (UE) {
+            // the matrix core applies both exponents and accumulates in place
+            acc[mt][nt] = mfma_scaled_e4m3_16x16x128(bf[nt], sbb, af[mt], sab[mt], acc[mt][nt]);
           } else {
-            const int pm = (j - LAG) / NT, pn = (j - LAG) % NT;
+            const int r = j % LAG;
+            if (j < LAG) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[pm][pn][i] = fmaf(part[r][i], scur[pm], acc[pm][pn][i]);
+              for (int i = 0; i < 4; ++i)
+                acc[MT - 1][j + NT - LAG][i] = fmaf(part[r][i], sprev, acc[MT - 1][j + NT - LAG][i]);
+            } else {
+              const int pm = (j - LAG) / NT, pn = (j - LAG) % NT;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[pm][pn][i] = fmaf(part[r][i], scur[pm], acc[pm][pn][i]);
+            }
+            part[r] = mfma_e4m3_16x16x128(bf[nt], af[mt], v4f{0.f, 0.f, 0.f, 0.f});
           }
-          part[r] = mfma_e4m3_16x16x128(bf[nt], af[mt], v4f{0.f, 0.f, 0.f, 0.f});
           const bool copy_here = STEADY && ILV_STEP * ILV <= NBLK && j % ILV_STEP == ILV_STEP - 1 && j / ILV_STEP < ILV;
           if (copy_here) issue_ab(j / ILV_STEP, kb + STAGES - 1, wr_slot);
           // keep the schedule: the promotion FMAs of block j ride with its matrix
           // instruction, and a copy follows every ILV_STEP-th one
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (promotion)
+          if constexpr (!UE) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (promotion)
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
           if (copy_here) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM read (copy)
         }
       }
-      sprev = scur[MT - 1];
+      if constexpr (!UE) sprev = scur[MT - 1];
       rd_slot = (rd_slot + STAGE == STAGES * STAGE) ? 0u : rd_slot + STAGE;
       wr_slot = (wr_slot + STAGE == STAGES * STAGE) ? 0u : wr_slot + STAGE;
     };
@@ -440,11 +468,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
 #pragma clang loop unroll(disable)
     for (; kb < KT; ++kb) kstep(kb, std::false_type{});
     // promote the last LAG partials (blocks NBLK - LAG .. NBLK - 1: row MT - 1)
+    if constexpr (!UE) {
 #pragma unroll
-    for (int j = 0; j < LAG; ++j)
+      for (int j = 0; j < LAG; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[MT - 1][NT - LAG + j][i] = fmaf(part[(NBLK - LAG + j) % LAG][i], sprev, acc[MT - 1][NT - LAG + j][i]);
+        for (int i = 0; i < 4; ++i)
+          acc[MT - 1][NT - LAG + j][i] = fmaf(part[(NBLK - LAG + j) % LAG][i], sprev, acc[MT - 1][NT - LAG + j][i]);
+    }
     const Tile done = cur;
 
     // Epilogue, part 1: D = acc (+ C) rounded to bf16, still in registers.  Lane
@@ -698,10 +728,14 @@ static hipError_t launch_mode(const Fp8GemmParams& p, int kernel_id, int grid, h
 
 hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mode, hipStream_t stream) {
   if (plan.num_workgroups <= 0) return hipSuccess;
+  const int g = plan.num_workgroups, id = plan.kernel_id;
   switch (mode) {
-    case MODE_DENSE: return launch_mode<MODE_DENSE>(p, plan.kernel_id, plan.num_workgroups, stream);
-    case MODE_CONTIG: return launch_mode<MODE_CONTIG>(p, plan.kernel_id, plan.num_workgroups, stream);
-    case MODE_MASKED: return launch_mode<MODE_MASKED>(p, plan.kernel_id, plan.num_workgroups, stream);
+    case MODE_DENSE: return launch_mode<MODE_DENSE>(p, id, g, stream);
+    case MODE_CONTIG: return launch_mode<MODE_CONTIG>(p, id, g, stream);
+    case MODE_MASKED: return launch_mode<MODE_MASKED>(p, id, g, stream);
+    case MODE_DENSE | MODE_UE8M0: return launch_mode<MODE_DENSE | MODE_UE8M0>(p, id, g, stream);
+    case MODE_CONTIG | MODE_UE8M0: return launch_mode<MODE_CONTIG | MODE_UE8M0>(p, id, g, stream);
+    case MODE_MASKED | MODE_UE8M0: return launch_mode<MODE_MASKED | MODE_UE8M0>(p, id, g, stream);
   }
   return hipErrorInvalidValue;
 }

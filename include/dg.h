@@ -125,6 +125,35 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
                                     void* stream);
 
 /*
+ * The same three GEMMs with packed UE8M0 scale factors instead of fp32 ones
+ * (usage guide "DeepGEMM：统一高性能张量核心 GEMM 计算库编译与使用指南", 五、使用方法 /
+ * 基础非分组 FP8 GEMM: the older architecture takes fp32 scale factors, the newer
+ * one power-of-two scale factors packed four to an int32).  The scale granularity is that of
+ * the fp32 forms (A per row per 128-wide K block, B per 128x128 block); a scale is
+ * 2^(e - 127) for the exponent byte e.  Byte i (from the least significant) of
+ * word j holds K block 4j + i.  The matrix instruction applies both exponents
+ * exactly, so D is the fp32 sum of exact products rounded once to bf16 (no
+ * separate promotion step).
+ *   dg_fp8_gemm_nt_ue8m0:               sfa [m, ceil(k/512)], sfb [ceil(n/128), ceil(k/512)], c optional
+ *   dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0:
+ *                                       sfa [m, ceil(k/512)], sfb [num_groups, ceil(n/128), ceil(k/512)]
+ *   dg_m_grouped_fp8_gemm_nt_masked_ue8m0:
+ *                                       sfa [num_groups, max_m, ceil(k/512)], sfb as contiguous
+ * All other arguments, requirements, row rules (padding rows, rows past masked_m
+ * not written) and errors are those of the fp32-scale form.  Exponent byte 255
+ * (NaN scale) gives NaN results.
+ */
+int dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b, const int32_t* sfb,
+                         const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
+                                              const int32_t* sfb, const int32_t* m_indices, uint16_t* d,
+                                              int m, int n, int k, int num_groups, void* stream);
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
+                                          const int32_t* sfb, const int32_t* masked_m, uint16_t* d,
+                                          int num_groups, int max_m, int n, int k, int expected_m,
+                                          void* stream);
+
+/*
  * Weight pre-transform for the FP8 x FP4 entry points (news page "DeepSeek 发布
  * DeepGEMM 重大更新：Mega MoE 融合算子与 FP4 精度支持": section FP4 精度支持, the
  * weight pre-transform tool, and section Mega MoE, whose expert weights are

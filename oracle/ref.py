@@ -136,6 +136,41 @@ def fp8_gemm_nt_entries(a, sfa, b, sfb, c, rows, cols) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# the same GEMMs with packed UE8M0 scale factors (usage guide, 五、使用方法 /
+# 基础非分组 FP8 GEMM: power-of-two scale factors packed four to an int32 on the
+# newer architecture).  Same granularity as above; scale = 2**(byte - 127).
+# ----------------------------------------------------------------------------
+
+def _row_scales_kb_major(sf_packed, KB) -> np.ndarray:
+    """packed words [..., R, W] -> float64 scales [..., KB, R] (K-block-major, as dequant_a takes them)."""
+    return np.swapaxes(unpack_ue8m0_int32(sf_packed)[..., :KB], -1, -2)
+
+
+def fp8_gemm_nt_ue8m0(a, sfa, b, sfb, c=None) -> np.ndarray:
+    """Dense form with sfa int32 [M, ceil(K/512)] and sfb int32 [ceil(N/128), ceil(K/512)]."""
+    KB = np.asarray(a).shape[1] // BLOCK_K
+    return fp8_gemm_nt(a, _row_scales_kb_major(sfa, KB), b, unpack_ue8m0_int32(sfb)[:, :KB], c)
+
+
+def fp8_gemm_nt_ue8m0_entries(a, sfa, b, sfb, c, rows, cols) -> np.ndarray:
+    """Selected entries of the dense form with packed UE8M0 scales (see fp8_gemm_nt_entries)."""
+    KB = np.asarray(a).shape[1] // BLOCK_K
+    return fp8_gemm_nt_entries(a, _row_scales_kb_major(sfa, KB), b, unpack_ue8m0_int32(sfb)[:, :KB], c, rows, cols)
+
+
+def m_grouped_contiguous_ue8m0(a, sfa, b, sfb, m_indices):
+    """Contiguous form: sfa [M, ceil(K/512)], sfb [G, ceil(N/128), ceil(K/512)]."""
+    KB = np.asarray(a).shape[1] // BLOCK_K
+    return m_grouped_contiguous(a, _row_scales_kb_major(sfa, KB), b, unpack_ue8m0_int32(sfb)[..., :KB], m_indices)
+
+
+def m_grouped_masked_ue8m0(a, sfa, b, sfb, masked_m):
+    """Masked form: sfa [G, max_m, ceil(K/512)], sfb [G, ceil(N/128), ceil(K/512)]."""
+    KB = np.asarray(a).shape[2] // BLOCK_K
+    return m_grouped_masked(a, _row_scales_kb_major(sfa, KB), b, unpack_ue8m0_int32(sfb)[..., :KB], masked_m)
+
+
+# ----------------------------------------------------------------------------
 # FP8 x FP4 expert FFN (linear1 -> SwiGLU -> requant -> linear2 -> weighted sum)
 # ----------------------------------------------------------------------------
 

@@ -154,6 +154,26 @@ def quant_rows_pow2_1x128(x: torch.Tensor):
     return q, pack_ue8m0(e)
 
 
+def _pack_exponent_rows(e: torch.Tensor) -> torch.Tensor:
+    """int exponents [..., S] -> packed UE8M0 int32 [..., ceil(S/4)] (zero exponents pad the last word)."""
+    pad = (-e.shape[-1]) % 4
+    if pad:
+        e = torch.cat([e, torch.zeros(*e.shape[:-1], pad, dtype=e.dtype, device=e.device)], dim=-1)
+    return pack_ue8m0(e)
+
+
+def quant_blocks_pow2_128x128(w: torch.Tensor):
+    """[N, K] float32 -> (e4m3 codes [N, K], packed UE8M0 int32 [ceil(N/128), ceil(K/512)]);
+    one power-of-two scale 2**ceil(log2(amax/448)) per 128x128 block (amax over the valid rows)."""
+    N, K = w.shape
+    nb = (N + 127) // 128
+    wp = torch.zeros(nb * 128, K, dtype=w.dtype, device=w.device)
+    wp[:N] = w
+    e = _pow2_exponent(wp.view(nb, 128, K // 128, 128).abs().amax(dim=(1, 3)), 448.0)   # [nb, K/128]
+    e_full = e.repeat_interleave(128, 0)[:N].repeat_interleave(128, 1)
+    return e4m3_codes(w * torch.exp2(-e_full.float())), _pack_exponent_rows(e)
+
+
 _E2M1_MAGS = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
@@ -267,6 +287,51 @@ def gen_masked(G, max_m, N, K, seed, masked_m=None, backend="numpy", device="cpu
     for g, mg in enumerate(masked_m):
         a[g, mg:] = E4M3_NAN
         sfa[g, :, mg:] = float("nan")
+    return dict(a=a, sfa=sfa, b=torch.stack(bs), sfb=torch.stack(sbs),
+                masked_m=torch.tensor(masked_m, dtype=torch.int32, device=device),
+                G=G, max_m=max_m, N=N, K=K)
+
+
+def gen_dense_ue8m0(M, N, K, seed, with_c=True, backend="numpy", device="cpu"):
+    """Dense NT GEMM inputs with packed UE8M0 scales: A per 1x128 (power-of-two scale),
+    B per 128x128 block, C bf16."""
+    d = _Draw(seed, backend, device)
+    a, sfa = quant_rows_pow2_1x128(d.normal(M, K))
+    b, sfb = quant_blocks_pow2_128x128(d.normal(N, K))
+    c = bf16_bits(d.normal(M, N)) if with_c else None
+    return dict(a=a, sfa=sfa, b=b, sfb=sfb, c=c, M=M, N=N, K=K)
+
+
+def gen_contiguous_ue8m0(G, total_rows, N, K, seed, align=128, counts=None, backend="numpy", device="cpu"):
+    """Contiguous-layout grouped inputs with packed UE8M0 scales; padding rows hold NaN codes and
+    exponent bytes 0xFF."""
+    d = _Draw(seed, backend, device)
+    if counts is None:
+        counts = d.multinomial_counts(total_rows, G)
+    m_idx, _ = padded_group_layout(counts, align)
+    M = len(m_idx)
+    m_indices = torch.tensor(m_idx, dtype=torch.int32, device=device)
+    a, sfa = quant_rows_pow2_1x128(d.normal(M, K))
+    pad_rows = m_indices < 0
+    a[pad_rows] = E4M3_NAN
+    sfa[pad_rows] = -1
+    bs, sbs = zip(*[quant_blocks_pow2_128x128(d.normal(N, K)) for _ in range(G)])
+    return dict(a=a, sfa=sfa, b=torch.stack(bs), sfb=torch.stack(sbs), m_indices=m_indices,
+                counts=counts, M=M, N=N, K=K, G=G)
+
+
+def gen_masked_ue8m0(G, max_m, N, K, seed, masked_m=None, backend="numpy", device="cpu"):
+    """Masked-layout grouped inputs with packed UE8M0 scales; rows past masked_m are garbage."""
+    d = _Draw(seed, backend, device)
+    as_, sas = zip(*[quant_rows_pow2_1x128(d.normal(max_m, K)) for _ in range(G)])
+    a = torch.stack(as_)
+    sfa = torch.stack(sas)                                          # [G, max_m, ceil(K/512)]
+    bs, sbs = zip(*[quant_blocks_pow2_128x128(d.normal(N, K)) for _ in range(G)])
+    if masked_m is None:
+        masked_m = d.integers(0, max_m, G)
+    for g, mg in enumerate(masked_m):
+        a[g, max(mg, 0):] = E4M3_NAN
+        sfa[g, max(mg, 0):] = -1
     return dict(a=a, sfa=sfa, b=torch.stack(bs), sfb=torch.stack(sbs),
                 masked_m=torch.tensor(masked_m, dtype=torch.int32, device=device),
                 G=G, max_m=max_m, N=N, K=K)

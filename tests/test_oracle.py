@@ -602,6 +602,97 @@ def test_fp4_weight_sf_k_major_fixture_and_labelled_words():
                 assert (w >> 20, (w >> 8) & 0xFFF, w & 0xFF) == (g, r, kb)
 
 
+# ----------------------------------------------------------------------------
+# packed UE8M0 scale factors
+# ----------------------------------------------------------------------------
+
+def _torch_e4m3(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _pack_bytes(e):
+    """exponent bytes [..., S] -> int32 words [..., ceil(S/4)], written out byte by byte."""
+    e = np.asarray(e, np.int64)
+    S = e.shape[-1]
+    W = (S + 3) // 4
+    out = np.zeros(e.shape[:-1] + (W,), np.int64)
+    for j in range(S):
+        out[..., j // 4] |= e[..., j] << (8 * (j % 4))
+    return out.astype(np.uint32).view(np.int32)
+
+
+def test_ue8m0_dense_exact_rational_brute_force():
+    """Random codes and per-(row, K block) / per-(128-row block, K block) exponents,
+    K = 640 (five K blocks: the second word is partly padding), N = 130 (two B blocks);
+    sampled entries against exact rationals with decoding done here independently."""
+    rng = np.random.default_rng(11)
+    M, N, K = 3, 130, 640
+    KB = K // 128
+    a = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    b = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x38                 # no NaN codes
+    b[(b & 0x7F) == 0x7F] = 0x40
+    ea = rng.integers(118, 136, (M, KB))
+    eb = rng.integers(118, 136, ((N + 127) // 128, KB))
+    c = synth.to_numpy(synth.bf16_bits(torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32))))
+    got = R.fp8_gemm_nt_ue8m0(a, _pack_bytes(ea), b, _pack_bytes(eb), c)
+    av, bv = _torch_e4m3(a), _torch_e4m3(b)
+    cv = torch.from_numpy(c.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for m, n in [(0, 0), (1, 127), (2, 128), (0, 129), (1, 64), (2, 5)]:
+        want = Fraction(float(cv[m, n]))
+        for k in range(K):
+            kb = k // 128
+            want += (Fraction(float(av[m, k])) * Fraction(float(bv[n, k])) *
+                     Fraction(2) ** int(ea[m, kb] - 127) * Fraction(2) ** int(eb[n // 128, kb] - 127))
+        assert abs(got[m, n] - float(want)) <= 1e-13 * max(1.0, abs(float(want)))
+
+
+def test_ue8m0_byte_order_and_block_indexing_closed_form():
+    """All-ones operands, A exponents 127 + i + r (K block i, row r), B exponents
+    127 + 3 - i (+1 for the second 128-row block): D[r, n] = 128 * 4 * 2**(3 + r) (doubled
+    for n >= 128).  Reversed byte order, a transposed exponent table or a wrong B
+    block gives a different value."""
+    M, N, K = 3, 256, 512
+    a = np.full((M, K), 0x38, np.uint8)          # 1.0
+    b = np.full((N, K), 0x38, np.uint8)
+    ea = np.array([[127 + i + r for i in range(4)] for r in range(M)])
+    eb = np.array([[127 + 3 - i + blk for i in range(4)] for blk in range(2)])
+    got = R.fp8_gemm_nt_ue8m0(a, _pack_bytes(ea), b, _pack_bytes(eb))
+    for r in range(M):
+        assert np.all(got[r, :128] == 128 * 4 * 2.0 ** (3 + r))
+        assert np.all(got[r, 128:] == 2 * 128 * 4 * 2.0 ** (3 + r))
+
+
+def test_ue8m0_grouped_forms_agree_with_dense():
+    """Contiguous (padding rows skipped) and masked forms equal the dense form on each
+    group's rows."""
+    g = synth.gen_contiguous_ue8m0(3, 300, 48, 384, seed=5, counts=[100, 0, 200])
+    a, sfa, b, sfb, mi = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "m_indices"))
+    ref, written = R.m_grouped_contiguous_ue8m0(a, sfa, b, sfb, mi)
+    assert written.sum() == 300 and np.all(mi[written] >= 0)
+    for grp in (0, 2):
+        rows = np.nonzero(mi == grp)[0]
+        assert np.array_equal(ref[rows], R.fp8_gemm_nt_ue8m0(a[rows], sfa[rows], b[grp], sfb[grp]))
+    mm = [7, 0, 64]
+    gm = synth.gen_masked_ue8m0(3, 64, 48, 384, seed=6, masked_m=mm)
+    a, sfa, b, sfb = (synth.to_numpy(gm[k]) for k in ("a", "sfa", "b", "sfb"))
+    ref, written = R.m_grouped_masked_ue8m0(a, sfa, b, sfb, mm)
+    assert written.sum() == 71
+    for grp in (0, 2):
+        assert np.array_equal(ref[grp, :mm[grp]],
+                              R.fp8_gemm_nt_ue8m0(a[grp, :mm[grp]], sfa[grp, :mm[grp]], b[grp], sfb[grp]))
+
+
+def test_ue8m0_generator_scales_are_powers_of_two_within_range():
+    """The generator's block exponents put every block's amax in (224, 448] (a check of
+    the input recipe, not of the oracle)."""
+    g = synth.gen_dense_ue8m0(5, 200, 640, seed=3, with_c=False)
+    a, sfa, b = synth.to_numpy(g["a"]), synth.to_numpy(g["sfa"]), synth.to_numpy(g["b"])
+    av = np.abs(_torch_e4m3(a)).reshape(5, 5, 128).max(axis=-1)
+    assert np.all(av <= 448) and np.all(av > 200)
+    assert synth.to_numpy(g["sfb"]).shape == (2, 2)
+
+
 def test_planted_mistakes_fail_dense_pins():
     assert _pins_dense(R.fp8_gemm_nt)
 
