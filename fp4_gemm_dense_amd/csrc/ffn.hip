@@ -12,19 +12,26 @@
 // gfx950 design (four kernels on one stream, no host synchronisation):
 //   1. route   (one workgroup): per-expert pair counts, starts, and a pair list
 //              (token of each pair; pair index of each (token, slot)).
-//   2. linear1 (persistent): for each (expert, 64-row block of its pairs,
-//              128 intermediate columns) the gathered e4m3 token rows times the
-//              matching 128 gate rows and 128 up rows of W1 with
+//   2. linear1 (persistent, 8 waves): for each (expert, 128-row block of its
+//              pairs, 128 intermediate columns) the gathered e4m3 token rows times
+//              the matching 128 gate rows and 128 up rows of W1 with
 //              v_mfma_scale_f32_16x16x128_f8f6f4 (A e4m3, B e2m1; both UE8M0
 //              scales applied by the matrix core per 32-element K chunk), then in
 //              registers: s = silu(gate) * up, per-row 128-column amax across the
-//              four waves (LDS), power-of-two scale, e4m3 round-to-nearest-even;
-//              writes the e4m3 intermediate and its UE8M0 exponents.
-//   3. linear2 (persistent): (expert, 64-row block, 256 output columns) of the
+//              two waves sharing the row (LDS), power-of-two scale, e4m3
+//              round-to-nearest-even; writes the e4m3 intermediate and its UE8M0
+//              exponents.
+//   3. linear2 (persistent): (expert, 128-row block, 256 output columns) of the
 //              intermediate times W2 with the same scaled MFMA; writes fp32 per pair.
 //   4. combine: y[t] = sum over slots j (in order) of w[t,j] * o[pair(t,j)], bf16.
-// Operand tiles and their scale words are staged through a 3-stage LDS ring with
-// global_load_lds (the token gather happens in the DMA addresses).
+// Activations and weight-scale words are staged per 128-wide K block through a
+// 4-slot LDS ring, the weights per pair of K blocks through a 2-slot ring, and
+// the activation-scale words (four K blocks each) through a ring of their own,
+// all with LDS-DMA loads (the token gather happens in the DMA addresses).  The
+// weight-scale words are K-block-major (written once by the weight
+// pre-transform).  Each K block's operand fragments are read into registers
+// during the previous block.  The same GEMM kernel also serves the exported
+// M-grouped FP8 x FP4 GEMM (contiguous and masked forms, bf16 out).
 #include <type_traits>
 
 #include "../../include/dg.h"
