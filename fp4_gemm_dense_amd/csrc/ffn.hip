@@ -233,7 +233,8 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
   const int K = GEMM ? p.gk : (MODE == 1 ? H : I);
   const int KB = K >> 7;
   const int NOUT = GEMM ? p.gn : H;                 // output row length (modes 2-4)
-  const int tiles_n = MODE == 1 ? I / 128 : NOUT / FFN_BN;   // H % 512 == 0, N % 256 == 0
+  // H % 512 == 0; the GEMM forms allow N % 16 == 0 (a last, partial column tile)
+  const int tiles_n = MODE == 1 ? I / 128 : (NOUT + FFN_BN - 1) / FFN_BN;
   const int tiles_m4 = (p.gm + FFN_BM - 1) / FFN_BM;        // contiguous form: 128-row blocks
   // rows of row list e (expert pairs, or a masked group's valid rows) and where they start
   auto list_cnt = [&](int e) -> int {
@@ -343,7 +344,7 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
       const int r = (wave * RB + j) * 8 + (lane >> 3);             // tile weight row
       const uint32_t wr = MODE == 1 ? (uint32_t)((r < 128 ? 0 : I) + tn * 128 + (r & 127))
                                     : (uint32_t)(tn * FFN_BN + r);
-      b_off[j] = wr * wrow_bytes + (((lane & 7) ^ swz(r)) << 4);
+      b_off[j] = wr < e_rows ? wr * wrow_bytes + (((lane & 7) ^ swz(r)) << 4) : kBufferOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {                 // scale-word quarter j: rows j*BM/4 + wave*SAQ + lane
@@ -355,7 +356,7 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
       const int r = wave * SBW + (lane < SBW ? lane : 0);
       const uint32_t wr = MODE == 1 ? (uint32_t)((r < 128 ? 0 : I) + tn * 128 + (r & 127))
                                     : (uint32_t)(tn * FFN_BN + r);
-      sb_off = wr * 4u;
+      sb_off = wr < e_rows ? wr * 4u : kBufferOutOfRange;   // rows past N: a partial last tile
     }
     const int NPAIR = (KB + 1) >> 1;
     // activation-scale quarter j of K-block group q into its slot (q beyond the K range: read nothing)
@@ -541,6 +542,7 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
         uint16_t* drow = p.d + (size_t)(row0 + r) * NOUT + tn * FFN_BN + wave_n * 128 + 4 * lgrp;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
+          if (tn * FFN_BN + wave_n * 128 + nt * 16 >= NOUT) break;   // columns past N (N % 16 == 0)
           const v4f v = acc[mt][nt];
           *reinterpret_cast<uint2*>(drow + nt * 16) = uint2{pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])};
         }
@@ -683,7 +685,7 @@ static int gemm4_check(const uint8_t* a, const int32_t* a_sf, const uint8_t* b, 
                        const int32_t* meta, uint16_t* d, long long rows, int n, int k, int groups) {
   if (!a || !a_sf || !b || !b_sf || !meta || !d) return DG_ERR_INVALID_ARG;
   if (rows <= 0 || n <= 0 || k <= 0 || groups <= 0) return DG_ERR_INVALID_ARG;
-  if (k % 128 != 0 || n % 256 != 0) return DG_ERR_UNSUPPORTED;
+  if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
   const long long lim = 1LL << 31;
   if (rows * k > lim || (long long)n * (k / 2) > lim || rows * 4LL * ((k / 128 + 3) / 4) > lim ||
       (long long)n * (k / 128) * 4 > lim)

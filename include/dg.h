@@ -229,7 +229,7 @@ int dg_fp8_fp4_expert_ffn(const uint8_t* x, const int32_t* x_sf, const int32_t* 
  *   b_sf   [num_groups, k/128, n] int32, four UE8M0 exponents per word (1x32 blocks),
  *          K-block-major as dg_transform_fp4_weight_sf writes it
  *   d      bf16 rows of n, 16-byte aligned
- * Requirements: n % 256 == 0; k % 128 == 0; (rows of A) * k, n * k / 2 and
+ * Requirements: n % 16 == 0; k % 128 == 0; (rows of A) * k, n * k / 2 and
  *   (rows of A) * 4 * ceil(k/512) at most 2^31 (else DG_ERR_UNSUPPORTED).
  *
  * Contiguous: a [m, k], a_sf [m, ceil(k/512)], m_indices [m] (group of each row,

@@ -79,7 +79,8 @@ def test_fp8_fp4_grouped_argument_validation():
     assert f(A16, A16, A16, A16, A16, A16, 256, 256, 128, 0, None) == 1         # no groups
     assert f(A16 + 8, A16, A16, A16, A16, A16, 256, 256, 128, 4, None) == 1     # misaligned a
     assert f(A16, A16 + 2, A16, A16, A16, A16, 256, 256, 128, 4, None) == 1     # misaligned a_sf
-    assert f(A16, A16, A16, A16, A16, A16, 256, 272, 128, 4, None) == 2         # N % 256
+    assert f(A16, A16, A16, A16, A16, A16, 256, 264, 128, 4, None) == 2         # N % 16
+    assert f(A16, A16, A16, A16, A16, A16, 256, 272, 128, 4, None) in (0, 4)    # partial column tile: valid
     assert f(A16, A16, A16, A16, A16, A16, 256, 256, 200, 4, None) == 2         # K % 128
     assert f(A16, A16, A16, A16, A16, A16, 1 << 21, 256, 1152, 4, None) == 2    # A above 2 GiB
     assert f(A16, A16, A16, A16, A16, A16, 256, 256, 128, 4, None) in (0, 4)    # valid: device check

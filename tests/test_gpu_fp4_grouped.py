@@ -58,6 +58,8 @@ def _check(d, ref, written, what):
     ([1, 127, 128], 512, 384),        # 3 K blocks: the last weight pair is half used
     ([130], 256, 128),                # one K block
     ([0, 0, 5], 768, 1024),
+    ([100, 0, 129, 300], 400, 512),   # N % 256 != 0: a partial last column tile
+    ([5, 60], 16, 256),               # N smaller than one column tile
 ])
 def test_fp4_contiguous_parity_and_padding(dg, counts, N, K):
     g = synth.gen_fp4_contiguous(len(counts), sum(counts), N, K, seed=sum(counts) + N + K, counts=counts)
@@ -71,6 +73,7 @@ def test_fp4_contiguous_parity_and_padding(dg, counts, N, K):
     ([0, 1, 127, 128, 129, 256], 256, 256, 640),
     ([300, -5, 40], 128, 512, 256),   # counts outside [0, max_m] are clamped
     ([3], 200, 256, 896),
+    ([0, 129, 7], 160, 272, 640),     # partial last column tile
 ])
 def test_fp4_masked_parity_and_clamping(dg, mm, max_m, N, K):
     clamped = [min(max(m, 0), max_m) for m in mm]
