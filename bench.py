@@ -20,6 +20,7 @@ Other workloads:
               (UE8M0 per 1x32) and UE8M0 activation scales per 1x128
   --config 6  the config-1 dense sweep with packed UE8M0 scales (power-of-two,
               A per 1x128, B per 128x128), applied by the scaled matrix instruction
+  --config 7  config 2 in the NN layout (each group's B stored [K, N])
 
 Caches: one dense-sweep step touches more than 1 GB of distinct inputs and
 outputs, so no shape's operands survive in the 4 MB L2s or the 256 MB
@@ -59,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--shape", type=str, default=None,
@@ -118,13 +119,15 @@ def items_dense(config, only=None):
     return items
 
 
-def items_contiguous():
+def items_contiguous(nn=False):
     import torch
     import synth
     import fp4_gemm_dense_amd as dg
     items = []
+    gen = synth.gen_contiguous_nn if nn else synth.gen_contiguous
+    gemm = dg.dg_m_grouped_fp8_gemm_nn_contiguous if nn else dg.dg_m_grouped_fp8_gemm_nt_contiguous
     for j, (N, K) in enumerate(synth.GROUPED_NK):
-        g = synth.gen_contiguous(8, 32768, N, K, synth.seed_for(2, j), backend="torch", device="cuda")
+        g = gen(8, 32768, N, K, synth.seed_for(7 if nn else 2, j), backend="torch", device="cuda")
         M = g["M"]
         d = torch.empty(M, N, dtype=torch.int16, device="cuda")
         valid = sum(g["counts"])
@@ -132,8 +135,9 @@ def items_contiguous():
         nbytes = valid * K + groups_hit * (N * K + 4 * nb(N) * (K // 128)) + 4 * (K // 128) * valid + 4 * M + 2 * valid * N
 
         def run(g=g, d=d):
-            dg.dg_m_grouped_fp8_gemm_nt_contiguous(g["a"], g["sfa"], g["b"], g["sfb"], g["m_indices"], d)
-        items.append(dict(run=run, g=g, flops=2.0 * valid * N * K, bytes=nbytes, label=f"G8_contig_N{N}_K{K}",
+            gemm(g["a"], g["sfa"], g["b"], g["sfb"], g["m_indices"], d)
+        items.append(dict(run=run, g=g, flops=2.0 * valid * N * K, bytes=nbytes,
+                          label=f"G8_contig{'_nn' if nn else ''}_N{N}_K{K}",
                           shape=(M, N, K)))
     return items
 
@@ -292,13 +296,13 @@ def _cpu_pass(config, items, budget_s, t_start, npass, t_total, flops, desc):
                 flops += 2.0 * len(rows) * N * K
             if npass == 0:
                 desc.append(f"up to 16 valid rows per group of {it['label']}")
-        elif config in (2, 3):
+        elif config in (2, 3, 7):
             M, N, K = it["shape"]
-            G = 8 if config == 2 else 32
+            G = 32 if config == 3 else 8
             for grp in range(G):
                 if time.perf_counter() - t_start > budget_s:
                     break
-                if config == 2:
+                if config != 3:
                     rows = np.nonzero(synth.to_numpy(g["m_indices"]) == grp)[0]
                     rows = rows[16 * npass:16 * npass + 16]
                     a, sfa = synth.to_numpy(g["a"][rows]), synth.to_numpy(g["sfa"][:, rows])
@@ -311,7 +315,7 @@ def _cpu_pass(config, items, budget_s, t_start, npass, t_total, flops, desc):
                     continue
                 b, sfb = synth.to_numpy(g["b"][grp]), synth.to_numpy(g["sfb"][grp])
                 t0 = time.perf_counter()
-                R.fp8_gemm_nt(a, sfa, b, sfb)
+                (R.fp8_gemm_nn if config == 7 else R.fp8_gemm_nt)(a, sfa, b, sfb)
                 t_total += time.perf_counter() - t0
                 flops += 2.0 * len(rows) * N * K
             if npass == 0:
@@ -347,6 +351,8 @@ WORKLOADS = {
        "e4m3 1x128 / 128x128 fp32 scales",
     4: "FP8xFP4 expert FFN, 4096 tokens, hidden 7168, intermediate 2048, 32 local experts of 256, top-8, "
        "e4m3 activations (UE8M0/128), E2M1 weights (UE8M0/32)",
+    7: "M-grouped contiguous GEMM in the NN layout (B stored [K,N]), 8 groups from 32768 routed rows "
+       "(multinomial, padded to 128), (N,K){(4096,7168),(7168,2048)}, e4m3 1x128 / 128x128 fp32 scales",
     6: "dense NT GEMM sweep, M{64,4096} x (N,K){(2112,7168),(24576,1536),(32768,512),(7168,16384),(4096,7168),"
        "(7168,2048)}, C bf16, e4m3 with packed UE8M0 scales (A 1x128, B 128x128, power-of-two amax/448)",
     5: "M-grouped FP8xFP4 GEMM, contiguous, 8 groups from 32768 routed rows (multinomial, padded to 128), "
@@ -380,8 +386,8 @@ def main():
     cfg = args.config
     if cfg in (0, 1, 6):
         items = items_dense(cfg, args.shape)
-    elif cfg == 2:
-        items = items_contiguous()
+    elif cfg in (2, 7):
+        items = items_contiguous(nn=cfg == 7)
     elif cfg == 3:
         items = items_masked()
     elif cfg == 5:
@@ -435,8 +441,8 @@ def main():
         bm, bn = dom[0]["plan"]["block_m"], dom[0]["plan"]["block_n"]
         kname = f"fp8_gemm_kernel {bm}x{bn} tile, dense{' UE8M0' if cfg == 6 else ''} (kernel id {kid})"
         bound = "mfma"
-    elif cfg == 2:
-        dom, kname, bound = items, "fp8_gemm_kernel, contiguous grouped", "mfma"
+    elif cfg in (2, 7):
+        dom, kname, bound = items, f"fp8_gemm_kernel, contiguous grouped{', NN layout' if cfg == 7 else ''}", "mfma"
     elif cfg == 3:
         dom, kname, bound = items, "fp8_gemm_kernel, masked grouped", "hbm"
     elif cfg == 5:

@@ -32,6 +32,8 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "dg_fp8_gemm_nn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "dg_m_grouped_fp8_gemm_nn_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_fp8_gemm_nt_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_masked_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -171,6 +173,40 @@ def dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked_m, d, expected_m=0):
     _check("dg_m_grouped_fp8_gemm_nt_masked",
            L.dg_m_grouped_fp8_gemm_nt_masked(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m), _ptr(d),
                                              G, max_m, N, K, int(expected_m), _stream(a)))
+    return d
+
+
+def dg_fp8_gemm_nn(a, sfa, b, sfb, c, d):
+    """d = c + a . b with b stored [K, N] (NN layout)."""
+    L = lib()
+    M, K = a.shape
+    N = b.shape[1]
+    _req(a, _U8, (M, K), "a")
+    _req(b, _U8, (K, N), "b")
+    _req(sfa, torch.float32, (K // 128, M), "sfa")
+    _req(sfb, torch.float32, (_nb(N), K // 128), "sfb")
+    if c is not None:
+        _req_bf16(c, (M, N), "c")
+    _req_bf16(d, (M, N), "d")
+    _check("dg_fp8_gemm_nn", L.dg_fp8_gemm_nn(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c), _ptr(d),
+                                              M, N, K, _stream(a)))
+    return d
+
+
+def dg_m_grouped_fp8_gemm_nn_contiguous(a, sfa, b, sfb, m_indices, d):
+    """Contiguous grouped form with each group's b stored [K, N]."""
+    L = lib()
+    M, K = a.shape
+    G, N = b.shape[0], b.shape[2]
+    _req(a, _U8, (M, K), "a")
+    _req(sfa, torch.float32, (K // 128, M), "sfa")
+    _req(b, _U8, (G, K, N), "b")
+    _req(sfb, torch.float32, (G, _nb(N), K // 128), "sfb")
+    _req(m_indices, torch.int32, (M,), "m_indices")
+    _req_bf16(d, (M, N), "d")
+    _check("dg_m_grouped_fp8_gemm_nn_contiguous",
+           L.dg_m_grouped_fp8_gemm_nn_contiguous(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(m_indices), _ptr(d),
+                                                 M, N, K, G, _stream(a)))
     return d
 
 

@@ -108,18 +108,21 @@ static float* split_workspace(int dev, hipStream_t stream, size_t bytes, hipErro
   return static_cast<float*>(e.first);
 }
 
+// flags: MODE_UE8M0 and / or MODE_NN, or-ed into the form's mode at launch
 static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream, const char* name,
-                        bool ue8m0 = false) {
+                        int flags = 0) {
   DeviceInfo di = current_device_info();
   if (!di.ok) return DG_ERR_NO_DEVICE;
   int cus = effective_cus(di);
-  GemmPlan plan = plan_fp8_gemm(p.m, p.n, p.k, p.num_groups, mode, cus, expected_m);
+  const int required_bn = 0;   // every compiled tile width suits both layouts
+  GemmPlan plan = plan_fp8_gemm(p.m, p.n, p.k, p.num_groups, mode, cus, expected_m, required_bn);
   if (plan.kernel_id < 0) return DG_ERR_UNSUPPORTED;
   // DG_FORCE_KERNEL=<id>: override the heuristic's tile choice (for tuning)
   if (const char* fk = std::getenv("DG_FORCE_KERNEL")) {
     int id = std::atoi(fk);
     if (id >= 0 && id < num_tile_configs() &&
-        !(mode == MODE_CONTIG && (128 % tile_config(id).block_m) != 0))
+        !(mode == MODE_CONTIG && (128 % tile_config(id).block_m) != 0) &&
+        !(required_bn > 0 && tile_config(id).block_n != required_bn))
       plan = plan_with_kernel(p.m, p.n, p.k, p.num_groups, mode, cus, id);
   }
   p.tiles_m = plan.tiles_m;
@@ -168,7 +171,7 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
     std::fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %dx%d (kernel %d), %d tiles (%d whole, the rest "
                  "x %d K slices), %d workgroups\n", name, p.m, p.n, p.k, p.num_groups, plan.block_m, plan.block_n,
                  plan.kernel_id, plan.num_tiles, plan.full_tiles, plan.splits, plan.num_workgroups);
-  hipError_t e = launch_fp8_gemm(p, plan, mode | (ue8m0 ? MODE_UE8M0 : 0), hs);
+  hipError_t e = launch_fp8_gemm(p, plan, mode | flags, hs);
   if (e == hipSuccess && plan.splits > 1) e = launch_splitk_reduce(p, plan, cus, hs);
   if (e == hipSuccess && p.device_split == 1) e = launch_masked_splitk_reduce(p, plan, masked_slots, hs);
   return e == hipSuccess ? DG_OK : DG_ERR_HIP;
@@ -180,7 +183,7 @@ using namespace dg;
 
 // The three forms; ue8m0 selects packed UE8M0 scale words instead of fp32 scales.
 static int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, const uint16_t* c,
-                       uint16_t* d, int m, int n, int k, void* stream, bool ue8m0) {
+                       uint16_t* d, int m, int n, int k, void* stream, int flags) {
   try {
     if (!a || !sfa || !b || !sfb || !d) return DG_ERR_INVALID_ARG;
     if (m <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
@@ -191,7 +194,8 @@ static int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, cons
     Fp8GemmParams p{};
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = c; p.d = d;
     p.m = m; p.n = n; p.k = k; p.num_groups = 1;
-    return run_fp8_gemm(p, MODE_DENSE, 0, stream, ue8m0 ? "fp8_gemm_nt_ue8m0" : "fp8_gemm_nt", ue8m0);
+    const char* name = (flags & MODE_NN) ? "fp8_gemm_nn" : ((flags & MODE_UE8M0) ? "fp8_gemm_nt_ue8m0" : "fp8_gemm_nt");
+    return run_fp8_gemm(p, MODE_DENSE, 0, stream, name, flags);
   } catch (...) {
     return DG_ERR_HIP;
   }
@@ -199,7 +203,7 @@ static int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, cons
 
 static int contiguous_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb,
                             const int32_t* m_indices, uint16_t* d, int m, int n, int k, int num_groups, void* stream,
-                            bool ue8m0) {
+                            int flags) {
   try {
     if (!a || !sfa || !b || !sfb || !m_indices || !d) return DG_ERR_INVALID_ARG;
     if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERR_INVALID_ARG;
@@ -210,8 +214,10 @@ static int contiguous_entry(const uint8_t* a, const void* sfa, const uint8_t* b,
     Fp8GemmParams p{};
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
     p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
-    return run_fp8_gemm(p, MODE_CONTIG, 0, stream,
-                        ue8m0 ? "m_grouped_fp8_gemm_nt_contiguous_ue8m0" : "m_grouped_fp8_gemm_nt_contiguous", ue8m0);
+    const char* name = (flags & MODE_NN) ? "m_grouped_fp8_gemm_nn_contiguous"
+                                         : ((flags & MODE_UE8M0) ? "m_grouped_fp8_gemm_nt_contiguous_ue8m0"
+                                                                 : "m_grouped_fp8_gemm_nt_contiguous");
+    return run_fp8_gemm(p, MODE_CONTIG, 0, stream, name, flags);
   } catch (...) {
     return DG_ERR_HIP;
   }
@@ -219,7 +225,7 @@ static int contiguous_entry(const uint8_t* a, const void* sfa, const uint8_t* b,
 
 static int masked_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb,
                         const int32_t* masked_m, uint16_t* d, int num_groups, int max_m, int n, int k, int expected_m,
-                        void* stream, bool ue8m0) {
+                        void* stream, int flags) {
   try {
     if (!a || !sfa || !b || !sfb || !masked_m || !d) return DG_ERR_INVALID_ARG;
     if (num_groups <= 0 || max_m <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
@@ -234,7 +240,8 @@ static int masked_entry(const uint8_t* a, const void* sfa, const uint8_t* b, con
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
     p.m = max_m; p.n = n; p.k = k; p.num_groups = num_groups;
     return run_fp8_gemm(p, MODE_MASKED, expected_m, stream,
-                        ue8m0 ? "m_grouped_fp8_gemm_nt_masked_ue8m0" : "m_grouped_fp8_gemm_nt_masked", ue8m0);
+                        (flags & MODE_UE8M0) ? "m_grouped_fp8_gemm_nt_masked_ue8m0" : "m_grouped_fp8_gemm_nt_masked",
+                        flags);
   } catch (...) {
     return DG_ERR_HIP;
   }
@@ -244,38 +251,49 @@ extern "C" {
 
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
-  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, false);
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, 0);
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
                                         const float* sfb, const int32_t* m_indices, uint16_t* d,
                                         int m, int n, int k, int num_groups, void* stream) {
-  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, false);
+  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, 0);
 }
 
 int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
                                     const float* sfb, const int32_t* masked_m, uint16_t* d,
                                     int num_groups, int max_m, int n, int k, int expected_m,
                                     void* stream) {
-  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, stream, false);
+  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, stream, 0);
+}
+
+int dg_fp8_gemm_nn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, MODE_NN);
+}
+
+int dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                        const float* sfb, const int32_t* m_indices, uint16_t* d,
+                                        int m, int n, int k, int num_groups, void* stream) {
+  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, MODE_NN);
 }
 
 int dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b, const int32_t* sfb,
                          const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
-  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, true);
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, MODE_UE8M0);
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
                                               const int32_t* sfb, const int32_t* m_indices, uint16_t* d,
                                               int m, int n, int k, int num_groups, void* stream) {
-  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, true);
+  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, MODE_UE8M0);
 }
 
 int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
                                           const int32_t* sfb, const int32_t* masked_m, uint16_t* d,
                                           int num_groups, int max_m, int n, int k, int expected_m,
                                           void* stream) {
-  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, stream, true);
+  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, stream, MODE_UE8M0);
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }

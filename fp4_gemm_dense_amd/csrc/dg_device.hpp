@@ -27,6 +27,12 @@ __device__ __forceinline__ v4f mfma_e4m3_16x16x128(const v8i& a, const v8i& b, c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT_E4M3, FMT_E4M3, 0, 0, 0, 0);
 }
 
+// ds_read_b64_tr_b8: a transposing LDS read of 8 bytes per lane (lane layout
+// documented where it is used).  lds points into shared memory.
+__device__ __forceinline__ v2i ds_read_tr8_b64(const uint8_t* lds) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(const_cast<uint8_t*>(lds)));
+}
+
 // 16x16x128 e4m3 x e4m3 with hardware block scales: each lane supplies one
 // UE8M0 byte for its operand row's K chunk of A and one for B.
 __device__ __forceinline__ v4f mfma_scaled_e4m3_16x16x128(const v8i& a, int sa, const v8i& b, int sb,

@@ -12,6 +12,8 @@ enum GemmMode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
 // Flag or-ed into a mode: A and B scales are packed UE8M0 words (four K blocks
 // per int32) instead of fp32, applied by the scaled matrix instruction.
 constexpr int MODE_UE8M0 = 4;
+// Flag or-ed into a mode: B is stored [K][N], N contiguous (the NN layout).
+constexpr int MODE_NN = 8;
 
 // Arguments of one FP8 block-scaled GEMM launch (dense or grouped).
 struct Fp8GemmParams {
@@ -68,7 +70,9 @@ struct GemmPlan {
   int full_tiles;             // tiles computed whole; tiles [full_tiles, num_tiles) are split
   int num_workgroups;
 };
-GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m);
+// required_bn > 0: only tile shapes of that width (the NN layout needs 128)
+GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m,
+                       int required_bn = 0);
 GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id);
 // Resident workgroup slots of a compiled tile shape on num_cus CUs.
 int plan_slots(int kernel_id, int num_cus);

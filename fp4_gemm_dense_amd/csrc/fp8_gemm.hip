@@ -43,6 +43,7 @@ template <int MT, int NT, int WM, int WN, int STAGES, int MODE_SF>
 __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams p) {
   constexpr int MODE = MODE_SF & 3;
   constexpr bool UE = (MODE_SF & MODE_UE8M0) != 0;
+  constexpr bool NN = (MODE_SF & MODE_NN) != 0;   // B stored [K][N]
   constexpr int NW = WM * WN;                 // waves per workgroup
   constexpr int BM = WM * MT * 16;
   constexpr int BN = WN * NT * 16;
@@ -57,6 +58,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   constexpr int SPW = BM / NW;
   static_assert(SPW <= 64, "scale copy must fit one instruction per wave");
   constexpr int LPS = RA + RB + 1;            // DMA instructions per wave per stage
+  // NN: the B slot holds the tile's 128 K rows of BN bytes (columns), as BN/128
+  // column halves of 128 rows x 128 bytes, so its copies have the shape of the
+  // NT B tile's BN rows of 128 K bytes (8-row x 128-byte regions)
+  static_assert(!NN || BN % 128 == 0, "the NN layout uses 128-column B sub-tiles");
   // all of a wave's columns lie in one 128-wide B-scale block, so one sb per
   // K block serves the whole wave
   static_assert(128 % (NT * 16) == 0 && (BN % 128 == 0 || 128 % BN == 0), "one B scale per wave");
@@ -102,6 +107,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   const uint32_t b_lo = A_BYTES + (wave_n * NT * 16 + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
   const uint32_t b_hi = A_BYTES + (wave_n * NT * 16 + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
   const uint32_t sa_rd = A_BYTES + B_BYTES + (wave_m * MT * 16 + lrow * MT) * 4;
+  // NN B fragments (ds_read_b64_tr_b8).  Within each 16-lane group the read
+  // hands lane l byte b of the 8-byte row addressed by lane 2b + (l >= 8),
+  // taken at column l % 8.  Lane s addresses K row 32g + 8i + s/2 and the half
+  // s % 2 of the block's 16 columns, so lane l receives K 32g + 8i .. +7 of
+  // column l: read i gives bytes 8i .. 8i+7 of the lane's 32 K values (the A
+  // fragment's K order).  In the slot, 16-byte chunk c of K row r sits at
+  // c ^ (r % 8); the 8 rows one read touches then fall on distinct banks.
+  // Column chunk q (16 columns) of the tile lies in sub-tile q / 8 at chunk q % 8.
+  const uint32_t b_nn_row = A_BYTES + (32 * lgrp + (lrow >> 1)) * 128 + (lrow & 1) * 8;
+  const int b_nn_sw = lrow >> 1;
   const int dma_row = lane >> 3;              // DMA row inside an 8-row region
   const uint32_t a_dst = wave * RA * 1024;
   const uint32_t b_dst = A_BYTES + wave * RB * 1024;
@@ -233,8 +248,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const int row = (wave * RB + j) * 8 + dma_row;
-      b_off[j] = tile.n0 + row < N ? (uint32_t)(tile.n0 + row) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4)
-                                   : kBufferOutOfRange;
+      if constexpr (NN) {
+        // region q = row / 8: column sub-tile q / 16, K rows 8 (q % 16) ..; position
+        // lane % 8 holds chunk (lane % 8) ^ (K row % 8) of the sub-tile's 128 columns
+        const int krow = row & 127;
+        const int col = tile.n0 + (row >> 7) * 128 + (((lane & 7) ^ (krow & 7)) << 4);
+        b_off[j] = col < N ? (uint32_t)krow * (uint32_t)N + (uint32_t)col : kBufferOutOfRange;
+      } else {
+        b_off[j] = tile.n0 + row < N ? (uint32_t)(tile.n0 + row) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4)
+                                     : kBufferOutOfRange;
+      }
     }
     {
       // LDS position q of a tile's A scales holds row g*MT*16 + mt*16 + r for
@@ -254,11 +277,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   auto issue = [&](int kb, uint32_t slot_off) {
     const int kp = __builtin_amdgcn_readfirstlane(kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d));   // K block in memory
     const uint32_t kofs = (uint32_t)kp * 128u;
+    const uint32_t kofs_b = NN ? (uint32_t)kp * 128u * (uint32_t)N : kofs;   // NN: 128 rows of B down
     const uint32_t sofs = UE ? (uint32_t)(kp >> 2) * 4u : (uint32_t)kp * (uint32_t)M * 4u;
 #pragma unroll
     for (int j = 0; j < RA; ++j) buf16_to_lds(rsA, a_off[j], kofs, smem + slot_off + a_dst + j * 1024);
 #pragma unroll
-    for (int j = 0; j < RB; ++j) buf16_to_lds(rsB, b_off[j], kofs, smem + slot_off + b_dst + j * 1024);
+    for (int j = 0; j < RB; ++j) buf16_to_lds(rsB, b_off[j], kofs_b, smem + slot_off + b_dst + j * 1024);
     if (SPW == 64 || lane < SPW) buf4_to_lds(rsSA, sa_off, sofs, smem + slot_off + sa_dst);
   };
   // The same copies one instruction at a time (idx < RA: A region idx, then the
@@ -267,12 +291,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   auto issue_ab = [&](int idx, int kb, uint32_t slot_off) {
     const int kp = __builtin_amdgcn_readfirstlane(kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d));
     const uint32_t kofs = (uint32_t)kp * 128u;
+    const uint32_t kofs_b = NN ? (uint32_t)kp * 128u * (uint32_t)N : kofs;
 #pragma unroll
     for (int j = 0; j < RA; ++j)
       if (idx == j) buf16_to_lds(rsA, a_off[j], kofs, smem + slot_off + a_dst + j * 1024);
 #pragma unroll
     for (int j = 0; j < RB; ++j)
-      if (idx == RA + j) buf16_to_lds(rsB, b_off[j], kofs, smem + slot_off + b_dst + j * 1024);
+      if (idx == RA + j) buf16_to_lds(rsB, b_off[j], kofs_b, smem + slot_off + b_dst + j * 1024);
   };
   auto issue_sa = [&](int kb, uint32_t slot_off) {
     const int kp = __builtin_amdgcn_readfirstlane(kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d));
@@ -415,9 +440,18 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       v8i af[MT], bf[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        v4i lo = *reinterpret_cast<const v4i*>(rb_lo + nt * 2048);
-        v4i hi = *reinterpret_cast<const v4i*>(rb_hi + nt * 2048);
-        bf[nt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        if constexpr (NN) {
+          const int q = wave_n * NT + nt;   // column chunk of the tile
+          const uint8_t* rb = smem + rd_slot + b_nn_row + (q >> 3) * (128 * 128) + (((q & 7) ^ b_nn_sw) << 4);
+          v2i r[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = ds_read_tr8_b64(rb + i * 1024);
+          bf[nt] = v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+        } else {
+          v4i lo = *reinterpret_cast<const v4i*>(rb_lo + nt * 2048);
+          v4i hi = *reinterpret_cast<const v4i*>(rb_hi + nt * 2048);
+          bf[nt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) af[mt] = load_a(mt);
@@ -709,6 +743,8 @@ static hipError_t launch_mode(const Fp8GemmParams& p, int kernel_id, int grid, h
   switch (kernel_id) {
 #define X(id, MT, NT, WM, WN, ST, OCC)                                                              \
   case id: {                                                                                      \
+    if constexpr ((MODE & MODE_NN) != 0 && (WN * NT * 16) % 128 != 0) return hipErrorInvalidValue; \
+    else {                                                                                        \
     const TileConfig& tc = kTileConfigs[id];                                                      \
     static const hipError_t attr = hipFuncSetAttribute(                                           \
         reinterpret_cast<const void*>(&fp8_gemm_kernel<MT, NT, WM, WN, ST, MODE>),                \
@@ -717,6 +753,7 @@ static hipError_t launch_mode(const Fp8GemmParams& p, int kernel_id, int grid, h
     hipLaunchKernelGGL((fp8_gemm_kernel<MT, NT, WM, WN, ST, MODE>), dim3(grid), dim3(tc.threads), \
                        tc.lds_bytes, stream, p);                                                  \
     break;                                                                                        \
+    }                                                                                             \
   }
     DG_TILE_CONFIGS(X)
 #undef X
@@ -736,6 +773,8 @@ hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mod
     case MODE_DENSE | MODE_UE8M0: return launch_mode<MODE_DENSE | MODE_UE8M0>(p, id, g, stream);
     case MODE_CONTIG | MODE_UE8M0: return launch_mode<MODE_CONTIG | MODE_UE8M0>(p, id, g, stream);
     case MODE_MASKED | MODE_UE8M0: return launch_mode<MODE_MASKED | MODE_UE8M0>(p, id, g, stream);
+    case MODE_DENSE | MODE_NN: return launch_mode<MODE_DENSE | MODE_NN>(p, id, g, stream);
+    case MODE_CONTIG | MODE_NN: return launch_mode<MODE_CONTIG | MODE_NN>(p, id, g, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -125,6 +125,23 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
                                     void* stream);
 
 /*
+ * NN layout (usage guide "DeepGEMM：统一高性能张量核心 GEMM 计算库编译与使用指南",
+ * 五、使用方法 / 基础非分组 FP8 GEMM: the newer architecture takes the NT, TN, NN and
+ * TT layouts; 分组 GEMM（MoE）: the contiguous grouped form in NN for the training
+ * backward pass): B is stored K-major, not transposed, so D = C + A @ B with
+ *   b    [k, n]          e4m3, n contiguous (grouped: [num_groups, k, n])
+ * and every other argument, scale layout (sfb stays [ceil(n/128)][k/128], indexed
+ * by n-block then k-block), requirement and row rule as in dg_fp8_gemm_nt and
+ * dg_m_grouped_fp8_gemm_nt_contiguous.  The kernel reads B's tiles with gfx950's
+ * transposing LDS loads.
+ */
+int dg_fp8_gemm_nn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+int dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                        const float* sfb, const int32_t* m_indices, uint16_t* d,
+                                        int m, int n, int k, int num_groups, void* stream);
+
+/*
  * The same three GEMMs with packed UE8M0 scale factors instead of fp32 ones
  * (usage guide "DeepGEMM：统一高性能张量核心 GEMM 计算库编译与使用指南", 五、使用方法 /
  * 基础非分组 FP8 GEMM: the older architecture takes fp32 scale factors, the newer

@@ -113,6 +113,44 @@ def m_grouped_masked(a, sfa, b, sfb, masked_m):
     return ref, written
 
 
+def dequant_b_kn(b_kn, sfb) -> np.ndarray:
+    """B stored [K, N] (NN layout): B[k, n] * sfb[n // 128, k // 128] in float64, as [K, N]."""
+    b_kn = np.asarray(b_kn)
+    K, N = b_kn.shape
+    s = np.asarray(sfb, dtype=np.float64)                 # [ceil(N/128), K/128]
+    s_full = np.repeat(np.repeat(s, BLOCK_K, axis=0)[:N], BLOCK_K, axis=1)[:, :K]   # [N, K]
+    return decode_e4m3(b_kn) * s_full.T
+
+
+def fp8_gemm_nn(a, sfa, b_kn, sfb, c=None) -> np.ndarray:
+    """D = C + A @ B with B stored [K, N], not transposed (usage guide, 五、使用方法: the
+    NN layout of the newer architecture).  Scales as in fp8_gemm_nt."""
+    ref = dequant_a(a, sfa) @ dequant_b_kn(b_kn, sfb)
+    if c is not None:
+        ref = ref + bf16_bits_to_f64(c)
+    return ref
+
+
+def m_grouped_nn_contiguous(a, sfa, b_kn, sfb, m_indices):
+    """Contiguous M-grouped form with each group's B stored [K, N] (usage guide,
+    分组 GEMM（MoE）: the NN contiguous form of the training backward pass).  Rows with
+    index -1 are not part of the result.  Returns (ref float64 [M, N], written bool [M])."""
+    a = np.asarray(a)
+    m_idx = np.asarray(m_indices).astype(np.int64)
+    G, _, N = np.asarray(b_kn).shape
+    M = a.shape[0]
+    ref = np.full((M, N), np.nan)
+    written = np.zeros(M, dtype=bool)
+    sfa = np.asarray(sfa)
+    for g in range(G):
+        rows = np.nonzero(m_idx == g)[0]
+        if rows.size == 0:
+            continue
+        ref[rows] = fp8_gemm_nn(a[rows], sfa[:, rows], b_kn[g], sfb[g])
+        written[rows] = True
+    return ref, written
+
+
 def fp8_gemm_nt_entries(a, sfa, b, sfb, c, rows, cols) -> np.ndarray:
     """Selected entries D[rows[i], cols[i]] of the dense NT GEMM, one by one.
 

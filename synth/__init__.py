@@ -213,6 +213,20 @@ def gen_dense(M, N, K, seed, with_c=True, backend="numpy", device="cpu"):
     return dict(a=a, sfa=sfa, b=b, sfb=sfb, c=c, M=M, N=N, K=K)
 
 
+def gen_dense_nn(M, N, K, seed, with_c=True, backend="numpy", device="cpu"):
+    """gen_dense's inputs with B stored [K, N] (the NN layout; same values and scales)."""
+    g = gen_dense(M, N, K, seed, with_c=with_c, backend=backend, device=device)
+    g["b"] = g["b"].t().contiguous()
+    return g
+
+
+def gen_contiguous_nn(G, total_rows, N, K, seed, align=128, counts=None, backend="numpy", device="cpu"):
+    """gen_contiguous's inputs with each group's B stored [K, N]."""
+    g = gen_contiguous(G, total_rows, N, K, seed, align=align, counts=counts, backend=backend, device=device)
+    g["b"] = g["b"].transpose(1, 2).contiguous()
+    return g
+
+
 def padded_group_layout(counts, align=128):
     """Row counts -> (m_indices list, group start offsets) for the contiguous layout."""
     m_idx = []

@@ -1,0 +1,98 @@
+"""Parity of the NN-layout FP8 GEMMs (dg_fp8_gemm_nn, dg_m_grouped_fp8_gemm_nn_contiguous:
+B stored [K, N]) against the oracle on the GPU.
+
+Tolerance: the FP8 GEMM's bar, per element |D - ref| <= 8e-3 * max(|ref|, rms(ref)) and
+Frobenius 3e-3; padding rows bit-exact against the bf16 sentinel; an integer case whose
+every fp32 partial sum is exact bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ref as R
+from tests.helpers import SENTINEL, bits, check_bit_exact, check_parity, sentinel_like
+from tests.test_oracle import make_exact_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x):
+    if x is None:
+        return None
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        x = x.view(np.int16)
+    return torch.from_numpy(x).cuda()
+
+
+def _run(dg, a, sfa, b_kn, sfb, c):
+    d = sentinel_like((a.shape[0], b_kn.shape[1]))
+    dg.dg_fp8_gemm_nn(_dev(a), _dev(sfa), _dev(b_kn), _dev(sfb), _dev(c), d)
+    torch.cuda.synchronize()
+    return bits(d)
+
+
+@pytest.mark.parametrize("M,N,K,with_c", [
+    (1, 16, 128, False),
+    (9, 144, 384, True),        # N: one full and one partial 128-column tile
+    (130, 400, 1024, True),
+    (256, 256, 512, False),
+    (513, 1040, 1152, True),
+    (64, 2112, 7168, False),    # skinny: split along K
+])
+def test_nn_dense_parity(dg, M, N, K, with_c):
+    g = synth.gen_dense_nn(M, N, K, seed=M + 3 * N + K, with_c=with_c)
+    a, sfa, b, sfb, c = (None if g[k] is None else synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+    d = _run(dg, a, sfa, b, sfb, c)
+    check_parity(d, R.fp8_gemm_nn(a, sfa, b, sfb, c), what=f"nn {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,with_c", [(9, 144, 384, True), (130, 400, 1024, True), (256, 1024, 2048, False)])
+def test_nn_dense_exact_integer_case_bit_exact(dg, M, N, K, with_c):
+    rng = np.random.default_rng(M + N + K + 5)
+    a, sfa, b, sfb, c, exact = make_exact_case(rng, M, N, K, with_c)
+    d = _run(dg, a, sfa, np.ascontiguousarray(b.T), sfb, c)
+    check_bit_exact(d, exact, f"nn exact {M}x{N}x{K}")
+
+
+def test_nn_contiguous_parity_and_padding_rows(dg):
+    g = synth.gen_contiguous_nn(4, 700, 400, 1152, seed=33, counts=[130, 0, 1, 569])
+    a, sfa, b, sfb, mi = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "m_indices"))
+    d = sentinel_like((a.shape[0], b.shape[2]))
+    dg.dg_m_grouped_fp8_gemm_nn_contiguous(_dev(a), _dev(sfa), _dev(b), _dev(sfb), _dev(mi), d)
+    torch.cuda.synchronize()
+    db = bits(d)
+    ref, written = R.m_grouped_nn_contiguous(a, sfa, b, sfb, mi)
+    assert np.all(db[~written] == SENTINEL) and not np.any(db[written] == SENTINEL)
+    check_parity(db[written], ref[written], what="nn contiguous")
+
+
+def test_nn_dense_full_size_sampled(dg):
+    """M 4096, N 7168, K 7168 with C on the device; 8 columns in each of 64 sampled rows
+    against the oracle entry by entry (B transposed back for the NT entry evaluator)."""
+    M, N, K = 4096, 7168, 7168
+    g = synth.gen_dense_nn(M, N, K, seed=707, backend="torch", device="cuda")
+    d = sentinel_like((M, N))
+    dg.dg_fp8_gemm_nn(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(70)
+    rows = np.repeat(rng.choice(M, 64, replace=False), 8)
+    cols = np.concatenate([rng.choice(N, 8, replace=False) for _ in range(64)])
+    a, sfa, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "sfb", "c"))
+    b_nk = synth.to_numpy(g["b"].t().contiguous())
+    want = R.fp8_gemm_nt_entries(a, sfa, b_nk, sfb, c, rows, cols)
+    check_parity(bits(d)[rows, cols], want, what="nn full size sampled")
+
+
+@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3])
+def test_nn_every_tile_shape(dg, kernel_id, monkeypatch):
+    """Each compiled tile shape (256x128, 128x256, 128x128, 64x128) on the NN path, with a
+    partial last column tile and C."""
+    monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
+    M, N, K = 300, 656, 1024
+    g = synth.gen_dense_nn(M, N, K, seed=90 + kernel_id)
+    a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+    d = _run(dg, a, sfa, b, sfb, c)
+    check_parity(d, R.fp8_gemm_nn(a, sfa, b, sfb, c), what=f"nn kernel {kernel_id}")

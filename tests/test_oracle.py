@@ -603,6 +603,42 @@ def test_fp4_weight_sf_k_major_fixture_and_labelled_words():
 
 
 # ----------------------------------------------------------------------------
+# NN layout (B stored [K, N])
+# ----------------------------------------------------------------------------
+
+def test_nn_exact_rational_brute_force():
+    """Codes decoded by torch's float8 cast, B indexed as [k][n], scales per (row, K block)
+    and (128-column block, K block); N = 130 spans a partial B block."""
+    rng = np.random.default_rng(17)
+    M, N, K = 2, 130, 256
+    a = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    b_kn = rng.integers(0, 256, (K, N), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x38
+    b_kn[(b_kn & 0x7F) == 0x7F] = 0x40
+    sfa = rng.uniform(0.5, 2.0, (K // 128, M)).astype(np.float32)
+    sfb = rng.uniform(0.5, 2.0, (2, K // 128)).astype(np.float32)
+    got = R.fp8_gemm_nn(a, sfa, b_kn, sfb)
+    av, bv = _torch_e4m3(a), _torch_e4m3(b_kn)
+    for m, n in [(0, 0), (1, 127), (0, 128), (1, 129), (0, 77)]:
+        want = sum(Fraction(float(av[m, k])) * Fraction(float(bv[k, n])) * Fraction(float(sfa[k // 128, m])) *
+                   Fraction(float(sfb[n // 128, k // 128])) for k in range(K))
+        assert abs(got[m, n] - float(want)) <= 1e-13 * max(1.0, abs(float(want)))
+
+
+def test_nn_equals_nt_of_the_transposed_operand_and_grouped_forms():
+    g = synth.gen_dense_nn(5, 144, 384, seed=8)
+    a, sfa, b_kn, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+    x, y = R.fp8_gemm_nn(a, sfa, b_kn, sfb, c), R.fp8_gemm_nt(a, sfa, b_kn.T.copy(), sfb, c)
+    assert np.allclose(x, y, rtol=1e-12, atol=1e-12 * np.abs(y).max())   # float64 sums in another order
+    gc = synth.gen_contiguous_nn(3, 200, 48, 256, seed=9, counts=[60, 0, 140])
+    a, sfa, b_kn, sfb, mi = (synth.to_numpy(gc[k]) for k in ("a", "sfa", "b", "sfb", "m_indices"))
+    ref, written = R.m_grouped_nn_contiguous(a, sfa, b_kn, sfb, mi)
+    ref_t, written_t = R.m_grouped_contiguous(a, sfa, np.ascontiguousarray(np.swapaxes(b_kn, 1, 2)), sfb, mi)
+    assert np.array_equal(written, written_t)
+    assert np.allclose(ref[written], ref_t[written], rtol=1e-12, atol=1e-12 * np.abs(ref_t[written]).max())
+
+
+# ----------------------------------------------------------------------------
 # packed UE8M0 scale factors
 # ----------------------------------------------------------------------------
 
