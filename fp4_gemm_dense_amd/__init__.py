@@ -33,6 +33,8 @@ _SIGNATURES = {
     "dg_m_grouped_fp8_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "dg_fp8_gemm_nn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "dg_fp8_gemm_tn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "dg_fp8_gemm_tt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nn_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_fp8_gemm_nt_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -191,6 +193,34 @@ def dg_fp8_gemm_nn(a, sfa, b, sfb, c, d):
     _check("dg_fp8_gemm_nn", L.dg_fp8_gemm_nn(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c), _ptr(d),
                                               M, N, K, _stream(a)))
     return d
+
+
+def _dense_layout(name, a, sfa, b, sfb, c, d, a_km, b_kn):
+    L = lib()
+    if a_km:
+        K, M = a.shape
+    else:
+        M, K = a.shape
+    N = b.shape[1] if b_kn else b.shape[0]
+    _req(a, _U8, (K, M) if a_km else (M, K), "a")
+    _req(b, _U8, (K, N) if b_kn else (N, K), "b")
+    _req(sfa, torch.float32, (K // 128, M), "sfa")
+    _req(sfb, torch.float32, (_nb(N), K // 128), "sfb")
+    if c is not None:
+        _req_bf16(c, (M, N), "c")
+    _req_bf16(d, (M, N), "d")
+    _check(name, getattr(L, name)(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c), _ptr(d), M, N, K, _stream(a)))
+    return d
+
+
+def dg_fp8_gemm_tn(a, sfa, b, sfb, c, d):
+    """d = c + a^T b with a stored [K, M] and b stored [K, N] (TN layout)."""
+    return _dense_layout("dg_fp8_gemm_tn", a, sfa, b, sfb, c, d, a_km=True, b_kn=True)
+
+
+def dg_fp8_gemm_tt(a, sfa, b, sfb, c, d):
+    """d = c + a^T b^T with a stored [K, M] and b stored [N, K] (TT layout)."""
+    return _dense_layout("dg_fp8_gemm_tt", a, sfa, b, sfb, c, d, a_km=True, b_kn=False)
 
 
 def dg_m_grouped_fp8_gemm_nn_contiguous(a, sfa, b, sfb, m_indices, d):

@@ -114,15 +114,15 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
   DeviceInfo di = current_device_info();
   if (!di.ok) return DG_ERR_NO_DEVICE;
   int cus = effective_cus(di);
-  const int required_bn = 0;   // every compiled tile width suits both layouts
-  GemmPlan plan = plan_fp8_gemm(p.m, p.n, p.k, p.num_groups, mode, cus, expected_m, required_bn);
+  const int bm_multiple = (flags & MODE_AT) ? 128 : 0;   // A stored [K][M]: 128-row sub-tiles
+  GemmPlan plan = plan_fp8_gemm(p.m, p.n, p.k, p.num_groups, mode, cus, expected_m, bm_multiple);
   if (plan.kernel_id < 0) return DG_ERR_UNSUPPORTED;
   // DG_FORCE_KERNEL=<id>: override the heuristic's tile choice (for tuning)
   if (const char* fk = std::getenv("DG_FORCE_KERNEL")) {
     int id = std::atoi(fk);
     if (id >= 0 && id < num_tile_configs() &&
         !(mode == MODE_CONTIG && (128 % tile_config(id).block_m) != 0) &&
-        !(required_bn > 0 && tile_config(id).block_n != required_bn))
+        !(bm_multiple > 0 && tile_config(id).block_m % bm_multiple != 0))
       plan = plan_with_kernel(p.m, p.n, p.k, p.num_groups, mode, cus, id);
   }
   p.tiles_m = plan.tiles_m;
@@ -191,10 +191,13 @@ static int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, cons
         (c && !aligned(c, 16)))
       return DG_ERR_INVALID_ARG;
     if (k % 128 != 0 || n % 16 != 0 || !operands_fit(m, n, k)) return DG_ERR_UNSUPPORTED;
+    if ((flags & MODE_AT) && m % 16 != 0) return DG_ERR_UNSUPPORTED;   // A's K rows: whole 16-byte chunks
     Fp8GemmParams p{};
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.c = c; p.d = d;
     p.m = m; p.n = n; p.k = k; p.num_groups = 1;
-    const char* name = (flags & MODE_NN) ? "fp8_gemm_nn" : ((flags & MODE_UE8M0) ? "fp8_gemm_nt_ue8m0" : "fp8_gemm_nt");
+    const char* name = (flags & MODE_AT) ? ((flags & MODE_NN) ? "fp8_gemm_tn" : "fp8_gemm_tt")
+                       : (flags & MODE_NN) ? "fp8_gemm_nn"
+                       : ((flags & MODE_UE8M0) ? "fp8_gemm_nt_ue8m0" : "fp8_gemm_nt");
     return run_fp8_gemm(p, MODE_DENSE, 0, stream, name, flags);
   } catch (...) {
     return DG_ERR_HIP;
@@ -270,6 +273,16 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
 int dg_fp8_gemm_nn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
   return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, MODE_NN);
+}
+
+int dg_fp8_gemm_tn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, MODE_AT | MODE_NN);
+}
+
+int dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, MODE_AT);
 }
 
 int dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,

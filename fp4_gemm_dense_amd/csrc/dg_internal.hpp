@@ -14,6 +14,9 @@ enum GemmMode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
 constexpr int MODE_UE8M0 = 4;
 // Flag or-ed into a mode: B is stored [K][N], N contiguous (the NN layout).
 constexpr int MODE_NN = 8;
+// Flag or-ed into a mode: A is stored [K][M], M contiguous (the TN / TT layouts:
+// MODE_AT | MODE_NN is TN, MODE_AT alone TT); 128-row A sub-tiles.
+constexpr int MODE_AT = 16;
 
 // Arguments of one FP8 block-scaled GEMM launch (dense or grouped).
 struct Fp8GemmParams {
@@ -70,9 +73,10 @@ struct GemmPlan {
   int full_tiles;             // tiles computed whole; tiles [full_tiles, num_tiles) are split
   int num_workgroups;
 };
-// required_bn > 0: only tile shapes of that width (the NN layout needs 128)
+// bm_multiple > 0: only tile shapes whose height is a multiple of it (an A stored
+// [K][M] is staged in 128-row sub-tiles)
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m,
-                       int required_bn = 0);
+                       int bm_multiple = 0);
 GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id);
 // Resident workgroup slots of a compiled tile shape on num_cus CUs.
 int plan_slots(int kernel_id, int num_cus);

@@ -44,6 +44,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   constexpr int MODE = MODE_SF & 3;
   constexpr bool UE = (MODE_SF & MODE_UE8M0) != 0;
   constexpr bool NN = (MODE_SF & MODE_NN) != 0;   // B stored [K][N]
+  constexpr bool AT = (MODE_SF & MODE_AT) != 0;   // A stored [K][M]
   constexpr int NW = WM * WN;                 // waves per workgroup
   constexpr int BM = WM * MT * 16;
   constexpr int BN = WN * NT * 16;
@@ -62,6 +63,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // column halves of 128 rows x 128 bytes, so its copies have the shape of the
   // NT B tile's BN rows of 128 K bytes (8-row x 128-byte regions)
   static_assert(!NN || BN % 128 == 0, "the NN layout uses 128-column B sub-tiles");
+  // AT: the A slot holds 128 K rows of BM bytes (rows of D) the same way
+  static_assert(!AT || BM % 128 == 0, "an A stored [K][M] uses 128-row sub-tiles");
   // all of a wave's columns lie in one 128-wide B-scale block, so one sb per
   // K block serves the whole wave
   static_assert(128 % (NT * 16) == 0 && (BN % 128 == 0 || 128 % BN == 0), "one B scale per wave");
@@ -116,6 +119,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // c ^ (r % 8); the 8 rows one read touches then fall on distinct banks.
   // Column chunk q (16 columns) of the tile lies in sub-tile q / 8 at chunk q % 8.
   const uint32_t b_nn_row = A_BYTES + (32 * lgrp + (lrow >> 1)) * 128 + (lrow & 1) * 8;
+  const uint32_t a_t_row = (32 * lgrp + (lrow >> 1)) * 128 + (lrow & 1) * 8;   // AT: the same for A
   const int b_nn_sw = lrow >> 1;
   const int dma_row = lane >> 3;              // DMA row inside an 8-row region
   const uint32_t a_dst = wave * RA * 1024;
@@ -241,9 +245,15 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
 #pragma unroll
     for (int j = 0; j < RA; ++j) {
       const int row = (wave * RA + j) * 8 + dma_row;
-      a_off[j] = tile.m0 + row < tile.rows_valid
-                     ? (uint32_t)(tile.m0 + row) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4)
-                     : kBufferOutOfRange;
+      if constexpr (AT) {   // as B in the NN layout: sub-tile row / 128, K row row % 128
+        const int krow = row & 127;
+        const int col = tile.m0 + (row >> 7) * 128 + (((lane & 7) ^ (krow & 7)) << 4);
+        a_off[j] = col < tile.rows_valid ? (uint32_t)krow * (uint32_t)M + (uint32_t)col : kBufferOutOfRange;
+      } else {
+        a_off[j] = tile.m0 + row < tile.rows_valid
+                       ? (uint32_t)(tile.m0 + row) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4)
+                       : kBufferOutOfRange;
+      }
     }
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
@@ -278,9 +288,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     const int kp = __builtin_amdgcn_readfirstlane(kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d));   // K block in memory
     const uint32_t kofs = (uint32_t)kp * 128u;
     const uint32_t kofs_b = NN ? (uint32_t)kp * 128u * (uint32_t)N : kofs;   // NN: 128 rows of B down
+    const uint32_t kofs_a = AT ? (uint32_t)kp * 128u * (uint32_t)M : kofs;
     const uint32_t sofs = UE ? (uint32_t)(kp >> 2) * 4u : (uint32_t)kp * (uint32_t)M * 4u;
 #pragma unroll
-    for (int j = 0; j < RA; ++j) buf16_to_lds(rsA, a_off[j], kofs, smem + slot_off + a_dst + j * 1024);
+    for (int j = 0; j < RA; ++j) buf16_to_lds(rsA, a_off[j], kofs_a, smem + slot_off + a_dst + j * 1024);
 #pragma unroll
     for (int j = 0; j < RB; ++j) buf16_to_lds(rsB, b_off[j], kofs_b, smem + slot_off + b_dst + j * 1024);
     if (SPW == 64 || lane < SPW) buf4_to_lds(rsSA, sa_off, sofs, smem + slot_off + sa_dst);
@@ -292,9 +303,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     const int kp = __builtin_amdgcn_readfirstlane(kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d));
     const uint32_t kofs = (uint32_t)kp * 128u;
     const uint32_t kofs_b = NN ? (uint32_t)kp * 128u * (uint32_t)N : kofs;
+    const uint32_t kofs_a = AT ? (uint32_t)kp * 128u * (uint32_t)M : kofs;
 #pragma unroll
     for (int j = 0; j < RA; ++j)
-      if (idx == j) buf16_to_lds(rsA, a_off[j], kofs, smem + slot_off + a_dst + j * 1024);
+      if (idx == j) buf16_to_lds(rsA, a_off[j], kofs_a, smem + slot_off + a_dst + j * 1024);
 #pragma unroll
     for (int j = 0; j < RB; ++j)
       if (idx == RA + j) buf16_to_lds(rsB, b_off[j], kofs_b, smem + slot_off + b_dst + j * 1024);
@@ -433,9 +445,18 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
         }
       }
       auto load_a = [&](int mt) -> v8i {
-        const v4i lo = *reinterpret_cast<const v4i*>(ra_lo + mt * 2048);
-        const v4i hi = *reinterpret_cast<const v4i*>(ra_hi + mt * 2048);
-        return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        if constexpr (AT) {   // transposing reads, as for B in the NN layout
+          const int q = wave_m * MT + mt;   // row chunk (16 rows of D) of the tile
+          const uint8_t* ra = smem + rd_slot + a_t_row + (q >> 3) * (128 * 128) + (((q & 7) ^ b_nn_sw) << 4);
+          v2i r[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = ds_read_tr8_b64(ra + i * 1024);
+          return v8i{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+        } else {
+          const v4i lo = *reinterpret_cast<const v4i*>(ra_lo + mt * 2048);
+          const v4i hi = *reinterpret_cast<const v4i*>(ra_hi + mt * 2048);
+          return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
       };
       v8i af[MT], bf[NT];
 #pragma unroll
@@ -743,7 +764,9 @@ static hipError_t launch_mode(const Fp8GemmParams& p, int kernel_id, int grid, h
   switch (kernel_id) {
 #define X(id, MT, NT, WM, WN, ST, OCC)                                                              \
   case id: {                                                                                      \
-    if constexpr ((MODE & MODE_NN) != 0 && (WN * NT * 16) % 128 != 0) return hipErrorInvalidValue; \
+    if constexpr (((MODE & MODE_NN) != 0 && (WN * NT * 16) % 128 != 0) ||                           \
+                  ((MODE & MODE_AT) != 0 && (WM * MT * 16) % 128 != 0))                             \
+      return hipErrorInvalidValue;                                                                \
     else {                                                                                        \
     const TileConfig& tc = kTileConfigs[id];                                                      \
     static const hipError_t attr = hipFuncSetAttribute(                                           \
@@ -775,6 +798,8 @@ hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mod
     case MODE_MASKED | MODE_UE8M0: return launch_mode<MODE_MASKED | MODE_UE8M0>(p, id, g, stream);
     case MODE_DENSE | MODE_NN: return launch_mode<MODE_DENSE | MODE_NN>(p, id, g, stream);
     case MODE_CONTIG | MODE_NN: return launch_mode<MODE_CONTIG | MODE_NN>(p, id, g, stream);
+    case MODE_DENSE | MODE_AT | MODE_NN: return launch_mode<MODE_DENSE | MODE_AT | MODE_NN>(p, id, g, stream);
+    case MODE_DENSE | MODE_AT: return launch_mode<MODE_DENSE | MODE_AT>(p, id, g, stream);
   }
   return hipErrorInvalidValue;
 }

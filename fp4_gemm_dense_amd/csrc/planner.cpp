@@ -56,7 +56,7 @@ GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num
   return plan;
 }
 
-GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m, int required_bn) {
+GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m, int bm_multiple) {
   int best_id = -1;
   // rows each group contributes (masked: the expected count if given, else capacity)
   int rows = m;
@@ -66,7 +66,7 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
   for (int id = 0; id < num_tile_configs(); ++id) {
     TileConfig tc = tile_config(id);
     if (mode == MODE_CONTIG && (128 % tc.block_m) != 0) continue;   // blocks must be group-pure
-    if (required_bn > 0 && tc.block_n != required_bn) continue;
+    if (bm_multiple > 0 && tc.block_m % bm_multiple != 0) continue;
     int tm = cdiv(rows, tc.block_m);
     int tn = cdiv(n, tc.block_n);
     long long tiles = (long long)tm * tn * (mode == MODE_DENSE ? 1 : (mode == MODE_MASKED ? num_groups : 1));

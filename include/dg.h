@@ -142,6 +142,19 @@ int dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa, cons
                                         int m, int n, int k, int num_groups, void* stream);
 
 /*
+ * TN and TT layouts (same usage-guide passage): A is stored [k, m], m contiguous,
+ * so D[i][j] = C[i][j] + sum_k A[k][i] * B(k, j), with B stored [k, n] (TN) or
+ * [n, k] (TT).  sfa stays [k/128][m] (one scale per row of D per 128-wide K
+ * block), sfb [ceil(n/128)][k/128].  Both read A's tiles with the transposing
+ * LDS loads (in 128-row sub-tiles).  Requirements as dg_fp8_gemm_nt plus
+ * m % 16 == 0.
+ */
+int dg_fp8_gemm_tn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+int dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+
+/*
  * The same three GEMMs with packed UE8M0 scale factors instead of fp32 ones
  * (usage guide "DeepGEMM：统一高性能张量核心 GEMM 计算库编译与使用指南", 五、使用方法 /
  * 基础非分组 FP8 GEMM: the older architecture takes fp32 scale factors, the newer

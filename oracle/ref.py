@@ -131,6 +131,29 @@ def fp8_gemm_nn(a, sfa, b_kn, sfb, c=None) -> np.ndarray:
     return ref
 
 
+def fp8_gemm_tn(a_km, sfa, b_kn, sfb, c=None) -> np.ndarray:
+    """TN layout: A stored [K, M], B stored [K, N]; D[m, n] = C + sum_k A[k, m] B[k, n] with
+    the scales of fp8_gemm_nt (sfa [K/128][M], sfb [ceil(N/128)][K/128])."""
+    a_km = np.asarray(a_km)
+    K, M = a_km.shape
+    sa = np.repeat(np.asarray(sfa, dtype=np.float64), BLOCK_K, axis=0)[:K]     # [K, M]
+    ref = (decode_e4m3(a_km) * sa).T @ dequant_b_kn(b_kn, sfb)
+    if c is not None:
+        ref = ref + bf16_bits_to_f64(c)
+    return ref
+
+
+def fp8_gemm_tt(a_km, sfa, b, sfb, c=None) -> np.ndarray:
+    """TT layout: A stored [K, M], B stored [N, K]."""
+    a_km = np.asarray(a_km)
+    K, M = a_km.shape
+    sa = np.repeat(np.asarray(sfa, dtype=np.float64), BLOCK_K, axis=0)[:K]
+    ref = (decode_e4m3(a_km) * sa).T @ dequant_b(b, sfb).T
+    if c is not None:
+        ref = ref + bf16_bits_to_f64(c)
+    return ref
+
+
 def m_grouped_nn_contiguous(a, sfa, b_kn, sfb, m_indices):
     """Contiguous M-grouped form with each group's B stored [K, N] (usage guide,
     分组 GEMM（MoE）: the NN contiguous form of the training backward pass).  Rows with

@@ -220,6 +220,15 @@ def gen_dense_nn(M, N, K, seed, with_c=True, backend="numpy", device="cpu"):
     return g
 
 
+def gen_dense_tn(M, N, K, seed, with_c=True, b_kn=True, backend="numpy", device="cpu"):
+    """gen_dense's inputs with A stored [K, M] and B stored [K, N] (TN; b_kn=False: [N, K], TT)."""
+    g = gen_dense(M, N, K, seed, with_c=with_c, backend=backend, device=device)
+    g["a"] = g["a"].t().contiguous()
+    if b_kn:
+        g["b"] = g["b"].t().contiguous()
+    return g
+
+
 def gen_contiguous_nn(G, total_rows, N, K, seed, align=128, counts=None, backend="numpy", device="cpu"):
     """gen_contiguous's inputs with each group's B stored [K, N]."""
     g = gen_contiguous(G, total_rows, N, K, seed, align=align, counts=counts, backend=backend, device=device)

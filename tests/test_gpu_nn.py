@@ -1,5 +1,6 @@
-"""Parity of the NN-layout FP8 GEMMs (dg_fp8_gemm_nn, dg_m_grouped_fp8_gemm_nn_contiguous:
-B stored [K, N]) against the oracle on the GPU.
+"""Parity of the FP8 GEMMs in the NN, TN and TT layouts (dg_fp8_gemm_nn,
+dg_m_grouped_fp8_gemm_nn_contiguous: B stored [K, N]; dg_fp8_gemm_tn / _tt: A stored [K, M])
+against the oracle on the GPU.
 
 Tolerance: the FP8 GEMM's bar, per element |D - ref| <= 8e-3 * max(|ref|, rms(ref)) and
 Frobenius 3e-3; padding rows bit-exact against the bf16 sentinel; an integer case whose
@@ -96,3 +97,58 @@ def test_nn_every_tile_shape(dg, kernel_id, monkeypatch):
     a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
     d = _run(dg, a, sfa, b, sfb, c)
     check_parity(d, R.fp8_gemm_nn(a, sfa, b, sfb, c), what=f"nn kernel {kernel_id}")
+
+
+
+def _run_t(dg, fn, a_km, sfa, b, sfb, c, N):
+    d = sentinel_like((a_km.shape[1], N))
+    fn(_dev(a_km), _dev(sfa), _dev(b), _dev(sfb), _dev(c), d)
+    torch.cuda.synchronize()
+    return bits(d)
+
+
+@pytest.mark.parametrize("b_kn", [True, False], ids=["tn", "tt"])
+@pytest.mark.parametrize("M,N,K,with_c,kernel_id", [
+    (16, 16, 128, False, None),
+    (144, 400, 1024, True, None),     # partial row and column tiles
+    (512, 1040, 1152, True, None),
+    (64, 2112, 7168, False, None),    # skinny: split along K
+    (272, 656, 1024, True, 0),        # each tile shape whose height is a multiple of 128
+    (272, 656, 1024, True, 1),
+    (272, 656, 1024, True, 2),
+])
+def test_tn_tt_dense_parity(dg, monkeypatch, b_kn, M, N, K, with_c, kernel_id):
+    if kernel_id is not None:
+        monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
+    g = synth.gen_dense_tn(M, N, K, seed=M + 5 * N + K + b_kn, with_c=with_c, b_kn=b_kn)
+    a, sfa, b, sfb, c = (None if g[k] is None else synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+    fn = dg.dg_fp8_gemm_tn if b_kn else dg.dg_fp8_gemm_tt
+    d = _run_t(dg, fn, a, sfa, b, sfb, c, N)
+    ref = (R.fp8_gemm_tn if b_kn else R.fp8_gemm_tt)(a, sfa, b, sfb, c)
+    check_parity(d, ref, what=f"{'tn' if b_kn else 'tt'} {M}x{N}x{K} kernel {kernel_id}")
+
+
+@pytest.mark.parametrize("b_kn", [True, False], ids=["tn", "tt"])
+def test_tn_tt_exact_integer_case_bit_exact(dg, b_kn):
+    M, N, K = 144, 400, 1024
+    rng = np.random.default_rng(31 + b_kn)
+    a, sfa, b, sfb, c, exact = make_exact_case(rng, M, N, K, True)
+    fn = dg.dg_fp8_gemm_tn if b_kn else dg.dg_fp8_gemm_tt
+    d = _run_t(dg, fn, np.ascontiguousarray(a.T), sfa, np.ascontiguousarray(b.T) if b_kn else b, sfb, c, N)
+    check_bit_exact(d, exact, f"{'tn' if b_kn else 'tt'} exact")
+
+
+def test_tn_dense_full_size_sampled(dg):
+    M, N, K = 4096, 7168, 7168
+    g = synth.gen_dense_tn(M, N, K, seed=808, backend="torch", device="cuda")
+    d = sentinel_like((M, N))
+    dg.dg_fp8_gemm_tn(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(80)
+    rows = np.repeat(rng.choice(M, 64, replace=False), 8)
+    cols = np.concatenate([rng.choice(N, 8, replace=False) for _ in range(64)])
+    sfa, sfb, c = (synth.to_numpy(g[k]) for k in ("sfa", "sfb", "c"))
+    a_mk = synth.to_numpy(g["a"].t().contiguous())
+    b_nk = synth.to_numpy(g["b"].t().contiguous())
+    want = R.fp8_gemm_nt_entries(a_mk, sfa, b_nk, sfb, c, rows, cols)
+    check_parity(bits(d)[rows, cols], want, what="tn full size sampled")

@@ -625,6 +625,25 @@ def test_nn_exact_rational_brute_force():
         assert abs(got[m, n] - float(want)) <= 1e-13 * max(1.0, abs(float(want)))
 
 
+@pytest.mark.parametrize("b_kn", [True, False])
+def test_tn_tt_exact_rational_brute_force(b_kn):
+    """A stored [k][m]; B stored [k][n] (TN) or [n][k] (TT); decoding and indexing here."""
+    rng = np.random.default_rng(23 + b_kn)
+    M, N, K = 3, 130, 256
+    a_km = rng.integers(0, 256, (K, M), dtype=np.uint8)
+    b = rng.integers(0, 256, (K, N) if b_kn else (N, K), dtype=np.uint8)
+    a_km[(a_km & 0x7F) == 0x7F] = 0x38
+    b[(b & 0x7F) == 0x7F] = 0x40
+    sfa = rng.uniform(0.5, 2.0, (K // 128, M)).astype(np.float32)
+    sfb = rng.uniform(0.5, 2.0, (2, K // 128)).astype(np.float32)
+    got = (R.fp8_gemm_tn if b_kn else R.fp8_gemm_tt)(a_km, sfa, b, sfb)
+    av, bv = _torch_e4m3(a_km), _torch_e4m3(b)
+    for m, n in [(0, 0), (1, 127), (2, 128), (0, 129), (2, 64)]:
+        want = sum(Fraction(float(av[k, m])) * Fraction(float(bv[k, n] if b_kn else bv[n, k])) *
+                   Fraction(float(sfa[k // 128, m])) * Fraction(float(sfb[n // 128, k // 128])) for k in range(K))
+        assert abs(got[m, n] - float(want)) <= 1e-13 * max(1.0, abs(float(want)))
+
+
 def test_nn_equals_nt_of_the_transposed_operand_and_grouped_forms():
     g = synth.gen_dense_nn(5, 144, 384, seed=8)
     a, sfa, b_kn, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
