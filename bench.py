@@ -21,6 +21,8 @@ Other workloads:
   --config 6  the config-1 dense sweep with packed UE8M0 scales (power-of-two,
               A per 1x128, B per 128x128), applied by the scaled matrix instruction
   --config 7  config 2 in the NN layout (each group's B stored [K, N])
+  --config 8  K-grouped GEMM in the TN layout: 8 groups from 32768 tokens (a
+              weight-gradient shape), (M,N) in {(4096,7168), (7168,2048)}
 
 Caches: one dense-sweep step touches more than 1 GB of distinct inputs and
 outputs, so no shape's operands survive in the 4 MB L2s or the 256 MB
@@ -60,7 +62,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--shape", type=str, default=None,
@@ -138,6 +140,25 @@ def items_contiguous(nn=False):
             gemm(g["a"], g["sfa"], g["b"], g["sfb"], g["m_indices"], d)
         items.append(dict(run=run, g=g, flops=2.0 * valid * N * K, bytes=nbytes,
                           label=f"G8_contig{'_nn' if nn else ''}_N{N}_K{K}",
+                          shape=(M, N, K)))
+    return items
+
+
+def items_kgrouped():
+    import torch
+    import synth
+    import fp4_gemm_dense_amd as dg
+    items = []
+    for j, (M, N) in enumerate(synth.GROUPED_NK):
+        g = synth.gen_kgrouped_tn(8, 32768, M, N, synth.seed_for(8, j), backend="torch", device="cuda")
+        K = g["K"]
+        d = torch.empty(8, M, N, dtype=torch.int16, device="cuda")
+        valid = sum(g["counts"])
+        nbytes = K * (M + N) + 4 * (K // 128) * (M + nb(N)) + 4 * 8 + 2 * 8 * M * N
+
+        def run(g=g, d=d):
+            dg.dg_k_grouped_fp8_gemm_tn_contiguous(g["a"], g["sfa"], g["b"], g["sfb"], g["ks"], d)
+        items.append(dict(run=run, g=g, flops=2.0 * valid * M * N, bytes=nbytes, label=f"G8_kgrouped_tn_M{M}_N{N}",
                           shape=(M, N, K)))
     return items
 
@@ -279,6 +300,27 @@ def _cpu_pass(config, items, budget_s, t_start, npass, t_total, flops, desc):
             flops += 2.0 * r * N * K
             if npass == 0:
                 desc.append(f"{r} rows of {it['label']}")
+        elif config == 8:
+            M, N, K = it["shape"]
+            ks = synth.to_numpy(g["ks"]).tolist()
+            rows = np.arange(16 * npass, 16 * npass + 16) % M
+            k0 = 0
+            for kg in ks:
+                if time.perf_counter() - t_start > budget_s:
+                    break
+                if kg > 0:
+                    b0, b1 = k0 // 128, (k0 + kg) // 128
+                    a = synth.to_numpy(g["a"][k0:k0 + kg][:, rows])
+                    sfa = synth.to_numpy(g["sfa"][b0:b1][:, rows])
+                    b = synth.to_numpy(g["b"][k0:k0 + kg])
+                    sfb = synth.to_numpy(g["sfb"][:, b0:b1])
+                    t0 = time.perf_counter()
+                    R.fp8_gemm_tn(a, sfa, b, sfb)
+                    t_total += time.perf_counter() - t0
+                    flops += 2.0 * len(rows) * N * kg
+                k0 += kg
+            if npass == 0:
+                desc.append(f"16 output rows of every group of {it['label']}")
         elif config == 5:
             M, N, K = it["shape"]
             mi = synth.to_numpy(g["m_indices"])
@@ -351,6 +393,8 @@ WORKLOADS = {
        "e4m3 1x128 / 128x128 fp32 scales",
     4: "FP8xFP4 expert FFN, 4096 tokens, hidden 7168, intermediate 2048, 32 local experts of 256, top-8, "
        "e4m3 activations (UE8M0/128), E2M1 weights (UE8M0/32)",
+    8: "K-grouped GEMM, TN layout (A [K,M], B [K,N], one D per group), 8 groups from 32768 tokens "
+       "(multinomial, padded to 128), (M,N){(4096,7168),(7168,2048)}, e4m3 1x128 / 128x128 fp32 scales",
     7: "M-grouped contiguous GEMM in the NN layout (B stored [K,N]), 8 groups from 32768 routed rows "
        "(multinomial, padded to 128), (N,K){(4096,7168),(7168,2048)}, e4m3 1x128 / 128x128 fp32 scales",
     6: "dense NT GEMM sweep, M{64,4096} x (N,K){(2112,7168),(24576,1536),(32768,512),(7168,16384),(4096,7168),"
@@ -392,6 +436,8 @@ def main():
         items = items_masked()
     elif cfg == 5:
         items = items_fp4_contiguous()
+    elif cfg == 8:
+        items = items_kgrouped()
     else:
         items = items_ffn()
     torch.cuda.synchronize()
@@ -445,6 +491,8 @@ def main():
         dom, kname, bound = items, f"fp8_gemm_kernel, contiguous grouped{', NN layout' if cfg == 7 else ''}", "mfma"
     elif cfg == 3:
         dom, kname, bound = items, "fp8_gemm_kernel, masked grouped", "hbm"
+    elif cfg == 8:
+        dom, kname, bound = items, "fp8_gemm_kernel, K-grouped TN layout", "mfma"
     elif cfg == 5:
         # the e2m1 x e4m3 matrix instruction runs at the e4m3 rate: FP8 peak
         dom, kname, bound = items, "ffn_gemm_kernel (FP8xFP4), contiguous grouped", "mfma"

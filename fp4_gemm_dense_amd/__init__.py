@@ -34,6 +34,7 @@ _SIGNATURES = {
     "dg_m_grouped_fp8_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "dg_fp8_gemm_nn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dg_fp8_gemm_tn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "dg_k_grouped_fp8_gemm_tn_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_fp8_gemm_tt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_gemm_nn_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_fp8_gemm_nt_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
@@ -221,6 +222,24 @@ def dg_fp8_gemm_tn(a, sfa, b, sfb, c, d):
 def dg_fp8_gemm_tt(a, sfa, b, sfb, c, d):
     """d = c + a^T b^T with a stored [K, M] and b stored [N, K] (TT layout)."""
     return _dense_layout("dg_fp8_gemm_tt", a, sfa, b, sfb, c, d, a_km=True, b_kn=False)
+
+
+def dg_k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d):
+    """d[g] = a[rows of g]^T . b[rows of g] with a stored [K, M], b [K, N], groups along K (ks on the device)."""
+    L = lib()
+    K, M = a.shape
+    N = b.shape[1]
+    G = ks.shape[0]
+    _req(a, _U8, (K, M), "a")
+    _req(sfa, torch.float32, (K // 128, M), "sfa")
+    _req(b, _U8, (K, N), "b")
+    _req(sfb, torch.float32, (_nb(N), K // 128), "sfb")
+    _req(ks, torch.int32, (G,), "ks")
+    _req_bf16(d, (G, M, N), "d")
+    _check("dg_k_grouped_fp8_gemm_tn_contiguous",
+           L.dg_k_grouped_fp8_gemm_tn_contiguous(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(ks), _ptr(d),
+                                                 M, N, K, G, _stream(a)))
+    return d
 
 
 def dg_m_grouped_fp8_gemm_nn_contiguous(a, sfa, b, sfb, m_indices, d):

@@ -115,7 +115,9 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
   if (!di.ok) return DG_ERR_NO_DEVICE;
   int cus = effective_cus(di);
   const int bm_multiple = (flags & MODE_AT) ? 128 : 0;   // A stored [K][M]: 128-row sub-tiles
-  GemmPlan plan = plan_fp8_gemm(p.m, p.n, p.k, p.num_groups, mode, cus, expected_m, bm_multiple);
+  // K-grouped: plan for a group's mean K
+  const int k_plan = mode == MODE_KGROUP ? std::max(128, p.k / p.num_groups / 128 * 128) : p.k;
+  GemmPlan plan = plan_fp8_gemm(p.m, p.n, k_plan, p.num_groups, mode, cus, expected_m, bm_multiple);
   if (plan.kernel_id < 0) return DG_ERR_UNSUPPORTED;
   // DG_FORCE_KERNEL=<id>: override the heuristic's tile choice (for tuning)
   if (const char* fk = std::getenv("DG_FORCE_KERNEL")) {
@@ -307,6 +309,32 @@ int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t* sfa, 
                                           int num_groups, int max_m, int n, int k, int expected_m,
                                           void* stream) {
   return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, stream, MODE_UE8M0);
+}
+
+int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                                        const int32_t* ks, uint16_t* d, int m, int n, int k, int num_groups,
+                                        void* stream) {
+  try {
+    if (!a || !sfa || !b || !sfb || !ks || !d) return DG_ERR_INVALID_ARG;
+    if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(sfa, 4) || !aligned(sfb, 4) ||
+        !aligned(ks, 4))
+      return DG_ERR_INVALID_ARG;
+    if (k % 128 != 0 || n % 16 != 0 || m % 16 != 0 || !operands_fit(m, n, k)) return DG_ERR_UNSUPPORTED;
+    if (num_groups > 65535) return DG_ERR_UNSUPPORTED;
+    const long long tiles = (long long)num_groups * ((m + 15) / 16) * ((n + 15) / 16);
+    if (tiles > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
+    DeviceInfo di = current_device_info();
+    if (!di.ok) return DG_ERR_NO_DEVICE;
+    Fp8GemmParams p{};
+    p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.ks = ks;
+    p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
+    const hipError_t e = launch_kgroup_zero(p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return DG_ERR_HIP;
+    return run_fp8_gemm(p, MODE_KGROUP, 0, stream, "k_grouped_fp8_gemm_tn_contiguous", MODE_AT | MODE_NN);
+  } catch (...) {
+    return DG_ERR_HIP;
+  }
 }
 
 int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }

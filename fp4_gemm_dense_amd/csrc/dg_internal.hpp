@@ -8,7 +8,8 @@
 
 namespace dg {
 
-enum GemmMode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2 };
+// MODE_KGROUP: groups along K (each group its own D), with A and B stored [K][..]
+enum GemmMode : int { MODE_DENSE = 0, MODE_CONTIG = 1, MODE_MASKED = 2, MODE_KGROUP = 3 };
 // Flag or-ed into a mode: A and B scales are packed UE8M0 words (four K blocks
 // per int32) instead of fp32, applied by the scaled matrix instruction.
 constexpr int MODE_UE8M0 = 4;
@@ -28,6 +29,7 @@ struct Fp8GemmParams {
   uint16_t* d;
   const int32_t* m_indices;   // contiguous only
   const int32_t* masked_m;    // masked only
+  const int32_t* ks;          // K-grouped only: K rows of each group (multiples of 128), on the device
   int m;                      // rows (dense / contiguous) or max_m (masked)
   int n, k;
   int num_groups;             // 1 for dense
@@ -143,6 +145,9 @@ __host__ __device__ inline void raster_tile(int tl, int tiles_m, int tiles_n, in
   *tm = first_m + r % gm;
   *tn = r / gm;
 }
+
+// K-grouped form: zeroes D of every group without K rows (before the GEMM).
+hipError_t launch_kgroup_zero(const Fp8GemmParams& p, hipStream_t stream);
 
 // Launches the kernel chosen by plan on stream; returns a hipError_t.
 hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mode, hipStream_t stream);

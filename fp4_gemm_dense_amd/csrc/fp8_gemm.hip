@@ -179,16 +179,27 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       g = mg;
       tl = t - mg_base;
       tiles_m = mg_cnt / p.tiles_n;
-    } else if (MODE == MODE_MASKED) {
+    } else if (MODE == MODE_MASKED || MODE == MODE_KGROUP) {
       const int per = p.tiles_m * p.tiles_n;
       g = t / per;
       tl = t - g * per;
+    }
+    if (MODE == MODE_KGROUP) {
+      // the group's K blocks: after those of the groups before it; counts are
+      // rounded down to whole blocks and cut at K (malformed device data stays in
+      // bounds).  A group without K rows has no tiles (its D is zeroed apart).
+      int kb_start = 0;
+      for (int h = 0; h < g; ++h) kb_start += max(p.ks[h], 0) >> 7;
+      const int nkb = kb_start < KB ? min(max(p.ks[g], 0) >> 7, KB - kb_start) : 0;
+      if (nkb == 0) return false;
+      tile.kb0 = kb_start;
+      tile.nkb = nkb;
     }
     int tm, tn;
     raster_tile(tl, tiles_m, p.tiles_n, p.group_m, &tm, &tn);
     tile.m0 = tm * BM;
     tile.n0 = tn * BN;
-    tile.rot = tile.part >= 0 ? 0 : (p.k_rot * ((tm + tn) & 7)) % KB;
+    tile.rot = (tile.part >= 0 || MODE == MODE_KGROUP) ? 0 : (p.k_rot * ((tm + tn) & 7)) % KB;
     tile.rows_valid = M;
     if (MODE == MODE_MASKED) {
       const int mm = p.masked_m[g];
@@ -230,7 +241,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       A += (size_t)tile.g * M * K;
       SA += (size_t)tile.g * sa_bytes;
     }
-    if (MODE != MODE_DENSE) B += (size_t)tile.g * N * K;
+    if (MODE == MODE_CONTIG || MODE == MODE_MASKED) B += (size_t)tile.g * N * K;   // (K-grouped: one B)
     rot = tile.rot;
     kb0_d = tile.kb0;
     nkb_d = tile.nkb;
@@ -281,7 +292,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     // B-scale element offsets from the kernel argument p.sfb, kept in SGPRs so the
     // per-K-block reads are scalar loads (which vmcnt does not count)
     const int sb_row = UE ? KW : KB;   // scale entries per 128-row block of B
-    const int sb_group = MODE != MODE_DENSE ? tile.g * NB * sb_row : 0;
+    const int sb_group = (MODE == MODE_CONTIG || MODE == MODE_MASKED) ? tile.g * NB * sb_row : 0;
     sb_idx = __builtin_amdgcn_readfirstlane(sb_group + (min(tile.n0 + wave_n * NT * 16, N - 1) >> 7) * sb_row);
   };
   auto issue = [&](int kb, uint32_t slot_off) {
@@ -597,7 +608,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     // Epilogue, part 2: exactly NST stores per wave; masked-off pieces go to an
     // out-of-range offset.
     const uint16_t* D = p.d;
-    if (MODE == MODE_MASKED) D += (size_t)done.g * M * N;
+    if (MODE == MODE_MASKED || MODE == MODE_KGROUP) D += (size_t)done.g * M * N;
     const v4i rsD = make_buffer_rsrc(D, (uint32_t)M * (uint32_t)N * 2u);
     const int grow0 = done.m0 + wave_m * MT * 16 + lrow;
     const int gcol0 = done.n0 + wave_n * NT * 16 + 4 * lgrp;
@@ -732,6 +743,28 @@ __global__ void __launch_bounds__(256) masked_splitk_reduce_kernel(const float* 
   }
 }
 
+// K-grouped form: the GEMM has no tiles for a group without K rows, whose D is
+// zero; this writes it (groups with K rows return at once).  Same rounding and
+// cut of the counts as the GEMM's decode.
+__global__ void __launch_bounds__(256) kgroup_zero_kernel(const int32_t* __restrict__ ks, uint16_t* d, int m, int n,
+                                                          int kb_total) {
+  const int g = blockIdx.y;
+  int kb_start = 0;
+  for (int h = 0; h < g; ++h) kb_start += max(ks[h], 0) >> 7;
+  const int nkb = kb_start < kb_total ? min(max(ks[g], 0) >> 7, kb_total - kb_start) : 0;
+  if (nkb > 0) return;
+  uint4* dg = reinterpret_cast<uint4*>(d + (size_t)g * m * n);
+  const size_t vecs = (size_t)m * n / 8;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < vecs; i += (size_t)gridDim.x * 256)
+    dg[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_kgroup_zero(const Fp8GemmParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(kgroup_zero_kernel, dim3(64, p.num_groups), dim3(256), 0, stream, p.ks, p.d, p.m, p.n,
+                     p.k / 128);
+  return hipGetLastError();
+}
+
 hipError_t launch_masked_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& plan, int slots, hipStream_t stream) {
   hipLaunchKernelGGL(masked_splitk_reduce_kernel, dim3(slots), dim3(256), 0, stream, p.ws, p.d, p.masked_m,
                      p.num_groups, p.m, p.n, p.k / 128, plan.block_m, plan.block_n, p.tiles_n, p.group_m, slots);
@@ -800,6 +833,7 @@ hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mod
     case MODE_CONTIG | MODE_NN: return launch_mode<MODE_CONTIG | MODE_NN>(p, id, g, stream);
     case MODE_DENSE | MODE_AT | MODE_NN: return launch_mode<MODE_DENSE | MODE_AT | MODE_NN>(p, id, g, stream);
     case MODE_DENSE | MODE_AT: return launch_mode<MODE_DENSE | MODE_AT>(p, id, g, stream);
+    case MODE_KGROUP | MODE_AT | MODE_NN: return launch_mode<MODE_KGROUP | MODE_AT | MODE_NN>(p, id, g, stream);
   }
   return hipErrorInvalidValue;
 }

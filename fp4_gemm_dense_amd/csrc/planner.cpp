@@ -39,13 +39,14 @@ GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num
   plan.block_n = tc.block_n;
   plan.tiles_m = cdiv(m, tc.block_m);
   plan.tiles_n = cdiv(n, tc.block_n);
-  long long total = (long long)plan.tiles_m * plan.tiles_n * (mode == MODE_MASKED ? num_groups : 1);
+  const bool per_group = mode == MODE_MASKED || mode == MODE_KGROUP;   // every group has its own tile grid
+  long long total = (long long)plan.tiles_m * plan.tiles_n * (per_group ? num_groups : 1);
   plan.num_tiles = (int)std::min<long long>(total, 0x7fffffff);
   long long slots = (long long)num_cus * blocks_per_cu_for(kernel_id);
   plan.splits = 1;
   plan.kb_per_split = k / 128;
   plan.full_tiles = plan.num_tiles;
-  if (mode != MODE_MASKED) {   // (the masked form's split is planned on the device)
+  if (!per_group) {   // (the masked form's split is planned on the device; K-grouped: no split)
     long long full = total;
     plan.splits = choose_splits(total, slots, k / 128, &full);
     plan.kb_per_split = cdiv(k / 128, plan.splits);
@@ -69,7 +70,7 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     if (bm_multiple > 0 && tc.block_m % bm_multiple != 0) continue;
     int tm = cdiv(rows, tc.block_m);
     int tn = cdiv(n, tc.block_n);
-    long long tiles = (long long)tm * tn * (mode == MODE_DENSE ? 1 : (mode == MODE_MASKED ? num_groups : 1));
+    long long tiles = (long long)tm * tn * (mode == MODE_MASKED || mode == MODE_KGROUP ? num_groups : 1);
     // useful fraction of the MFMA work (padding in M and N is wasted)
     double util = (double)rows / (tm * tc.block_m) * (double)n / (tn * tc.block_n);
     // wave quantisation: busy fraction of the workgroup slots over the call, in
@@ -78,7 +79,7 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     int slots = num_cus * blocks_per_cu_for(id);
     const int kb = k / 128;
     long long full = tiles;
-    const int splits = mode != MODE_MASKED ? choose_splits(tiles, slots, kb, &full) : 1;
+    const int splits = mode != MODE_MASKED && mode != MODE_KGROUP ? choose_splits(tiles, slots, kb, &full) : 1;
     const long long units = full + (tiles - full) * splits;
     double fill;
     if (splits > 1 && full > 0) {

@@ -282,6 +282,28 @@ int dg_m_grouped_fp8_fp4_gemm_nt_masked(const uint8_t* a, const int32_t* a_sf, c
                                         int num_groups, int max_m, int n, int k, int expected_m,
                                         void* stream);
 
+/*
+ * K-grouped GEMM in the TN layout, contiguous (usage guide
+ * "DeepGEMM：统一高性能张量核心 GEMM 计算库编译与使用指南", 分组 GEMM（MoE）: the
+ * K-axis grouped form of the training backward pass, e.g. each expert's weight
+ * gradient): the K rows (tokens) are split into consecutive groups and each group
+ * has its own output:
+ *   d[g][i][j] = bf16( sum over k in group g of A[k][i] * B[k][j] )
+ *   a    [k, m]            e4m3, m contiguous; sfa [k/128][m] fp32
+ *   b    [k, n]            e4m3, n contiguous; sfb [ceil(n/128)][k/128] fp32
+ *   ks   [num_groups]      int32 on the device: K rows of each group, multiples of
+ *                          128 (the contiguous layout pads each group to 128 rows;
+ *                          padding rows should hold zeros), in order; read only on
+ *                          the device.  Counts are rounded down to multiples of 128
+ *                          and cut at k.
+ *   d    [num_groups, m, n] bf16, every element written (0 for a group without rows)
+ * No C input.  Requirements: m % 16 == 0, n % 16 == 0, k % 128 == 0, m*k, n*k and
+ * 2*m*n at most 2^31, num_groups <= 65535 (else DG_ERR_UNSUPPORTED).
+ */
+int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                                        const int32_t* ks, uint16_t* d, int m, int n, int k, int num_groups,
+                                        void* stream);
+
 /* Row alignment of each group in the contiguous layout (usage guide, 工具函数). Returns 128. */
 int dg_get_mk_alignment_for_contiguous_layout(void);
 

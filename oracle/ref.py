@@ -154,6 +154,30 @@ def fp8_gemm_tt(a_km, sfa, b, sfb, c=None) -> np.ndarray:
     return ref
 
 
+def k_grouped_tn_contiguous(a_km, sfa, b_kn, sfb, ks) -> np.ndarray:
+    """K-grouped GEMM, TN layout, contiguous (usage guide, 分组 GEMM（MoE）: the K-axis grouped
+    form of the training backward pass).  Group g owns the next ks[g] K rows (a multiple
+    of 128); D[g] = sum over its rows of A[k, :]^T B[k, :], 0 for a group without rows.
+
+    a_km [K, M], sfa [K/128, M], b_kn [K, N], sfb [ceil(N/128), K/128]; returns float64 [G, M, N].
+    """
+    a_km = np.asarray(a_km)
+    b_kn = np.asarray(b_kn)
+    sfa = np.asarray(sfa)
+    sfb = np.asarray(sfb)
+    K, M = a_km.shape
+    N = b_kn.shape[1]
+    out = np.zeros((len(ks), M, N))
+    k0 = 0
+    for g, kg in enumerate(ks):
+        kg = int(kg)
+        if kg > 0:
+            b0, b1 = k0 // BLOCK_K, (k0 + kg) // BLOCK_K
+            out[g] = fp8_gemm_tn(a_km[k0:k0 + kg], sfa[b0:b1], b_kn[k0:k0 + kg], sfb[:, b0:b1])
+        k0 += kg
+    return out
+
+
 def m_grouped_nn_contiguous(a, sfa, b_kn, sfb, m_indices):
     """Contiguous M-grouped form with each group's B stored [K, N] (usage guide,
     分组 GEMM（MoE）: the NN contiguous form of the training backward pass).  Rows with

@@ -229,6 +229,26 @@ def gen_dense_tn(M, N, K, seed, with_c=True, b_kn=True, backend="numpy", device=
     return g
 
 
+def gen_kgrouped_tn(G, total_rows, M, N, seed, align=128, counts=None, backend="numpy", device="cpu"):
+    """K-grouped TN inputs: per-group token counts (multinomial unless given), each padded to
+    `align` rows of K; A [K, M] and B [K, N] hold N(0,1) values quantised per 1x128 along K
+    (A, per output row) and per 128x128 block (B); padding rows hold zeros."""
+    d = _Draw(seed, backend, device)
+    if counts is None:
+        counts = d.multinomial_counts(total_rows, G)
+    ks = [((c + align - 1) // align) * align for c in counts]
+    K = sum(ks)
+    pad = torch.ones(K, dtype=torch.bool, device=device)
+    k0 = 0
+    for c, kg in zip(counts, ks):
+        pad[k0:k0 + c] = False
+        k0 += kg
+    a_mk, sfa = quant_rows_1x128(torch.where(pad, 0.0, d.normal(M, K)))
+    b_nk, sfb = quant_blocks_128x128(torch.where(pad, 0.0, d.normal(N, K)))
+    return dict(a=a_mk.t().contiguous(), sfa=sfa, b=b_nk.t().contiguous(), sfb=sfb,
+                ks=torch.tensor(ks, dtype=torch.int32, device=device), counts=counts, K=K, M=M, N=N, G=G)
+
+
 def gen_contiguous_nn(G, total_rows, N, K, seed, align=128, counts=None, backend="numpy", device="cpu"):
     """gen_contiguous's inputs with each group's B stored [K, N]."""
     g = gen_contiguous(G, total_rows, N, K, seed, align=align, counts=counts, backend=backend, device=device)

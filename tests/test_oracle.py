@@ -644,6 +644,25 @@ def test_tn_tt_exact_rational_brute_force(b_kn):
         assert abs(got[m, n] - float(want)) <= 1e-13 * max(1.0, abs(float(want)))
 
 
+def test_k_grouped_tn_brute_force_and_empty_group():
+    """Each group's output is its own K rows only (exact rationals on sampled entries), an
+    empty group gives exact zeros, and the groups' sum is the TN GEMM over all rows."""
+    g = synth.gen_kgrouped_tn(3, 300, 32, 144, seed=4, counts=[100, 0, 200])
+    a, sfa, b, sfb = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb"))
+    ks = synth.to_numpy(g["ks"]).tolist()
+    assert ks == [128, 0, 256]
+    out = R.k_grouped_tn_contiguous(a, sfa, b, sfb, ks)
+    assert np.all(out[1] == 0)
+    av, bv = _torch_e4m3(a), _torch_e4m3(b)
+    for grp, (k0, k1) in ((0, (0, 128)), (2, (128, 384))):
+        for m, n in [(0, 0), (31, 129), (7, 64)]:
+            want = sum(Fraction(float(av[k, m])) * Fraction(float(bv[k, n])) * Fraction(float(sfa[k // 128, m])) *
+                       Fraction(float(sfb[n // 128, k // 128])) for k in range(k0, k1))
+            assert abs(out[grp, m, n] - float(want)) <= 1e-13 * max(1.0, abs(float(want)))
+    whole = R.fp8_gemm_tn(a, sfa, b, sfb)
+    assert np.allclose(out.sum(0), whole, rtol=1e-12, atol=1e-12 * np.abs(whole).max())
+
+
 def test_nn_equals_nt_of_the_transposed_operand_and_grouped_forms():
     g = synth.gen_dense_nn(5, 144, 384, seed=8)
     a, sfa, b_kn, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
