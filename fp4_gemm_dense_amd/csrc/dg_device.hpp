@@ -83,6 +83,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
 // addresses differ by a constant that fits an instruction offset).
 __device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 
+// Chunk swizzle of a K-row-major tile (an operand stored with K outermost) read
+// with the transposing loads: K row r holds its 16-byte chunk c at c ^ kt_swz(r).
+// It depends on r % 8 and bit 5 of r only, so rows r and r + 8i share it.
+__device__ __forceinline__ int kt_swz(int r) { return (r & 7) ^ ((r >> 5) & 1); }
+
 // Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1, in order: a loop
 // whose index is a compile-time constant in the body (register arrays indexed by
 // it stay in registers, and `if constexpr` can select per iteration).

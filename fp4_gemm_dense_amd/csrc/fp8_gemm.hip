@@ -116,11 +116,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // s % 2 of the block's 16 columns, so lane l receives K 32g + 8i .. +7 of
   // column l: read i gives bytes 8i .. 8i+7 of the lane's 32 K values (the A
   // fragment's K order).  In the slot, 16-byte chunk c of K row r sits at
-  // c ^ (r % 8); the 8 rows one read touches then fall on distinct banks.
+  // c ^ kt_swz(r): the 8 rows one lane group reads fall on distinct banks, and
+  // the rows of the neighbouring group (32 rows on) on the other positions of
+  // each half of the banks (measured: the plain r % 8 key left 2-way conflicts).
   // Column chunk q (16 columns) of the tile lies in sub-tile q / 8 at chunk q % 8.
   const uint32_t b_nn_row = A_BYTES + (32 * lgrp + (lrow >> 1)) * 128 + (lrow & 1) * 8;
   const uint32_t a_t_row = (32 * lgrp + (lrow >> 1)) * 128 + (lrow & 1) * 8;   // AT: the same for A
-  const int b_nn_sw = lrow >> 1;
+  const int b_nn_sw = kt_swz(32 * lgrp + (lrow >> 1));   // constant over the four reads (rows + 8i)
   const int dma_row = lane >> 3;              // DMA row inside an 8-row region
   const uint32_t a_dst = wave * RA * 1024;
   const uint32_t b_dst = A_BYTES + wave * RB * 1024;
@@ -258,7 +260,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       const int row = (wave * RA + j) * 8 + dma_row;
       if constexpr (AT) {   // as B in the NN layout: sub-tile row / 128, K row row % 128
         const int krow = row & 127;
-        const int col = tile.m0 + (row >> 7) * 128 + (((lane & 7) ^ (krow & 7)) << 4);
+        const int col = tile.m0 + (row >> 7) * 128 + (((lane & 7) ^ kt_swz(krow)) << 4);
         a_off[j] = col < tile.rows_valid ? (uint32_t)krow * (uint32_t)M + (uint32_t)col : kBufferOutOfRange;
       } else {
         a_off[j] = tile.m0 + row < tile.rows_valid
@@ -271,9 +273,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       const int row = (wave * RB + j) * 8 + dma_row;
       if constexpr (NN) {
         // region q = row / 8: column sub-tile q / 16, K rows 8 (q % 16) ..; position
-        // lane % 8 holds chunk (lane % 8) ^ (K row % 8) of the sub-tile's 128 columns
+        // lane % 8 holds chunk (lane % 8) ^ kt_swz(K row) of the sub-tile's 128 columns
         const int krow = row & 127;
-        const int col = tile.n0 + (row >> 7) * 128 + (((lane & 7) ^ (krow & 7)) << 4);
+        const int col = tile.n0 + (row >> 7) * 128 + (((lane & 7) ^ kt_swz(krow)) << 4);
         b_off[j] = col < N ? (uint32_t)krow * (uint32_t)N + (uint32_t)col : kBufferOutOfRange;
       } else {
         b_off[j] = tile.n0 + row < N ? (uint32_t)(tile.n0 + row) * (uint32_t)K + (((lane & 7) ^ swz(row)) << 4)
