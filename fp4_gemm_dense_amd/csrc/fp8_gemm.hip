@@ -23,8 +23,10 @@
 //     sa[row]*sb a few matrix instructions later, so the vector ALU never waits
 //     on the matrix core.
 //   * Epilogue: C is copied into the ring slots the last two K blocks leave
-//     free; the next tile's first loads are issued before this tile's stores,
-//     which then drain while the next tile computes.
+//     free.  The next tile's first stage is copied into the last block's slot
+//     while this tile waits for C (the ring's start moves from tile to tile),
+//     its other stages once C has been read, and this tile's stores follow
+//     them, draining while the next tile computes.
 //   * Persistent workgroups walk a group-M raster of tiles; block ids are
 //     remapped so that each XCD (workgroups are dealt round-robin to the 8
 //     XCDs) works on a contiguous stretch of the raster and shares its L2.
@@ -75,15 +77,19 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // Epilogue traffic.  The C tile (BM x BN bf16) is copied into two ring slots
   // that the last two K blocks leave free, in halves of BM/2 rows; each wave
   // copies CPW 1-KB pieces of a half.  A C row holds CPR 16-byte chunks, chunk c
-  // of row r sits at position c ^ (r % 16).  Every wave then issues exactly NST
-  // 8-byte stores of D.
+  // of row r sits at position c ^ (r % 16).  D is staged in the same place and
+  // layout, and every wave then issues exactly NSTD 16-byte stores of it (NPART
+  // 16-byte stores of fp32 partials for a split slice).
   constexpr int CPR = BN / 8;
   constexpr int C_HALF = BM / 2 * BN * 2;
   static_assert(CPR >= 16 && 1024 % (BN * 2) == 0, "C rows must be 256 or 512 bytes");
   static_assert(C_HALF % (NW * 1024) == 0 && C_HALF <= STAGE, "C halves must fit a slot");
   static_assert((BM / 2) % 16 == 0, "a 16-row block must not straddle the C halves");
   constexpr int CPW = C_HALF / (NW * 1024);
-  constexpr int NST = MT * NT;
+  constexpr int NSTD = BM * BN / 8 / (NW * 64);
+  static_assert((BM * BN / 8) % (NW * 64) == 0, "D chunks must split evenly over the lanes");
+  constexpr int NPART = MT * NT;
+  constexpr int NST = NSTD > NPART ? NSTD : NPART;
   static_assert((STAGES - 2) * LPS + NST + CPW < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -350,38 +356,42 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   // Waits until stage kb of the ring has landed.  Operations of one wave retire
   // in issue order (loads and stores alike), so stage kb is complete once no
   // more remain than were issued after it: the stages kb+1.. already in flight,
-  // the previous tile's NST stores while kb was a prologue stage, and the first
-  // C half before the last block.
-  auto wait_stage = [&](int kb, int KT, bool stores_after) {
+  // the previous tile's stores while kb was a prologue stage (stores_after: 0
+  // none, 1 its NSTD stores of D, 2 its NPART stores of a split partial), and
+  // the first C half before the last block.
+  auto wait_stage = [&](int kb, int KT, int stores_after) {
     const int after = min(STAGES - 2, KT - 1 - kb);
-    const bool st = stores_after && kb <= STAGES - 2;
+    const int st = kb <= STAGES - 2 ? stores_after : 0;
     const bool ch = STAGES >= 3 && has_c && KT >= 2 && kb == KT - 1;
-    if (STAGES >= 4 && after == 2) {
-      if (st) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS + NST>();
-      else wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LPS>();
-    } else if (after == 1) {
-      if (st) wait_vmcnt<LPS + NST>();
-      else wait_vmcnt<LPS>();
-    } else {
-      if (st && ch) wait_vmcnt<NST + CPW>();
-      else if (st) wait_vmcnt<NST>();
-      else if (ch) wait_vmcnt<CPW>();
-      else wait_vmcnt<0>();
-    }
+    auto wait_plus = [&](auto loads_tag) {   // loads_tag: memory loads issued after stage kb
+      constexpr int L = decltype(loads_tag)::value;
+      if (st == 1) wait_vmcnt<L + NSTD>();
+      else if (st == 2) wait_vmcnt<L + NPART>();
+      else wait_vmcnt<L>();
+    };
+    if (STAGES >= 4 && after == 2) wait_plus(std::integral_constant<int, (STAGES >= 4 ? 2 : 0) * LPS>{});
+    else if (after == 1) wait_plus(std::integral_constant<int, LPS>{});
+    else if (ch) wait_plus(std::integral_constant<int, CPW>{});
+    else wait_plus(std::integral_constant<int, 0>{});
   };
-  auto prologue = [&]() {
+  // Stage s of a tile lives in ring slot (s0 + s) % STAGES; s0 moves from tile
+  // to tile (the next tile starts in the slot of this tile's last K block).
+  int s0 = 0;
+  auto slot_of = [&](int i) -> uint32_t { return (uint32_t)(i % STAGES) * (uint32_t)STAGE; };
+  // copies of stages [from, to) of the tile set up last
+  auto prologue = [&](int from, int to) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nkb_d) issue(s, s * STAGE);
+      if (s >= from && s < to && s < nkb_d) issue(s, slot_of(s0 + s));
   };
 
   int t = vb;
   Tile cur;
-  bool stores_after = false;   // the previous tile's stores were issued after this tile's prologue
+  int stores_after = 0;   // the previous tile's stores issued after this tile's prologue (see wait_stage)
   bool have = next_tile(t, cur);
   if (have) {
     setup(cur);
-    prologue();
+    prologue(0, STAGES - 1);
   }
   while (have) {
     has_c = dense_c && cur.part < 0;
@@ -397,8 +407,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
 
     const int KT = cur.nkb;                        // K blocks of this work unit
     const int kb0 = cur.kb0;
-    uint32_t rd_slot = 0;                          // slot of stage kb
-    uint32_t wr_slot = (STAGES - 1) * STAGE;       // slot of stage kb + STAGES - 1
+    uint32_t rd_slot = slot_of(s0);                // slot of stage kb
+    uint32_t wr_slot = slot_of(s0 + STAGES - 1);   // slot of stage kb + STAGES - 1
     // One K block.  STEADY: a later stage is copied in this block, its copy
     // instructions spread between the matrix instructions (a copy that finds
     // the memory pipeline full then stalls the wave while matrix work is
@@ -418,12 +428,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
           for (int idx = 0; idx < ILV; ++idx) issue_ab(idx, kb + STAGES - 1, wr_slot);
         }
       } else if (has_c) {
-        // slot (KT + h) % STAGES takes half h: free from block KT - 2 + h on
+        // slot (s0 + KT + h) % STAGES takes half h: free from block KT - 2 + h on
         if (kb == KT - 1) {
-          if (KT == 1) issue_c(cur, 0, (uint32_t)(KT % STAGES) * STAGE);
-          issue_c(cur, 1, (uint32_t)((KT + 1) % STAGES) * STAGE);
+          if (KT == 1) issue_c(cur, 0, slot_of(s0 + KT));
+          issue_c(cur, 1, slot_of(s0 + KT + 1));
         } else if (kb == KT - 2) {
-          issue_c(cur, 0, (uint32_t)(KT % STAGES) * STAGE);
+          issue_c(cur, 0, slot_of(s0 + KT));
         }
       }
 
@@ -544,39 +554,59 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
           acc[MT - 1][NT - LAG + j][i] = fmaf(part[(NBLK - LAG + j) % LAG][i], sprev, acc[MT - 1][NT - LAG + j][i]);
     }
     const Tile done = cur;
+    const int c_base = s0 + KT;   // C half h sits in slot (c_base + h) % STAGES
 
-    // Epilogue, part 1: D = acc (+ C) rounded to bf16, still in registers.  Lane
-    // (lgrp, lrow) holds, for block (mt, nt), row mt*16 + lrow and the four
-    // columns nt*16 + 4*lgrp .. +3 of the wave's sub-tile: 8 bytes of one row.
-    v2i o[MT][NT];
+    // The next tile's loads start before this tile's epilogue.  Once every wave
+    // has read the last K block, the ring is free but for the two C slots: the
+    // next tile's stage 0 goes into the last block's slot and lands while this
+    // tile waits for C; its later stages follow once C has been read.  Without
+    // C they all go at once.
+    t += G;
+    have = next_tile(t, cur);
+    wait_lgkmcnt0();
+    block_barrier();   // every wave is done with the last K block
+    const bool whole = done.part < 0;   // D is staged in the C slots (a split slice stores its partial)
+    if (have) {
+      setup(cur);
+      s0 = __builtin_amdgcn_readfirstlane((c_base + STAGES - 1) % STAGES);
+      prologue(0, whole ? 1 : STAGES - 1);
+    }
+
+    // Epilogue, part 1: D = acc (+ C) rounded to bf16, written over C in LDS.
+    // Lane (lgrp, lrow) holds, for block (mt, nt), row mt*16 + lrow and the four
+    // columns nt*16 + 4*lgrp .. +3 of the wave's sub-tile: 8 bytes of one row,
+    // at the place of the same 8 bytes of C.
     if (has_c) {
-      wait_vmcnt<0>();   // this wave's C pieces have landed
+      // this wave's C pieces have landed: only the next tile's stage 0 (LPS
+      // copies, every tile has at least one K block) was issued after them
+      if (have) wait_vmcnt<LPS>();
+      else wait_vmcnt<0>();
       block_barrier();   // ... and every other wave's
     }
     // (a split tile's slice stores its fp32 partial instead, below)
 #pragma unroll
-    for (int mt = 0; mt < (done.part >= 0 ? 0 : MT); ++mt) {
+    for (int mt = 0; mt < (whole ? MT : 0); ++mt) {
       const int rr0 = wave_m * MT * 16 + mt * 16;       // first tile row of the block
       const int h = rr0 >= BM / 2 ? 1 : 0;
-      const uint32_t c_row = (uint32_t)((KT + h) % STAGES) * STAGE + (uint32_t)(rr0 - h * (BM / 2) + lrow) * (BN * 2) +
+      const uint32_t c_row = slot_of(c_base + h) + (uint32_t)(rr0 - h * (BM / 2) + lrow) * (BN * 2) +
                              (uint32_t)((lgrp & 1) << 3);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const v4f v = acc[mt][nt];
         float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+        const int c = (wave_n * NT * 16 + nt * 16 + 4 * lgrp) >> 3;   // chunk; tile row % 16 is lrow
+        uint2* const cd = reinterpret_cast<uint2*>(smem + c_row + ((c ^ lrow) << 4));
         if (has_c) {
-          const int c = (wave_n * NT * 16 + nt * 16 + 4 * lgrp) >> 3;   // C chunk; tile row % 16 is lrow
-          const uint2 cv = *reinterpret_cast<const uint2*>(smem + c_row + ((c ^ lrow) << 4));
+          const uint2 cv = *cd;
           v0 += __uint_as_float(cv.x << 16);
           v1 += __uint_as_float(cv.x & 0xffff0000u);
           v2 += __uint_as_float(cv.y << 16);
           v3 += __uint_as_float(cv.y & 0xffff0000u);
         }
-        o[mt][nt].x = (int)pack_bf16x2_rne(v0, v1);
-        o[mt][nt].y = (int)pack_bf16x2_rne(v2, v3);
+        *cd = make_uint2(pack_bf16x2_rne(v0, v1), pack_bf16x2_rne(v2, v3));
       }
     }
-    if (done.part >= 0) {
+    if (!whole) {
       // split K: this slice's fp32 partial tile (BM x BN, row-major) goes to
       // workspace tile `part`, 4 consecutive columns = 16 bytes per lane and
       // block.  Rows and columns beyond D are stored too and never read.
@@ -592,40 +622,40 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
         }
       }
     }
+    // This tile's stores (D, or a split slice's fp32 partial) follow the next
+    // tile's prologue and drain while it computes its first blocks.
+    stores_after = whole ? 1 : 2;
+    if (!whole) continue;
+
+    // Epilogue, part 2: the staged D, read back as whole rows (16-byte chunk c
+    // of tile row rr by one lane; CPR lanes cover a row), then the rest of the
+    // next tile's prologue into the freed slots, then exactly NSTD 16-byte
+    // stores per wave; masked-off chunks go to an out-of-range offset.
     wait_lgkmcnt0();
-    block_barrier();   // every wave is done with the LDS ring (and C)
-
-    // Start the next tile's loads before this tile's stores: the stores then
-    // drain while the next tile computes its first blocks.
-    t += G;
-    have = next_tile(t, cur);
-    if (have) {
-      setup(cur);
-      prologue();
+    block_barrier();   // D staged by every wave
+    v4i dv[NSTD];
+#pragma unroll
+    for (int j = 0; j < NSTD; ++j) {
+      const int idx = (j * NW + wave) * 64 + lane;
+      const int rr = idx / CPR, c = idx % CPR;
+      const int h = rr >= BM / 2 ? 1 : 0;
+      dv[j] = *reinterpret_cast<const v4i*>(smem + slot_of(c_base + h) + (uint32_t)(rr - h * (BM / 2)) * (BN * 2) +
+                                            (uint32_t)((c ^ (rr & 15)) << 4));
     }
-    // (split K: the partial stores precede the next tile's loads)
-    stores_after = done.part < 0;
-    if (done.part >= 0) continue;
-
-    // Epilogue, part 2: exactly NST stores per wave; masked-off pieces go to an
-    // out-of-range offset.
+    wait_lgkmcnt0();
+    block_barrier();   // every wave has read D: the C slots are free
+    if (have) prologue(1, STAGES - 1);
     const uint16_t* D = p.d;
     if (MODE == MODE_MASKED || MODE == MODE_KGROUP) D += (size_t)done.g * M * N;
     const v4i rsD = make_buffer_rsrc(D, (uint32_t)M * (uint32_t)N * 2u);
-    const int grow0 = done.m0 + wave_m * MT * 16 + lrow;
-    const int gcol0 = done.n0 + wave_n * NT * 16 + 4 * lgrp;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int grow = grow0 + mt * 16;
-      bool row_ok = grow < done.rows_valid;
-      if (MODE == MODE_CONTIG) row_ok = row_ok && p.m_indices[min(grow, M - 1)] == done.g;
-      const uint32_t row_off = ((uint32_t)grow * (uint32_t)N + (uint32_t)gcol0) * 2u;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const bool ok = row_ok && done.n0 + wave_n * NT * 16 + nt * 16 < N;
-        const uint32_t off = ok ? row_off + nt * 32 : kBufferOutOfRange;
-        dg_raw_buffer_store_v2i32(o[mt][nt], rsD, (int)off, 0, 0);
-      }
+    for (int j = 0; j < NSTD; ++j) {
+      const int idx = (j * NW + wave) * 64 + lane;
+      const int grow = done.m0 + idx / CPR, gcol = done.n0 + (idx % CPR) * 8;
+      bool ok = grow < done.rows_valid && gcol < N;
+      if (MODE == MODE_CONTIG) ok = ok && p.m_indices[min(grow, M - 1)] == done.g;
+      const uint32_t off = ok ? ((uint32_t)grow * (uint32_t)N + (uint32_t)gcol) * 2u : kBufferOutOfRange;
+      dg_raw_buffer_store_v4i32(dv[j], rsD, (int)off, 0, 0);
     }
   }
 }
