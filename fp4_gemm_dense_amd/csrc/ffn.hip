@@ -103,11 +103,24 @@ __global__ void __launch_bounds__(1024) ffn_route_kernel(FfnParams p) {
   __shared__ int cur[FFN_MAX_EXPERTS];
   const int tid = threadIdx.x;
   const int total = p.T * p.k;
-  for (int e = tid; e < p.E; e += blockDim.x) cnt[e] = 0;
+  const int nt = blockDim.x;
+  // The entries are read RU per thread at a time, all loads issued before any
+  // is used (one workgroup: the loop is bound by load latency, not bandwidth).
+  constexpr int RU = 16;
+  for (int e = tid; e < p.E; e += nt) cnt[e] = 0;
   __syncthreads();
-  for (int i = tid; i < total; i += blockDim.x) {
-    const int e = p.topk_idx[i] - p.offset;
-    if (e >= 0 && e < p.E) atomicAdd(&cnt[e], 1);
+  for (int base = 0; base < total; base += RU * nt) {
+    int ev[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int i = base + u * nt + tid;
+      ev[u] = i < total ? p.topk_idx[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int e = ev[u] - p.offset;
+      if (base + u * nt + tid < total && e >= 0 && e < p.E) atomicAdd(&cnt[e], 1);
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -123,14 +136,25 @@ __global__ void __launch_bounds__(1024) ffn_route_kernel(FfnParams p) {
   __syncthreads();
   // The order of pairs inside an expert does not affect any result: each pair's
   // output row depends only on its token, and the combine sums slots in order.
-  for (int i = tid; i < total; i += blockDim.x) {
-    const int e = p.topk_idx[i] - p.offset;
-    int pr = -1;
-    if (e >= 0 && e < p.E) {
-      pr = atomicAdd(&cur[e], 1);
-      p.pair_token[pr] = i / p.k;
+  for (int base = 0; base < total; base += RU * nt) {
+    int ev[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int i = base + u * nt + tid;
+      ev[u] = i < total ? p.topk_idx[i] : 0;
     }
-    p.pair_of[i] = pr;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int i = base + u * nt + tid;
+      if (i >= total) continue;
+      const int e = ev[u] - p.offset;
+      int pr = -1;
+      if (e >= 0 && e < p.E) {
+        pr = atomicAdd(&cur[e], 1);
+        p.pair_token[pr] = i / p.k;
+      }
+      p.pair_of[i] = pr;
+    }
   }
 }
 
