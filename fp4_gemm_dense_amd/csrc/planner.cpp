@@ -97,8 +97,10 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     // 4-slot 64x128 shape beats the 3-slot ones at M = 64 and 128)
     if (splits > 1 && full == 0) intensity = tc.stages;
     double score = util * fill * intensity;
-    // short K loops are bound by the epilogue: wide tiles write longer rows of D
-    if (k <= 1024 && tc.block_n > tc.block_m) score *= 1.05;
+    // wide tiles store longer rows of D (512 bytes): measured 2-7 % faster than
+    // the tall tile of the same area up to K = 8192 (the shorter the K loop, the
+    // more the epilogue weighs), and about 1 % slower at K = 16384
+    if (k <= 8192 && tc.block_n > tc.block_m) score *= 1.05;
     if (score > best_score + 1e-9) {
       best_score = score;
       best_id = id;
