@@ -172,10 +172,10 @@ def test_planner_splits_only_the_last_partial_round(m, n, k):
 
 
 def test_planner_split_tail_with_a_cu_cap():
-    # the same rule on a capped part: 40 tiles of 256 x 128 on 32 CUs leave a
-    # remainder of 8, split 4 ways over K = 128 * 32
+    # the same rule on a capped part: 40 tiles (256 x 128 or 128 x 256) on 32
+    # CUs leave a remainder of 8, split 4 ways over K = 128 * 32
     p = dgm.dg_query_plan(1280, 1024, 128 * 32, 1, 32)
-    if p["block_m"] == 256 and p["block_n"] == 128:
+    if p["block_m"] * p["block_n"] == 256 * 128:
         assert p["full_tiles"] == 32 and p["splits"] == 4
     assert p["full_tiles"] % 32 == 0 or p["full_tiles"] == p["num_tiles"]
 

@@ -139,9 +139,9 @@ def test_split_tail_exact_integer_case_bit_exact(dg):
 
 
 def test_split_tail_full_size_sampled_rows(dg):
-    """4096 x 2112 x 7168 on the whole chip: 272 tiles of 256 x 128, of which 256
-    run whole and 16 (in the lower half of the rows, last two tile columns) are
-    split.  Sampled rows from both halves are checked against the oracle."""
+    """4096 x 2112 x 7168 on the whole chip: 288 tiles of 128 x 256, of which 256
+    run whole and 32 (the last rows of the raster) are split.  Sampled rows from
+    both halves are checked against the oracle."""
     M, N, K = 4096, 2112, 7168
     ncu = dgm.dg_get_num_cus()
     p = dgm.dg_query_plan(M, N, K, 1, ncu)
@@ -209,9 +209,9 @@ def _masked_device_plan(mm, max_m, N, K, cus):
 
 @pytest.mark.parametrize("mm,max_m,N,K,cus", [
     ([256, 200, 3, 0], 256, 512, 128 * 48, 8),       # a partial last round, split
-    ([256, 200, 3, 0], 256, 512, 128 * 40, 10),
+    ([256, 200, 3, 0], 256, 512, 128 * 40, 9),
     ([256, 3, 0], 256, 256, 128 * 32, 32),            # too few tiles to fill 32 CUs: every tile split
-    ([100, 0, 256, 130, 7, 255], 256, 784, 128 * 40, 16),
+    ([100, 0, 256, 130, 7, 255], 256, 784, 128 * 40, 10),
     ([0, 0, 0], 128, 256, 128 * 32, 8),               # no valid rows at all
 ])
 def test_masked_device_split_parity(dg, mm, max_m, N, K, cus):
