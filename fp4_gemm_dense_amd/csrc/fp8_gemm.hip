@@ -237,6 +237,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   typedef const __attribute__((address_space(4))) uint32_t cword;
   cword* const SBw = (cword*)(uintptr_t)p.sfb;      // the same, packed UE8M0 words
   uint32_t a_off[RA], b_off[RB], sa_off = 0;
+  // contiguous form: group index of the row of each of the lane's D stores,
+  // loaded when the tile is set up and compared after its K loop, when no load
+  // is outstanding any more (a later first use would wait for the next tile's
+  // copies, issued after these loads)
+  int midx[NSTD];
   int rot = 0, kb0_d = 0, nkb_d = 1;   // K range and rotation of the tile whose loads are issued
   int sb_idx = 0;
   auto setup = [&](const Tile& tile) {
@@ -302,6 +307,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     const int sb_row = UE ? KW : KB;   // scale entries per 128-row block of B
     const int sb_group = (MODE == MODE_CONTIG || MODE == MODE_MASKED) ? tile.g * NB * sb_row : 0;
     sb_idx = __builtin_amdgcn_readfirstlane(sb_group + (min(tile.n0 + wave_n * NT * 16, N - 1) >> 7) * sb_row);
+    if constexpr (MODE == MODE_CONTIG) {
+#pragma unroll
+      for (int j = 0; j < NSTD; ++j) midx[j] = p.m_indices[min(tile.m0 + ((j * NW + wave) * 64 + lane) / CPR, M - 1)];
+    }
   };
   auto issue = [&](int kb, uint32_t slot_off) {
     const int kp = __builtin_amdgcn_readfirstlane(kb0_d + (kb + rot < nkb_d ? kb + rot : kb + rot - nkb_d));   // K block in memory
@@ -561,6 +570,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     // next tile's stage 0 goes into the last block's slot and lands while this
     // tile waits for C; its later stages follow once C has been read.  Without
     // C they all go at once.
+    uint32_t grp_ok = ~0u;   // contiguous form: bit j, the row of store j is in the tile's group
+    if constexpr (MODE == MODE_CONTIG) {
+      grp_ok = 0;
+#pragma unroll
+      for (int j = 0; j < NSTD; ++j) grp_ok |= (midx[j] == done.g ? 1u : 0u) << j;
+    }
     t += G;
     have = next_tile(t, cur);
     wait_lgkmcnt0();
@@ -652,8 +667,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
     for (int j = 0; j < NSTD; ++j) {
       const int idx = (j * NW + wave) * 64 + lane;
       const int grow = done.m0 + idx / CPR, gcol = done.n0 + (idx % CPR) * 8;
-      bool ok = grow < done.rows_valid && gcol < N;
-      if (MODE == MODE_CONTIG) ok = ok && p.m_indices[min(grow, M - 1)] == done.g;
+      const bool ok = grow < done.rows_valid && gcol < N && ((grp_ok >> j) & 1u);
       const uint32_t off = ok ? ((uint32_t)grow * (uint32_t)N + (uint32_t)gcol) * 2u : kBufferOutOfRange;
       dg_raw_buffer_store_v4i32(dv[j], rsD, (int)off, 0, 0);
     }
