@@ -674,6 +674,34 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
   }
 }
 
+// split K: 8 consecutive fp32 columns of one row summed over the slices in
+// slice order (slice s at w + s * stride4 float4s).  The loads of four slices
+// are issued before any is added: one load at a time left the reduce bound by
+// memory latency.
+__device__ __forceinline__ void sum_slices(const float4* w, int splits, size_t stride4, float4& lo, float4& hi) {
+  lo = w[0];
+  hi = w[1];
+  int s = 1;
+  for (; s + 4 <= splits; s += 4) {
+    float4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = w[(s + u) * stride4];
+      b[u] = w[(s + u) * stride4 + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lo.x += a[u].x; lo.y += a[u].y; lo.z += a[u].z; lo.w += a[u].w;
+      hi.x += b[u].x; hi.y += b[u].y; hi.z += b[u].z; hi.w += b[u].w;
+    }
+  }
+  for (; s < splits; ++s) {
+    const float4 a = w[s * stride4], b = w[s * stride4 + 1];
+    lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+    hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // split K: for every split tile, the sum of its slices' fp32 partials (in slice
 // order), plus C, rounded to bf16
@@ -704,13 +732,8 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
       if (g < 0 || g >= groups || m_indices[row] != g) continue;
     }
     const float4* w = reinterpret_cast<const float4*>(ws + (size_t)st * splits * tile_elems + (size_t)r * bn + c8 * 8);
-    float4 lo = w[0], hi = w[1];
-    for (int s = 1; s < splits; ++s) {
-      const float4* ws_s = w + s * (tile_elems / 4);
-      const float4 a = ws_s[0], b = ws_s[1];
-      lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
-      hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
-    }
+    float4 lo, hi;
+    sum_slices(w, splits, tile_elems / 4, lo, hi);
     float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     const size_t o8 = ((size_t)row * n + col) / 8;   // n % 16 == 0: 16-byte aligned
     if (c) {
@@ -775,13 +798,8 @@ __global__ void __launch_bounds__(256) masked_splitk_reduce_kernel(const float* 
     const int row = tm * bm + r, col = tn * bn + c8 * 8;
     if (r >= bm || row >= mm || col >= n) continue;
     const float4* w = reinterpret_cast<const float4*>(ws + (size_t)st * splits * tile_elems + (size_t)r * bn + c8 * 8);
-    float4 lo = w[0], hi = w[1];
-    for (int sl = 1; sl < splits; ++sl) {
-      const float4* ws_s = w + sl * (tile_elems / 4);
-      const float4 a = ws_s[0], b = ws_s[1];
-      lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
-      hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
-    }
+    float4 lo, hi;
+    sum_slices(w, splits, tile_elems / 4, lo, hi);
     const uint4 o = {pack_bf16x2_rne(lo.x, lo.y), pack_bf16x2_rne(lo.z, lo.w), pack_bf16x2_rne(hi.x, hi.y),
                      pack_bf16x2_rne(hi.z, hi.w)};
     uint16_t* dg = d + (size_t)mg * max_m * n;
