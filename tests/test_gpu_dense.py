@@ -79,6 +79,29 @@ def test_dense_identity_b_and_all_ones(dg):
     assert np.all(F.bf16_bits_to_f64(d) == K * 0.5 * 0.25 + 3.0)
 
 
+@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3])
+@pytest.mark.parametrize("K", [128, 256, 384, 640])
+def test_dense_many_tiles_per_workgroup_bit_exact(dg, monkeypatch, kernel_id, K):
+    """Three workgroups walk every tile in turn, so each runs many tiles back to
+    back with C.  A tile starts its LDS ring in the slot of the previous tile's
+    last K block and stages D over C in LDS; one to five K blocks per tile cover
+    every step of the ring start (K blocks - 1 modulo the slot count).  Exact
+    integer inputs: the result is unique."""
+    import fp4_gemm_dense_amd as dgm
+    rng = np.random.default_rng(kernel_id * 10 + K)
+    M, N = 520, 784                     # ragged in both dimensions for every tile shape
+    a, sfa, b, sfb, c, exact = make_exact_case(rng, M, N, K, True)
+    monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
+    dgm.dg_set_num_cus(3)
+    try:
+        p = dgm.dg_query_plan(M, N, K, 1, 3)
+        assert p["splits"] == 1
+        got = _run(dg, a, sfa, b, sfb, c)
+    finally:
+        dgm.dg_set_num_cus(0)
+    check_bit_exact(got, exact, f"many tiles per workgroup, kernel {kernel_id}, K={K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (17, 144, 384), (64, 528, 1024), (130, 2112, 256),
                                    (300, 400, 640), (513, 1040, 384)])
 def test_dense_random_parity(dg, M, N, K):

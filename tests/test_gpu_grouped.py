@@ -81,6 +81,25 @@ def test_contiguous_exact_integer_groups_bit_exact(dg):
     check_bit_exact(d[written], ref[written], "contig exact")
 
 
+@pytest.mark.parametrize("kernel_id", [1, 2, 3])
+def test_contiguous_many_tiles_per_workgroup(dg, monkeypatch, kernel_id):
+    """Two workgroups walk every tile in turn (short K, so many tiles each): the
+    rows' group indices are loaded when a tile is set up and tested after its K
+    loop, while the next tile's copies are already in flight."""
+    import fp4_gemm_dense_amd as dgm
+    counts = [100, 0, 200, 7, 129]
+    g = synth.gen_contiguous(len(counts), sum(counts), 400, 256, seed=77 + kernel_id, counts=counts)
+    a, sfa, b, sfb, mi = _np(g, "a", "sfa", "b", "sfb", "m_indices")
+    monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
+    dgm.dg_set_num_cus(2)
+    try:
+        d = _run_contig(dg, a, sfa, b, sfb, mi)
+    finally:
+        dgm.dg_set_num_cus(0)
+    ref, written = R.m_grouped_contiguous(a, sfa, b, sfb, mi)
+    _check_contig(d, ref, written, f"contig many tiles per workgroup, kernel {kernel_id}")
+
+
 def test_contiguous_malformed_indices_are_skipped(dg):
     g = synth.gen_contiguous(3, 256, 144, 256, seed=9, counts=[128, 64, 64])
     a, sfa, b, sfb, mi = _np(g, "a", "sfa", "b", "sfb", "m_indices")
