@@ -75,7 +75,8 @@ def parse():
 def kernel_source_hash(cfg):
     """Hash of the sources that decide the kernels (and their plans) a config runs."""
     h = hashlib.sha256()
-    files = ("ffn.hip", "dg_device.hpp") if cfg in (4, 5) else ("fp8_gemm.hip", "planner.cpp", "dg_device.hpp")
+    files = (("ffn.hip", "dg_device.hpp", "dg_internal.hpp") if cfg in (4, 5)
+             else ("fp8_gemm.hip", "planner.cpp", "api.cpp", "dg_device.hpp", "dg_internal.hpp"))
     for f in files:
         p = os.path.join(ROOT, "fp4_gemm_dense_amd", "csrc", f)
         if os.path.exists(p):
