@@ -375,7 +375,7 @@ def requant_e4m3_pow2(s32) -> tuple:
 
 
 def expert_ffn(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, expert_offset,
-               num_local_experts, return_intermediate=False, codes_override=None):
+               num_local_experts, return_intermediate=False):
     """Single-GPU share of the fused FP8xFP4 MoE layer.
 
     News page on the update ("Mega MoE：把整个 MoE 层融成一个核函数"): per expert,
@@ -397,13 +397,6 @@ def expert_ffn(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, expert_offset,
     Returns (y_ref float64 [T, H], info dict).  info holds, per local expert,
     the pair list (token, slot) and, when ``return_intermediate`` is set, the
     intermediate codes/exponents and the float32 SwiGLU values they round.
-
-    ``codes_override`` ({expert: (codes, exponents)} in the expert's pair order)
-    replaces steps 2-5 with given intermediate codes: the rest of the pipeline
-    (linear2 and the weighted sum) is then evaluated on them.  A requantised
-    code is a rounding decision; where two fp32 evaluations of the same value
-    straddle a rounding midpoint, both codes are valid, and this lets a caller
-    evaluate the remainder of the pipeline on either.
     """
     x = np.asarray(x)
     T, H = x.shape
@@ -423,19 +416,15 @@ def expert_ffn(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, expert_offset,
                 info["exps"].append(np.zeros((0, I // 128), np.int64))
                 info["s32"].append(np.zeros((0, I), np.float32))
             continue
-        if codes_override is not None:
-            codes, ex = codes_override[e]
-            s32 = None
-        else:
-            if h_all is None:
-                h_all = dequant_x_ue8m0(x, x_sf)
-            h = h_all[tok]                                                 # [m_e, H]
-            W1 = dequant_w_fp4(np.asarray(w1)[e], np.asarray(w1_sf)[e])    # [2I, H]
-            u = h @ W1.T                                                   # [m_e, 2I] float64
-            gate = u[:, :I].astype(np.float32).astype(np.float64)
-            up = u[:, I:].astype(np.float32).astype(np.float64)
-            s32 = (silu(gate) * up).astype(np.float32)
-            codes, ex = requant_e4m3_pow2(s32)
+        if h_all is None:
+            h_all = dequant_x_ue8m0(x, x_sf)
+        h = h_all[tok]                                                 # [m_e, H]
+        W1 = dequant_w_fp4(np.asarray(w1)[e], np.asarray(w1_sf)[e])    # [2I, H]
+        u = h @ W1.T                                                   # [m_e, 2I] float64
+        gate = u[:, :I].astype(np.float32).astype(np.float64)
+        up = u[:, I:].astype(np.float32).astype(np.float64)
+        s32 = (silu(gate) * up).astype(np.float32)
+        codes, ex = requant_e4m3_pow2(s32)
         if return_intermediate:
             info["codes"].append(codes)
             info["exps"].append(ex)

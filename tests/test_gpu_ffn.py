@@ -7,11 +7,12 @@ The requantised intermediate is a rounding decision taken in fp32 on both
 sides.  The kernel's fp32 linear1 accumulates in another order than the
 oracle's float64 product rounded to fp32, so where a value lies within fp32
 accumulation error of an e4m3 rounding midpoint the two codes can legitimately
-differ by one step.  The tests therefore check (1) that codes agree except for
-such neighbours, each of which must sit at a midpoint of the oracle's own
-value, (2) y against the oracle's linear2 + weighted sum evaluated on the
-kernel's codes, at the tolerance above, and (3) y against the plain oracle in
-Frobenius norm.
+differ by one step.  Such a flip moves an output element by about one e4m3
+step of one of I products, far inside the tolerance.  The tests therefore
+check (1) y against the plain oracle, element by element and in Frobenius norm,
+at the tolerance above, and (2) as a diagnostic of the intermediate, that the
+kernel's codes agree with the oracle's except for neighbours at a rounding
+midpoint of the oracle's own value.
 """
 
 import numpy as np
@@ -46,26 +47,22 @@ def _run(dg, g, topk_w=None, offset=None, ws_extra=0):
     return bits(y), ws
 
 
-def _oracle(g, offset=None, topk_w=None, codes_override=None):
+def _oracle(g, offset=None, topk_w=None):
     n = {k: synth.to_numpy(g[k]) for k in ("x", "x_sf", "topk_idx", "topk_w", "w1", "w1_sf", "w2", "w2_sf")}
     if topk_w is not None:
         n["topk_w"] = topk_w
     return R.expert_ffn(n["x"], n["x_sf"], n["topk_idx"], n["topk_w"], n["w1"], n["w1_sf"], n["w2"], n["w2_sf"],
-                        g["expert_offset"] if offset is None else offset, g["E"], return_intermediate=True,
-                        codes_override=codes_override)
+                        g["expert_offset"] if offset is None else offset, g["E"], return_intermediate=True)
 
 
 def _check_ffn(g, y, ws, what):
     ref, info = _oracle(g)
-    kern = _kernel_intermediate(g, ws, info)
-    _check_codes(kern, info, g)
-    ref_k, _ = _oracle(g, codes_override=kern)
     idx = synth.to_numpy(g["topk_idx"])
     off, E = g["expert_offset"], g["E"]
     hit = ((idx >= off) & (idx < off + E)).any(1)
     if hit.any():
-        check_parity(y[hit], ref_k[hit], ELEM_TOL, FRO_TOL, what=what + " (oracle on kernel codes)")
-        check_parity(y[hit], ref[hit], np.inf, FRO_TOL, what=what + " (plain oracle, Frobenius)")
+        check_parity(y[hit], ref[hit], ELEM_TOL, FRO_TOL, what=what + " (plain oracle)")
+    _check_codes(_kernel_intermediate(g, ws, info), info, g)
     return hit
 
 
@@ -236,8 +233,5 @@ def test_ffn_full_size_sampled_tokens(dg):
     for e in range(32):
         tok, slot = np.nonzero(idx_s == e)
         full_info["pairs"].append((toks[tok], slot))
-    kern = _kernel_intermediate(g, ws, full_info)
-    _check_codes(kern, info, sub)
-    ref_k, _ = _oracle(sub, codes_override=kern)
-    check_parity(y[toks], ref_k, ELEM_TOL, FRO_TOL, what="ffn full size (oracle on kernel codes)")
-    check_parity(y[toks], ref, np.inf, FRO_TOL, what="ffn full size (plain oracle, Frobenius)")
+    check_parity(y[toks], ref, ELEM_TOL, FRO_TOL, what="ffn full size (plain oracle)")
+    _check_codes(_kernel_intermediate(g, ws, full_info), info, sub)
