@@ -29,22 +29,23 @@ _I = ctypes.c_int
 _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
-    "dg_fp8_gemm_nt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
-    "dg_m_grouped_fp8_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
-    "dg_m_grouped_fp8_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
-    "dg_fp8_gemm_nn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
-    "dg_fp8_gemm_tn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "dg_fp8_gemm_nt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "dg_m_grouped_fp8_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
+    "dg_m_grouped_fp8_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "dg_fp8_gemm_nn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "dg_fp8_gemm_tn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "dg_k_grouped_fp8_gemm_tn_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
-    "dg_fp8_gemm_tt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
-    "dg_m_grouped_fp8_gemm_nn_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
-    "dg_fp8_gemm_nt_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
-    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
-    "dg_m_grouped_fp8_gemm_nt_masked_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "dg_fp8_gemm_tt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "dg_m_grouped_fp8_gemm_nn_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
+    "dg_fp8_gemm_nt_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _SZ, _P]),
+    "dg_m_grouped_fp8_gemm_nt_masked_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "dg_m_grouped_fp8_fp4_gemm_nt_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "dg_m_grouped_fp8_fp4_gemm_nt_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "dg_transform_fp4_weight_sf": (_I, [_P, _P, _I, _I, _I, _P]),
     "dg_fp8_fp4_expert_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "dg_fp8_fp4_expert_ffn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "dg_fp8_gemm_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "dg_get_mk_alignment_for_contiguous_layout": (_I, []),
     "dg_set_num_cus": (_I, [_I]),
     "dg_get_num_cus": (_I, []),
@@ -126,12 +127,38 @@ def _nb(n):
     return (n + 127) // 128
 
 
+# dg_gemm_form (include/dg.h): which FP8 GEMM entry point a workspace query is for
+FORM_NT, FORM_NN, FORM_TN, FORM_TT, FORM_NT_UE8M0 = 0, 1, 2, 3, 4
+FORM_CONTIGUOUS_NT, FORM_CONTIGUOUS_NN, FORM_CONTIGUOUS_NT_UE8M0 = 5, 6, 7
+FORM_MASKED_NT, FORM_MASKED_NT_UE8M0 = 8, 9
+
+
+def dg_fp8_gemm_workspace_bytes(form, m, n, k, num_groups=1, expected_m=0, num_cus=0):
+    """Bytes of workspace the FP8 GEMM entry point `form` needs for these sizes (0: none)."""
+    return int(lib().dg_fp8_gemm_workspace_bytes(int(form), m, n, k, num_groups, int(expected_m), int(num_cus)))
+
+
+def _workspace(form, m, n, k, num_groups, expected_m, device, workspace):
+    """(pointer, bytes) of the workspace for one call: the caller's uint8 tensor, or a
+    new one from torch's caching allocator when none is given and the plan needs one."""
+    if workspace is not None:
+        _req(workspace, _U8, (workspace.numel(),), "workspace")
+        return _ptr(workspace), workspace.numel(), workspace
+    need = dg_fp8_gemm_workspace_bytes(form, m, n, k, num_groups, expected_m)
+    if need == 0:
+        return None, 0, None
+    ws = torch.empty(need, dtype=_U8, device=device)
+    return _ptr(ws), need, ws
+
+
 # ----------------------------------------------------------------------------
 # C entry points (caller-allocated outputs)
 # ----------------------------------------------------------------------------
 
-def dg_fp8_gemm_nt(a, sfa, b, sfb, c, d):
-    """d = c + a . b^T (see include/dg.h).  a/b uint8 e4m3, sfa [K/128, M], sfb [ceil(N/128), K/128]."""
+def dg_fp8_gemm_nt(a, sfa, b, sfb, c, d, workspace=None):
+    """d = c + a . b^T (see include/dg.h).  a/b uint8 e4m3, sfa [K/128, M], sfb [ceil(N/128), K/128].
+    workspace: optional uint8 device tensor for the split-K partials (allocated here when needed
+    and not given)."""
     L = lib()
     M, K = a.shape
     N = b.shape[0]
@@ -142,12 +169,13 @@ def dg_fp8_gemm_nt(a, sfa, b, sfb, c, d):
     if c is not None:
         _req_bf16(c, (M, N), "c")
     _req_bf16(d, (M, N), "d")
+    wp, wn, _keep = _workspace(FORM_NT, M, N, K, 1, 0, a.device, workspace)
     _check("dg_fp8_gemm_nt", L.dg_fp8_gemm_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c), _ptr(d),
-                                              M, N, K, _stream(a)))
+                                              M, N, K, wp, wn, _stream(a)))
     return d
 
 
-def dg_m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, m_indices, d):
+def dg_m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, m_indices, d, workspace=None):
     L = lib()
     M, K = a.shape
     G, N = b.shape[0], b.shape[1]
@@ -157,13 +185,14 @@ def dg_m_grouped_fp8_gemm_nt_contiguous(a, sfa, b, sfb, m_indices, d):
     _req(sfb, torch.float32, (G, _nb(N), K // 128), "sfb")
     _req(m_indices, torch.int32, (M,), "m_indices")
     _req_bf16(d, (M, N), "d")
+    wp, wn, _keep = _workspace(FORM_CONTIGUOUS_NT, M, N, K, G, 0, a.device, workspace)
     _check("dg_m_grouped_fp8_gemm_nt_contiguous",
            L.dg_m_grouped_fp8_gemm_nt_contiguous(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(m_indices),
-                                                 _ptr(d), M, N, K, G, _stream(a)))
+                                                 _ptr(d), M, N, K, G, wp, wn, _stream(a)))
     return d
 
 
-def dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked_m, d, expected_m=0):
+def dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked_m, d, expected_m=0, workspace=None):
     L = lib()
     G, max_m, K = a.shape
     N = b.shape[1]
@@ -173,13 +202,14 @@ def dg_m_grouped_fp8_gemm_nt_masked(a, sfa, b, sfb, masked_m, d, expected_m=0):
     _req(sfb, torch.float32, (G, _nb(N), K // 128), "sfb")
     _req(masked_m, torch.int32, (G,), "masked_m")
     _req_bf16(d, (G, max_m, N), "d")
+    wp, wn, _keep = _workspace(FORM_MASKED_NT, max_m, N, K, G, expected_m, a.device, workspace)
     _check("dg_m_grouped_fp8_gemm_nt_masked",
            L.dg_m_grouped_fp8_gemm_nt_masked(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m), _ptr(d),
-                                             G, max_m, N, K, int(expected_m), _stream(a)))
+                                             G, max_m, N, K, int(expected_m), wp, wn, _stream(a)))
     return d
 
 
-def dg_fp8_gemm_nn(a, sfa, b, sfb, c, d):
+def dg_fp8_gemm_nn(a, sfa, b, sfb, c, d, workspace=None):
     """d = c + a . b with b stored [K, N] (NN layout)."""
     L = lib()
     M, K = a.shape
@@ -191,12 +221,13 @@ def dg_fp8_gemm_nn(a, sfa, b, sfb, c, d):
     if c is not None:
         _req_bf16(c, (M, N), "c")
     _req_bf16(d, (M, N), "d")
+    wp, wn, _keep = _workspace(FORM_NN, M, N, K, 1, 0, a.device, workspace)
     _check("dg_fp8_gemm_nn", L.dg_fp8_gemm_nn(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c), _ptr(d),
-                                              M, N, K, _stream(a)))
+                                              M, N, K, wp, wn, _stream(a)))
     return d
 
 
-def _dense_layout(name, a, sfa, b, sfb, c, d, a_km, b_kn):
+def _dense_layout(name, form, a, sfa, b, sfb, c, d, a_km, b_kn, workspace):
     L = lib()
     if a_km:
         K, M = a.shape
@@ -210,18 +241,20 @@ def _dense_layout(name, a, sfa, b, sfb, c, d, a_km, b_kn):
     if c is not None:
         _req_bf16(c, (M, N), "c")
     _req_bf16(d, (M, N), "d")
-    _check(name, getattr(L, name)(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c), _ptr(d), M, N, K, _stream(a)))
+    wp, wn, _keep = _workspace(form, M, N, K, 1, 0, a.device, workspace)
+    _check(name, getattr(L, name)(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c), _ptr(d), M, N, K, wp, wn,
+                                  _stream(a)))
     return d
 
 
-def dg_fp8_gemm_tn(a, sfa, b, sfb, c, d):
+def dg_fp8_gemm_tn(a, sfa, b, sfb, c, d, workspace=None):
     """d = c + a^T b with a stored [K, M] and b stored [K, N] (TN layout)."""
-    return _dense_layout("dg_fp8_gemm_tn", a, sfa, b, sfb, c, d, a_km=True, b_kn=True)
+    return _dense_layout("dg_fp8_gemm_tn", FORM_TN, a, sfa, b, sfb, c, d, True, True, workspace)
 
 
-def dg_fp8_gemm_tt(a, sfa, b, sfb, c, d):
+def dg_fp8_gemm_tt(a, sfa, b, sfb, c, d, workspace=None):
     """d = c + a^T b^T with a stored [K, M] and b stored [N, K] (TT layout)."""
-    return _dense_layout("dg_fp8_gemm_tt", a, sfa, b, sfb, c, d, a_km=True, b_kn=False)
+    return _dense_layout("dg_fp8_gemm_tt", FORM_TT, a, sfa, b, sfb, c, d, True, False, workspace)
 
 
 def dg_k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d):
@@ -242,7 +275,7 @@ def dg_k_grouped_fp8_gemm_tn_contiguous(a, sfa, b, sfb, ks, d):
     return d
 
 
-def dg_m_grouped_fp8_gemm_nn_contiguous(a, sfa, b, sfb, m_indices, d):
+def dg_m_grouped_fp8_gemm_nn_contiguous(a, sfa, b, sfb, m_indices, d, workspace=None):
     """Contiguous grouped form with each group's b stored [K, N]."""
     L = lib()
     M, K = a.shape
@@ -253,9 +286,10 @@ def dg_m_grouped_fp8_gemm_nn_contiguous(a, sfa, b, sfb, m_indices, d):
     _req(sfb, torch.float32, (G, _nb(N), K // 128), "sfb")
     _req(m_indices, torch.int32, (M,), "m_indices")
     _req_bf16(d, (M, N), "d")
+    wp, wn, _keep = _workspace(FORM_CONTIGUOUS_NN, M, N, K, G, 0, a.device, workspace)
     _check("dg_m_grouped_fp8_gemm_nn_contiguous",
            L.dg_m_grouped_fp8_gemm_nn_contiguous(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(m_indices), _ptr(d),
-                                                 M, N, K, G, _stream(a)))
+                                                 M, N, K, G, wp, wn, _stream(a)))
     return d
 
 
@@ -263,7 +297,7 @@ def _kw(K):
     return (K // 128 + 3) // 4
 
 
-def dg_fp8_gemm_nt_ue8m0(a, sfa, b, sfb, c, d):
+def dg_fp8_gemm_nt_ue8m0(a, sfa, b, sfb, c, d, workspace=None):
     L = lib()
     M, K = a.shape
     N = b.shape[0]
@@ -274,13 +308,14 @@ def dg_fp8_gemm_nt_ue8m0(a, sfa, b, sfb, c, d):
     if c is not None:
         _req_bf16(c, (M, N), "c")
     _req_bf16(d, (M, N), "d")
+    wp, wn, _keep = _workspace(FORM_NT_UE8M0, M, N, K, 1, 0, a.device, workspace)
     _check("dg_fp8_gemm_nt_ue8m0",
            L.dg_fp8_gemm_nt_ue8m0(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c),
-                                  _ptr(d), M, N, K, _stream(a)))
+                                  _ptr(d), M, N, K, wp, wn, _stream(a)))
     return d
 
 
-def dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(a, sfa, b, sfb, m_indices, d):
+def dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(a, sfa, b, sfb, m_indices, d, workspace=None):
     L = lib()
     M, K = a.shape
     G, N = b.shape[0], b.shape[1]
@@ -290,13 +325,14 @@ def dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(a, sfa, b, sfb, m_indices, d):
     _req(sfb, torch.int32, (G, _nb(N), _kw(K)), "sfb")
     _req(m_indices, torch.int32, (M,), "m_indices")
     _req_bf16(d, (M, N), "d")
+    wp, wn, _keep = _workspace(FORM_CONTIGUOUS_NT_UE8M0, M, N, K, G, 0, a.device, workspace)
     _check("dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
            L.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(m_indices),
-                                                       _ptr(d), M, N, K, G, _stream(a)))
+                                                       _ptr(d), M, N, K, G, wp, wn, _stream(a)))
     return d
 
 
-def dg_m_grouped_fp8_gemm_nt_masked_ue8m0(a, sfa, b, sfb, masked_m, d, expected_m=0):
+def dg_m_grouped_fp8_gemm_nt_masked_ue8m0(a, sfa, b, sfb, masked_m, d, expected_m=0, workspace=None):
     L = lib()
     G, max_m, K = a.shape
     N = b.shape[1]
@@ -306,9 +342,10 @@ def dg_m_grouped_fp8_gemm_nt_masked_ue8m0(a, sfa, b, sfb, masked_m, d, expected_
     _req(sfb, torch.int32, (G, _nb(N), _kw(K)), "sfb")
     _req(masked_m, torch.int32, (G,), "masked_m")
     _req_bf16(d, (G, max_m, N), "d")
+    wp, wn, _keep = _workspace(FORM_MASKED_NT_UE8M0, max_m, N, K, G, expected_m, a.device, workspace)
     _check("dg_m_grouped_fp8_gemm_nt_masked_ue8m0",
            L.dg_m_grouped_fp8_gemm_nt_masked_ue8m0(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m),
-                                                   _ptr(d), G, max_m, N, K, int(expected_m), _stream(a)))
+                                                   _ptr(d), G, max_m, N, K, int(expected_m), wp, wn, _stream(a)))
     return d
 
 

@@ -78,47 +78,24 @@ static bool operands_fit(int m, int n, int k) {
   return fits_buffer(m, k, 1) && fits_buffer(n, k, 1) && fits_buffer(m, n, 2);
 }
 
-// Split-K workspace: one fp32 buffer per (device, stream), grown on demand and
-// kept until the process ends, so calls on one stream reuse it in stream order.
-static std::mutex g_ws_mu;
-static std::map<std::pair<int, void*>, std::pair<void*, size_t>> g_ws;
+// Host-side decisions of one GEMM call: the tile plan (with the tuning
+// overrides), the raster, and the bytes of caller workspace the plan needs.
+struct CallPlan {
+  GemmPlan plan;
+  int masked_slots;   // masked form: workgroups of the device-planned walk
+  size_t ws_bytes;    // split-K partial tiles (0: the plan does not split)
+};
 
-static float* split_workspace(int dev, hipStream_t stream, size_t bytes, hipError_t* err) {
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  auto& e = g_ws[{dev, reinterpret_cast<void*>(stream)}];
-  if (e.second < bytes) {
-    if (e.first) {
-      // earlier calls on this stream may still read the old buffer
-      hipError_t r = hipStreamSynchronize(stream);
-      if (r == hipSuccess) r = hipFree(e.first);
-      e = {nullptr, 0};
-      if (r != hipSuccess) {
-        *err = r;
-        return nullptr;
-      }
-    }
-    void* ptr = nullptr;
-    hipError_t r = hipMalloc(&ptr, bytes);
-    if (r != hipSuccess) {
-      *err = r;
-      return nullptr;
-    }
-    e = {ptr, bytes};
-  }
-  return static_cast<float*>(e.first);
-}
-
-// flags: MODE_UE8M0 and / or MODE_NN, or-ed into the form's mode at launch
-static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream, const char* name,
-                        int flags = 0) {
-  DeviceInfo di = current_device_info();
-  if (!di.ok) return DG_ERR_NO_DEVICE;
-  int cus = effective_cus(di);
+static CallPlan plan_call(Fp8GemmParams& p, int mode, int expected_m, int flags, int cus) {
+  CallPlan cp{};
   const int bm_multiple = (flags & MODE_AT) ? 128 : 0;   // A stored [K][M]: 128-row sub-tiles
   // K-grouped: plan for a group's mean K
   const int k_plan = mode == MODE_KGROUP ? std::max(128, p.k / p.num_groups / 128 * 128) : p.k;
   GemmPlan plan = plan_fp8_gemm(p.m, p.n, k_plan, p.num_groups, mode, cus, expected_m, bm_multiple);
-  if (plan.kernel_id < 0) return DG_ERR_UNSUPPORTED;
+  if (plan.kernel_id < 0) {
+    cp.plan = plan;
+    return cp;
+  }
   // DG_FORCE_KERNEL=<id>: override the heuristic's tile choice (for tuning)
   if (const char* fk = std::getenv("DG_FORCE_KERNEL")) {
     int id = std::atoi(fk);
@@ -134,32 +111,21 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
   p.full_tiles = plan.full_tiles;
   p.total_tiles = (int)std::min<long long>(
       (long long)plan.full_tiles + (long long)(plan.num_tiles - plan.full_tiles) * plan.splits, 0x7fffffff);
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   // Masked form: the kernel walks only the tiles holding valid rows, spread
   // evenly over one full set of workgroup slots, and over long K splits a small
   // last round along K (decided on the device from masked_m; the reduce kernel
   // re-derives the same plan and does nothing when there is no split).
-  int masked_slots = 0;
   p.device_split = 0;
+  const size_t tile_bytes = (size_t)plan.block_m * plan.block_n * 4;
   if (mode == MODE_MASKED) {
-    masked_slots = plan_slots(plan.kernel_id, cus);
-    plan.num_workgroups = masked_slots;
+    cp.masked_slots = plan_slots(plan.kernel_id, cus);
+    plan.num_workgroups = cp.masked_slots;
     p.device_split = p.k / 128 >= 4 + kTailMinGain ? 1 : 2;
-  }
-  if (p.device_split == 1) {
-    // at most one partial tile per workgroup slot
-    const size_t ws_bytes = (size_t)masked_slots * plan.block_m * plan.block_n * 4;
-    hipError_t werr = hipSuccess;
-    p.ws = split_workspace(di.device, hs, ws_bytes, &werr);
-    if (!p.ws) return DG_ERR_HIP;
-  }
-  if (plan.splits > 1) {
-    // one fp32 block_m x block_n partial per slice of every split tile (at most
-    // one per workgroup slot, so a few tens of MB at most)
-    const size_t ws_bytes = (size_t)(plan.num_tiles - plan.full_tiles) * plan.splits * plan.block_m * plan.block_n * 4;
-    hipError_t werr = hipSuccess;
-    p.ws = split_workspace(di.device, hs, ws_bytes, &werr);
-    if (!p.ws) return DG_ERR_HIP;
+    // the device's split rule yields at most one partial tile per workgroup slot
+    if (p.device_split == 1) cp.ws_bytes = (size_t)cp.masked_slots * tile_bytes;
+  } else if (plan.splits > 1) {
+    // one partial per slice of every split tile (at most one per workgroup slot)
+    cp.ws_bytes = (size_t)(plan.num_tiles - plan.full_tiles) * plan.splits * tile_bytes;
   }
   // raster band: the 32 tiles an XCD runs at once share the fewest A and B rows
   // as a 4 x 8 block of 256 x 128 tiles (1024 + 1024 rows) or an 8 x 4 block of
@@ -169,13 +135,32 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* stream
   // DG_KROT=<s>: K-block rotation step between neighbouring tiles (tuning)
   p.k_rot = 0;
   if (const char* kr = std::getenv("DG_KROT")) p.k_rot = std::max(0, std::atoi(kr));
+  cp.plan = plan;
+  return cp;
+}
+
+// flags: MODE_UE8M0, MODE_NN and / or MODE_AT, or-ed into the form's mode at launch
+static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* workspace, size_t workspace_bytes,
+                        void* stream, const char* name, int flags = 0) {
+  DeviceInfo di = current_device_info();
+  if (!di.ok) return DG_ERR_NO_DEVICE;
+  const int cus = effective_cus(di);
+  CallPlan cp = plan_call(p, mode, expected_m, flags, cus);
+  const GemmPlan& plan = cp.plan;
+  if (plan.kernel_id < 0) return DG_ERR_UNSUPPORTED;
+  if (cp.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < cp.ws_bytes || !aligned(workspace, 16)) return DG_ERR_INVALID_ARG;
+    p.ws = static_cast<float*>(workspace);
+  }
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (log_enabled())
     std::fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d -> tile %dx%d (kernel %d), %d tiles (%d whole, the rest "
-                 "x %d K slices), %d workgroups\n", name, p.m, p.n, p.k, p.num_groups, plan.block_m, plan.block_n,
-                 plan.kernel_id, plan.num_tiles, plan.full_tiles, plan.splits, plan.num_workgroups);
+                 "x %d K slices), %d workgroups, workspace %zu bytes\n", name, p.m, p.n, p.k, p.num_groups,
+                 plan.block_m, plan.block_n, plan.kernel_id, plan.num_tiles, plan.full_tiles, plan.splits,
+                 plan.num_workgroups, cp.ws_bytes);
   hipError_t e = launch_fp8_gemm(p, plan, mode | flags, hs);
-  if (e == hipSuccess && plan.splits > 1) e = launch_splitk_reduce(p, plan, cus, hs);
-  if (e == hipSuccess && p.device_split == 1) e = launch_masked_splitk_reduce(p, plan, masked_slots, hs);
+  if (e == hipSuccess && plan.splits > 1 && mode != MODE_MASKED) e = launch_splitk_reduce(p, plan, cus, hs);
+  if (e == hipSuccess && p.device_split == 1) e = launch_masked_splitk_reduce(p, plan, cp.masked_slots, hs);
   return e == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
@@ -185,7 +170,7 @@ using namespace dg;
 
 // The three forms; ue8m0 selects packed UE8M0 scale words instead of fp32 scales.
 static int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, const uint16_t* c,
-                       uint16_t* d, int m, int n, int k, void* stream, int flags) {
+                       uint16_t* d, int m, int n, int k, void* ws, size_t ws_bytes, void* stream, int flags) {
   try {
     if (!a || !sfa || !b || !sfb || !d) return DG_ERR_INVALID_ARG;
     if (m <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
@@ -200,15 +185,15 @@ static int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, cons
     const char* name = (flags & MODE_AT) ? ((flags & MODE_NN) ? "fp8_gemm_tn" : "fp8_gemm_tt")
                        : (flags & MODE_NN) ? "fp8_gemm_nn"
                        : ((flags & MODE_UE8M0) ? "fp8_gemm_nt_ue8m0" : "fp8_gemm_nt");
-    return run_fp8_gemm(p, MODE_DENSE, 0, stream, name, flags);
+    return run_fp8_gemm(p, MODE_DENSE, 0, ws, ws_bytes, stream, name, flags);
   } catch (...) {
     return DG_ERR_HIP;
   }
 }
 
 static int contiguous_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb,
-                            const int32_t* m_indices, uint16_t* d, int m, int n, int k, int num_groups, void* stream,
-                            int flags) {
+                            const int32_t* m_indices, uint16_t* d, int m, int n, int k, int num_groups, void* ws,
+                            size_t ws_bytes, void* stream, int flags) {
   try {
     if (!a || !sfa || !b || !sfb || !m_indices || !d) return DG_ERR_INVALID_ARG;
     if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERR_INVALID_ARG;
@@ -222,7 +207,7 @@ static int contiguous_entry(const uint8_t* a, const void* sfa, const uint8_t* b,
     const char* name = (flags & MODE_NN) ? "m_grouped_fp8_gemm_nn_contiguous"
                                          : ((flags & MODE_UE8M0) ? "m_grouped_fp8_gemm_nt_contiguous_ue8m0"
                                                                  : "m_grouped_fp8_gemm_nt_contiguous");
-    return run_fp8_gemm(p, MODE_CONTIG, 0, stream, name, flags);
+    return run_fp8_gemm(p, MODE_CONTIG, 0, ws, ws_bytes, stream, name, flags);
   } catch (...) {
     return DG_ERR_HIP;
   }
@@ -230,7 +215,7 @@ static int contiguous_entry(const uint8_t* a, const void* sfa, const uint8_t* b,
 
 static int masked_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb,
                         const int32_t* masked_m, uint16_t* d, int num_groups, int max_m, int n, int k, int expected_m,
-                        void* stream, int flags) {
+                        void* ws, size_t ws_bytes, void* stream, int flags) {
   try {
     if (!a || !sfa || !b || !sfb || !masked_m || !d) return DG_ERR_INVALID_ARG;
     if (num_groups <= 0 || max_m <= 0 || n <= 0 || k <= 0) return DG_ERR_INVALID_ARG;
@@ -244,7 +229,7 @@ static int masked_entry(const uint8_t* a, const void* sfa, const uint8_t* b, con
     Fp8GemmParams p{};
     p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
     p.m = max_m; p.n = n; p.k = k; p.num_groups = num_groups;
-    return run_fp8_gemm(p, MODE_MASKED, expected_m, stream,
+    return run_fp8_gemm(p, MODE_MASKED, expected_m, ws, ws_bytes, stream,
                         (flags & MODE_UE8M0) ? "m_grouped_fp8_gemm_nt_masked_ue8m0" : "m_grouped_fp8_gemm_nt_masked",
                         flags);
   } catch (...) {
@@ -255,60 +240,104 @@ static int masked_entry(const uint8_t* a, const void* sfa, const uint8_t* b, con
 extern "C" {
 
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
-  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, 0);
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, workspace, workspace_bytes, stream, 0);
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
                                         const float* sfb, const int32_t* m_indices, uint16_t* d,
-                                        int m, int n, int k, int num_groups, void* stream) {
-  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, 0);
+                                        int m, int n, int k, int num_groups, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, workspace, workspace_bytes, stream, 0);
 }
 
 int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
                                     const float* sfb, const int32_t* masked_m, uint16_t* d,
                                     int num_groups, int max_m, int n, int k, int expected_m,
-                                    void* stream) {
-  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, stream, 0);
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, workspace, workspace_bytes,
+                      stream, 0);
 }
 
 int dg_fp8_gemm_nn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
-  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, MODE_NN);
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, workspace, workspace_bytes, stream, MODE_NN);
 }
 
 int dg_fp8_gemm_tn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
-  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, MODE_AT | MODE_NN);
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, workspace, workspace_bytes, stream, MODE_AT | MODE_NN);
 }
 
 int dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
-  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, MODE_AT);
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, workspace, workspace_bytes, stream, MODE_AT);
 }
 
 int dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
                                         const float* sfb, const int32_t* m_indices, uint16_t* d,
-                                        int m, int n, int k, int num_groups, void* stream) {
-  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, MODE_NN);
+                                        int m, int n, int k, int num_groups, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, workspace, workspace_bytes, stream,
+                          MODE_NN);
 }
 
 int dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b, const int32_t* sfb,
-                         const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream) {
-  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, stream, MODE_UE8M0);
+                         const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return dense_entry(a, sfa, b, sfb, c, d, m, n, k, workspace, workspace_bytes, stream, MODE_UE8M0);
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
                                               const int32_t* sfb, const int32_t* m_indices, uint16_t* d,
-                                              int m, int n, int k, int num_groups, void* stream) {
-  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, stream, MODE_UE8M0);
+                                              int m, int n, int k, int num_groups, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  return contiguous_entry(a, sfa, b, sfb, m_indices, d, m, n, k, num_groups, workspace, workspace_bytes, stream,
+                          MODE_UE8M0);
 }
 
 int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
                                           const int32_t* sfb, const int32_t* masked_m, uint16_t* d,
                                           int num_groups, int max_m, int n, int k, int expected_m,
-                                          void* stream) {
-  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, stream, MODE_UE8M0);
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  return masked_entry(a, sfa, b, sfb, masked_m, d, num_groups, max_m, n, k, expected_m, workspace, workspace_bytes,
+                      stream, MODE_UE8M0);
+}
+
+size_t dg_fp8_gemm_workspace_bytes(int form, int m, int n, int k, int num_groups, int expected_m, int num_cus) {
+  try {
+    if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0 || k % 128 != 0 || n % 16 != 0) return 0;
+    int mode, flags;
+    switch (form) {
+      case DG_FORM_NT: mode = MODE_DENSE; flags = 0; break;
+      case DG_FORM_NN: mode = MODE_DENSE; flags = MODE_NN; break;
+      case DG_FORM_TN: mode = MODE_DENSE; flags = MODE_AT | MODE_NN; break;
+      case DG_FORM_TT: mode = MODE_DENSE; flags = MODE_AT; break;
+      case DG_FORM_NT_UE8M0: mode = MODE_DENSE; flags = MODE_UE8M0; break;
+      case DG_FORM_CONTIGUOUS_NT: mode = MODE_CONTIG; flags = 0; break;
+      case DG_FORM_CONTIGUOUS_NN: mode = MODE_CONTIG; flags = MODE_NN; break;
+      case DG_FORM_CONTIGUOUS_NT_UE8M0: mode = MODE_CONTIG; flags = MODE_UE8M0; break;
+      case DG_FORM_MASKED_NT: mode = MODE_MASKED; flags = 0; break;
+      case DG_FORM_MASKED_NT_UE8M0: mode = MODE_MASKED; flags = MODE_UE8M0; break;
+      default: return 0;
+    }
+    if (mode == MODE_DENSE) num_groups = 1;
+    if (num_cus <= 0) {
+      DeviceInfo di = current_device_info();
+      if (!di.ok) return 0;
+      num_cus = effective_cus(di);
+    }
+    Fp8GemmParams p{};
+    p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
+    const CallPlan cp = plan_call(p, mode, expected_m, flags, num_cus);
+    return cp.plan.kernel_id < 0 ? 0 : cp.ws_bytes;
+  } catch (...) {
+    return 0;
+  }
 }
 
 int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
@@ -331,7 +360,7 @@ int dg_k_grouped_fp8_gemm_tn_contiguous(const uint8_t* a, const float* sfa, cons
     p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
     const hipError_t e = launch_kgroup_zero(p, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return DG_ERR_HIP;
-    return run_fp8_gemm(p, MODE_KGROUP, 0, stream, "k_grouped_fp8_gemm_tn_contiguous", MODE_AT | MODE_NN);
+    return run_fp8_gemm(p, MODE_KGROUP, 0, nullptr, 0, stream, "k_grouped_fp8_gemm_tn_contiguous", MODE_AT | MODE_NN);
   } catch (...) {
     return DG_ERR_HIP;
   }

@@ -17,16 +17,17 @@
  *   - Tensor arguments are DEVICE pointers to dense row-major arrays (last index
  *     contiguous).  Sizes are element counts.  Operand and output pointers must
  *     be 16-byte aligned; scale pointers 4-byte aligned.
- *   - The caller owns every buffer, including outputs and workspaces.  The
+ *   - The caller owns every buffer, including outputs and workspaces (the
+ *     Mega MoE call of the update news page writes a caller-allocated y).  The
  *     library keeps only host-side state (a device-property cache and the CU
- *     cap) and allocates no device memory, with one exception: the dense
- *     GEMM's split-K workspace (see dg_query_plan), which the first split call
- *     on a (device, stream) allocates and a later call needing more grows.
+ *     cap) and never allocates or frees device memory.  Scratch memory a call
+ *     needs (the FP8 GEMMs' split-K partial tiles, the FFN's routing lists and
+ *     intermediates) comes from a caller workspace whose size a query function
+ *     returns; its contents on entry are ignored.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
- *     There is no host read of device data and no host synchronisation, except
- *     that growing the split-K workspace first synchronises its stream.  Calls
- *     may be captured in a HIP graph once that stream's workspace is as large
- *     as the captured calls need (run them once before capturing).
+ *     There is no host read of device data and no host synchronisation, so
+ *     every call may be captured in a HIP graph.  Calls that share a workspace
+ *     must be ordered (the same stream, or synchronised streams).
  *   - e4m3 means OCP e4m3fn (bias 7, max 448, NaN = 0x7F/0xFF).  bf16 values
  *     are passed as their uint16 bit patterns.  Outputs are rounded from fp32
  *     to bf16 with round-to-nearest-even (a NaN result stays a quiet NaN).
@@ -73,11 +74,16 @@ typedef enum dg_status {
  *   sfb  [ceil(n/128), k/128] fp32, one scale per 128x128 block
  *   c    [m, n]               bf16, or NULL for C = 0 (16-byte aligned)
  *   d    [m, n]               bf16 output (may alias c only if identical)
+ *   workspace, workspace_bytes
+ *        device scratch of at least dg_fp8_gemm_workspace_bytes(DG_FORM_NT, m, n, k, 1, 0, 0)
+ *        bytes, 16-byte aligned; may be NULL when that is 0.  Too small (or NULL when
+ *        needed): DG_ERR_INVALID_ARG, nothing enqueued.
  * Requirements: m, n, k > 0; k % 128 == 0; n % 16 == 0; m*k, n*k and 2*m*n
  *   (the bytes of A, B and D) at most 2^31, else DG_ERR_UNSUPPORTED.
  */
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /*
  * M-grouped GEMM, contiguous layout (prefill / training forward).  Rows of all
@@ -95,12 +101,14 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
  *   sfb       [num_groups, ceil(n/128), k/128]  fp32
  *   m_indices [m]                               int32, device memory
  *   d         [m, n]                            bf16
+ *   workspace as dg_fp8_gemm_nt, sized by DG_FORM_CONTIGUOUS_NT
  * Requirements: m, n, k, num_groups > 0; k % 128 == 0; n % 16 == 0; m*k, n*k and
  *   2*m*n at most 2^31 (B: one group), else DG_ERR_UNSUPPORTED.
  */
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
                                         const float* sfb, const int32_t* m_indices, uint16_t* d,
-                                        int m, int n, int k, int num_groups, void* stream);
+                                        int m, int n, int k, int num_groups, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /*
  * M-grouped GEMM, masked layout (decode).  Each group has a fixed-capacity
@@ -116,13 +124,14 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* a, const float* sfa, cons
  *   sfb      [num_groups, ceil(n/128), k/128]  fp32
  *   masked_m [num_groups]                      int32, device memory
  *   d        [num_groups, max_m, n]            bf16
+ *   workspace as dg_fp8_gemm_nt, sized by DG_FORM_MASKED_NT with m = max_m
  * Requirements: num_groups, max_m, n, k > 0; k % 128 == 0; n % 16 == 0; per group,
  *   max_m*k, n*k and 2*max_m*n at most 2^31, else DG_ERR_UNSUPPORTED.
  */
 int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
                                     const float* sfb, const int32_t* masked_m, uint16_t* d,
                                     int num_groups, int max_m, int n, int k, int expected_m,
-                                    void* stream);
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * NN layout (usage guide "DeepGEMM：统一高性能张量核心 GEMM 计算库编译与使用指南",
@@ -132,14 +141,17 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* a, const float* sfa, const ui
  *   b    [k, n]          e4m3, n contiguous (grouped: [num_groups, k, n])
  * and every other argument, scale layout (sfb stays [ceil(n/128)][k/128], indexed
  * by n-block then k-block), requirement and row rule as in dg_fp8_gemm_nt and
- * dg_m_grouped_fp8_gemm_nt_contiguous.  The kernel reads B's tiles with gfx950's
- * transposing LDS loads.
+ * dg_m_grouped_fp8_gemm_nt_contiguous (workspace sized by DG_FORM_NN and
+ * DG_FORM_CONTIGUOUS_NN).  The kernel reads B's tiles with gfx950's transposing
+ * LDS loads.
  */
 int dg_fp8_gemm_nn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, void* stream);
 int dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
                                         const float* sfb, const int32_t* m_indices, uint16_t* d,
-                                        int m, int n, int k, int num_groups, void* stream);
+                                        int m, int n, int k, int num_groups, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /*
  * TN and TT layouts (same usage-guide passage): A is stored [k, m], m contiguous,
@@ -147,12 +159,14 @@ int dg_m_grouped_fp8_gemm_nn_contiguous(const uint8_t* a, const float* sfa, cons
  * [n, k] (TT).  sfa stays [k/128][m] (one scale per row of D per 128-wide K
  * block), sfb [ceil(n/128)][k/128].  Both read A's tiles with the transposing
  * LDS loads (in 128-row sub-tiles).  Requirements as dg_fp8_gemm_nt plus
- * m % 16 == 0.
+ * m % 16 == 0; workspace sized by DG_FORM_TN and DG_FORM_TT.
  */
 int dg_fp8_gemm_tn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, void* stream);
 int dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+                   const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /*
  * The same three GEMMs with packed UE8M0 scale factors instead of fp32 ones
@@ -170,18 +184,52 @@ int dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
  *   dg_m_grouped_fp8_gemm_nt_masked_ue8m0:
  *                                       sfa [num_groups, max_m, ceil(k/512)], sfb as contiguous
  * All other arguments, requirements, row rules (padding rows, rows past masked_m
- * not written) and errors are those of the fp32-scale form.  Exponent byte 255
- * (NaN scale) gives NaN results.
+ * not written) and errors are those of the fp32-scale form (workspace sized by
+ * DG_FORM_NT_UE8M0, DG_FORM_CONTIGUOUS_NT_UE8M0, DG_FORM_MASKED_NT_UE8M0).
+ * Exponent byte 255 (NaN scale) gives NaN results.
  */
 int dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b, const int32_t* sfb,
-                         const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
+                         const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
+                         size_t workspace_bytes, void* stream);
 int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
                                               const int32_t* sfb, const int32_t* m_indices, uint16_t* d,
-                                              int m, int n, int k, int num_groups, void* stream);
+                                              int m, int n, int k, int num_groups, void* workspace,
+                                              size_t workspace_bytes, void* stream);
 int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* a, const int32_t* sfa, const uint8_t* b,
                                           const int32_t* sfb, const int32_t* masked_m, uint16_t* d,
                                           int num_groups, int max_m, int n, int k, int expected_m,
-                                          void* stream);
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace of the FP8 GEMM entry points above.  Skinny problems (and the
+ * partial last round of some large ones) are split along K: each slice of a
+ * split tile sums a range of 128-wide K blocks into an fp32 partial tile, and a
+ * second kernel adds a tile's partials in slice order (plus C) and rounds to
+ * bf16.  The partials live in the caller's workspace.  This returns the bytes
+ * the call with these sizes needs (0: the plan does not split, and workspace may
+ * be NULL), for the entry point named by `form`:
+ *   dense forms:   m, n, k of the call; num_groups and expected_m ignored
+ *   contiguous:    m = total rows of the layout, num_groups
+ *   masked:        m = max_m, num_groups, expected_m as passed to the call
+ * num_cus: the CU count the call will run with (<= 0: the current cap of the
+ * current device; > 0: host-only, no HIP call).  The need never exceeds one
+ * fp32 block_m x block_n tile per workgroup slot (dg_query_plan).  Returns 0 for
+ * invalid sizes, whose calls then fail with their own status.
+ */
+typedef enum dg_gemm_form {
+  DG_FORM_NT = 0,                   /* dg_fp8_gemm_nt */
+  DG_FORM_NN = 1,                   /* dg_fp8_gemm_nn */
+  DG_FORM_TN = 2,                   /* dg_fp8_gemm_tn */
+  DG_FORM_TT = 3,                   /* dg_fp8_gemm_tt */
+  DG_FORM_NT_UE8M0 = 4,             /* dg_fp8_gemm_nt_ue8m0 */
+  DG_FORM_CONTIGUOUS_NT = 5,        /* dg_m_grouped_fp8_gemm_nt_contiguous */
+  DG_FORM_CONTIGUOUS_NN = 6,        /* dg_m_grouped_fp8_gemm_nn_contiguous */
+  DG_FORM_CONTIGUOUS_NT_UE8M0 = 7,  /* dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0 */
+  DG_FORM_MASKED_NT = 8,            /* dg_m_grouped_fp8_gemm_nt_masked */
+  DG_FORM_MASKED_NT_UE8M0 = 9       /* dg_m_grouped_fp8_gemm_nt_masked_ue8m0 */
+} dg_gemm_form;
+size_t dg_fp8_gemm_workspace_bytes(int form, int m, int n, int k, int num_groups, int expected_m,
+                                   int num_cus);
 
 /*
  * Weight pre-transform for the FP8 x FP4 entry points (news page "DeepSeek 发布
@@ -325,12 +373,8 @@ int dg_get_num_cus(void);
  * whole and the number of workgroups launched.  Dense problems may be split
  * along K: when the tiles cannot fill the chip (skinny M) every tile is split,
  * and when the last round of tiles would leave at least half of the workgroup
- * slots idle over a long K loop, only that round's tiles are.  Each slice of a
- * split tile sums a range of 128-wide K blocks into an fp32 partial tile of an
- * internal workspace, and a second kernel adds a tile's partials (in slice
- * order) and C and rounds to bf16.  The workspace is allocated by the library,
- * one per (device, stream), on first need, and grows to at most one partial
- * tile per workgroup slot.
+ * slots idle over a long K loop, only that round's tiles are (partials in the
+ * caller's workspace, see dg_fp8_gemm_workspace_bytes).
  * The masked form's tile list depends on masked_m, which only the device
  * reads: its kernel walks just the tiles that hold valid rows, spread evenly
  * over the workgroups, and for K >= 3584 applies the same split rule to their

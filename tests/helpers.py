@@ -41,3 +41,45 @@ def check_bit_exact(d_bits, exact, what=""):
     want = f64_to_bf16_bits(exact)
     mism = d_bits != want
     assert not mism.any(), f"{what}: {mism.sum()} bit mismatches, first at {np.argwhere(mism)[0]}"
+
+
+def stratified_entries(M, N, rng, valid_rows=None, block=64):
+    """(rows, cols) of output entries to check at full size: in every block x block block
+    of an M x N output, one element at a random place and the element at the block's
+    last (valid) row and last column.  Every tile the library may use is a multiple of 64
+    rows and columns, so every output tile -- and every split-K tile -- gets checked,
+    its last row and last column included.  valid_rows (bool [M]) restricts the rows to
+    the written ones; blocks without a valid row are skipped."""
+    nbc = (N + block - 1) // block
+    c0 = np.arange(nbc) * block
+    c1 = np.minimum(c0 + block, N)
+    rows, cols = [], []
+    for r0 in range(0, M, block):
+        r1 = min(r0 + block, M)
+        vr = np.arange(r0, r1) if valid_rows is None else np.nonzero(valid_rows[r0:r1])[0] + r0
+        if vr.size == 0:
+            continue
+        rows.append(rng.choice(vr, nbc))
+        cols.append(c0 + (rng.random(nbc) * (c1 - c0)).astype(np.int64))
+        rows.append(np.full(nbc, vr[-1]))
+        cols.append(c1 - 1)
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+def stratified_lines(n, rng, valid=None, block=64):
+    """Indices along one output axis: per block of 64, one random (valid) index and the
+    last (valid) one.  The cross product of such row and column sets meets every 64 x 64
+    block at a random place and at its last row and column."""
+    out = []
+    for r0 in range(0, n, block):
+        r1 = min(r0 + block, n)
+        v = np.arange(r0, r1) if valid is None else np.nonzero(valid[r0:r1])[0] + r0
+        if v.size:
+            out += sorted({int(rng.choice(v)), int(v[-1])})
+    return np.asarray(out, dtype=np.int64)
+
+
+def entries_in_chunks(fn, rows, cols, chunk=2048):
+    """fn(rows, cols) -> values, evaluated over chunks of the entry list (bounds the
+    oracle's memory at full size)."""
+    return np.concatenate([fn(rows[i:i + chunk], cols[i:i + chunk]) for i in range(0, len(rows), chunk)])

@@ -64,7 +64,7 @@ A16 = 0x10000   # fake 16-byte-aligned "device" addresses: never dereferenced on
 ])
 def test_dense_argument_validation(args, status):
     lib = dgm.load_library()
-    got = lib.dg_fp8_gemm_nt(*args, None)
+    got = lib.dg_fp8_gemm_nt(*args, None, 0, None)
     if status < 0:
         # passes validation; without a gfx950 device the call stops at the device check
         assert got in (0, 4)
@@ -107,14 +107,14 @@ def test_transform_fp4_weight_sf_argument_validation():
 def test_grouped_and_ffn_argument_validation():
     lib = dgm.load_library()
     f = lib.dg_m_grouped_fp8_gemm_nt_contiguous
-    assert f(A16, A16, A16, A16, 0, A16, 256, 64, 128, 4, None) == 1            # null m_indices
-    assert f(A16, A16, A16, A16, A16, A16, 256, 64, 128, 0, None) == 1          # no groups
-    assert f(A16, A16, A16, A16, A16, A16, 256, 64, 384 + 1, 4, None) == 2
+    assert f(A16, A16, A16, A16, 0, A16, 256, 64, 128, 4, None, 0, None) == 1            # null m_indices
+    assert f(A16, A16, A16, A16, A16, A16, 256, 64, 128, 0, None, 0, None) == 1          # no groups
+    assert f(A16, A16, A16, A16, A16, A16, 256, 64, 384 + 1, 4, None, 0, None) == 2
     g = lib.dg_m_grouped_fp8_gemm_nt_masked
-    assert g(A16, A16, A16, A16, 0, A16, 4, 256, 64, 128, 0, None) == 1         # null masked_m
-    assert g(A16, A16, A16, A16, A16, A16, 4, 0, 64, 128, 0, None) == 1         # max_m = 0
-    assert g(A16, A16, A16, A16, A16, A16, 4, 256, 72, 128, 0, None) == 2       # N % 16
-    assert g(A16, A16, A16, A16, A16, A16, 4, 1 << 15, (1 << 15) + 16, 128, 0, None) == 2  # a group's D > 2 GiB
+    assert g(A16, A16, A16, A16, 0, A16, 4, 256, 64, 128, 0, None, 0, None) == 1         # null masked_m
+    assert g(A16, A16, A16, A16, A16, A16, 4, 0, 64, 128, 0, None, 0, None) == 1         # max_m = 0
+    assert g(A16, A16, A16, A16, A16, A16, 4, 256, 72, 128, 0, None, 0, None) == 2       # N % 16
+    assert g(A16, A16, A16, A16, A16, A16, 4, 1 << 15, (1 << 15) + 16, 128, 0, None, 0, None) == 2  # D > 2 GiB
     h = lib.dg_fp8_fp4_expert_ffn
     ws = lib.dg_fp8_fp4_expert_ffn_workspace_bytes(64, 8, 4, 512, 256)
     assert lib.dg_fp8_fp4_expert_ffn_workspace_bytes(0, 8, 4, 512, 256) == 0
@@ -201,3 +201,71 @@ def test_contiguous_plan_query_is_host_only_and_may_split():
     assert p["splits"] > 1 and p["full_tiles"] % 256 == 0 and p["full_tiles"] < p["num_tiles"]
     p = dgm.dg_query_plan_contiguous(33280, 7168, 2048, 8, 256)
     assert p["splits"] == 1 and p["full_tiles"] == p["num_tiles"]
+
+
+# ---------------------------------------------------------------------------
+# split-K workspace: sized by a host-only query, bounded by one fp32 partial
+# tile per workgroup slot, never allocated by the library
+# ---------------------------------------------------------------------------
+_DENSE_FORMS = [dgm.FORM_NT, dgm.FORM_NN, dgm.FORM_TN, dgm.FORM_TT, dgm.FORM_NT_UE8M0]
+_CONFIG_SHAPES = [(128, 2112, 7168)] + [(m, n, k) for m in (64, 4096) for (n, k) in
+                                       [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168),
+                                        (7168, 2048)]]
+
+
+def _check_ws_bound(form, m, n, k, groups, cus, expected_m=0):
+    ws = dgm.dg_fp8_gemm_workspace_bytes(form, m, n, k, groups, expected_m, cus)
+    if form in _DENSE_FORMS or form in (dgm.FORM_CONTIGUOUS_NT, dgm.FORM_CONTIGUOUS_NN,
+                                        dgm.FORM_CONTIGUOUS_NT_UE8M0):
+        q = dgm.dg_query_plan_contiguous(m, n, k, groups, cus) if form >= dgm.FORM_CONTIGUOUS_NT else None
+        if form in (dgm.FORM_NT, dgm.FORM_NT_UE8M0, dgm.FORM_NN):
+            q = dgm.dg_query_plan(m, n, k, 1, cus)
+        if q is not None:
+            split_tiles = q["num_tiles"] - q["full_tiles"]
+            want = split_tiles * q["splits"] * q["block_m"] * q["block_n"] * 4 if q["splits"] > 1 else 0
+            assert ws == want, (form, m, n, k, q, ws)
+            assert split_tiles * q["splits"] <= cus, "at most one partial tile per workgroup slot"
+    # the bound every plan respects: one fp32 partial of the largest tile per slot
+    assert ws <= cus * 256 * 256 * 4, (form, m, n, k, groups, ws)
+    return ws
+
+
+def test_workspace_query_matches_the_plan_and_the_bound():
+    for (m, n, k) in _CONFIG_SHAPES:
+        for form in _DENSE_FORMS:
+            _check_ws_bound(form, m, n, k, 1, 256)
+    assert dgm.dg_fp8_gemm_workspace_bytes(dgm.FORM_NT, 128, 2112, 7168, 1, 0, 256) > 0   # skinny: split
+    assert dgm.dg_fp8_gemm_workspace_bytes(dgm.FORM_NT, 4096, 4096, 7168, 1, 0, 256) == 0  # whole rounds
+    # grouped configurations: 8 groups padded to 128 (contiguous), 32 x 256 (masked)
+    for (n, k) in [(4096, 7168), (7168, 2048)]:
+        for form in (dgm.FORM_CONTIGUOUS_NT, dgm.FORM_CONTIGUOUS_NN, dgm.FORM_CONTIGUOUS_NT_UE8M0):
+            _check_ws_bound(form, 33280, n, k, 8, 256)
+        for form in (dgm.FORM_MASKED_NT, dgm.FORM_MASKED_NT_UE8M0):
+            ws = _check_ws_bound(form, 256, n, k, 32, 256, expected_m=128)
+            p = dgm.dg_query_plan(256, n, k, 32, 256)
+            assert ws in (0, 256 * p["block_m"] * p["block_n"] * 4)
+
+
+def test_workspace_query_random_shapes_fit_the_bound():
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    for _ in range(1000):
+        m = int(rng.integers(1, 8193))
+        n = int(rng.integers(1, 2049)) * 16
+        k = int(rng.integers(1, 161)) * 128
+        cus = int(rng.choice([256, 255, 200, 128, 80, 32, 7, 1]))
+        form = int(rng.integers(0, 10))
+        groups = int(rng.integers(1, 33))
+        if form >= dgm.FORM_MASKED_NT:
+            _check_ws_bound(form, min(m, 1024), n, k, groups, cus, expected_m=int(rng.integers(0, 300)))
+        elif form >= dgm.FORM_CONTIGUOUS_NT:
+            _check_ws_bound(form, (m + 127) // 128 * 128, n, k, groups, cus)
+        else:
+            if form in (dgm.FORM_TN, dgm.FORM_TT):
+                m = (m + 15) // 16 * 16
+            _check_ws_bound(form, m, n, k, 1, cus)
+
+
+def test_workspace_query_rejects_invalid_sizes():
+    for args in [(dgm.FORM_NT, 0, 64, 128), (dgm.FORM_NT, 64, 40, 128), (dgm.FORM_NT, 64, 64, 100), (99, 64, 64, 128)]:
+        assert dgm.dg_fp8_gemm_workspace_bytes(*args, 1, 0, 256) == 0

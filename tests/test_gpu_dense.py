@@ -7,7 +7,7 @@ import torch
 import synth
 from oracle import formats as F
 from oracle import ref as R
-from tests.helpers import bits, check_bit_exact, check_parity, sentinel_like
+from tests.helpers import bits, check_bit_exact, check_parity, entries_in_chunks, sentinel_like, stratified_entries
 from tests.test_oracle import make_exact_case
 
 pytestmark = pytest.mark.gpu
@@ -123,7 +123,8 @@ def test_dense_config0_full_parity(dg):
 @pytest.mark.parametrize("mi,nki", [(m, j) for m in range(2) for j in range(6)])
 def test_dense_sweep_full_size_sampled(dg, mi, nki):
     """The dense sweep shapes at full size, generated on the device; the oracle
-    evaluates 4096 sampled outputs one by one (all rows for M=64)."""
+    evaluates, one by one, a random entry and the last-row/last-column entry of every
+    64 x 64 block of D, so every output tile of the plan is checked."""
     M = synth.DENSE_M[mi]
     N, K = synth.DENSE_NK[nki]
     g = synth.gen_dense(M, N, K, seed=synth.seed_for(1, mi * 6 + nki), backend="torch", device="cuda")
@@ -133,10 +134,7 @@ def test_dense_sweep_full_size_sampled(dg, mi, nki):
     db = bits(d)
     assert not (db == 0xFFFF).any()
     rng = np.random.default_rng(mi * 6 + nki)
-    rows = rng.integers(0, M, 4096)
-    cols = rng.integers(0, N, 4096)
-    rows[:8] = M - 1
-    cols[:8] = N - 1
+    rows, cols = stratified_entries(M, N, rng)
     a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
-    ref = R.fp8_gemm_nt_entries(a, sfa, b, sfb, c, rows, cols)
+    ref = entries_in_chunks(lambda r, q: R.fp8_gemm_nt_entries(a, sfa, b, sfb, c, r, q), rows, cols)
     check_parity(db[rows, cols], ref, what=f"sweep M={M} N={N} K={K}")

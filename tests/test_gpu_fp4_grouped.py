@@ -13,7 +13,7 @@ import torch
 
 import synth
 from oracle import ref as R
-from tests.helpers import SENTINEL, bits, check_bit_exact, check_parity, sentinel_like
+from tests.helpers import SENTINEL, bits, check_bit_exact, check_parity, sentinel_like, stratified_lines
 
 pytestmark = pytest.mark.gpu
 
@@ -128,8 +128,11 @@ def test_fp4_masked_exact_integer_case_bit_exact(dg):
 
 
 def test_fp4_contiguous_full_size_sampled(dg):
-    """8 groups, ~32k rows, N 4096, K 7168 on the device; 48 sampled rows per group
-    against the oracle."""
+    """8 groups, ~32k rows, N 4096, K 7168 on the device; per group, the oracle evaluates
+    the rows x columns made of one random and the last index of every 64-row block of the
+    group's rows and every 64-column block, so every output tile is checked, its last row
+    and column included.  (The weight scales are per row of B, so a column subset of B is
+    an exact subproblem.)"""
     G, N, K = 8, 4096, 7168
     g = synth.gen_fp4_contiguous(G, 32768, N, K, seed=515, backend="torch", device="cuda")
     M = int(g["M"])
@@ -144,14 +147,14 @@ def test_fp4_contiguous_full_size_sampled(dg):
     got, want = [], []
     b, b_sf = synth.to_numpy(g["b"]), synth.to_numpy(g["b_sf"])
     for grp in range(G):
-        rows = np.nonzero(mi == grp)[0]
+        rows = stratified_lines(M, rng, valid=mi == grp)
         if rows.size == 0:
             continue
-        rows = np.sort(rng.choice(rows, min(48, rows.size), replace=False))
+        cols = stratified_lines(N, rng)
         t_rows = torch.from_numpy(rows).cuda()
         a, a_sf = synth.to_numpy(g["a"][t_rows]), synth.to_numpy(g["a_sf"][t_rows])
-        want.append(R.fp8_fp4_gemm_nt(a, a_sf, b[grp], b_sf[grp]))
-        got.append(db[rows])
+        want.append(R.fp8_fp4_gemm_nt(a, a_sf, b[grp][cols], b_sf[grp][cols]).ravel())
+        got.append(db[np.ix_(rows, cols)].ravel())
     check_parity(np.concatenate(got), np.concatenate(want), what="fp4 contig full size")
 
 

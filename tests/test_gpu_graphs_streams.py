@@ -1,6 +1,7 @@
 """Stream behaviour of the C ABI on the GPU: calls enqueue on the caller's stream without
-host synchronisation, so they can be captured into a HIP graph and replayed, and calls on
-different streams may run at the same time (the split-K workspace is per stream).
+host synchronisation or allocation, so they can be captured into a HIP graph and replayed,
+and calls on different streams may run at the same time (each call's split-K workspace is
+the caller's).
 
 Each replay is checked bit for bit against an eager call of the same inputs, with eager
 work on the same buffers between the replays.
@@ -30,9 +31,6 @@ def test_dense_graph_capture_replays_match_eager(dg, M, N, K):
     want = bits(d_ref)
     s = torch.cuda.Stream()
     d = torch.empty(M, N, dtype=torch.int16, device="cuda")
-    with torch.cuda.stream(s):
-        _dense_call(dg, g, d)            # first call on this stream: its workspace exists before capture
-    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s):
         _dense_call(dg, g, d)
@@ -44,6 +42,39 @@ def test_dense_graph_capture_replays_match_eager(dg, M, N, K):
         assert np.array_equal(bits(d), want), f"replay {rep} differs from the eager result"
 
 
+def test_graph_replay_after_a_larger_eager_split_call(dg):
+    """A captured split call keeps its own workspace: a larger split call run eagerly on
+    the same stream after the capture (its own, larger workspace) does not disturb the
+    replays, which match the eager result bit for bit."""
+    small, large = (16, 256, 2048), (64, 2112, 7168)
+    gs = synth.gen_dense(*small, seed=31, backend="torch", device="cuda")
+    gl = synth.gen_dense(*large, seed=32, backend="torch", device="cuda")
+    for shp in (small, large):
+        assert dg.dg_fp8_gemm_workspace_bytes(dg.FORM_NT, *shp) > 0, "both calls must split along K"
+    assert dg.dg_fp8_gemm_workspace_bytes(dg.FORM_NT, *large) > dg.dg_fp8_gemm_workspace_bytes(dg.FORM_NT, *small)
+    want_s = torch.empty(small[0], small[1], dtype=torch.int16, device="cuda")
+    want_l = torch.empty(large[0], large[1], dtype=torch.int16, device="cuda")
+    _dense_call(dg, gs, want_s)
+    _dense_call(dg, gl, want_l)
+    torch.cuda.synchronize()
+    ws_s, ws_l = bits(want_s), bits(want_l)
+    s = torch.cuda.Stream()
+    d = torch.empty(small[0], small[1], dtype=torch.int16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        _dense_call(dg, gs, d)
+    dl = torch.empty(large[0], large[1], dtype=torch.int16, device="cuda")
+    for rep in range(3):
+        with torch.cuda.stream(s):
+            dl.fill_(-1)
+            _dense_call(dg, gl, dl)          # larger split call, eager, same stream
+            d.fill_(-1)
+            graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(d), ws_s), f"replay {rep} differs from the eager result"
+        assert np.array_equal(bits(dl), ws_l), f"eager large call {rep} differs"
+
+
 def test_masked_graph_capture_replays_match_eager(dg):
     """The masked form reads masked_m only on the device: new counts written into the
     same buffer between replays change what each replay computes."""
@@ -53,9 +84,6 @@ def test_masked_graph_capture_replays_match_eager(dg):
     mm = g["masked_m"]
     s = torch.cuda.Stream()
     d = torch.full((G, max_m, N), -1, dtype=torch.int16, device="cuda")
-    with torch.cuda.stream(s):
-        dg.dg_m_grouped_fp8_gemm_nt_masked(g["a"], g["sfa"], g["b"], g["sfb"], mm, d, 128)
-    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s):
         dg.dg_m_grouped_fp8_gemm_nt_masked(g["a"], g["sfa"], g["b"], g["sfb"], mm, d, 128)
@@ -97,7 +125,7 @@ def test_ffn_graph_capture_replays_match_eager(dg):
 
 
 def test_two_streams_concurrently_match_single_stream(dg):
-    """Split-K calls on two streams at once (each stream has its own workspace) give the
+    """Split-K calls on two streams at once (each call with its own workspace) give the
     single-stream results."""
     shapes = [(64, 2112, 7168), (96, 4096, 7168)]
     gens = [synth.gen_dense(M, N, K, seed=500 + M, backend="torch", device="cuda") for M, N, K in shapes]

@@ -12,7 +12,7 @@ import torch
 
 import synth
 from oracle import ref as R
-from tests.helpers import SENTINEL, bits, check_bit_exact, check_parity, sentinel_like
+from tests.helpers import SENTINEL, bits, check_bit_exact, check_parity, entries_in_chunks, sentinel_like, stratified_entries
 from tests.test_oracle import make_exact_case
 
 pytestmark = pytest.mark.gpu
@@ -133,15 +133,14 @@ def test_contiguous_full_size_sampled(dg, nki):
     assert not np.any(db[valid] == SENTINEL)
     a, sfa, b, sfb = _np(g, "a", "sfa", "b", "sfb")
     rng = np.random.default_rng(nki)
-    vrows = np.nonzero(valid)[0]
-    rows = rng.choice(vrows, 4096)
-    cols = rng.integers(0, N, 4096)
+    rows, cols = stratified_entries(M, N, rng, valid_rows=valid)   # every tile of valid rows
     got, want = [], []
     for grp in range(8):
         sel = mi[rows] == grp
         if not sel.any():
             continue
-        want.append(R.fp8_gemm_nt_entries(a, sfa, b[grp], sfb[grp], None, rows[sel], cols[sel]))
+        want.append(entries_in_chunks(lambda r, q: R.fp8_gemm_nt_entries(a, sfa, b[grp], sfb[grp], None, r, q),
+                                      rows[sel], cols[sel]))
         got.append(db[rows[sel], cols[sel]])
     check_parity(np.concatenate(got), np.concatenate(want), what=f"contig full N{N} K{K}")
 

@@ -12,7 +12,7 @@ import torch
 
 import synth
 from oracle import ref as R
-from tests.helpers import bits, check_bit_exact, check_parity, sentinel_like
+from tests.helpers import bits, check_bit_exact, check_parity, entries_in_chunks, sentinel_like, stratified_entries
 from tests.test_oracle import make_exact_case
 
 pytestmark = pytest.mark.gpu
@@ -72,8 +72,8 @@ def test_k_grouped_counts_are_rounded_and_cut_at_k(dg):
 
 
 def test_k_grouped_full_size_sampled(dg):
-    """8 groups from 32768 tokens, M 4096, N 7168 on the device; sampled entries of every
-    group against the oracle."""
+    """8 groups from 32768 tokens, M 4096, N 7168 on the device; in every group, a random
+    entry and the last-row / last-column entry of every 64 x 64 block against the oracle."""
     G, M, N = 8, 4096, 7168
     g = synth.gen_kgrouped_tn(G, 32768, M, N, seed=909, backend="torch", device="cuda")
     d = sentinel_like((G, M, N))
@@ -84,12 +84,11 @@ def test_k_grouped_full_size_sampled(dg):
     rng = np.random.default_rng(90)
     k0 = 0
     for grp, kg in enumerate(ks):
-        rows = np.repeat(rng.choice(M, 8, replace=False), 4)
-        cols = rng.choice(N, 32)
+        rows, cols = stratified_entries(M, N, rng)
         a_mk = synth.to_numpy(g["a"][k0:k0 + kg].t().contiguous())
         b_nk = synth.to_numpy(g["b"][k0:k0 + kg].t().contiguous())
         sfa = synth.to_numpy(g["sfa"][k0 // 128:(k0 + kg) // 128])
         sfb = synth.to_numpy(g["sfb"][:, k0 // 128:(k0 + kg) // 128])
-        want = R.fp8_gemm_nt_entries(a_mk, sfa, b_nk, sfb, None, rows, cols)
+        want = entries_in_chunks(lambda r, q: R.fp8_gemm_nt_entries(a_mk, sfa, b_nk, sfb, None, r, q), rows, cols)
         check_parity(db[grp][rows, cols], want, what=f"k-grouped full size group {grp}")
         k0 += kg

@@ -13,7 +13,7 @@ import torch
 
 import synth
 from oracle import ref as R
-from tests.helpers import SENTINEL, bits, check_bit_exact, check_parity, sentinel_like
+from tests.helpers import SENTINEL, bits, check_bit_exact, check_parity, entries_in_chunks, sentinel_like, stratified_entries
 from tests.test_oracle import make_exact_case
 
 pytestmark = pytest.mark.gpu
@@ -71,19 +71,19 @@ def test_nn_contiguous_parity_and_padding_rows(dg):
 
 
 def test_nn_dense_full_size_sampled(dg):
-    """M 4096, N 7168, K 7168 with C on the device; 8 columns in each of 64 sampled rows
-    against the oracle entry by entry (B transposed back for the NT entry evaluator)."""
+    """M 4096, N 7168, K 7168 with C on the device; a random entry and the last-row /
+    last-column entry of every 64 x 64 block against the oracle entry by entry (B
+    transposed back for the NT entry evaluator)."""
     M, N, K = 4096, 7168, 7168
     g = synth.gen_dense_nn(M, N, K, seed=707, backend="torch", device="cuda")
     d = sentinel_like((M, N))
     dg.dg_fp8_gemm_nn(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
     torch.cuda.synchronize()
     rng = np.random.default_rng(70)
-    rows = np.repeat(rng.choice(M, 64, replace=False), 8)
-    cols = np.concatenate([rng.choice(N, 8, replace=False) for _ in range(64)])
+    rows, cols = stratified_entries(M, N, rng)
     a, sfa, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "sfb", "c"))
     b_nk = synth.to_numpy(g["b"].t().contiguous())
-    want = R.fp8_gemm_nt_entries(a, sfa, b_nk, sfb, c, rows, cols)
+    want = entries_in_chunks(lambda r, q: R.fp8_gemm_nt_entries(a, sfa, b_nk, sfb, c, r, q), rows, cols)
     check_parity(bits(d)[rows, cols], want, what="nn full size sampled")
 
 
@@ -145,10 +145,9 @@ def test_tn_dense_full_size_sampled(dg):
     dg.dg_fp8_gemm_tn(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
     torch.cuda.synchronize()
     rng = np.random.default_rng(80)
-    rows = np.repeat(rng.choice(M, 64, replace=False), 8)
-    cols = np.concatenate([rng.choice(N, 8, replace=False) for _ in range(64)])
+    rows, cols = stratified_entries(M, N, rng)
     sfa, sfb, c = (synth.to_numpy(g[k]) for k in ("sfa", "sfb", "c"))
     a_mk = synth.to_numpy(g["a"].t().contiguous())
     b_nk = synth.to_numpy(g["b"].t().contiguous())
-    want = R.fp8_gemm_nt_entries(a_mk, sfa, b_nk, sfb, c, rows, cols)
+    want = entries_in_chunks(lambda r, q: R.fp8_gemm_nt_entries(a_mk, sfa, b_nk, sfb, c, r, q), rows, cols)
     check_parity(bits(d)[rows, cols], want, what="tn full size sampled")

@@ -1,7 +1,7 @@
-"""Split K (skinny M): the dense GEMM sums K slices into an fp32 workspace and a
-second kernel adds them in slice order, then C, then rounds to bf16.  Parity
-against the oracle, bit-exact integer cases, uneven slices, C aliased with D and
-workspace growth on one stream."""
+"""Split K (skinny M): the dense GEMM sums K slices into fp32 partial tiles in the
+caller's workspace and a second kernel adds them in slice order, then C, then
+rounds to bf16.  Parity against the oracle, bit-exact integer cases, uneven
+slices, C aliased with D, and workspaces of every size on one stream."""
 
 import numpy as np
 import pytest
@@ -67,10 +67,37 @@ def test_splitk_d_aliases_c(dg):
     check_parity(bits(cd), R.fp8_gemm_nt(a, sfa, b, sfb, c), what="split, d == c")
 
 
-def test_splitk_workspace_grows_on_one_stream(dg):
-    """A small split problem, then a larger one, then the small one again on a
-    side stream: the workspace is reallocated and each result stays correct."""
+def test_splitk_caller_workspace(dg):
+    """The partials live in the caller's workspace: a too-small one is rejected before
+    anything is enqueued (D keeps its sentinel), an exact-size one and a larger one
+    holding garbage give the same bits, and one workspace serves a small call, a
+    larger call and the small call again on a side stream."""
+    M, N, K = 128, 2112, 128 * 32
+    need = dgm.dg_fp8_gemm_workspace_bytes(dgm.FORM_NT, M, N, K)
+    assert need > 0
+    g = synth.gen_dense(M, N, K, seed=99, with_c=True)
+    a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+    ins = [_dev(x) for x in (a, sfa, b, sfb, c)]
+    d = sentinel_like((M, N))
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dgm.DgError) as e:
+        dg.dg_fp8_gemm_nt(*ins, d, workspace=small)
+    assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert (bits(d) == 0xFFFF).all(), "a rejected call must write nothing"
+    exact = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dg.dg_fp8_gemm_nt(*ins, d, workspace=exact)
+    torch.cuda.synchronize()
+    want = bits(d)
+    check_parity(want, R.fp8_gemm_nt(a, sfa, b, sfb, c), what="split, exact workspace")
+    big = torch.full((need + 4096,), 0xAB, dtype=torch.uint8, device="cuda")
+    d2 = sentinel_like((M, N))
+    dg.dg_fp8_gemm_nt(*ins, d2, workspace=big)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d2), want)
     shapes = [(16, 256, 128 * 16), (128, 2112, 128 * 32), (16, 256, 128 * 16)]
+    ws = torch.empty(max(dgm.dg_fp8_gemm_workspace_bytes(dgm.FORM_NT, *s) for s in shapes), dtype=torch.uint8,
+                     device="cuda")
     side = torch.cuda.Stream()
     for i, (M, N, K) in enumerate(shapes):
         assert _splits(M, N, K) > 1
@@ -81,9 +108,9 @@ def test_splitk_workspace_grows_on_one_stream(dg):
         torch.cuda.synchronize()
         if i == 2:
             with torch.cuda.stream(side):
-                dg.dg_fp8_gemm_nt(*ins, d)
+                dg.dg_fp8_gemm_nt(*ins, d, workspace=ws)
         else:
-            dg.dg_fp8_gemm_nt(*ins, d)
+            dg.dg_fp8_gemm_nt(*ins, d, workspace=ws)
         torch.cuda.synchronize()
         check_parity(bits(d), R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"split ws {M}x{N}x{K}")
 

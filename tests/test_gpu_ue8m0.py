@@ -13,7 +13,7 @@ import torch
 
 import synth
 from oracle import ref as R
-from tests.helpers import SENTINEL, bits, check_bit_exact, check_parity, sentinel_like
+from tests.helpers import SENTINEL, bits, check_bit_exact, check_parity, entries_in_chunks, sentinel_like, stratified_entries
 from tests.test_oracle import make_exact_case
 
 pytestmark = pytest.mark.gpu
@@ -106,17 +106,16 @@ def test_ue8m0_masked_parity_and_masked_rows(dg, K):
 
 
 def test_ue8m0_dense_full_size_sampled(dg):
-    """M 4096, N 7168, K 16384 with C, on the device; 8 columns in each of 64 sampled rows
-    against the oracle entry by entry."""
+    """M 4096, N 7168, K 16384 with C, on the device; a random entry and the last-row /
+    last-column entry of every 64 x 64 block against the oracle entry by entry."""
     M, N, K = 4096, 7168, 16384
     g = synth.gen_dense_ue8m0(M, N, K, seed=606, backend="torch", device="cuda")
     d = sentinel_like((M, N))
     dg.dg_fp8_gemm_nt_ue8m0(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
     torch.cuda.synchronize()
     rng = np.random.default_rng(60)
-    rows = np.repeat(rng.choice(M, 64, replace=False), 8)
-    cols = np.concatenate([rng.choice(N, 8, replace=False) for _ in range(64)])
+    rows, cols = stratified_entries(M, N, rng)
     a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
-    want = R.fp8_gemm_nt_ue8m0_entries(a, sfa, b, sfb, c, rows, cols)
+    want = entries_in_chunks(lambda r, q: R.fp8_gemm_nt_ue8m0_entries(a, sfa, b, sfb, c, r, q), rows, cols)
     got = bits(d)[rows, cols]
     check_parity(got, want, what="ue8m0 full size sampled")
