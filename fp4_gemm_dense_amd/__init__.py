@@ -22,7 +22,7 @@ _lib = None
 
 DG_OK = 0
 STATUS_NAMES = {0: "DG_OK", 1: "DG_ERR_INVALID_ARG", 2: "DG_ERR_UNSUPPORTED", 3: "DG_ERR_HIP",
-                4: "DG_ERR_NO_DEVICE"}
+                4: "DG_ERR_NO_DEVICE", 5: "DG_ERR_SCRATCH_LIMIT"}
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -46,6 +46,7 @@ _SIGNATURES = {
     "dg_fp8_fp4_expert_ffn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "dg_fp8_fp4_expert_ffn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "dg_fp8_gemm_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "dg_fp8_gemm_nt_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "dg_get_mk_alignment_for_contiguous_layout": (_I, []),
     "dg_set_num_cus": (_I, [_I]),
     "dg_get_num_cus": (_I, []),
@@ -172,6 +173,25 @@ def dg_fp8_gemm_nt(a, sfa, b, sfb, c, d, workspace=None):
     wp, wn, _keep = _workspace(FORM_NT, M, N, K, 1, 0, a.device, workspace)
     _check("dg_fp8_gemm_nt", L.dg_fp8_gemm_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c), _ptr(d),
                                               M, N, K, wp, wn, _stream(a)))
+    return d
+
+
+def dg_fp8_gemm_nt_noalloc(a, sfa, b, sfb, c, d):
+    """d = c + a . b^T like dg_fp8_gemm_nt, with the split-K partials in the library's static
+    per-GPU scratch buffer (24 MiB): the call allocates nothing.  Calls that overlap in time
+    on one GPU race on that buffer."""
+    L = lib()
+    M, K = a.shape
+    N = b.shape[0]
+    _req(a, _U8, (M, K), "a")
+    _req(b, _U8, (N, K), "b")
+    _req(sfa, torch.float32, (K // 128, M), "sfa")
+    _req(sfb, torch.float32, (_nb(N), K // 128), "sfb")
+    if c is not None:
+        _req_bf16(c, (M, N), "c")
+    _req_bf16(d, (M, N), "d")
+    _check("dg_fp8_gemm_nt_noalloc", L.dg_fp8_gemm_nt_noalloc(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(c),
+                                                              _ptr(d), M, N, K, _stream(a)))
     return d
 
 

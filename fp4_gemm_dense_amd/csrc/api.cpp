@@ -164,12 +164,8 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* worksp
   return e == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
-}  // namespace dg
-
-using namespace dg;
-
 // The three forms; ue8m0 selects packed UE8M0 scale words instead of fp32 scales.
-static int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, const uint16_t* c,
+int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, const uint16_t* c,
                        uint16_t* d, int m, int n, int k, void* ws, size_t ws_bytes, void* stream, int flags) {
   try {
     if (!a || !sfa || !b || !sfb || !d) return DG_ERR_INVALID_ARG;
@@ -190,6 +186,10 @@ static int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, cons
     return DG_ERR_HIP;
   }
 }
+
+}  // namespace dg
+
+using namespace dg;
 
 static int contiguous_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb,
                             const int32_t* m_indices, uint16_t* d, int m, int n, int k, int num_groups, void* ws,
@@ -423,6 +423,7 @@ const char* dg_status_string(int status) {
     case DG_ERR_UNSUPPORTED: return "unsupported shape";
     case DG_ERR_HIP: return "HIP runtime error";
     case DG_ERR_NO_DEVICE: return "no gfx950 device";
+    case DG_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the library's static buffer holds";
   }
   return "unknown status";
 }

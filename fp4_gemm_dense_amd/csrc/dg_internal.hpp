@@ -152,6 +152,11 @@ hipError_t launch_kgroup_zero(const Fp8GemmParams& p, hipStream_t stream);
 // Launches the kernel chosen by plan on stream; returns a hipError_t.
 hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mode, hipStream_t stream);
 
+// The dense GEMM entry (argument checks, plan, launch) behind dg_fp8_gemm_nt and its
+// layout / UE8M0 variants; flags as MODE_* above.  Returns a dg_status.
+int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, const uint16_t* c,
+                uint16_t* d, int m, int n, int k, void* ws, size_t ws_bytes, void* stream, int flags);
+
 // Workgroups per CU the given kernel reaches (cached; computed on first use).
 int fp8_gemm_blocks_per_cu(int kernel_id, int mode);
 

@@ -58,7 +58,8 @@ typedef enum dg_status {
   DG_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, misalignment, small workspace */
   DG_ERR_UNSUPPORTED = 2,   /* shape outside what the kernels support (e.g. K % 128 != 0)   */
   DG_ERR_HIP = 3,           /* a HIP runtime error while launching                            */
-  DG_ERR_NO_DEVICE = 4      /* no usable gfx950 device is current                             */
+  DG_ERR_NO_DEVICE = 4,     /* no usable gfx950 device is current                             */
+  DG_ERR_SCRATCH_LIMIT = 5  /* dg_fp8_gemm_nt_noalloc: the plan needs more than its static scratch */
 } dg_status;
 
 /*
@@ -84,6 +85,23 @@ typedef enum dg_status {
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    const uint16_t* c, uint16_t* d, int m, int n, int k, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * The dense NT GEMM for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same operation, arguments (without the workspace), kernels and results as
+ * dg_fp8_gemm_nt, with the split-K partial tiles in a static device buffer of
+ * this library instead of a caller workspace.  The buffer holds 24 MiB per GPU
+ * (a file-scope device array: each GPU the library runs on keeps its copy until
+ * the process ends); a problem whose plan needs more (dg_fp8_gemm_workspace_bytes
+ * with DG_FORM_NT above 24 MiB) is rejected with DG_ERR_SCRATCH_LIMIT before
+ * anything is enqueued.  The call allocates nothing: no hipMalloc, no allocating
+ * library routine.  All calls on one GPU share the buffer and its contents are
+ * left from the last call (nothing in it needs clearing), so calls that may
+ * overlap in time on one GPU -- on different streams without ordering -- race.
+ */
+int dg_fp8_gemm_nt_noalloc(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                           const uint16_t* c, uint16_t* d, int m, int n, int k, void* stream);
 
 /*
  * M-grouped GEMM, contiguous layout (prefill / training forward).  Rows of all
