@@ -32,18 +32,20 @@ Other workloads (one form per run):
   --config 8  K-grouped GEMM in the TN layout: 8 groups from 32768 tokens (a
               weight-gradient shape), (M,N) in {(4096,7168), (7168,2048)}
 
-Caches: before every timed call a 512 MiB scratch buffer is written (outside
-the call's events), so no operand is left in the 4 MB L2s or the 256 MB
-Infinity Cache from an earlier call: every call starts from HBM.
+Caches: each call is timed in a batch over rotating copies of its inputs and
+outputs (as many as make 768 MB of distinct data, at least one), so no call
+finds its operands in the 4 MB L2s or the 256 MB Infinity Cache: every call
+starts from HBM.  A timed batch needs one pair of events (which alone read
+about 4.6 us on this system) for many calls.
 
 Algorithmic work: flops = 2 * (valid rows) * N * K (the FFN counts linear1 and
 linear2 over routed pairs); bytes = every distinct operand and scale byte read
 once plus valid outputs written once (re-reads, padding rows and workspace
-traffic excluded).  Timing: HIP events on the launch stream around each call,
-inside one timed region of K steps bracketed by device synchronisation; per
-call the median and the minimum over the steps are reported, and ms_per_step
-is the mean over the steps of the summed call times (the cache flushes between
-calls are not part of it; step_wall_ms, which includes them, is reported too).
+traffic excluded).  Timing: HIP events on the launch stream around each
+call's batch, inside one timed region of K steps bracketed by device
+synchronisation; per call the median and the minimum over the steps are
+reported, and ms_per_step is the mean over the steps of the summed per-call
+times (step_wall_ms, the whole region over K, is reported too).
 
 Prints ONE JSON line.
 """
@@ -79,7 +81,6 @@ def parse():
                     help="M,N,K: time only this dense shape (C bf16), for profiling")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
-    ap.add_argument("--no-flush", action="store_true", help="do not write the cache-flush buffer between calls")
     ap.add_argument("--only", type=str, default=None,
                     help="time only the calls of one kernel group (e.g. 'contiguous 128x256'), for counter runs")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CALIB_DIR", "KEY"),
@@ -117,6 +118,22 @@ def _tile(plan):
     return f"{plan['block_m']}x{plan['block_n']}"
 
 
+# Calls are timed in batches over rotating copies of their inputs and outputs:
+# a batch touches at least this many distinct bytes (three times the 256 MB
+# Infinity Cache), so every call finds its operands in HBM, not in a cache.
+ROTATE_BYTES = 768 << 20
+
+
+def _replicas(g, d, nbytes):
+    """[(inputs, output)] copies for one call: g and d, then device copies of them."""
+    import torch
+    n = max(1, min(64, -(-ROTATE_BYTES // max(int(nbytes), 1))))
+    out = [(g, d)]
+    for _ in range(n - 1):
+        out.append(({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in g.items()}, torch.empty_like(d)))
+    return out
+
+
 # ----------------------------------------------------------------------------
 # workloads: each item = one library call with its algorithmic flops / bytes
 # ----------------------------------------------------------------------------
@@ -147,9 +164,9 @@ def items_dense(config, only=None):
         ws = _ws(dg.FORM_NT_UE8M0 if ue else dg.FORM_NT, M, N, K)
         plan = dg.dg_query_plan(M, N, K)
 
-        def run(g=g, d=d, gemm=gemm, ws=ws):
-            gemm(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d, workspace=ws)
-        items.append(dict(kind=kind, run=run, g=g, flops=2.0 * M * N * K, bytes=nbytes, label=f"M{M}_N{N}_K{K}",
+        def mk(g, d, gemm=gemm, ws=ws):
+            return lambda: gemm(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d, workspace=ws)
+        items.append(dict(kind=kind, runs=[mk(*r) for r in _replicas(g, d, nbytes)], g=g, flops=2.0 * M * N * K, bytes=nbytes, label=f"M{M}_N{N}_K{K}",
                           shape=(M, N, K), plan=plan, kernel=f"{kind} {_tile(plan)}"))
     return items
 
@@ -172,9 +189,9 @@ def items_contiguous(nn=False):
         ws = _ws(dg.FORM_CONTIGUOUS_NN if nn else dg.FORM_CONTIGUOUS_NT, M, N, K, 8)
         plan = dg.dg_query_plan_contiguous(M, N, K, 8)
 
-        def run(g=g, d=d, ws=ws):
-            gemm(g["a"], g["sfa"], g["b"], g["sfb"], g["m_indices"], d, workspace=ws)
-        items.append(dict(kind=kind, run=run, g=g, flops=2.0 * valid * N * K, bytes=nbytes,
+        def mk(g, d, ws=ws):
+            return lambda: gemm(g["a"], g["sfa"], g["b"], g["sfb"], g["m_indices"], d, workspace=ws)
+        items.append(dict(kind=kind, runs=[mk(*r) for r in _replicas(g, d, nbytes)], g=g, flops=2.0 * valid * N * K, bytes=nbytes,
                           label=f"G8_contig{'_nn' if nn else ''}_N{N}_K{K}", shape=(M, N, K), plan=plan,
                           kernel=f"{kind} {_tile(plan)}"))
     return items
@@ -192,9 +209,9 @@ def items_kgrouped():
         valid = sum(g["counts"])
         nbytes = K * (M + N) + 4 * (K // 128) * (M + nb(N)) + 4 * 8 + 2 * 8 * M * N
 
-        def run(g=g, d=d):
-            dg.dg_k_grouped_fp8_gemm_tn_contiguous(g["a"], g["sfa"], g["b"], g["sfb"], g["ks"], d)
-        items.append(dict(kind="kgrouped", run=run, g=g, flops=2.0 * valid * M * N, bytes=nbytes,
+        def mk(g, d):
+            return lambda: dg.dg_k_grouped_fp8_gemm_tn_contiguous(g["a"], g["sfa"], g["b"], g["sfb"], g["ks"], d)
+        items.append(dict(kind="kgrouped", runs=[mk(*r) for r in _replicas(g, d, nbytes)], g=g, flops=2.0 * valid * M * N, bytes=nbytes,
                           label=f"G8_kgrouped_tn_M{M}_N{N}", shape=(M, N, K), kernel="kgrouped"))
     return items
 
@@ -213,10 +230,10 @@ def items_masked():
         nbytes = valid * K + groups_hit * (N * K + 4 * nb(N) * (K // 128)) + 4 * (K // 128) * valid + 4 * 32 + 2 * valid * N
         ws = _ws(dg.FORM_MASKED_NT, 256, N, K, 32, 128)
 
-        def run(g=g, d=d, ws=ws):
-            dg.dg_m_grouped_fp8_gemm_nt_masked(g["a"], g["sfa"], g["b"], g["sfb"], g["masked_m"], d, 128,
-                                               workspace=ws)
-        items.append(dict(kind="masked", run=run, g=g, flops=2.0 * valid * N * K, bytes=nbytes,
+        def mk(g, d, ws=ws):
+            return lambda: dg.dg_m_grouped_fp8_gemm_nt_masked(g["a"], g["sfa"], g["b"], g["sfb"], g["masked_m"], d,
+                                                              128, workspace=ws)
+        items.append(dict(kind="masked", runs=[mk(*r) for r in _replicas(g, d, nbytes)], g=g, flops=2.0 * valid * N * K, bytes=nbytes,
                           label=f"G32_masked_N{N}_K{K}", shape=(256, N, K), masked_m=mm, kernel="masked"))
     return items
 
@@ -234,11 +251,12 @@ def items_fp4_contiguous():
         groups_hit = sum(1 for c in g["counts"] if c > 0)
         nbytes = (valid * K + groups_hit * (N * K // 2 + N * (K // 32)) + valid * 4 * ((K // 128 + 3) // 4)
                   + 4 * M + 2 * valid * N)
-        b_sf_t = dg.dg_transform_fp4_weight_sf(g["b_sf"])     # weight pre-transform, once per weight set
+        g["b_sf_t"] = dg.dg_transform_fp4_weight_sf(g["b_sf"])     # weight pre-transform, once per weight set
 
-        def run(g=g, d=d, b_sf_t=b_sf_t):
-            dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(g["a"], g["a_sf"], g["b"], b_sf_t, g["m_indices"], d)
-        items.append(dict(kind="fp4_contiguous", run=run, g=g, flops=2.0 * valid * N * K, bytes=nbytes,
+        def mk(g, d):
+            return lambda: dg.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(g["a"], g["a_sf"], g["b"], g["b_sf_t"],
+                                                                      g["m_indices"], d)
+        items.append(dict(kind="fp4_contiguous", runs=[mk(*r) for r in _replicas(g, d, nbytes)], g=g, flops=2.0 * valid * N * K, bytes=nbytes,
                           label=f"G8_fp4_contig_N{N}_K{K}", shape=(M, N, K), kernel="fp4_contiguous"))
     return items
 
@@ -262,11 +280,13 @@ def items_ffn():
     nbytes = w_bytes + T * H + T * (H // 128) + T * k * 8 + T * H * 2
 
     # weight pre-transform, once per weight set (outside the timed step)
-    (w1, w1_sf), (w2, w2_sf) = dg.transform_weights_for_expert_ffn((g["w1"], g["w1_sf"]), (g["w2"], g["w2_sf"]))
+    (g["w1t"], g["w1_sft"]), (g["w2t"], g["w2_sft"]) = dg.transform_weights_for_expert_ffn(
+        (g["w1"], g["w1_sf"]), (g["w2"], g["w2_sf"]))
 
-    def run():
-        dg.dg_fp8_fp4_expert_ffn(g["x"], g["x_sf"], g["topk_idx"], g["topk_w"], w1, w1_sf, w2, w2_sf, y, 0, ws)
-    return [dict(kind="ffn", run=run, g=g, flops=2.0 * P * (2 * I * H + H * I), bytes=nbytes,
+    def mk(g, y):
+        return lambda: dg.dg_fp8_fp4_expert_ffn(g["x"], g["x_sf"], g["topk_idx"], g["topk_w"], g["w1t"], g["w1_sft"],
+                                                g["w2t"], g["w2_sft"], y, 0, ws)
+    return [dict(kind="ffn", runs=[mk(*r) for r in _replicas(g, y, nbytes)], g=g, flops=2.0 * P * (2 * I * H + H * I), bytes=nbytes,
                  label=f"ffn_T{T}_H{H}_I{I}_E{E}_pairs{P}", shape=(T, H, I), pairs=P, kernel="ffn")]
 
 
@@ -596,13 +616,10 @@ def main():
             sys.exit(f"--only {args.only!r}: no call of this workload uses that kernel group")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    # written before every timed call, outside its events: no operand of an earlier
-    # call is left in the L2s or the Infinity Cache
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-
     for w in range(args.warmup):
         for it in items:
-            it["run"]()
+            for run in it["runs"]:
+                run()
     torch.cuda.synchronize()
 
     n = len(items)
@@ -615,10 +632,9 @@ def main():
     t_start.record(stream)
     for s in range(args.steps):
         for i, it in enumerate(items):
-            if flush is not None:
-                flush.fill_((s * n + i) & 0x7f)
             ev[s][i][0].record(stream)
-            it["run"]()
+            for run in it["runs"]:
+                run()
             ev[s][i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -627,18 +643,19 @@ def main():
 
     per = []
     for i, it in enumerate(items):
-        durs = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        durs = [ev[s][i][0].elapsed_time(ev[s][i][1]) / len(it["runs"]) for s in range(args.steps)]
         it["durs"] = durs
         it["mean_ms"] = statistics.mean(durs)
         it["med_ms"] = med = statistics.median(durs)
         it["min_ms"] = mn = min(durs)
-        per.append(dict(shape=it["label"], form=it["kind"], kernel=it["kernel"], ms=med, min_ms=mn,
+        per.append(dict(shape=it["label"], form=it["kind"], kernel=it["kernel"], batch=len(it["runs"]), ms=med,
+                        min_ms=mn,
                         tflops=it["flops"] / med / 1e9, gbs=it["bytes"] / med / 1e6,
                         mfma_frac=it["flops"] / med / 1e9 / PEAK_FP8_TFLOPS,
                         hbm_frac=it["bytes"] / med / 1e6 / PEAK_HBM_GBS,
                         bound=bound_of(it), roofline_frac=roofline_time(it) / (med / 1e3)))
-    ms_per_step = statistics.mean(sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(n))
-                                  for s in range(args.steps))
+    ms_per_step = statistics.mean(sum(ev[s][i][0].elapsed_time(ev[s][i][1]) / len(items[i]["runs"])
+                                      for i in range(n)) for s in range(args.steps))
     step_flops = sum(it["flops"] for it in items)
     value = step_flops / (ms_per_step / 1e3) / 1e12
 
@@ -686,7 +703,7 @@ def main():
         "data": "synthetic (seeded N(0,1), quantised as the workload states)",
         "config": {"workload": WORKLOADS[cfg] if args.shape is None else f"dense NT {args.shape}",
                    "calls_per_step": n, "parallelism": "none (1 GPU)",
-                   "cache": "none" if flush is None else "L2 and Infinity Cache flushed before every call"},
+                   "cache": "cold: each call timed in a batch over rotating copies of >= 768 MB of operands"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "forms": forms,

@@ -97,12 +97,25 @@ static CallPlan plan_call(Fp8GemmParams& p, int mode, int expected_m, int flags,
     return cp;
   }
   // DG_FORCE_KERNEL=<id>: override the heuristic's tile choice (for tuning)
-  if (const char* fk = std::getenv("DG_FORCE_KERNEL")) {
+  const char* fk = std::getenv("DG_FORCE_KERNEL");
+  if (fk) {
     int id = std::atoi(fk);
     if (id >= 0 && id < num_tile_configs() &&
         !(mode == MODE_CONTIG && (128 % tile_config(id).block_m) != 0) &&
         !(bm_multiple > 0 && tile_config(id).block_m % bm_multiple != 0))
       plan = plan_with_kernel(p.m, p.n, p.k, p.num_groups, mode, cus, id);
+  }
+  // Skinny M (dense NT, fp32 scales, m <= 128): the streaming kernel with all rows
+  // of A in one tile.  DG_FORCE_SKINNY=<id>[,<splits>] pins its configuration
+  // (for tuning); DG_FORCE_KERNEL keeps the square-tile kernel.
+  if (mode == MODE_DENSE && flags == 0 && !fk) {
+    int force_id = -1, force_splits = -1;
+    if (const char* fs = std::getenv("DG_FORCE_SKINNY")) {
+      force_id = std::atoi(fs);
+      if (const char* comma = std::strchr(fs, ',')) force_splits = std::atoi(comma + 1);
+    }
+    GemmPlan sk = plan_skinny(p.m, p.n, p.k, cus, p.c != nullptr, force_id, force_splits);
+    if (sk.skinny_id >= 0) plan = sk;
   }
   p.tiles_m = plan.tiles_m;
   p.tiles_n = plan.tiles_n;
@@ -158,7 +171,17 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* worksp
                  "x %d K slices), %d workgroups, workspace %zu bytes\n", name, p.m, p.n, p.k, p.num_groups,
                  plan.block_m, plan.block_n, plan.kernel_id, plan.num_tiles, plan.full_tiles, plan.splits,
                  plan.num_workgroups, cp.ws_bytes);
-  hipError_t e = launch_fp8_gemm(p, plan, mode | flags, hs);
+  hipError_t e;
+  if (plan.skinny_id >= 0) {
+    SkinnyParams sp{};
+    sp.a = p.a; sp.sfa = static_cast<const float*>(p.sfa); sp.b = p.b; sp.sfb = static_cast<const float*>(p.sfb);
+    sp.c = p.c; sp.d = p.d; sp.ws = p.ws;
+    sp.m = p.m; sp.n = p.n; sp.k = p.k;
+    sp.tiles_n = plan.tiles_n; sp.splits = plan.splits; sp.kb_per_split = plan.kb_per_split;
+    e = launch_skinny_gemm(sp, plan.skinny_id, plan.num_workgroups, hs);
+  } else {
+    e = launch_fp8_gemm(p, plan, mode | flags, hs);
+  }
   if (e == hipSuccess && plan.splits > 1 && mode != MODE_MASKED) e = launch_splitk_reduce(p, plan, cus, hs);
   if (e == hipSuccess && p.device_split == 1) e = launch_masked_splitk_reduce(p, plan, cp.masked_slots, hs);
   return e == hipSuccess ? DG_OK : DG_ERR_HIP;
@@ -397,14 +420,17 @@ static int query_plan(int m, int n, int k, int num_groups, int mode, int num_cus
     if (!di.ok) return DG_ERR_NO_DEVICE;
     num_cus = effective_cus(di);
   }
-  GemmPlan p = plan_fp8_gemm(m, n, k, num_groups, mode, num_cus, 0);
-  out->block_m = p.block_m;
-  out->block_n = p.block_n;
-  out->num_tiles = p.num_tiles;
-  out->num_workgroups = p.num_workgroups;
-  out->kernel_id = p.kernel_id;
-  out->splits = p.splits;
-  out->full_tiles = p.full_tiles;
+  Fp8GemmParams p{};
+  p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
+  const GemmPlan pl = plan_call(p, mode, 0, 0, num_cus).plan;
+  if (pl.kernel_id < 0) return DG_ERR_UNSUPPORTED;
+  out->block_m = pl.block_m;
+  out->block_n = pl.block_n;
+  out->num_tiles = pl.num_tiles;
+  out->num_workgroups = pl.num_workgroups;
+  out->kernel_id = pl.kernel_id;
+  out->splits = pl.splits;
+  out->full_tiles = pl.full_tiles;
   return DG_OK;
 }
 

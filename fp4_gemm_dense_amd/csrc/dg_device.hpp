@@ -158,6 +158,14 @@ extern "C" __device__ void dg_raw_buffer_store_v4i32(v4i data, v4i rsrc, int vof
                                                      int aux) __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // valid with resources below 2 GiB
 
+// LLVM's raw buffer loads into registers: lane l reads base + voffset(l) + soffset;
+// a lane whose offset lies at or beyond the resource's size reads zeros and sends
+// no memory request.
+extern "C" __device__ v4i dg_raw_buffer_load_v4i32(v4i rsrc, int voffset, int soffset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+extern "C" __device__ v2i dg_raw_buffer_load_v2i32(v4i rsrc, int voffset, int soffset,
+                                                   int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
+
 // Direct global -> LDS copies: lane l's 16 (or 4) bytes land at
 // lds_base + 16*l (or 4*l).  lds_base must be the same for the whole wave.
 __device__ __forceinline__ void dma16_to_lds(const void* g, void* lds_base) {

@@ -45,6 +45,38 @@ struct Fp8GemmParams {
                               // device (launch the masked reduce after); 2 valid tiles only, no split
 };
 
+// Arguments of the skinny-M kernel (all rows of A in one tile; dense NT, fp32 scales).
+struct SkinnyParams {
+  const uint8_t* a;
+  const float* sfa;           // [K/128][M]
+  const uint8_t* b;
+  const float* sfb;           // [ceil(N/128)][K/128]
+  const uint16_t* c;          // may be null
+  uint16_t* d;
+  float* ws;                  // split K: fp32 partial tiles [(tile * splits + slice)][BM][BN]
+  int m, n, k;
+  int tiles_n;                // column tiles
+  int splits;                 // K slices per tile (1: whole tiles, D written directly)
+  int kb_per_split;           // K blocks per slice (the last one may hold fewer)
+};
+
+// Skinny-M kernel configurations (skinny id indexes this table).
+struct SkinnyConfig {
+  int block_m, block_n;
+  int threads;
+  int prefetch;         // K blocks of B in flight per wave (register sets)
+};
+constexpr int kSkinnyLdsBytes = 160 * 1024;   // LDS of one workgroup (one per CU)
+// LDS of a skinny unit of kb K blocks: its slice of A (block_m rows of 128 bytes
+// per block) and the row scales, copied 64 entries at a time
+inline long long skinny_lds_bytes(const SkinnyConfig& sc, int kb) {
+  const long long sa = ((long long)kb * sc.block_m + 63) / 64 * 64 * 4;
+  return (long long)kb * sc.block_m * 128 + sa;
+}
+int num_skinny_configs();
+SkinnyConfig skinny_config(int id);
+hipError_t launch_skinny_gemm(const SkinnyParams& p, int id, int grid, hipStream_t stream);
+
 // Tile shapes compiled into the library (kernel_id indexes this table).
 struct TileConfig {
   int block_m, block_n;
@@ -74,7 +106,14 @@ struct GemmPlan {
   int kb_per_split;
   int full_tiles;             // tiles computed whole; tiles [full_tiles, num_tiles) are split
   int num_workgroups;
+  int skinny_id;              // >= 0: the skinny-M kernel of that configuration (kernel_id is then
+                              // kSkinnyIdBase + skinny_id); -1: the square-tile kernel kernel_id
 };
+constexpr int kSkinnyIdBase = 100;
+// The skinny-M plan for a dense NT problem with fp32 scales and m <= 128 rows
+// (skinny_id < 0 when the kernel does not apply).  force_id / force_splits >= 0
+// pin the configuration / the K slices (for tuning).
+GemmPlan plan_skinny(int m, int n, int k, int num_cus, bool has_c, int force_id = -1, int force_splits = -1);
 // bm_multiple > 0: only tile shapes whose height is a multiple of it (an A stored
 // [K][M] is staged in 128-row sub-tiles)
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m,

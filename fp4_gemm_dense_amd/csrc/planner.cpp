@@ -33,6 +33,7 @@ static int choose_splits(long long tiles, long long slots, int kb, long long* fu
 
 GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id) {
   GemmPlan plan{};
+  plan.skinny_id = -1;
   TileConfig tc = tile_config(kernel_id);
   plan.kernel_id = kernel_id;
   plan.block_m = tc.block_m;
@@ -109,9 +110,70 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
   if (best_id < 0) {
     GemmPlan none{};
     none.kernel_id = -1;
+    none.skinny_id = -1;
     return none;
   }
   return plan_with_kernel(m, n, k, num_groups, mode, num_cus, best_id);
+}
+
+// Skinny M (all rows of A in one tile).  Such a problem streams B from HBM once;
+// the choice is between column-tile widths and K slices.  Each candidate is
+// scored with a simple time model (microseconds):
+//   * the chip moves B, A, C and D (and a split plan's partials twice, written
+//     by the slices and read by the reduce) at about 5.5 TB/s;
+//   * a CU streams its unit's bytes at about 25 B/clk (bytes in flight over
+//     HBM latency), so one round of units takes the largest unit's bytes / rate;
+//   * a unit costs about 1 us of pipeline fill and drain, a split plan a second
+//     launch (about 3 us with its reads).
+// Split plans keep every unit in one round of workgroups (at most one partial
+// tile per workgroup slot, the bound of the caller's workspace).
+GemmPlan plan_skinny(int m, int n, int k, int num_cus, bool has_c, int force_id, int force_splits) {
+  GemmPlan best{};
+  best.kernel_id = -1;
+  best.skinny_id = -1;
+  if (m <= 0 || m > 128 || n <= 0 || k <= 0 || num_cus <= 0) return best;
+  const int kb = k / 128;
+  double best_t = 1e30;
+  // the smallest row block that holds every row
+  const int bm_need = m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128;
+  for (int id = 0; id < num_skinny_configs(); ++id) {
+    const SkinnyConfig sc = skinny_config(id);
+    if (force_id >= 0 ? id != force_id : sc.block_m != bm_need) continue;
+    if (sc.block_m < m) continue;
+    const int tiles = cdiv(n, sc.block_n);
+    for (int s = 1; s <= std::min(16, kb); ++s) {
+      const int per = cdiv(kb, s);
+      const int splits = cdiv(kb, per);
+      if (splits != s) continue;                       // each slice count once
+      if (force_splits > 0 && splits != force_splits) continue;
+      const long long units = (long long)tiles * splits;
+      if (splits > 1 && (units > num_cus || per < 2)) continue;
+      if (skinny_lds_bytes(sc, per) > kSkinnyLdsBytes) continue;   // the slice's A lives in LDS
+      const long long rounds = (units + num_cus - 1) / num_cus;
+      const double pad = (double)cdiv(per, sc.prefetch) * sc.prefetch;   // blocks a unit runs
+      const double unit_bytes = (double)sc.block_n * 128.0 * pad + 0.5 * m * 128.0 * pad;
+      double chip = (double)n * k + (double)m * k + (double)m * n * 2.0 * (has_c ? 2 : 1);
+      if (splits > 1) chip += 2.0 * units * sc.block_m * sc.block_n * 4.0;
+      const double t_chip = chip / 5.5e6;
+      const double t_cu = rounds * unit_bytes / (25.0 * 2400.0);
+      const double t = std::max(t_chip, t_cu) + rounds * 1.0 + (splits > 1 ? 3.0 : 0.0);
+      if (t < best_t - 1e-9) {
+        best_t = t;
+        best.skinny_id = id;
+        best.kernel_id = kSkinnyIdBase + id;
+        best.block_m = sc.block_m;
+        best.block_n = sc.block_n;
+        best.tiles_m = 1;
+        best.tiles_n = tiles;
+        best.num_tiles = tiles;
+        best.splits = splits;
+        best.kb_per_split = per;
+        best.full_tiles = splits > 1 ? 0 : tiles;
+        best.num_workgroups = (int)std::min<long long>(units, num_cus);
+      }
+    }
+  }
+  return best;
 }
 
 }  // namespace dg

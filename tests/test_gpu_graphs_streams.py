@@ -46,7 +46,7 @@ def test_graph_replay_after_a_larger_eager_split_call(dg):
     """A captured split call keeps its own workspace: a larger split call run eagerly on
     the same stream after the capture (its own, larger workspace) does not disturb the
     replays, which match the eager result bit for bit."""
-    small, large = (16, 256, 2048), (64, 2112, 7168)
+    small, large = (16, 512, 8192), (128, 2112, 7168)
     gs = synth.gen_dense(*small, seed=31, backend="torch", device="cuda")
     gl = synth.gen_dense(*large, seed=32, backend="torch", device="cuda")
     for shp in (small, large):

@@ -29,10 +29,21 @@ def _splits(M, N, K):
     return dgm.dg_query_plan(M, N, K, 1, 0)["splits"]
 
 
+@pytest.fixture(params=["skinny", "square"])
+def path(request, monkeypatch):
+    """Skinny shapes run on the skinny-M kernel by default; "square" pins the
+    square-tile kernel's 64 x 128 tile (DG_FORCE_KERNEL), whose split path also
+    serves large problems' split tails and the other layouts."""
+    if request.param == "square":
+        monkeypatch.setenv("DG_FORCE_KERNEL", "3")
+    return request.param
+
+
 @pytest.mark.parametrize("M,N,K", [(40, 400, 128 * 37), (1, 16, 128 * 40), (64, 2112, 128 * 9),
                                    (100, 1024, 128 * 64)])
-def test_splitk_random_parity(dg, M, N, K):
-    assert _splits(M, N, K) > 1, "shape must take the split-K path"
+def test_splitk_random_parity(dg, path, M, N, K):
+    if path == "square":
+        assert _splits(M, N, K) > 1, "shape must take the split-K path"
     g = synth.gen_dense(M, N, K, seed=M + N + K, with_c=True)
     a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
     d = sentinel_like((M, N))
@@ -44,10 +55,10 @@ def test_splitk_random_parity(dg, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,with_c", [(20, 144, 128 * 24, True), (64, 256, 128 * 24, False)])
-def test_splitk_exact_integer_case_bit_exact(dg, M, N, K, with_c):
+def test_splitk_exact_integer_case_bit_exact(dg, path, M, N, K, with_c):
     """Integer-valued products and power-of-two scales: every partial sum is exact
     in fp32, so the sliced sum must equal the oracle bit for bit."""
-    assert _splits(M, N, K) > 1
+    assert path == "skinny" or _splits(M, N, K) > 1
     rng = np.random.default_rng(M * N + K)
     a, sfa, b, sfb, c, exact = make_exact_case(rng, M, N, K, with_c)
     d = sentinel_like((M, N))
@@ -56,9 +67,9 @@ def test_splitk_exact_integer_case_bit_exact(dg, M, N, K, with_c):
     check_bit_exact(bits(d), exact, f"split exact {M}x{N}x{K}")
 
 
-def test_splitk_d_aliases_c(dg):
+def test_splitk_d_aliases_c(dg, path):
     M, N, K = 48, 528, 128 * 20
-    assert _splits(M, N, K) > 1
+    assert path == "skinny" or _splits(M, N, K) > 1
     g = synth.gen_dense(M, N, K, seed=5, with_c=True)
     a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
     cd = _dev(c)
@@ -67,7 +78,7 @@ def test_splitk_d_aliases_c(dg):
     check_parity(bits(cd), R.fp8_gemm_nt(a, sfa, b, sfb, c), what="split, d == c")
 
 
-def test_splitk_caller_workspace(dg):
+def test_splitk_caller_workspace(dg, path):
     """The partials live in the caller's workspace: a too-small one is rejected before
     anything is enqueued (D keeps its sentinel), an exact-size one and a larger one
     holding garbage give the same bits, and one workspace serves a small call, a
@@ -100,7 +111,6 @@ def test_splitk_caller_workspace(dg):
                      device="cuda")
     side = torch.cuda.Stream()
     for i, (M, N, K) in enumerate(shapes):
-        assert _splits(M, N, K) > 1
         g = synth.gen_dense(M, N, K, seed=100 + i, with_c=True)
         a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
         ins = [_dev(x) for x in (a, sfa, b, sfb, c)]
