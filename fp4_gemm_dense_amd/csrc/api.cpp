@@ -114,8 +114,23 @@ static CallPlan plan_call(Fp8GemmParams& p, int mode, int expected_m, int flags,
       force_id = std::atoi(fs);
       if (const char* comma = std::strchr(fs, ',')) force_splits = std::atoi(comma + 1);
     }
-    GemmPlan sk = plan_skinny(p.m, p.n, p.k, cus, p.c != nullptr, force_id, force_splits);
-    if (sk.skinny_id >= 0) plan = sk;
+    // Up to 128 rows the skinny kernel always applies.  Up to 256 rows it is taken
+    // only where the square-tile plan leaves more than a tenth of the workgroup
+    // slots idle in its last round and the skinny plan's column width (any
+    // multiple of 16, 112 among them) fills at least 95 % of them: the release
+    // article's case of non-power-of-two BLOCK_N (优化技术 / 非对齐块大小).  (C is
+    // not part of the choice: the workspace query, which has no C, plans the same.)
+    if (p.m <= 256 || force_id >= 0) {
+      const GemmPlan sk = plan_skinny(p.m, p.n, p.k, cus, false, force_id, force_splits);
+      auto fill = [&](const GemmPlan& g) {
+        const long long units = (long long)g.full_tiles + (long long)(g.num_tiles - g.full_tiles) * g.splits;
+        const long long rounds = (units + cus - 1) / cus;
+        return rounds > 0 ? (double)units / ((double)rounds * cus) : 0.0;
+      };
+      if (sk.skinny_id >= 0 &&
+          (p.m <= 128 || force_id >= 0 || (fill(plan) < 0.9 && fill(sk) >= 0.95)))
+        plan = sk;
+    }
   }
   p.tiles_m = plan.tiles_m;
   p.tiles_n = plan.tiles_n;
@@ -145,6 +160,7 @@ static CallPlan plan_call(Fp8GemmParams& p, int mode, int expected_m, int flags,
   // 128 x 256 ones; long K loops gain most from the L2 reuse
   p.group_m = (plan.block_m == 256 && plan.block_n == 128 && p.k >= 4096) ? 4 : 8;
   if (const char* gm = std::getenv("DG_GROUP_M")) p.group_m = std::max(1, std::atoi(gm));   // raster band (tuning)
+  if (plan.skinny_id >= 0) p.group_m = std::max(1, plan.tiles_m);   // skinny tiles are column-major
   // DG_KROT=<s>: K-block rotation step between neighbouring tiles (tuning)
   p.k_rot = 0;
   if (const char* kr = std::getenv("DG_KROT")) p.k_rot = std::max(0, std::atoi(kr));
@@ -177,7 +193,8 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* worksp
     sp.a = p.a; sp.sfa = static_cast<const float*>(p.sfa); sp.b = p.b; sp.sfb = static_cast<const float*>(p.sfb);
     sp.c = p.c; sp.d = p.d; sp.ws = p.ws;
     sp.m = p.m; sp.n = p.n; sp.k = p.k;
-    sp.tiles_n = plan.tiles_n; sp.splits = plan.splits; sp.kb_per_split = plan.kb_per_split;
+    sp.tiles_m = plan.tiles_m; sp.tiles_n = plan.tiles_n;
+    sp.splits = plan.splits; sp.kb_per_split = plan.kb_per_split;
     e = launch_skinny_gemm(sp, plan.skinny_id, plan.num_workgroups, hs);
   } else {
     e = launch_fp8_gemm(p, plan, mode | flags, hs);

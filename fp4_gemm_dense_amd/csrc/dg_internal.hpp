@@ -55,7 +55,7 @@ struct SkinnyParams {
   uint16_t* d;
   float* ws;                  // split K: fp32 partial tiles [(tile * splits + slice)][BM][BN]
   int m, n, k;
-  int tiles_n;                // column tiles
+  int tiles_m, tiles_n;       // row and column tiles (tile t: row tile t % tiles_m, column tile t / tiles_m)
   int splits;                 // K slices per tile (1: whole tiles, D written directly)
   int kb_per_split;           // K blocks per slice (the last one may hold fewer)
 };
@@ -64,15 +64,9 @@ struct SkinnyParams {
 struct SkinnyConfig {
   int block_m, block_n;
   int threads;
-  int prefetch;         // K blocks of B in flight per wave (register sets)
+  int prefetch;         // K blocks of B in flight per wave (register sets), and of A per chunk
+  int lds_bytes;
 };
-constexpr int kSkinnyLdsBytes = 160 * 1024;   // LDS of one workgroup (one per CU)
-// LDS of a skinny unit of kb K blocks: its slice of A (block_m rows of 128 bytes
-// per block) and the row scales, copied 64 entries at a time
-inline long long skinny_lds_bytes(const SkinnyConfig& sc, int kb) {
-  const long long sa = ((long long)kb * sc.block_m + 63) / 64 * 64 * 4;
-  return (long long)kb * sc.block_m * 128 + sa;
-}
 int num_skinny_configs();
 SkinnyConfig skinny_config(int id);
 hipError_t launch_skinny_gemm(const SkinnyParams& p, int id, int grid, hipStream_t stream);
@@ -110,8 +104,8 @@ struct GemmPlan {
                               // kSkinnyIdBase + skinny_id); -1: the square-tile kernel kernel_id
 };
 constexpr int kSkinnyIdBase = 100;
-// The skinny-M plan for a dense NT problem with fp32 scales and m <= 128 rows
-// (skinny_id < 0 when the kernel does not apply).  force_id / force_splits >= 0
+// The skinny-M plan for a dense NT problem with fp32 scales and m <= 256 rows, in
+// row tiles of at most 128 (skinny_id < 0 when the kernel does not apply).  force_id / force_splits >= 0
 // pin the configuration / the K slices (for tuning).
 GemmPlan plan_skinny(int m, int n, int k, int num_cus, bool has_c, int force_id = -1, int force_splits = -1);
 // bm_multiple > 0: only tile shapes whose height is a multiple of it (an A stored

@@ -118,11 +118,14 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
 
 // Skinny M (all rows of A in one tile).  Such a problem streams B from HBM once;
 // the choice is between column-tile widths and K slices.  Each candidate is
-// scored with a simple time model (microseconds):
+// scored with a simple time model (microseconds), from per-phase timestamps of
+// the kernel on MI355X:
 //   * the chip moves B, A, C and D (and a split plan's partials twice, written
 //     by the slices and read by the reduce) at about 5.5 TB/s;
-//   * a CU streams its unit's bytes at about 25 B/clk (bytes in flight over
-//     HBM latency), so one round of units takes the largest unit's bytes / rate;
+//   * a CU copies its unit's slice of A into LDS at about 20 B/clk, and streams
+//     B at about 25 B/clk (bytes in flight over HBM latency);
+//   * each K block a unit runs (its slice padded to a multiple of the prefetch
+//     depth) costs the waves' reads of A from LDS, about 0.4 us per 64 KB;
 //   * a unit costs about 1 us of pipeline fill and drain, a split plan a second
 //     launch (about 3 us with its reads).
 // Split plans keep every unit in one round of workgroups (at most one partial
@@ -131,16 +134,16 @@ GemmPlan plan_skinny(int m, int n, int k, int num_cus, bool has_c, int force_id,
   GemmPlan best{};
   best.kernel_id = -1;
   best.skinny_id = -1;
-  if (m <= 0 || m > 128 || n <= 0 || k <= 0 || num_cus <= 0) return best;
+  if (m <= 0 || m > 256 || n <= 0 || k <= 0 || num_cus <= 0) return best;
   const int kb = k / 128;
   double best_t = 1e30;
-  // the smallest row block that holds every row
+  // the smallest row block that holds every row (two 128-row tiles above 128)
   const int bm_need = m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128;
   for (int id = 0; id < num_skinny_configs(); ++id) {
     const SkinnyConfig sc = skinny_config(id);
     if (force_id >= 0 ? id != force_id : sc.block_m != bm_need) continue;
-    if (sc.block_m < m) continue;
-    const int tiles = cdiv(n, sc.block_n);
+    const int tiles_m = cdiv(m, sc.block_m);
+    const int tiles = tiles_m * cdiv(n, sc.block_n);
     for (int s = 1; s <= std::min(16, kb); ++s) {
       const int per = cdiv(kb, s);
       const int splits = cdiv(kb, per);
@@ -148,14 +151,16 @@ GemmPlan plan_skinny(int m, int n, int k, int num_cus, bool has_c, int force_id,
       if (force_splits > 0 && splits != force_splits) continue;
       const long long units = (long long)tiles * splits;
       if (splits > 1 && (units > num_cus || per < 2)) continue;
-      if (skinny_lds_bytes(sc, per) > kSkinnyLdsBytes) continue;   // the slice's A lives in LDS
       const long long rounds = (units + num_cus - 1) / num_cus;
       const double pad = (double)cdiv(per, sc.prefetch) * sc.prefetch;   // blocks a unit runs
-      const double unit_bytes = (double)sc.block_n * 128.0 * pad + 0.5 * m * 128.0 * pad;
-      double chip = (double)n * k + (double)m * k + (double)m * n * 2.0 * (has_c ? 2 : 1);
+      const double a_bytes = (double)std::min(m, sc.block_m) * 128.0 * per;
+      const double lds_reads = (double)sc.threads / 64 * sc.block_m * 128.0 * pad;   // every wave reads all of A
+      double chip = (double)n * k * tiles_m + (double)m * k + (double)m * n * 2.0 * (has_c ? 2 : 1);
       if (splits > 1) chip += 2.0 * units * sc.block_m * sc.block_n * 4.0;
       const double t_chip = chip / 5.5e6;
-      const double t_cu = rounds * unit_bytes / (25.0 * 2400.0);
+      const double t_cu = rounds * (a_bytes / (20.0 * 2400.0) +
+                                    std::max((double)sc.block_n * 128.0 * per / (25.0 * 2400.0),
+                                             lds_reads / 64e3 * 0.4));
       const double t = std::max(t_chip, t_cu) + rounds * 1.0 + (splits > 1 ? 3.0 : 0.0);
       if (t < best_t - 1e-9) {
         best_t = t;
@@ -163,8 +168,8 @@ GemmPlan plan_skinny(int m, int n, int k, int num_cus, bool has_c, int force_id,
         best.kernel_id = kSkinnyIdBase + id;
         best.block_m = sc.block_m;
         best.block_n = sc.block_n;
-        best.tiles_m = 1;
-        best.tiles_n = tiles;
+        best.tiles_m = tiles_m;
+        best.tiles_n = tiles / tiles_m;
         best.num_tiles = tiles;
         best.splits = splits;
         best.kb_per_split = per;

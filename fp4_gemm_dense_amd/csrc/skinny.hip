@@ -12,22 +12,21 @@
 // (N x K bytes) from HBM once and is bound by how many bytes each CU keeps in
 // flight, not by the matrix cores.  So the roles of the operands differ from the
 // square-tile kernel:
-//   * one tile holds ALL rows of A (BM = 16 * MT >= M) and BN = 16 * NT columns
-//     per wave; the waves split N and share A;
+//   * a tile holds BM = 16 * MT rows of A (all of them when M <= BM) and
+//     BN = 16 * NT columns per wave; the waves split N and share A;
 //   * B, the large operand, goes straight from HBM into registers: each wave
 //     loads its own 16 * NT rows of B, P K blocks ahead, into P register sets
 //     (no LDS round trip, and P * NW * NT * 2 KB of B in flight per CU);
-//   * A, the small shared operand, is copied into LDS once per work unit (its
-//     whole K slice, with buffer_load ... lds), so the waves meet at one barrier
-//     per unit and then stream B independently;
+//   * A, the small shared operand, is copied into LDS in chunks of P K blocks
+//     (buffer_load ... lds) through two chunk buffers, so the waves meet at one
+//     barrier per P blocks and otherwise stream B independently;
 //   * K is split into slices when the column tiles alone cannot fill the chip;
 //     a slice writes its fp32 partial tile into the caller's workspace and the
 //     split-K reduce kernel sums the slices in slice order (plus C).
 // The K loop is straight-line over groups of P blocks (the register set of a
 // block is a compile-time index); a slice is padded to a multiple of P with
 // blocks whose loads use a null buffer resource (no memory traffic) and whose
-// promotion weight is zero.  A slice's A must fit in LDS, which bounds its
-// length (the planner splits K accordingly).
+// promotion weight is zero.
 #include <algorithm>
 
 #include "dg_device.hpp"
@@ -42,7 +41,17 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
   constexpr int A_BLK = BM * 128;               // LDS bytes of A per K block
   constexpr int RG = BM / 8;                    // 1 KB regions (8 rows x 128 bytes) per K block
   constexpr int LB = 2 * NT;                    // B loads per wave per K block
-  static_assert(P * LB < 64, "vmcnt range");
+  // A goes through two chunk buffers of P K blocks each: A rows, then the row
+  // scales (copied 64 at a time); a 1 KB area takes the copies a wave issues
+  // beyond a chunk's real ones, so that every wave issues the same count
+  constexpr int CH_A = P * A_BLK;
+  constexpr int CH_SA_OPS = (P * BM + 63) / 64;
+  constexpr int CH_BYTES = CH_A + CH_SA_OPS * 256;
+  constexpr uint32_t DUMMY = 2 * CH_BYTES;
+  constexpr int RA = (P * RG + NW - 1) / NW;    // region copies per wave per chunk
+  constexpr int RS = (CH_SA_OPS + NW - 1) / NW; // scale copies per wave per chunk
+  constexpr int CC = RA + RS;                   // copies per wave per chunk
+  static_assert((P - 1) * LB + CC < 64 && P * LB < 64, "vmcnt range");
   static_assert(MT == 1 || MT == 2 || MT % 4 == 0, "row scales are read 1, 2 or 4 at a time");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -56,12 +65,9 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
 
   const int M = p.m, N = p.n, K = p.k;
   const int KB = K >> 7;
-  const int tiles_n = p.tiles_n, splits = p.splits, kbps = p.kb_per_split;
-  const int total = tiles_n * splits;
-  // LDS: the unit's K slice of A, [kb][BM rows x 128 bytes] (16-byte chunk c of
-  // row r at c ^ swz(r)), then its row scales [kb][BM] (position lrow * MT + mt
-  // of a block holds row mt * 16 + lrow, so a lane's MT scales are adjacent)
-  const uint32_t sa_base = (uint32_t)kbps * (uint32_t)A_BLK;   // the scale copies fill whole 64-entry runs
+  const int tiles_m = p.tiles_m, tiles_n = p.tiles_n, splits = p.splits, kbps = p.kb_per_split;
+  const int tiles = tiles_m * tiles_n;
+  const int total = tiles * splits;
 
   const v4i rsA = make_buffer_rsrc(p.a, (uint32_t)M * (uint32_t)K);
   const v4i rsSA = make_buffer_rsrc(p.sfa, (uint32_t)KB * (uint32_t)M * 4u);
@@ -77,11 +83,15 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
   if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
   for (int u = vb; u < total; u += G) {
-    const int t = u % tiles_n, sl = u / tiles_n;
-    const int n0 = t * BN;
+    // unit u: K slice u / tiles of tile u % tiles; tiles are column-major (row
+    // tile fastest), as the split-K reduce walks them
+    const int t = u % tiles, sl = u / tiles;
+    const int tm = t % tiles_m, tn = t / tiles_m;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows = min(BM, M - m0);          // valid rows of the tile
     const int kb0 = sl * kbps;
     const int nkb = min(kbps, KB - kb0);
-    const int nkb_pad = (nkb + P - 1) / P * P;
+    const int nch = (nkb + P - 1) / P;         // chunks of P blocks (the last one padded)
     const bool whole = splits == 1;
     const int col0 = n0 + wave * (NT * 16);   // the wave's first column
     // one B scale per wave and K block: its 16 * NT columns lie in one 128-row block of B
@@ -109,31 +119,49 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int row = mt * 16 + lrow, col = col0 + nt * 16 + 4 * lgrp;
-          const uint32_t off = (row < M && col < N) ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u
-                                                    : kBufferOutOfRange;
+          const uint32_t off = (row < rows && col < N)
+                                   ? ((uint32_t)(m0 + row) * (uint32_t)N + (uint32_t)col) * 2u
+                                   : kBufferOutOfRange;
           creg[mt][nt] = dg_raw_buffer_load_v2i32(rsC, (int)off, 0, 0);
         }
     }
 
-    // The unit's whole slice of A and its row scales, copied once: region o
-    // (dealt round-robin to the waves) is K block o / RG, rows 8 (o % RG) ..;
-    // lane l fills bytes [16 l, 16 l + 16): row 8 (o % RG) + l / 8, position
-    // l % 8, which holds chunk (l % 8) ^ swz(row).  Rows past M read zeros.
-    for (int o = wave; o < nkb * RG; o += NW) {
-      const int kb = o / RG, rg = o - kb * RG;
-      const int row = rg * 8 + (lane >> 3);
-      const uint32_t off = row < M ? (uint32_t)row * (uint32_t)K + (uint32_t)(((lane & 7) ^ swz(row)) << 4)
-                                   : kBufferOutOfRange;
-      buf16_to_lds(rsA, off, (uint32_t)(kb0 + kb) * 128u, smem + (uint32_t)kb * A_BLK + (uint32_t)rg * 1024u);
-    }
-    for (int o = wave; o * 64 < nkb * BM; o += NW) {
-      const int e = o * 64 + lane;               // scale entry kb * BM + pos of the slice
-      const int kb = e / BM, pos = e - kb * BM;
-      const int row = (pos % MT) * 16 + pos / MT;
-      const uint32_t off = (kb < nkb && row < M) ? (uint32_t)(kb0 + kb) * (uint32_t)M * 4u + (uint32_t)row * 4u
-                                                 : kBufferOutOfRange;
-      buf4_to_lds(rsSA, off, 0u, smem + sa_base + (uint32_t)o * 256u);
-    }
+    // Copies of chunk c (K blocks cP .. cP + P - 1 of the slice) into buffer c % 2:
+    // region o of the chunk (the wave's j-th is o = j * NW + wave) is block o / RG,
+    // rows 8 (o % RG) ..; lane l fills bytes [16 l, 16 l + 16): row 8 (o % RG) + l / 8,
+    // position l % 8, which holds chunk (l % 8) ^ swz(row).  Scale copy q moves
+    // entries 64 q .. of the chunk's [block][BM] scales.  Copies past the slice (or
+    // past the chunk) read nothing and land in the dummy area; rows past the tile
+    // read zeros.
+    auto copy_chunk = [&](int c) {
+      const uint32_t buf = (uint32_t)(c & 1) * (uint32_t)CH_BYTES;
+#pragma unroll
+      for (int j = 0; j < RA; ++j) {
+        const int o = j * NW + wave;
+        const int kb = c * P + o / RG, rg = o % RG;
+        const bool real = o < P * RG && kb < nkb;
+        const int row = rg * 8 + (lane >> 3);
+        const uint32_t off = row < rows
+                                 ? (uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)(((lane & 7) ^ swz(row)) << 4)
+                                 : kBufferOutOfRange;
+        buf16_to_lds(real ? rsA : rsNull, off, real ? (uint32_t)(kb0 + kb) * 128u : 0u,
+                     smem + (real ? buf + (uint32_t)(o / RG) * A_BLK + (uint32_t)rg * 1024u : DUMMY));
+      }
+#pragma unroll
+      for (int j = 0; j < RS; ++j) {
+        const int q = j * NW + wave;
+        const int e = q * 64 + lane;             // entry blk * BM + pos of the chunk
+        const int blk = e / BM, pos = e % BM;
+        const int row = (pos % MT) * 16 + pos / MT;
+        const int kb = c * P + blk;
+        const bool real = q < CH_SA_OPS;
+        const uint32_t off = (blk < P && kb < nkb && row < rows)
+                                 ? (uint32_t)(kb0 + kb) * (uint32_t)M * 4u + (uint32_t)(m0 + row) * 4u
+                                 : kBufferOutOfRange;
+        buf4_to_lds(real ? rsSA : rsNull, off, 0u, smem + (real ? buf + (uint32_t)CH_A + (uint32_t)q * 256u : DUMMY));
+      }
+    };
+    copy_chunk(0);
     asm volatile("" ::: "memory");
 
     // B of the first P K blocks (a padding block past the slice reads nothing)
@@ -158,12 +186,6 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
       asm volatile("" ::: "memory");
     });
 
-    // A and its scales have landed once only the B loads issued after them are
-    // outstanding; the barrier makes every wave's copies visible.  From here on
-    // each wave streams its own B with no further barrier.
-    wait_vmcnt<P * LB>();
-    block_barrier();
-
     v4f acc[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -172,16 +194,24 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
 
     // the B scale of the next K block is loaded one block ahead (scalar loads)
     float sb_next = SBc[sb_idx];
-    for (int kb_base = 0; kb_base < nkb_pad; kb_base += P) {
+    for (int c = 0; c < nch; ++c) {
+      // chunk c has landed once no more than the B loads issued after its copies
+      // are outstanding; the barrier makes every wave's copies visible and frees
+      // the other buffer (every wave is done with chunk c - 1), which takes chunk c + 1
+      wait_vmcnt<P * LB>();
+      block_barrier();
+      copy_chunk(c + 1);
+      asm volatile("" ::: "memory");
+      const uint32_t buf = (uint32_t)(c & 1) * (uint32_t)CH_BYTES;
       static_for<P>([&](auto jt) {
         constexpr int j = decltype(jt)::value;
-        const int kb = kb_base + j;
+        const int kb = c * P + j;
         const bool real = kb < nkb;
-        const int kr = real ? kb : 0;            // a padding block reads block 0 with weight 0
+        const int kr = real ? j : 0;             // a padding block reads the chunk's first block, weight 0
         const float wgt = real ? sb_next : 0.f;
         sb_next = SBc[sb_idx + (kb + 1 < nkb ? kb + 1 : 0)];
         float s[MT];
-        const uint8_t* srd = smem + sa_base + (uint32_t)kr * (BM * 4) + lrow * MT * 4;
+        const uint8_t* srd = smem + buf + CH_A + (uint32_t)kr * (BM * 4) + lrow * MT * 4;
         if constexpr (MT % 4 == 0) {
 #pragma unroll
           for (int q = 0; q < MT / 4; ++q) {
@@ -194,7 +224,7 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
           for (int mt = 0; mt < MT; ++mt) s[mt] = reinterpret_cast<const float*>(srd)[mt] * wgt;
         }
         // A fragments of the block, read one row block ahead of the matrix instructions
-        const uint8_t* ablk = smem + (uint32_t)kr * A_BLK + (uint32_t)lrow * 128u;
+        const uint8_t* ablk = smem + buf + (uint32_t)kr * A_BLK + (uint32_t)lrow * 128u;
         auto read_a = [&](int mt) -> v8i {
           const uint8_t* ar = ablk + (uint32_t)mt * 2048u;
           const v4i lo = *reinterpret_cast<const v4i*>(ar + ((lgrp ^ sw) << 4));
@@ -203,8 +233,9 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
         };
         v8i af[2];
         af[0] = read_a(0);
-        // B of block kb has landed once no more than the later blocks' loads are outstanding
-        wait_vmcnt<(P - 1) * LB>();
+        // B of block kb has landed once no more than the later blocks' loads and
+        // the next chunk's copies are outstanding
+        wait_vmcnt<(P - 1) * LB + CC>();
         v4f part[2][NT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -258,8 +289,9 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
             v2 += __uint_as_float((uint32_t)cv.y << 16);
             v3 += __uint_as_float((uint32_t)cv.y & 0xffff0000u);
           }
-          const uint32_t off = (row < M && col < N) ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u
-                                                    : kBufferOutOfRange;
+          const uint32_t off = (row < rows && col < N)
+                                   ? ((uint32_t)(m0 + row) * (uint32_t)N + (uint32_t)col) * 2u
+                                   : kBufferOutOfRange;
           const v2i w = {(int)pack_bf16x2_rne(v0, v1), (int)pack_bf16x2_rne(v2, v3)};
           dg_raw_buffer_store_v2i32(w, rsD, (int)off, 0, 0);
         }
@@ -276,17 +308,22 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
   X(0, 1, 1, 8, 8)           \
   X(1, 2, 1, 8, 8)           \
   X(2, 4, 1, 8, 8)           \
-  X(3, 8, 1, 8, 6)           \
+  X(3, 8, 1, 8, 4)           \
   X(4, 4, 1, 4, 8)           \
-  X(5, 8, 1, 4, 6)           \
+  X(5, 8, 1, 4, 4)           \
   X(6, 4, 1, 6, 8)           \
-  X(7, 8, 1, 6, 6)           \
+  X(7, 8, 1, 6, 4)           \
   X(8, 4, 2, 8, 6)           \
-  X(9, 2, 2, 8, 6)
+  X(9, 2, 2, 8, 6)           \
+  X(10, 8, 1, 7, 4)          \
+  X(11, 4, 1, 7, 8)          \
+  X(12, 8, 2, 7, 4)
 
-constexpr int kSkinnyLdsMax = kSkinnyLdsBytes;
+// LDS of a configuration: two chunk buffers of P K blocks (A rows and scales) and
+// the 1 KB area of the surplus copies
+#define DG_SKINNY_LDS(MT, P) (2 * ((P) * (MT) * 16 * 128 + ((P) * (MT) * 16 + 63) / 64 * 256) + 1024)
 static const SkinnyConfig kSkinnyConfigs[] = {
-#define X(id, MT, NT, NW, P) {MT * 16, NW * NT * 16, NW * 64, P},
+#define X(id, MT, NT, NW, P) {MT * 16, NW * NT * 16, NW * 64, P, DG_SKINNY_LDS(MT, P)},
     DG_SKINNY_CONFIGS(X)
 #undef X
 };
@@ -297,16 +334,16 @@ SkinnyConfig skinny_config(int id) { return kSkinnyConfigs[id]; }
 hipError_t launch_skinny_gemm(const SkinnyParams& p, int id, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   const SkinnyConfig sc = kSkinnyConfigs[id];
-  if (skinny_lds_bytes(sc, p.kb_per_split) > kSkinnyLdsMax) return hipErrorInvalidValue;
+
   switch (id) {
 #define X(i, MT, NT, NW, P)                                                                             \
   case i: {                                                                                             \
     static const hipError_t attr = hipFuncSetAttribute(                                                 \
         reinterpret_cast<const void*>(&skinny_gemm_kernel<MT, NT, NW, P>),                              \
-        hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLdsMax);                                     \
+        hipFuncAttributeMaxDynamicSharedMemorySize, sc.lds_bytes);                                      \
     if (attr != hipSuccess) return attr;                                                                \
     hipLaunchKernelGGL((skinny_gemm_kernel<MT, NT, NW, P>), dim3(grid), dim3(sc.threads),               \
-                       skinny_lds_bytes(sc, p.kb_per_split), stream, p);                                \
+                       sc.lds_bytes, stream, p);                                                        \
     return hipGetLastError();                                                                           \
   }
     DG_SKINNY_CONFIGS(X)

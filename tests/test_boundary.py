@@ -46,6 +46,29 @@ def test_tile_count_golden_from_pages():
         assert c["tiles"] <= c["units"]
 
 
+def test_planner_reproduces_the_pages_non_power_of_two_block_n():
+    """The release article's example as a planner decision: M=256, N=7168 on 132
+    compute units, where 128-wide tiles leave 20 units idle (112 tiles) and the
+    112-wide tile occupies 128.  With K short enough that splitting K does not pay,
+    the planner takes 128 x 112 tiles, one per workgroup."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "tile_counts.json")))
+    pow2, npow2 = g["cases"]
+    units = npow2["units"]
+    for k in (512, 1024, 1536):
+        p = dgm.dg_query_plan(npow2["m"], npow2["n"], k, 1, units)
+        assert (p["block_m"], p["block_n"]) == (npow2["block_m"], npow2["block_n"]), p
+        assert p["num_tiles"] == npow2["tiles"] and p["splits"] == 1, p
+        assert p["num_workgroups"] == npow2["tiles"] <= units
+        assert p["num_tiles"] > pow2["tiles"]
+    # on 256 units the same problem keeps the square-tile kernel, whose tiles fill
+    # the chip well enough; up to 128 rows non-power-of-two widths are ordinary
+    # choices (e.g. the 96-wide tile)
+    assert dgm.dg_query_plan(256, 7168, 1024, 1, 256)["kernel_id"] < 100
+    widths = {dgm.dg_query_plan(m, n, k, 1, 256)["block_n"] for m, n, k in
+              [(64, 24576, 1536), (128, 2112, 7168), (64, 7168, 16384), (192, 7168, 4096)]}
+    assert widths & {96, 112, 224}, widths
+
+
 A16 = 0x10000   # fake 16-byte-aligned "device" addresses: never dereferenced on the host
 
 

@@ -16,24 +16,15 @@ from tests.test_oracle import make_exact_case
 pytestmark = pytest.mark.gpu
 
 # id -> (block_m, block_n, prefetch): must match the library's table
-CONFIGS = {0: (16, 128, 8), 1: (32, 128, 8), 2: (64, 128, 8), 3: (128, 128, 6), 4: (64, 64, 8),
-           5: (128, 64, 6), 6: (64, 96, 8), 7: (128, 96, 6), 8: (64, 256, 6), 9: (32, 256, 6)}
-
-
-def _max_slice(bm):
-    """K blocks of a slice whose A (bm rows of 128 bytes plus fp32 scales) fits 160 KB of LDS."""
-    kb = 1
-    while (kb + 1) * bm * 128 + ((kb + 1) * bm + 63) // 64 * 256 <= 160 * 1024:
-        kb += 1
-    return kb
+CONFIGS = {0: (16, 128, 8), 1: (32, 128, 8), 2: (64, 128, 8), 3: (128, 128, 4), 4: (64, 64, 8),
+           5: (128, 64, 4), 6: (64, 96, 8), 7: (128, 96, 4), 8: (64, 256, 6), 9: (32, 256, 6),
+           10: (128, 112, 4), 11: (64, 112, 8), 12: (128, 224, 4)}
 
 
 def _kblocks(bm, pf, splits):
-    """A K length (in blocks) that ends mid-way through a prefetch group and whose slices fit LDS."""
-    nb = min(3 * pf + 5, splits * _max_slice(bm))
-    if nb % pf == 0:
-        nb -= 1
-    return nb
+    """A K length in blocks whose slices end mid-way through a prefetch group (padding
+    blocks) after several chunks."""
+    return (3 * pf + 5) * splits
 
 
 def _dev(x):
@@ -66,6 +57,8 @@ def _run(dg, a, sfa, b, sfb, c, M, N):
 def test_skinny_config_random_parity(dg, monkeypatch, sid, splits):
     bm, bn, pf = CONFIGS[sid]
     M = bm - 5 if bm > 16 else 11             # rows past M inside the tile
+    if splits == 1:
+        M += bm                               # a second row tile, partly filled
     N = 3 * bn + 48                           # a ragged last column tile
     K = 128 * _kblocks(bm, pf, splits)        # slices that end mid-way through a prefetch group
     _forced_plan(monkeypatch, sid, splits, M, N, K)
@@ -90,7 +83,7 @@ def test_skinny_config_exact_integer_bit_exact(dg, monkeypatch, sid):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 7168), (8, 2112, 1024), (33, 6144, 2048), (100, 1040, 128 * 9),
-                                   (128, 7168, 512)])
+                                   (128, 7168, 512), (128, 2112, 7168), (192, 7168, 4096)])
 def test_skinny_planner_choice_parity(dg, M, N, K):
     """Shapes the planner sends to the skinny kernel (its own choice of configuration and
     K slices), checked in full against the oracle."""
