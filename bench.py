@@ -94,7 +94,7 @@ def kernel_source_hash(kind):
     """Hash of the sources that decide the kernels (and their plans) a workload kind runs."""
     h = hashlib.sha256()
     files = (("ffn.hip", "dg_device.hpp", "dg_internal.hpp") if kind in ("ffn", "fp4_contiguous")
-             else ("fp8_gemm.hip", "planner.cpp", "api.cpp", "dg_device.hpp", "dg_internal.hpp"))
+             else ("fp8_gemm.hip", "skinny.hip", "planner.cpp", "api.cpp", "dg_device.hpp", "dg_internal.hpp"))
     for f in files:
         p = os.path.join(ROOT, "fp4_gemm_dense_amd", "csrc", f)
         if os.path.exists(p):
@@ -562,11 +562,14 @@ def summarize_counters(fetch_dir, write_dir, calib_dir, key):
     fetch_scale = n / copy_bytes(per_kernel(calib_dir, "FETCH_SIZE"))
     write_scale = n / copy_bytes(per_kernel(calib_dir, "WRITE_SIZE"))
     kind = key.split(" ")[0]
-    primary = "route" if kind == "ffn" else ("ffn_gemm_kernel" if kind == "fp4_contiguous" else "fp8_gemm_kernel")
+    # one dispatch per call names the call: the FFN's routing kernel, else the GEMM
+    # kernel (square, skinny or FP8xFP4); split-K reduces and the K-grouped zeroing
+    # kernel ride along
+    primary = "route" if kind == "ffn" else "gemm_kernel"
 
     def per_call(acc):
-        lib = {k: v for k, v in acc.items() if "dg::" in k}
-        calls = sum(len(v) for k, v in lib.items() if primary in k)
+        lib = {k: v for k, v in acc.items() if "dg::" in k and "transpose" not in k}   # (weight set-up excluded)
+        calls = sum(len(v) for k, v in lib.items() if primary in k and "reduce" not in k)
         return sum(sum(v) for v in lib.values()) / max(calls, 1), sorted(lib)
     fb, kernels = per_call(per_kernel(fetch_dir, "FETCH_SIZE"))
     wb, _ = per_call(per_kernel(write_dir, "WRITE_SIZE"))
