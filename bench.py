@@ -83,7 +83,8 @@ def parse():
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--only", type=str, default=None,
                     help="time only the calls of one kernel group (e.g. 'contiguous 128x256'), for counter runs")
-    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CALIB_DIR", "KEY"),
+    ap.add_argument("--summarize-counters", nargs=5,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CALIB_FETCH_DIR", "CALIB_WRITE_DIR", "KEY"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of `--only KEY` and one of "
                          "--copy-calib into calibrated HBM bytes per call, stored under KEY in "
                          "profiles/traffic.json")
@@ -162,7 +163,7 @@ def items_dense(config, only=None):
         nbytes = M * K + N * K + sf_bytes + 2 * M * N * (2 if with_c else 1)
         gemm = dg.dg_fp8_gemm_nt_ue8m0 if ue else dg.dg_fp8_gemm_nt
         ws = _ws(dg.FORM_NT_UE8M0 if ue else dg.FORM_NT, M, N, K)
-        plan = dg.dg_query_plan(M, N, K)
+        plan = dg.dg_query_plan_form(dg.FORM_NT_UE8M0 if ue else dg.FORM_NT, M, N, K)
 
         def mk(g, d, gemm=gemm, ws=ws):
             return lambda: gemm(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d, workspace=ws)
@@ -187,7 +188,7 @@ def items_contiguous(nn=False):
         groups_hit = sum(1 for c in g["counts"] if c > 0)
         nbytes = valid * K + groups_hit * (N * K + 4 * nb(N) * (K // 128)) + 4 * (K // 128) * valid + 4 * M + 2 * valid * N
         ws = _ws(dg.FORM_CONTIGUOUS_NN if nn else dg.FORM_CONTIGUOUS_NT, M, N, K, 8)
-        plan = dg.dg_query_plan_contiguous(M, N, K, 8)
+        plan = dg.dg_query_plan_form(dg.FORM_CONTIGUOUS_NN if nn else dg.FORM_CONTIGUOUS_NT, M, N, K, 8)
 
         def mk(g, d, ws=ws):
             return lambda: gemm(g["a"], g["sfa"], g["b"], g["sfb"], g["m_indices"], d, workspace=ws)
@@ -536,10 +537,10 @@ def lookup_traffic(key, kind):
     return None
 
 
-def summarize_counters(fetch_dir, write_dir, calib_dir, key):
+def summarize_counters(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir, key):
     """Calibrated HBM bytes per call of the kernel group `key` (e.g. "contiguous 128x256"),
     from two rocprofv3 --pmc runs of `bench.py --only <key>` (FETCH_SIZE, then WRITE_SIZE)
-    and one of `bench.py --copy-calib` (both counters).  The library's dispatches of a
+    and two of `bench.py --copy-calib` (the same two counters).  The library's dispatches of a
     call (GEMM plus split-K reduce, or the FFN's four kernels) are summed; torch's own
     kernels (the cache flush, input generation) are left out.  Each counter is scaled by
     what it reads for the plain 1 GiB copy."""
@@ -559,8 +560,8 @@ def summarize_counters(fetch_dir, write_dir, calib_dir, key):
         return statistics.median(vals) if vals else float("nan")
 
     n = 1 << 30
-    fetch_scale = n / copy_bytes(per_kernel(calib_dir, "FETCH_SIZE"))
-    write_scale = n / copy_bytes(per_kernel(calib_dir, "WRITE_SIZE"))
+    fetch_scale = n / copy_bytes(per_kernel(calib_fetch_dir, "FETCH_SIZE"))
+    write_scale = n / copy_bytes(per_kernel(calib_write_dir, "WRITE_SIZE"))
     kind = key.split(" ")[0]
     # one dispatch per call names the call: the FFN's routing kernel, else the GEMM
     # kernel (square, skinny or FP8xFP4); split-K reduces and the K-grouped zeroing

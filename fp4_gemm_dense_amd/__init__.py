@@ -52,6 +52,7 @@ _SIGNATURES = {
     "dg_get_num_cus": (_I, []),
     "dg_query_plan": (_I, [_I, _I, _I, _I, _I, _P]),
     "dg_query_plan_contiguous": (_I, [_I, _I, _I, _I, _I, _P]),
+    "dg_query_plan_form": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
     "dg_num_tiles": (_I, [_I, _I, _I, _I]),
     "dg_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -464,6 +465,14 @@ def dg_query_plan_contiguous(m, n, k, num_groups, num_cus=0):
     p = DgPlan()
     _check("dg_query_plan_contiguous",
            lib().dg_query_plan_contiguous(m, n, k, num_groups, num_cus, ctypes.byref(p)))
+    return {f: getattr(p, f) for f, _ in DgPlan._fields_}
+
+
+def dg_query_plan_form(form, m, n, k, num_groups=1, expected_m=0, num_cus=0):
+    """The plan of a call of the given form (FORM_* constant)."""
+    p = DgPlan()
+    _check("dg_query_plan_form",
+           lib().dg_query_plan_form(form, m, n, k, num_groups, expected_m, num_cus, ctypes.byref(p)))
     return {f: getattr(p, f) for f, _ in DgPlan._fields_}
 
 

@@ -205,6 +205,23 @@ static int run_fp8_gemm(Fp8GemmParams& p, int mode, int expected_m, void* worksp
 }
 
 // The three forms; ue8m0 selects packed UE8M0 scale words instead of fp32 scales.
+// Kernel mode and layout/scale flags of a dg_gemm_form (false: not a form with a plan).
+bool form_mode(int form, int* mode, int* flags) {
+  switch (form) {
+    case DG_FORM_NT: *mode = MODE_DENSE; *flags = 0; return true;
+    case DG_FORM_NN: *mode = MODE_DENSE; *flags = MODE_NN; return true;
+    case DG_FORM_TN: *mode = MODE_DENSE; *flags = MODE_AT | MODE_NN; return true;
+    case DG_FORM_TT: *mode = MODE_DENSE; *flags = MODE_AT; return true;
+    case DG_FORM_NT_UE8M0: *mode = MODE_DENSE; *flags = MODE_UE8M0; return true;
+    case DG_FORM_CONTIGUOUS_NT: *mode = MODE_CONTIG; *flags = 0; return true;
+    case DG_FORM_CONTIGUOUS_NN: *mode = MODE_CONTIG; *flags = MODE_NN; return true;
+    case DG_FORM_CONTIGUOUS_NT_UE8M0: *mode = MODE_CONTIG; *flags = MODE_UE8M0; return true;
+    case DG_FORM_MASKED_NT: *mode = MODE_MASKED; *flags = 0; return true;
+    case DG_FORM_MASKED_NT_UE8M0: *mode = MODE_MASKED; *flags = MODE_UE8M0; return true;
+  }
+  return false;
+}
+
 int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, const uint16_t* c,
                        uint16_t* d, int m, int n, int k, void* ws, size_t ws_bytes, void* stream, int flags) {
   try {
@@ -352,19 +369,7 @@ size_t dg_fp8_gemm_workspace_bytes(int form, int m, int n, int k, int num_groups
   try {
     if (m <= 0 || n <= 0 || k <= 0 || num_groups <= 0 || k % 128 != 0 || n % 16 != 0) return 0;
     int mode, flags;
-    switch (form) {
-      case DG_FORM_NT: mode = MODE_DENSE; flags = 0; break;
-      case DG_FORM_NN: mode = MODE_DENSE; flags = MODE_NN; break;
-      case DG_FORM_TN: mode = MODE_DENSE; flags = MODE_AT | MODE_NN; break;
-      case DG_FORM_TT: mode = MODE_DENSE; flags = MODE_AT; break;
-      case DG_FORM_NT_UE8M0: mode = MODE_DENSE; flags = MODE_UE8M0; break;
-      case DG_FORM_CONTIGUOUS_NT: mode = MODE_CONTIG; flags = 0; break;
-      case DG_FORM_CONTIGUOUS_NN: mode = MODE_CONTIG; flags = MODE_NN; break;
-      case DG_FORM_CONTIGUOUS_NT_UE8M0: mode = MODE_CONTIG; flags = MODE_UE8M0; break;
-      case DG_FORM_MASKED_NT: mode = MODE_MASKED; flags = 0; break;
-      case DG_FORM_MASKED_NT_UE8M0: mode = MODE_MASKED; flags = MODE_UE8M0; break;
-      default: return 0;
-    }
+    if (!dg::form_mode(form, &mode, &flags)) return 0;
     if (mode == MODE_DENSE) num_groups = 1;
     if (num_cus <= 0) {
       DeviceInfo di = current_device_info();
@@ -429,7 +434,8 @@ int dg_num_tiles(int m, int n, int block_m, int block_n) {
   return ((m + block_m - 1) / block_m) * ((n + block_n - 1) / block_n);
 }
 
-static int query_plan(int m, int n, int k, int num_groups, int mode, int num_cus, dg_plan* out) {
+static int query_plan(int m, int n, int k, int num_groups, int mode, int num_cus, dg_plan* out, int flags = 0,
+                      int expected_m = 0) {
   if (!out || m <= 0 || n <= 0 || k <= 0 || num_groups <= 0) return DG_ERR_INVALID_ARG;
   if (k % 128 != 0 || n % 16 != 0) return DG_ERR_UNSUPPORTED;
   if (num_cus <= 0) {
@@ -439,7 +445,7 @@ static int query_plan(int m, int n, int k, int num_groups, int mode, int num_cus
   }
   Fp8GemmParams p{};
   p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
-  const GemmPlan pl = plan_call(p, mode, 0, 0, num_cus).plan;
+  const GemmPlan pl = plan_call(p, mode, expected_m, flags, num_cus).plan;
   if (pl.kernel_id < 0) return DG_ERR_UNSUPPORTED;
   out->block_m = pl.block_m;
   out->block_n = pl.block_n;
@@ -457,6 +463,16 @@ int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out
 
 int dg_query_plan_contiguous(int m, int n, int k, int num_groups, int num_cus, dg_plan* out) {
   return query_plan(m, n, k, num_groups, MODE_CONTIG, num_cus, out);
+}
+
+int dg_query_plan_form(int form, int m, int n, int k, int num_groups, int expected_m, int num_cus, dg_plan* out) {
+  try {
+    int mode, flags;
+    if (!dg::form_mode(form, &mode, &flags)) return DG_ERR_INVALID_ARG;
+    return query_plan(m, n, k, mode == MODE_DENSE ? 1 : num_groups, mode, num_cus, out, flags, expected_m);
+  } catch (...) {
+    return DG_ERR_HIP;
+  }
 }
 
 const char* dg_status_string(int status) {

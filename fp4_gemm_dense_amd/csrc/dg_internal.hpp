@@ -187,6 +187,7 @@ hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mod
 
 // The dense GEMM entry (argument checks, plan, launch) behind dg_fp8_gemm_nt and its
 // layout / UE8M0 variants; flags as MODE_* above.  Returns a dg_status.
+bool form_mode(int form, int* mode, int* flags);
 int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, const uint16_t* c,
                 uint16_t* d, int m, int n, int k, void* ws, size_t ws_bytes, void* stream, int flags);
 

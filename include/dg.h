@@ -417,6 +417,14 @@ int dg_query_plan(int m, int n, int k, int num_groups, int num_cus, dg_plan* out
  * when num_cus > 0. */
 int dg_query_plan_contiguous(int m, int n, int k, int num_groups, int num_cus, dg_plan* out);
 
+/* The plan of the call of a given form (a dg_gemm_form value, as for
+ * dg_fp8_gemm_workspace_bytes), with that form's arguments: the forms differ
+ * in the kernels they may take (the skinny-M kernel of the dense NT form with
+ * fp32 scales, for one), so this is the query to use for any form but plain
+ * dense NT.  An unknown form returns DG_ERR_INVALID_ARG.  Host-only when
+ * num_cus > 0. */
+int dg_query_plan_form(int form, int m, int n, int k, int num_groups, int expected_m, int num_cus, dg_plan* out);
+
 /* Number of output tiles for a tile shape: ceil(m/block_m) * ceil(n/block_n). Host-only. */
 int dg_num_tiles(int m, int n, int block_m, int block_n);
 

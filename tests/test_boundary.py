@@ -242,17 +242,30 @@ def _check_ws_bound(form, m, n, k, groups, cus, expected_m=0):
     ws = dgm.dg_fp8_gemm_workspace_bytes(form, m, n, k, groups, expected_m, cus)
     if form in _DENSE_FORMS or form in (dgm.FORM_CONTIGUOUS_NT, dgm.FORM_CONTIGUOUS_NN,
                                         dgm.FORM_CONTIGUOUS_NT_UE8M0):
-        q = dgm.dg_query_plan_contiguous(m, n, k, groups, cus) if form == dgm.FORM_CONTIGUOUS_NT else None
-        if form == dgm.FORM_NT:   # dg_query_plan describes the NT form (other layouts may plan otherwise)
-            q = dgm.dg_query_plan(m, n, k, 1, cus)
-        if q is not None:
-            split_tiles = q["num_tiles"] - q["full_tiles"]
-            want = split_tiles * q["splits"] * q["block_m"] * q["block_n"] * 4 if q["splits"] > 1 else 0
-            assert ws == want, (form, m, n, k, q, ws)
-            assert split_tiles * q["splits"] <= cus, "at most one partial tile per workgroup slot"
+        q = dgm.dg_query_plan_form(form, m, n, k, groups, expected_m, cus)
+        split_tiles = q["num_tiles"] - q["full_tiles"]
+        want = split_tiles * q["splits"] * q["block_m"] * q["block_n"] * 4 if q["splits"] > 1 else 0
+        assert ws == want, (form, m, n, k, q, ws)
+        assert split_tiles * q["splits"] <= cus, "at most one partial tile per workgroup slot"
     # the bound every plan respects: one fp32 partial of the largest tile per slot
     assert ws <= cus * 256 * 256 * 4, (form, m, n, k, groups, ws)
     return ws
+
+
+def test_form_plan_query_names_each_forms_kernel():
+    """dg_query_plan_form plans each form as its call does: NT with fp32 scales takes
+    the skinny-M kernel for short M, the UE8M0 and transposed layouts keep the square
+    kernel; NT and contiguous NT agree with the older queries; a bad form is refused."""
+    for (m, n, k) in _CONFIG_SHAPES:
+        assert dgm.dg_query_plan_form(dgm.FORM_NT, m, n, k, 1, 0, 256) == dgm.dg_query_plan(m, n, k, 1, 256)
+        for form in (dgm.FORM_NN, dgm.FORM_TN, dgm.FORM_TT, dgm.FORM_NT_UE8M0):
+            assert dgm.dg_query_plan_form(form, m, n, k, 1, 0, 256)["kernel_id"] < 100, (form, m, n, k)
+    assert dgm.dg_query_plan_form(dgm.FORM_NT, 64, 4096, 7168, 1, 0, 256)["kernel_id"] >= 100
+    for (n, k) in [(4096, 7168), (7168, 2048)]:
+        assert (dgm.dg_query_plan_form(dgm.FORM_CONTIGUOUS_NT, 33280, n, k, 8, 0, 256)
+                == dgm.dg_query_plan_contiguous(33280, n, k, 8, 256))
+    with pytest.raises(RuntimeError):
+        dgm.dg_query_plan_form(99, 128, 128, 128, 1, 0, 256)
 
 
 def test_workspace_query_matches_the_plan_and_the_bound():
