@@ -860,7 +860,7 @@ hipError_t launch_masked_splitk_reduce(const Fp8GemmParams& p, const GemmPlan& p
   X(0, 4, 4, 4, 2, 3, 1)      \
   X(1, 4, 4, 2, 4, 3, 1)      \
   X(2, 4, 2, 2, 4, 3, 1)      \
-  X(3, 4, 2, 1, 4, 4, 1)
+  X(3, 4, 1, 1, 8, 4, 1)
 
 static const TileConfig kTileConfigs[] = {
 #define X(id, MT, NT, WM, WN, ST, OCC) {WM * MT * 16, WN * NT * 16, OCC, WM * WN * 64,                     \

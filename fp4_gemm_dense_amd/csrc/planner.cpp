@@ -69,6 +69,11 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     TileConfig tc = tile_config(id);
     if (mode == MODE_CONTIG && (128 % tc.block_m) != 0) continue;   // blocks must be group-pure
     if (bm_multiple > 0 && tc.block_m % bm_multiple != 0) continue;
+    // masked (decode) calls stream every group's B from HBM once per row tile of the
+    // group, so a tile shorter than 128 rows re-streams B for groups past its height:
+    // measured slower at every expected row count tried (32 groups x 7168 x 7168,
+    // masked_m ~ U{0..128}: 64-row tiles 353 us, 128x256 324 us)
+    if (mode == MODE_MASKED && m >= 128 && tc.block_m < 128) continue;
     int tm = cdiv(rows, tc.block_m);
     int tn = cdiv(n, tc.block_n);
     long long tiles = (long long)tm * tn * (mode == MODE_MASKED || mode == MODE_KGROUP ? num_groups : 1);
