@@ -10,7 +10,7 @@ each call on its own resident inputs:
     {(4096,7168), (7168,2048)};
   * the M-grouped masked GEMM, 32 groups x 256 rows, masked_m ~ U{0..256}, the
     same (N,K) pairs;
-all with e4m3 A/B and 1x128 / 128x128 fp32 scales: sixteen calls.
+all with e4m3 A/B and 1x128 / 128x128 fp32 scales: seventeen calls.
 value = algorithmic flops of the step / the summed time of its calls (TFLOPS);
 "forms" reports each form on its own with its roofline.
 
