@@ -169,6 +169,9 @@ def test_planner_is_host_only_and_fills_the_chip():
     assert p["splits"] > 1 and p["num_tiles"] * p["splits"] > 128
     assert p["splits"] <= 7168 // 128 // 4
     assert p["full_tiles"] == 0, "skinny M splits every tile"
+    # ... on the skinny-M kernel with all 128 rows of A in one tile, so that B (15 MB,
+    # the bulk of the call's bytes) streams from HBM once
+    assert p["kernel_id"] >= 100 and p["block_m"] == 128 and p["num_tiles"] == -(-2112 // p["block_n"])
     # a problem that already fills the chip is not split: 4096 x 7168 x 2048 has a
     # half-empty last round, but 16 K blocks are too few to gain from splitting it
     p = dgm.dg_query_plan(4096, 7168, 2048, 1, 256)
