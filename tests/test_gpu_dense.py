@@ -112,6 +112,34 @@ def test_dense_random_parity(dg, M, N, K):
     check_parity(d, R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3])
+@pytest.mark.parametrize("splits_wanted", [False, True])
+def test_dense_every_tile_random_parity(dg, monkeypatch, kernel_id, splits_wanted):
+    """Every square tile shape, pinned, on random inputs with C and ragged M and N:
+    per-row and per-block scales that differ everywhere, so a partial promoted with
+    another block's scale, or the last row block's partials promoted with the wrong
+    K block's scale, fails the tolerance (the exact-integer cases use equal scales).
+    With 64 CUs the 12 tiles cannot fill the chip and every tile is split along K,
+    which sends the partials through the workspace and the reduce kernel; with 5
+    CUs the workgroups walk several tiles each, unsplit."""
+    import fp4_gemm_dense_amd as dgm
+    bm, bn = {0: (256, 128), 1: (128, 256), 2: (128, 128), 3: (64, 128)}[kernel_id]
+    M, N, K = 2 * bm + bm // 2 + 3, 3 * bn + 48, 128 * 24
+    g = synth.gen_dense(M, N, K, seed=500 + kernel_id * 2 + splits_wanted, with_c=True)
+    a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+    monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
+    cus = 64 if splits_wanted else 5
+    dgm.dg_set_num_cus(cus)
+    try:
+        p = dgm.dg_query_plan(M, N, K, 1, cus)
+        assert p["kernel_id"] == kernel_id and (p["splits"] > 1) == splits_wanted, p
+        d = _run(dg, a, sfa, b, sfb, c)
+    finally:
+        dgm.dg_set_num_cus(0)
+    assert not (d == 0xFFFF).any(), "every output element must be written"
+    check_parity(d, R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"kernel {kernel_id} splits {splits_wanted} {M}x{N}x{K}")
+
+
 def test_dense_config0_full_parity(dg):
     """M=128, N=2112, K=7168, C = 0 (passed as NULL): the whole output vs the oracle."""
     g = synth.gen_dense(128, 2112, 7168, seed=synth.seed_for(0, 0), with_c=False)
