@@ -157,6 +157,12 @@ extern "C" __device__ void dg_raw_buffer_store_v2i32(v2i data, v4i rsrc, int vof
 extern "C" __device__ void dg_raw_buffer_store_v4i32(v4i data, v4i rsrc, int voffset, int soffset,
                                                      int aux) __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // valid with resources below 2 GiB
+// Cache policy of a buffer access (the intrinsics' aux operand): non-temporal.
+// The GEMMs' bf16 outputs are written once and never read back by the kernel, so
+// they are stored with it and evict first from L2, which the copies of A and B
+// need (measured: masked grouped GEMM 3-8 % faster; fp32 split-K partials, which
+// the reduce reads back, keep the default policy).
+constexpr int kStoreNonTemporal = 2;
 
 // LLVM's raw buffer loads into registers: lane l reads base + voffset(l) + soffset;
 // a lane whose offset lies at or beyond the resource's size reads zeros and sends

@@ -686,7 +686,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) fp8_gemm_kernel(Fp8GemmParams
       const int grow = done.m0 + idx / CPR, gcol = done.n0 + (idx % CPR) * 8;
       const bool ok = grow < done.rows_valid && gcol < N && ((grp_ok >> j) & 1u);
       const uint32_t off = ok ? ((uint32_t)grow * (uint32_t)N + (uint32_t)gcol) * 2u : kBufferOutOfRange;
-      dg_raw_buffer_store_v4i32(dv[j], rsD, (int)off, 0, 0);
+      dg_raw_buffer_store_v4i32(dv[j], rsD, (int)off, 0, kStoreNonTemporal);
     }
   }
 }

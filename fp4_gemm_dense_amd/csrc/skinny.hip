@@ -293,7 +293,7 @@ __global__ void __launch_bounds__(NW * 64, 1) skinny_gemm_kernel(SkinnyParams p)
                                    ? ((uint32_t)(m0 + row) * (uint32_t)N + (uint32_t)col) * 2u
                                    : kBufferOutOfRange;
           const v2i w = {(int)pack_bf16x2_rne(v0, v1), (int)pack_bf16x2_rne(v2, v3)};
-          dg_raw_buffer_store_v2i32(w, rsD, (int)off, 0, 0);
+          dg_raw_buffer_store_v2i32(w, rsD, (int)off, 0, kStoreNonTemporal);
         }
     }
   }
