@@ -95,7 +95,8 @@ def kernel_source_hash(kind):
     """Hash of the sources that decide the kernels (and their plans) a workload kind runs."""
     h = hashlib.sha256()
     files = (("ffn.hip", "dg_device.hpp", "dg_internal.hpp") if kind in ("ffn", "fp4_contiguous")
-             else ("fp8_gemm.hip", "skinny.hip", "planner.cpp", "api.cpp", "dg_device.hpp", "dg_internal.hpp"))
+             else ("fp8_gemm.hip", "fp8_gemm_wide.hip", "skinny.hip", "planner.cpp", "api.cpp", "dg_device.hpp",
+                   "dg_internal.hpp"))
     for f in files:
         p = os.path.join(ROOT, "fp4_gemm_dense_amd", "csrc", f)
         if os.path.exists(p):

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdg.so")
-SOURCES = ["api.cpp", "planner.cpp", "fp8_gemm.hip", "ffn.hip", "noalloc.hip", "skinny.hip"]
+SOURCES = ["api.cpp", "planner.cpp", "fp8_gemm.hip", "fp8_gemm_wide.hip", "ffn.hip", "noalloc.hip", "skinny.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -81,6 +81,14 @@ struct TileConfig {
 };
 int num_tile_configs();
 TileConfig tile_config(int kernel_id);
+// The 256x256 tile (fp8_gemm_wide.hip): dense NT with fp32 scales only.  Its
+// copies form (row) * K offsets in 32 bits for rows up to 255 past the last.
+constexpr int kWideTileId = 4;
+inline bool wide_fits(int m, int n, int k) {
+  return (long long)(m + 256) * k < (1LL << 32) && (long long)(n + 256) * k < (1LL << 32);
+}
+TileConfig wide_tile_config();
+hipError_t launch_fp8_gemm_wide(const Fp8GemmParams& p, int grid, hipStream_t stream);
 
 // Device facts the planner and launchers need (cached per device).
 struct DeviceInfo {
@@ -110,8 +118,9 @@ constexpr int kSkinnyIdBase = 100;
 GemmPlan plan_skinny(int m, int n, int k, int num_cus, bool has_c, int force_id = -1, int force_splits = -1);
 // bm_multiple > 0: only tile shapes whose height is a multiple of it (an A stored
 // [K][M] is staged in 128-row sub-tiles)
+// allow_wide: the 256x256 tile may be chosen (dense NT with fp32 scales)
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m,
-                       int bm_multiple = 0);
+                       int bm_multiple = 0, bool allow_wide = false);
 GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id);
 // Resident workgroup slots of a compiled tile shape on num_cus CUs.
 int plan_slots(int kernel_id, int num_cus);
@@ -190,8 +199,5 @@ hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mod
 bool form_mode(int form, int* mode, int* flags);
 int dense_entry(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, const uint16_t* c,
                 uint16_t* d, int m, int n, int k, void* ws, size_t ws_bytes, void* stream, int flags);
-
-// Workgroups per CU the given kernel reaches (cached; computed on first use).
-int fp8_gemm_blocks_per_cu(int kernel_id, int mode);
 
 }  // namespace dg

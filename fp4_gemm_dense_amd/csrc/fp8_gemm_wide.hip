@@ -1,0 +1,404 @@
+// Fine-grained-scaled FP8 GEMM for gfx950, 256x256 tiles: D = C + A.B^T (NT),
+// fp32 scales, bf16 out -- the dense form for problems large enough to fill the
+// chip with such tiles.
+//
+// What is computed is the dense GEMM of the usage guide ("DeepGEMM：统一高性能张量
+// 核心 GEMM 计算库编译与使用指南", 五、使用方法) with the two-level accumulation of
+// the release article ("DeepSeek 开源第三弹 ... DeepGEMM", DeepGEMM section): one
+// matrix instruction per 128-wide K block into a fresh fp32 partial, promoted on
+// the vector ALUs by sa * sb -- exactly as the 128- and 256-row tiles of
+// fp8_gemm.hip, in the same per-element order.
+//
+// Why a second kernel: every K block of a tile is copied from L2 into LDS by
+// LDS-DMA loads, and on gfx950 the copy path (texture address unit, LDS writes)
+// and the matrix cores are both about half busy on the 128x256 tile, which moves
+// 48 KB per 16 matrix instructions per wave.  A 256x256 tile moves 64 KB per 32:
+// a third fewer copy bytes and a quarter fewer LDS fragment bytes per matrix
+// instruction, half the barriers per instruction.  Its price is the LDS: a stage
+// is 65 KB, so the ring has two slots, and the stage copies of K block kb + 1
+// are issued right after block kb's barrier (one block of lead).
+//   * 8 waves as 4 x 2, each a 64 x 128 sub-tile of 16x16 blocks (MT = 4 row
+//     blocks, NT = 8 column blocks), computed transposed (B_nt . A_mt^T) so that
+//     a lane's four results lie in one row of D and share one A scale; a wave's
+//     128 columns lie in one 128-wide block of B scales;
+//   * the four A fragments of a K block are read once, the B fragments one at a
+//     time, each feeding four matrix instructions (the register file holds 128
+//     accumulators per lane, which the promotion FMAs need in VGPRs);
+//   * tile boundaries: the next unit's first stage is copied during this unit's
+//     last K block (or, with C, right after it, the last block copying half of
+//     C instead); C is staged through LDS, half a tile at a time, and D written
+//     straight from the accumulators (16 rows x 32 bytes per store instruction;
+//     the rows of a wave complete whole 128-byte lines).
+//   * split K (a partial last round) writes fp32 partial tiles to the caller's
+//     workspace, summed by the split-K reduce kernel of fp8_gemm.hip.
+#include <algorithm>
+
+#include "dg_device.hpp"
+#include "dg_internal.hpp"
+
+namespace dg {
+
+namespace {
+// The value x, opaque to the compiler: expressions of it are evaluated where
+// they are written.  Lane-dependent offsets that are needed only at a tile's
+// edges are derived from an opaque lane id there, so that the compiler cannot
+// hoist them out of the loops and hold them in registers through the K loop,
+// whose working set (accumulators, fragments, partials) fills the register file.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+constexpr int W_BM = 256, W_BN = 256, W_MT = 4, W_NT = 8, W_NW = 8;
+constexpr int W_A_BYTES = W_BM * 128, W_B_BYTES = W_BN * 128, W_SA_BYTES = W_BM * 4;
+constexpr int W_STAGE = W_A_BYTES + W_B_BYTES + W_SA_BYTES;
+constexpr int W_LDS = 2 * W_STAGE;
+constexpr int W_LAG = 4;        // matrix instructions between a partial's issue and its promotion
+constexpr int W_RA = 4, W_RB = 4;   // 1-KB copy regions of A and B per wave per stage
+constexpr int W_LPS = W_RA + W_RB + 1;   // copy instructions per wave per stage (+ the row scales)
+constexpr int W_NST = W_MT * W_NT;      // stores per wave per unit (D, or a split slice's partial)
+}  // namespace
+
+__global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  typedef const __attribute__((address_space(4))) float cfloat;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_m = wave >> 1, wave_n = wave & 1;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int M = p.m, N = p.n, K = p.k;
+  const int KB = K >> 7;
+
+  // XCD-aware remap of the persistent block id (workgroups are dealt to the 8
+  // XCDs round-robin; XCD x takes a contiguous stretch of the raster)
+  const int G = gridDim.x;
+  int vb = blockIdx.x;
+  if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+
+  // Work units: [0, full_tiles) whole tiles; then unit full_tiles + u is K slice
+  // u % splits of tile full_tiles + u / splits.
+  struct Unit {
+    int m0, n0, kb0, nkb, part;
+  };
+  auto decode = [&](int t, Unit& w) {
+    w.kb0 = 0;
+    w.nkb = KB;
+    w.part = -1;
+    if (p.splits > 1 && t >= p.full_tiles) {
+      const int u = t - p.full_tiles;
+      w.kb0 = (u % p.splits) * p.kb_per_split;
+      w.nkb = min(p.kb_per_split, KB - w.kb0);
+      w.part = u;
+      t = p.full_tiles + u / p.splits;
+    }
+    int tm, tn;
+    raster_tile(t, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
+    w.m0 = tm * W_BM;
+    w.n0 = tn * W_BN;
+  };
+
+  const v4i rsA = make_buffer_rsrc(p.a, (uint32_t)M * (uint32_t)K);
+  const v4i rsB = make_buffer_rsrc(p.b, (uint32_t)N * (uint32_t)K);
+  const v4i rsSA = make_buffer_rsrc(p.sfa, (uint32_t)KB * (uint32_t)M * 4u);
+  cfloat* const SBc = (cfloat*)(uintptr_t)p.sfb;
+
+  // Per-lane copy offsets of the unit whose stages are being copied.  Region j of
+  // a wave covers tile rows 8 (4 wave + j) .. + 7; lane l fills 16 bytes of row
+  // 8 (4 wave + j) + l / 8 at position l % 8, which holds chunk (l % 8) ^ swz(row).
+  // swz depends on the row modulo 16 only, so regions j and j + 2 (16 rows
+  // apart) share a lane's chunk and two offsets per operand serve the four
+  // regions.  A row past M (N) lies past the end of A (B): the buffer's range
+  // check makes it read zeros (its results are never stored).  Row scales:
+  // position q = g * 64 + r * 4 + mt of the slot's scale area holds row
+  // g * 64 + mt * 16 + r, so a lane's four scales are adjacent; waves w and w + 4
+  // copy the same 64 positions (identical bytes), so that every lane of every
+  // wave issues the same instructions.
+  uint32_t a_off[2], b_off[2], sa_off = 0;
+  int cp_kb0 = 0;   // first K block of that unit
+  auto setup_copies = [&](const Unit& w) {
+    cp_kb0 = w.kb0;
+    const int ln = opaque(lane);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = (wave * W_RA + e) * 8 + (ln >> 3);
+      const uint32_t chunk = (uint32_t)(((ln & 7) ^ swz(row)) << 4);
+      a_off[e] = (uint32_t)(w.m0 + row) * (uint32_t)K + chunk;
+      b_off[e] = (uint32_t)(w.n0 + row) * (uint32_t)K + chunk;
+    }
+    const int row = (wave & 3) * 64 + (ln & 3) * 16 + (ln >> 2);
+    sa_off = w.m0 + row < M ? (uint32_t)(w.m0 + row) * 4u : kBufferOutOfRange;
+  };
+  // Copy instruction idx (0-3 A regions, 4-7 B regions, 8 the row scales) of
+  // stage s (within the unit's K range) of the unit set up last, into the slot
+  // at byte offset slot.
+  auto issue = [&](int idx, int s, uint32_t slot) {
+    const uint32_t kofs = (uint32_t)(cp_kb0 + s) * 128u;
+    if (idx < W_RA) {
+      const uint32_t off = a_off[idx & 1] + (uint32_t)(idx >> 1) * 16u * (uint32_t)K;
+      buf16_to_lds(rsA, off, kofs, smem + slot + (wave * W_RA + idx) * 1024);
+    } else if (idx < W_RA + W_RB) {
+      const int j = idx - W_RA;
+      const uint32_t off = b_off[j & 1] + (uint32_t)(j >> 1) * 16u * (uint32_t)K;
+      buf16_to_lds(rsB, off, kofs, smem + slot + W_A_BYTES + (wave * W_RB + j) * 1024);
+    } else {
+      buf4_to_lds(rsSA, sa_off, (uint32_t)(cp_kb0 + s) * (uint32_t)M * 4u,
+                  smem + slot + W_A_BYTES + W_B_BYTES + (wave & 3) * 256);
+    }
+  };
+  // C of a whole tile is staged through a free LDS slot, half a tile at a time:
+  // half h holds row blocks 2h and 2h + 1 of every wave row, 128 rows of 512
+  // bytes; half row q is tile row (q / 32) * 64 + (2h + (q / 16) % 2) * 16 + q % 16
+  // and keeps its 16-byte chunk c at position c ^ (q % 16), so that the 16 rows a
+  // wave reads at once fall on distinct banks.  Copy j (0-7) of wave w fills half
+  // rows 16 w + 2 j and + 1 (lanes 0-31 and 32-63).  Elements past M or N read
+  // zeros (they are never stored).
+  const v4i rsC = make_buffer_rsrc(p.c, (uint32_t)M * (uint32_t)N * 2u);
+  auto issue_c = [&](int j, int h, const Unit& w, uint32_t slot) {
+    const int ln = opaque(lane);
+    const int r16 = 2 * j + (ln >> 5);
+    const int row = w.m0 + (wave >> 1) * 64 + (2 * h + (wave & 1)) * 16 + r16;
+    const int col = w.n0 + (((ln & 31) ^ r16) << 3);
+    const uint32_t off = row < M && col < N ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : kBufferOutOfRange;
+    buf16_to_lds(rsC, off, 0u, smem + slot + (wave * 8 + j) * 1024);
+  };
+  constexpr int W_CPH = 8;   // C copy instructions per wave per half tile
+
+  // LDS fragment read offsets (slot 0; block mt / nt adds mt * 2048 / nt * 2048)
+  const int sw = swz(lrow);
+  const uint32_t a_lo = (wave_m * 64 + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
+  const uint32_t a_hi = (wave_m * 64 + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
+  const uint32_t b_lo = W_A_BYTES + (wave_n * 128 + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
+  const uint32_t b_hi = W_A_BYTES + (wave_n * 128 + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
+  const uint32_t sa_rd = W_A_BYTES + W_B_BYTES + (wave_m * 64 + lrow * 4) * 4;
+
+  int t = vb;
+  if (t >= p.total_tiles) return;
+  Unit cur;
+  decode(t, cur);
+  setup_copies(cur);
+  // The ring: stage s of a unit sits in slot s0 ^ (s & 1); K block kb copies
+  // stage kb + 1 into the other slot right after its barrier (every wave is then
+  // done with stage kb - 1, which that slot held), and the last K block copies
+  // the next unit's stage 0, or the first half of C, which then goes first.
+  uint32_t s0 = 0;
+#pragma unroll
+  for (int idx = 0; idx < W_LPS; ++idx) issue(idx, 0, 0u);
+  bool stores_pending = false;   // the previous unit's stores were issued after this unit's stage 0
+
+  while (true) {
+    const int KT = cur.nkb;
+    const int kb0 = cur.kb0;
+    const int tn_col0 = min(cur.n0 + wave_n * 128, N - 1);
+    const int sb_idx = __builtin_amdgcn_readfirstlane((tn_col0 >> 7) * KB + kb0);
+    const int t_next = t + G;
+    const bool have_next = t_next < p.total_tiles;
+    Unit nxt{};
+    if (have_next) decode(t_next, nxt);
+    const bool c_lds = cur.part < 0 && p.c != nullptr;   // C is added (staged through LDS)
+
+    v4f acc[W_MT][W_NT];
+#pragma unroll
+    for (int mt = 0; mt < W_MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < W_NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+    v4f part[W_LAG];
+#pragma unroll
+    for (int r = 0; r < W_LAG; ++r) part[r] = v4f{0.f, 0.f, 0.f, 0.f};
+    float sprev[W_MT] = {0.f, 0.f, 0.f, 0.f};
+
+    // One K block from the slot at byte offset rd; copy(j) issues what goes
+    // after matrix instruction j (one copy instruction after each of the first
+    // nine).  Block j = nt * MT + mt goes into partial register j % LAG (= mt);
+    // the register's previous partial, of block (nt - 1, mt) -- for nt = 0 block
+    // (NT - 1, mt) of the previous K block, scale sprev -- is promoted first.
+    auto kblock = [&](int kb, uint32_t rd, auto&& copy) {
+      // Stage kb has landed once no more than the copies and stores issued after
+      // it remain (a wave's memory operations retire in issue order): at kb = 0
+      // the previous unit's stores, later nothing (stage kb was the last thing
+      // issued, in block kb - 1).
+      if (kb == 0 && stores_pending) wait_vmcnt<W_NST>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      const float sbv = SBc[sb_idx + kb];
+      const v4f sav = *reinterpret_cast<const v4f*>(smem + rd + sa_rd);
+      float scur[W_MT];
+#pragma unroll
+      for (int i = 0; i < W_MT; ++i) scur[i] = sav[i] * sbv;
+      v8i af[W_MT];
+#pragma unroll
+      for (int mt = 0; mt < W_MT; ++mt) {
+        const v4i lo = *reinterpret_cast<const v4i*>(smem + rd + a_lo + mt * 2048);
+        const v4i hi = *reinterpret_cast<const v4i*>(smem + rd + a_hi + mt * 2048);
+        af[mt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+#pragma unroll
+      for (int nt = 0; nt < W_NT; ++nt) {
+        const v4i lo = *reinterpret_cast<const v4i*>(smem + rd + b_lo + nt * 2048);
+        const v4i hi = *reinterpret_cast<const v4i*>(smem + rd + b_hi + nt * 2048);
+        const v8i bf = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int mt = 0; mt < W_MT; ++mt) {
+          const int j = nt * W_MT + mt;
+          if (nt == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][W_NT - 1][i] = fmaf(part[mt][i], sprev[mt], acc[mt][W_NT - 1][i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][nt - 1][i] = fmaf(part[mt][i], scur[mt], acc[mt][nt - 1][i]);
+          }
+          part[mt] = mfma_e4m3_16x16x128(bf, af[mt], v4f{0.f, 0.f, 0.f, 0.f});
+          if (j < W_LPS) copy(j);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (promotion)
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+          if (j < W_LPS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM (copy)
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < W_MT; ++i) sprev[i] = scur[i];
+    };
+
+#pragma clang loop unroll(disable)
+    for (int kb = 0; kb < KT - 1; ++kb) {
+      const uint32_t wr = (s0 ^ (uint32_t)((kb + 1) & 1)) * (uint32_t)W_STAGE;
+      kblock(kb, (s0 ^ (uint32_t)(kb & 1)) * (uint32_t)W_STAGE, [&](int j) { issue(j, kb + 1, wr); });
+    }
+    // the last K block: into the other slot goes half 0 of C, else the next
+    // unit's stage 0
+    const uint32_t last_slot = (s0 ^ (uint32_t)((KT - 1) & 1)) * (uint32_t)W_STAGE;
+    const uint32_t other_slot = last_slot ^ (uint32_t)W_STAGE;
+    const bool copy_next = have_next && !c_lds;
+    if (copy_next) setup_copies(nxt);
+    kblock(KT - 1, last_slot, [&](int j) {
+      if (c_lds) {
+        if (j < W_CPH) issue_c(j, 0, cur, other_slot);
+      } else if (copy_next) {
+        issue(j, 0, other_slot);
+      }
+    });
+    // promote the last K block's last column blocks
+#pragma unroll
+    for (int mt = 0; mt < W_MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][W_NT - 1][i] = fmaf(part[mt][i], sprev[mt], acc[mt][W_NT - 1][i]);
+
+    // ---------------- tile boundary ----------------
+    const Unit done = cur;
+    const bool whole = done.part < 0;
+    // Element (row block mt, column block nt) of a lane sits at the lane's offset
+    // in row block 0 plus a uniform (mt, nt) part, passed as the scalar offset.
+    // N is a multiple of 16, so a column block lies inside or outside D as a
+    // whole; an element outside D takes an out-of-range lane offset.
+    const int ln = opaque(lane);
+    const int row0 = done.m0 + wave_m * 64 + (ln & 15), col0 = done.n0 + wave_n * 128;
+    const uint32_t d_lane = ((uint32_t)row0 * (uint32_t)N + (uint32_t)(col0 + 4 * (ln >> 4))) * 2u;
+    auto d_off = [&](int mt, int nt) -> int {
+      return (int)(row0 + mt * 16 < M && col0 + nt * 16 < N ? d_lane : kBufferOutOfRange);
+    };
+    auto d_sofs = [&](int mt, int nt) -> int { return (mt * 16 * N + nt * 16) * 2; };
+    // (default cache policy: a store instruction writes 32 bytes of each of 16
+    // rows, and the lines of a row are completed by the wave's other column
+    // blocks -- in L2, which a non-temporal hint would make evict them before,
+    // writing partial lines to HBM: measured 25-40 % slower on whole-chip runs)
+    const v4i rsD = make_buffer_rsrc(p.d, (uint32_t)M * (uint32_t)N * 2u);
+    // bf16 of (row block 2h + i, column block nt) plus, with C, the lane's four
+    // C values from the half staged at slot
+    auto pack = [&](int h, int i, int nt, bool add_c, uint32_t slot) -> v2i {
+      const v4f a = acc[2 * h + i][nt];
+      float v0 = a[0], v1 = a[1], v2 = a[2], v3 = a[3];
+      if (add_c) {
+        const int q = wave_m * 32 + i * 16 + (ln & 15);
+        const v2i cv = *reinterpret_cast<const v2i*>(smem + slot + q * 512 + wave_n * 256 +
+                                                     (((2 * nt + (ln >> 5)) ^ (ln & 15)) << 4) + ((ln >> 4) & 1) * 8);
+        v0 += __uint_as_float((uint32_t)cv.x << 16);
+        v1 += __uint_as_float((uint32_t)cv.x & 0xffff0000u);
+        v2 += __uint_as_float((uint32_t)cv.y << 16);
+        v3 += __uint_as_float((uint32_t)cv.y & 0xffff0000u);
+      }
+      return v2i{(int)pack_bf16x2_rne(v0, v1), (int)pack_bf16x2_rne(v2, v3)};
+    };
+    if (c_lds) {
+      // Half 0 of C is in the other slot; the next unit's stage 0 goes into this
+      // one once every wave is done with it.  Half 0 is added and packed, half 1
+      // copied into the other slot once every wave has read half 0, and half 0's
+      // stores issued while it lands.  (The next unit's first K block copies its
+      // stage 1 into the other slot after its barrier, which every wave reaches
+      // only after reading half 1.)
+      wait_lgkmcnt0();
+      block_barrier();
+      if (have_next) {
+        setup_copies(nxt);
+#pragma unroll
+        for (int idx = 0; idx < W_LPS; ++idx) issue(idx, 0, last_slot);
+        wait_vmcnt<W_LPS>();   // half 0 has landed (only the next stage 0 was issued after it)
+      } else {
+        wait_vmcnt<0>();
+      }
+      block_barrier();
+      v2i w0[2][W_NT];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int nt = 0; nt < W_NT; ++nt) w0[i][nt] = pack(0, i, nt, true, other_slot);
+      wait_lgkmcnt0();
+      block_barrier();
+#pragma unroll
+      for (int j = 0; j < W_CPH; ++j) issue_c(j, 1, done, other_slot);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int nt = 0; nt < W_NT; ++nt)
+          dg_raw_buffer_store_v2i32(w0[i][nt], rsD, d_off(i, nt), d_sofs(i, nt), 0);
+      wait_vmcnt<W_NST / 2>();   // half 1 has landed (only half 0's stores were issued after it)
+      block_barrier();
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int nt = 0; nt < W_NT; ++nt)
+          dg_raw_buffer_store_v2i32(pack(1, i, nt, true, other_slot), rsD, d_off(2 + i, nt), d_sofs(2 + i, nt),
+                                    0);
+    } else if (whole) {
+#pragma unroll
+      for (int mt = 0; mt < W_MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < W_NT; ++nt)
+          dg_raw_buffer_store_v2i32(pack(mt >> 1, mt & 1, nt, false, 0u), rsD, d_off(mt, nt), d_sofs(mt, nt),
+                                    0);
+    } else {
+      // fp32 partial tile of this slice: ws[part][BM][BN], row-major (partials
+      // past M or N are written too: the reduce reads only valid ones)
+      const v4i rsW = make_buffer_rsrc(p.ws + (size_t)done.part * (W_BM * W_BN), (uint32_t)(W_BM * W_BN * 4));
+      const int w_lane = ((wave_m * 64 + (ln & 15)) * W_BN + wave_n * 128 + 4 * (ln >> 4)) * 4;
+#pragma unroll
+      for (int mt = 0; mt < W_MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < W_NT; ++nt) {
+          const v4i w = {__float_as_int(acc[mt][nt][0]), __float_as_int(acc[mt][nt][1]),
+                         __float_as_int(acc[mt][nt][2]), __float_as_int(acc[mt][nt][3])};
+          dg_raw_buffer_store_v4i32(w, rsW, w_lane, (mt * 16 * W_BN + nt * 16) * 4, 0);
+        }
+    }
+    if (!have_next) break;
+    t = t_next;
+    cur = nxt;
+    // the next unit's stage 0 sits in the last block's slot when C was staged,
+    // else in the other one
+    s0 = (c_lds ? last_slot : other_slot) / (uint32_t)W_STAGE;
+    stores_pending = true;
+  }
+  wait_vmcnt<0>();
+}
+
+TileConfig wide_tile_config() { return TileConfig{W_BM, W_BN, 1, W_NW * 64, W_LDS, 2}; }
+
+hipError_t launch_fp8_gemm_wide(const Fp8GemmParams& p, int grid, hipStream_t stream) {
+  if (!wide_fits(p.m, p.n, p.k)) return hipErrorInvalidValue;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fp8_gemm_wide_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, W_LDS);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(fp8_gemm_wide_kernel, dim3(grid), dim3(W_NW * 64), W_LDS, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -16,6 +16,7 @@ namespace dg {
 
 static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+
 // Resident workgroups per CU for each compiled tile shape: the smaller of the
 // LDS bound (160 KB per CU) and the occupancy the tile table records.
 static int blocks_per_cu_for(int kernel_id) {
@@ -58,7 +59,8 @@ GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num
   return plan;
 }
 
-GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m, int bm_multiple) {
+GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m, int bm_multiple,
+                       bool allow_wide) {
   int best_id = -1;
   // rows each group contributes (masked: the expected count if given, else capacity)
   int rows = m;
@@ -67,6 +69,7 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
   double best_score = -1.0;
   for (int id = 0; id < num_tile_configs(); ++id) {
     TileConfig tc = tile_config(id);
+    if (id == kWideTileId && (!allow_wide || mode != MODE_DENSE)) continue;
     if (mode == MODE_CONTIG && (128 % tc.block_m) != 0) continue;   // blocks must be group-pure
     if (bm_multiple > 0 && tc.block_m % bm_multiple != 0) continue;
     // masked (decode) calls stream every group's B from HBM once per row tile of the
@@ -102,6 +105,12 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     // HBM, and a deeper copy ring keeps more of it in flight (measured: the
     // 4-slot 64x128 shape beats the 3-slot ones at M = 64 and 128)
     if (splits > 1 && full == 0) intensity = tc.stages;
+    // The 256x256 tile: measured on MI355X against the 256x128 / 128x256 tiles
+    // at equal fill, about 12 % faster per K block on long K loops, but its
+    // fixed costs per tile (pipeline fill, C staging, the stores) weigh twice as
+    // much: relative speed about 1.12 kb / (kb + 2), below 1 up to K = 2048
+    // (0.75 at K = 512, 0.96 at 1536, 1.08 at 7168)
+    else if (id == kWideTileId) intensity = 256.0 * 128.0 / 384.0 * 1.12 * kb / (kb + 2.0);
     double score = util * fill * intensity;
     // wide tiles store longer rows of D (512 bytes): measured 2-7 % faster than
     // the tall tile of the same area up to K = 8192 (the shorter the K loop, the

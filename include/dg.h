@@ -405,7 +405,8 @@ typedef struct dg_plan {
   int block_n;
   int num_tiles;        /* output tiles */
   int num_workgroups;
-  int kernel_id;
+  int kernel_id;        /* 0-3: the 256x128, 128x256, 128x128, 64x128 tiles; 4: the 256x256 tile
+                           (dense NT with fp32 scales only); >= 100: the skinny-M kernel */
   int splits;           /* K slices per split tile (dense only; 1: no split) */
   int full_tiles;       /* tiles computed whole; the other num_tiles - full_tiles are split */
 } dg_plan;

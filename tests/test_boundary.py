@@ -271,6 +271,25 @@ def test_form_plan_query_names_each_forms_kernel():
         dgm.dg_query_plan_form(99, 128, 128, 128, 1, 0, 256)
 
 
+def test_wide_tile_is_dense_nt_only(monkeypatch):
+    """The 256 x 256 tile (kernel 4) serves the dense NT form with fp32 scales
+    only: pinned on another form the pin is ignored; pinned on NT it is planned,
+    with its workspace (split K) counted like any other tile's; a shape whose row
+    offsets would pass 2^32 bytes keeps the square tiles."""
+    monkeypatch.setenv("DG_FORCE_KERNEL", "4")
+    for form in (dgm.FORM_NN, dgm.FORM_TN, dgm.FORM_TT, dgm.FORM_NT_UE8M0):
+        assert dgm.dg_query_plan_form(form, 1024, 1024, 1024, 1, 0, 256)["kernel_id"] != 4, form
+    assert dgm.dg_query_plan_form(dgm.FORM_CONTIGUOUS_NT, 1024, 1024, 1024, 4, 0, 256)["kernel_id"] != 4
+    assert dgm.dg_query_plan_form(dgm.FORM_MASKED_NT, 256, 1024, 1024, 8, 128, 256)["kernel_id"] != 4
+    p = dgm.dg_query_plan_form(dgm.FORM_NT, 1000, 1040, 2048, 1, 0, 256)
+    assert (p["kernel_id"], p["block_m"], p["block_n"], p["num_tiles"]) == (4, 256, 256, 4 * 5)
+    _check_ws_bound(dgm.FORM_NT, 1000, 1040, 2048, 1, 256)
+    assert dgm.dg_query_plan_form(dgm.FORM_NT, 4096, 4096, 7168, 1, 0, 256)["splits"] == 1
+    # (m + 256) * k must stay below 2^32: 2^31 bytes of A and B at K = 2^24 do not
+    assert dgm.dg_query_plan_form(dgm.FORM_NT, 128, 128, 1 << 24, 1, 0, 256)["kernel_id"] != 4
+    assert dgm.dg_query_plan_form(dgm.FORM_NT, 128, 128, 1 << 22, 1, 0, 256)["kernel_id"] == 4
+
+
 def test_workspace_query_matches_the_plan_and_the_bound():
     for (m, n, k) in _CONFIG_SHAPES:
         for form in _DENSE_FORMS:

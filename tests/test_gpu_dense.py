@@ -79,18 +79,21 @@ def test_dense_identity_b_and_all_ones(dg):
     assert np.all(F.bf16_bits_to_f64(d) == K * 0.5 * 0.25 + 3.0)
 
 
-@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3])
+@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("K", [128, 256, 384, 640])
-def test_dense_many_tiles_per_workgroup_bit_exact(dg, monkeypatch, kernel_id, K):
+@pytest.mark.parametrize("with_c", [True, False], ids=["c", "no_c"])
+def test_dense_many_tiles_per_workgroup_bit_exact(dg, monkeypatch, kernel_id, K, with_c):
     """Three workgroups walk every tile in turn, so each runs many tiles back to
-    back with C.  A tile starts its LDS ring in the slot of the previous tile's
-    last K block and stages D over C in LDS; one to five K blocks per tile cover
-    every step of the ring start (K blocks - 1 modulo the slot count).  Exact
-    integer inputs: the result is unique."""
+    back, with and without C.  A tile starts its LDS ring in the slot of the
+    previous tile's last K block and stages C (or D over C) in LDS; one to five K
+    blocks per tile cover every step of the ring start (K blocks - 1 modulo the
+    slot count).  Kernel 4 is the 256 x 256 tile, whose next tile's first stage
+    goes to a different slot with C than without.  Exact integer inputs: the
+    result is unique."""
     import fp4_gemm_dense_amd as dgm
-    rng = np.random.default_rng(kernel_id * 10 + K)
+    rng = np.random.default_rng(kernel_id * 10 + K + (0 if with_c else 5))
     M, N = 520, 784                     # ragged in both dimensions for every tile shape
-    a, sfa, b, sfb, c, exact = make_exact_case(rng, M, N, K, True)
+    a, sfa, b, sfb, c, exact = make_exact_case(rng, M, N, K, with_c)
     monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
     dgm.dg_set_num_cus(3)
     try:
@@ -112,10 +115,10 @@ def test_dense_random_parity(dg, M, N, K):
     check_parity(d, R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3])
+@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("splits_wanted", [False, True])
 def test_dense_every_tile_random_parity(dg, monkeypatch, kernel_id, splits_wanted):
-    """Every square tile shape, pinned, on random inputs with C and ragged M and N:
+    """Every tile shape, pinned, on random inputs with C and ragged M and N:
     per-row and per-block scales that differ everywhere, so a partial promoted with
     another block's scale, or the last row block's partials promoted with the wrong
     K block's scale, fails the tolerance (the exact-integer cases use equal scales).
@@ -123,7 +126,7 @@ def test_dense_every_tile_random_parity(dg, monkeypatch, kernel_id, splits_wante
     which sends the partials through the workspace and the reduce kernel; with 5
     CUs the workgroups walk several tiles each, unsplit."""
     import fp4_gemm_dense_amd as dgm
-    bm, bn = {0: (256, 128), 1: (128, 256), 2: (128, 128), 3: (64, 128)}[kernel_id]
+    bm, bn = {0: (256, 128), 1: (128, 256), 2: (128, 128), 3: (64, 128), 4: (256, 256)}[kernel_id]
     M, N, K = 2 * bm + bm // 2 + 3, 3 * bn + 48, 128 * 24
     g = synth.gen_dense(M, N, K, seed=500 + kernel_id * 2 + splits_wanted, with_c=True)
     a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
@@ -166,3 +169,46 @@ def test_dense_sweep_full_size_sampled(dg, mi, nki):
     a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
     ref = entries_in_chunks(lambda r, q: R.fp8_gemm_nt_entries(a, sfa, b, sfb, c, r, q), rows, cols)
     check_parity(db[rows, cols], ref, what=f"sweep M={M} N={N} K={K}")
+
+
+def test_wide_tile_matches_square_tiles_bitwise(dg, monkeypatch):
+    """The 256 x 256 tile promotes each K block's partial with the same fused
+    multiply-add, in the same K order, as the square-tile template: on random
+    inputs with C its output is bit-identical to the 128 x 256 and 256 x 128
+    tiles' (a different accumulation order would differ in the last bit of many
+    elements)."""
+    M, N, K = 1000, 1040, 2048
+    g = synth.gen_dense(M, N, K, seed=4242, with_c=True)
+    a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
+    outs = {}
+    for kid in (0, 1, 4):
+        monkeypatch.setenv("DG_FORCE_KERNEL", str(kid))
+        outs[kid] = _run(dg, a, sfa, b, sfb, c)
+    assert not (outs[4] == 0xFFFF).any()
+    for kid in (0, 1):
+        mism = outs[4] != outs[kid]
+        assert not mism.any(), f"256x256 vs kernel {kid}: {mism.sum()} bit mismatches, first at {np.argwhere(mism)[0]}"
+    check_parity(outs[4], R.fp8_gemm_nt(a, sfa, b, sfb, c), what="256x256 1000x1040x2048")
+
+
+@pytest.mark.parametrize("mi,nki,with_c", [(1, 0, True), (1, 3, True), (1, 4, False), (0, 5, False)])
+def test_wide_tile_full_size_sampled(dg, monkeypatch, mi, nki, with_c):
+    """The 256 x 256 tile, pinned, on dense sweep shapes at full size (every
+    output tile sampled as in the sweep test), with and without C."""
+    monkeypatch.setenv("DG_FORCE_KERNEL", "4")
+    M = synth.DENSE_M[mi]
+    N, K = synth.DENSE_NK[nki]
+    assert dg.dg_query_plan_form(0, M, N, K)["kernel_id"] == 4
+    g = synth.gen_dense(M, N, K, seed=synth.seed_for(1, mi * 6 + nki) + 7, with_c=with_c, backend="torch",
+                        device="cuda")
+    d = sentinel_like((M, N))
+    dg.dg_fp8_gemm_nt(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
+    torch.cuda.synchronize()
+    db = bits(d)
+    assert not (db == 0xFFFF).any()
+    rng = np.random.default_rng(100 + mi * 6 + nki)
+    rows, cols = stratified_entries(M, N, rng)
+    a, sfa, b, sfb = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb"))
+    c = None if g["c"] is None else synth.to_numpy(g["c"])
+    ref = entries_in_chunks(lambda r, q: R.fp8_gemm_nt_entries(a, sfa, b, sfb, c, r, q), rows, cols)
+    check_parity(db[rows, cols], ref, what=f"256x256 M={M} N={N} K={K} c={with_c}")
