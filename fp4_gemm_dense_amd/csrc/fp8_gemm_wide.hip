@@ -26,9 +26,9 @@
 //     accumulators per lane, which the promotion FMAs need in VGPRs);
 //   * tile boundaries: the next unit's first stage is copied during this unit's
 //     last K block (or, with C, right after it, the last block copying half of
-//     C instead); C is staged through LDS, half a tile at a time, and D written
-//     straight from the accumulators (16 rows x 32 bytes per store instruction;
-//     the rows of a wave complete whole 128-byte lines).
+//     C instead); D leaves through a free LDS slot half a tile at a time, as
+//     bf16 (plus C, staged there in the same layout), and is stored from there
+//     in whole rows (two 512-byte rows per store instruction).
 //   * split K (a partial last round) writes fp32 partial tiles to the caller's
 //     workspace, summed by the split-K reduce kernel of fp8_gemm.hip.
 #include <algorithm>
@@ -56,7 +56,6 @@ constexpr int W_LDS = 2 * W_STAGE;
 constexpr int W_LAG = 4;        // matrix instructions between a partial's issue and its promotion
 constexpr int W_RA = 4, W_RB = 4;   // 1-KB copy regions of A and B per wave per stage
 constexpr int W_LPS = W_RA + W_RB + 1;   // copy instructions per wave per stage (+ the row scales)
-constexpr int W_NST = W_MT * W_NT;      // stores per wave per unit (D, or a split slice's partial)
 }  // namespace
 
 __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) {
@@ -165,14 +164,6 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
   };
   constexpr int W_CPH = 8;   // C copy instructions per wave per half tile
 
-  // LDS fragment read offsets (slot 0; block mt / nt adds mt * 2048 / nt * 2048)
-  const int sw = swz(lrow);
-  const uint32_t a_lo = (wave_m * 64 + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
-  const uint32_t a_hi = (wave_m * 64 + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
-  const uint32_t b_lo = W_A_BYTES + (wave_n * 128 + lrow) * 128 + (((2 * lgrp) ^ sw) << 4);
-  const uint32_t b_hi = W_A_BYTES + (wave_n * 128 + lrow) * 128 + (((2 * lgrp + 1) ^ sw) << 4);
-  const uint32_t sa_rd = W_A_BYTES + W_B_BYTES + (wave_m * 64 + lrow * 4) * 4;
-
   int t = vb;
   if (t >= p.total_tiles) return;
   Unit cur;
@@ -198,6 +189,17 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     if (have_next) decode(t_next, nxt);
     const bool c_lds = cur.part < 0 && p.c != nullptr;   // C is added (staged through LDS)
 
+    // LDS fragment read offsets (slot 0; block mt / nt adds mt * 2048 / nt *
+    // 2048), derived anew for every unit so that they need no register through
+    // the tile boundary
+    const int lf = opaque(lane);
+    const int fr = lf & 15, fg = lf >> 4, sw = swz(fr);
+    const uint32_t a_lo = (wave_m * 64 + fr) * 128 + (((2 * fg) ^ sw) << 4);
+    const uint32_t a_hi = (wave_m * 64 + fr) * 128 + (((2 * fg + 1) ^ sw) << 4);
+    const uint32_t b_lo = W_A_BYTES + (wave_n * 128 + fr) * 128 + (((2 * fg) ^ sw) << 4);
+    const uint32_t b_hi = W_A_BYTES + (wave_n * 128 + fr) * 128 + (((2 * fg + 1) ^ sw) << 4);
+    const uint32_t sa_rd = W_A_BYTES + W_B_BYTES + (wave_m * 64 + fr * 4) * 4;
+
     v4f acc[W_MT][W_NT];
 #pragma unroll
     for (int mt = 0; mt < W_MT; ++mt)
@@ -216,9 +218,10 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     auto kblock = [&](int kb, uint32_t rd, auto&& copy) {
       // Stage kb has landed once no more than the copies and stores issued after
       // it remain (a wave's memory operations retire in issue order): at kb = 0
-      // the previous unit's stores, later nothing (stage kb was the last thing
-      // issued, in block kb - 1).
-      if (kb == 0 && stores_pending) wait_vmcnt<W_NST>();
+      // the previous unit's last stores (16 of D's; a split unit's 32 partial
+      // stores are waited for down to 16), later nothing (stage kb was the last
+      // thing issued, in block kb - 1).
+      if (kb == 0 && stores_pending) wait_vmcnt<2 * W_CPH>();
       else wait_vmcnt<0>();
       block_barrier();
       const float sbv = SBc[sb_idx + kb];
@@ -286,45 +289,61 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     // ---------------- tile boundary ----------------
     const Unit done = cur;
     const bool whole = done.part < 0;
-    // Element (row block mt, column block nt) of a lane sits at the lane's offset
-    // in row block 0 plus a uniform (mt, nt) part, passed as the scalar offset.
-    // N is a multiple of 16, so a column block lies inside or outside D as a
-    // whole; an element outside D takes an out-of-range lane offset.
     const int ln = opaque(lane);
-    const int row0 = done.m0 + wave_m * 64 + (ln & 15), col0 = done.n0 + wave_n * 128;
-    const uint32_t d_lane = ((uint32_t)row0 * (uint32_t)N + (uint32_t)(col0 + 4 * (ln >> 4))) * 2u;
-    auto d_off = [&](int mt, int nt) -> int {
-      return (int)(row0 + mt * 16 < M && col0 + nt * 16 < N ? d_lane : kBufferOutOfRange);
-    };
-    auto d_sofs = [&](int mt, int nt) -> int { return (mt * 16 * N + nt * 16) * 2; };
-    // (default cache policy: a store instruction writes 32 bytes of each of 16
-    // rows, and the lines of a row are completed by the wave's other column
-    // blocks -- in L2, which a non-temporal hint would make evict them before,
-    // writing partial lines to HBM: measured 25-40 % slower on whole-chip runs)
     const v4i rsD = make_buffer_rsrc(p.d, (uint32_t)M * (uint32_t)N * 2u);
-    // bf16 of (row block 2h + i, column block nt) plus, with C, the lane's four
-    // C values from the half staged at slot
-    auto pack = [&](int h, int i, int nt, bool add_c, uint32_t slot) -> v2i {
-      const v4f a = acc[2 * h + i][nt];
-      float v0 = a[0], v1 = a[1], v2 = a[2], v3 = a[3];
-      if (add_c) {
-        const int q = wave_m * 32 + i * 16 + (ln & 15);
-        const v2i cv = *reinterpret_cast<const v2i*>(smem + slot + q * 512 + wave_n * 256 +
-                                                     (((2 * nt + (ln >> 5)) ^ (ln & 15)) << 4) + ((ln >> 4) & 1) * 8);
-        v0 += __uint_as_float((uint32_t)cv.x << 16);
-        v1 += __uint_as_float((uint32_t)cv.x & 0xffff0000u);
-        v2 += __uint_as_float((uint32_t)cv.y << 16);
-        v3 += __uint_as_float((uint32_t)cv.y & 0xffff0000u);
+    // LDS address of a lane's four values of (row block 2h + i, column block nt)
+    // in a staged half tile (C's layout)
+    auto cd_addr = [&](int i, int nt, uint32_t slot) -> uint32_t {
+      const int q = wave_m * 32 + i * 16 + (ln & 15);
+      return slot + q * 512 + wave_n * 256 + (((2 * nt + (ln >> 5)) ^ (ln & 15)) << 4) + ((ln >> 4) & 1) * 8;
+    };
+    // half h of D as bf16 into the half tile staged at slot (over C, plus C)
+    auto stage_d = [&](int h, bool add_c, uint32_t slot) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int nt = 0; nt < W_NT; ++nt) {
+          const uint32_t addr = cd_addr(i, nt, slot);
+          const v4f a = acc[2 * h + i][nt];
+          float v0 = a[0], v1 = a[1], v2 = a[2], v3 = a[3];
+          if (add_c) {
+            const v2i cv = *reinterpret_cast<const v2i*>(smem + addr);
+            v0 += __uint_as_float((uint32_t)cv.x << 16);
+            v1 += __uint_as_float((uint32_t)cv.x & 0xffff0000u);
+            v2 += __uint_as_float((uint32_t)cv.y << 16);
+            v3 += __uint_as_float((uint32_t)cv.y & 0xffff0000u);
+          }
+          *reinterpret_cast<v2i*>(smem + addr) = v2i{(int)pack_bf16x2_rne(v0, v1), (int)pack_bf16x2_rne(v2, v3)};
+        }
+    };
+    // a staged half tile's rows into registers (copy j's place of issue_c), then
+    // to D: every store instruction writes two whole 512-byte rows, so the lines
+    // are whole and the non-temporal hint lets them leave L2 first (stores of
+    // 32 bytes in each of 16 rows, straight from the accumulators, measured 5-25 %
+    // slower: partial lines, and a wave's stores stall its next tile's K loop)
+    v4i drow[W_CPH];
+    auto read_d = [&](uint32_t slot) {
+#pragma unroll
+      for (int j = 0; j < W_CPH; ++j) drow[j] = *reinterpret_cast<const v4i*>(smem + slot + (wave * 8 + j) * 1024 + ln * 16);
+    };
+    auto store_d = [&](int h) {
+#pragma unroll
+      for (int j = 0; j < W_CPH; ++j) {
+        const int r16 = 2 * j + (ln >> 5);
+        const int row = done.m0 + (wave >> 1) * 64 + (2 * h + (wave & 1)) * 16 + r16;
+        const int col = done.n0 + (((ln & 31) ^ r16) << 3);
+        const uint32_t off = row < M && col < N ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : kBufferOutOfRange;
+        dg_raw_buffer_store_v4i32(drow[j], rsD, (int)off, 0, kStoreNonTemporal);
       }
-      return v2i{(int)pack_bf16x2_rne(v0, v1), (int)pack_bf16x2_rne(v2, v3)};
     };
     if (c_lds) {
       // Half 0 of C is in the other slot; the next unit's stage 0 goes into this
-      // one once every wave is done with it.  Half 0 is added and packed, half 1
-      // copied into the other slot once every wave has read half 0, and half 0's
-      // stores issued while it lands.  (The next unit's first K block copies its
-      // stage 1 into the other slot after its barrier, which every wave reaches
-      // only after reading half 1.)
+      // one once every wave is done with it.  Each half of D is formed over its
+      // half of C in place (a lane reads and writes the same bytes), read back
+      // in rows and stored; half 1 of C is copied into the other slot once every
+      // wave has read half 0 of D, ahead of half 0's stores.  (The next unit's
+      // first K block copies its stage 1 into the other slot after its barrier,
+      // which every wave reaches only after reading half 1 of D.)
       wait_lgkmcnt0();
       block_barrier();
       if (have_next) {
@@ -336,35 +355,41 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
         wait_vmcnt<0>();
       }
       block_barrier();
-      v2i w0[2][W_NT];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int nt = 0; nt < W_NT; ++nt) w0[i][nt] = pack(0, i, nt, true, other_slot);
+      stage_d(0, true, other_slot);
       wait_lgkmcnt0();
-      block_barrier();
+      block_barrier();   // half 0 of D is staged
+      read_d(other_slot);
+      wait_lgkmcnt0();
+      block_barrier();   // every wave has read it: the slot takes half 1 of C
 #pragma unroll
       for (int j = 0; j < W_CPH; ++j) issue_c(j, 1, done, other_slot);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int nt = 0; nt < W_NT; ++nt)
-          dg_raw_buffer_store_v2i32(w0[i][nt], rsD, d_off(i, nt), d_sofs(i, nt), 0);
-      wait_vmcnt<W_NST / 2>();   // half 1 has landed (only half 0's stores were issued after it)
+      store_d(0);
+      wait_vmcnt<W_CPH>();   // half 1 of C has landed (only half 0's stores were issued after it)
       block_barrier();
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int nt = 0; nt < W_NT; ++nt)
-          dg_raw_buffer_store_v2i32(pack(1, i, nt, true, other_slot), rsD, d_off(2 + i, nt), d_sofs(2 + i, nt),
-                                    0);
+      stage_d(1, true, other_slot);
+      wait_lgkmcnt0();
+      block_barrier();
+      read_d(other_slot);
+      store_d(1);
     } else if (whole) {
-#pragma unroll
-      for (int mt = 0; mt < W_MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < W_NT; ++nt)
-          dg_raw_buffer_store_v2i32(pack(mt >> 1, mt & 1, nt, false, 0u), rsD, d_off(mt, nt), d_sofs(mt, nt),
-                                    0);
+      // D leaves through the last K block's slot (the next unit's stage 0 is in
+      // the other one); the next unit's first K block copies its stage 1 into
+      // this slot after its barrier, which every wave reaches only after
+      // reading half 1 of D
+      wait_lgkmcnt0();
+      block_barrier();
+      stage_d(0, false, last_slot);
+      wait_lgkmcnt0();
+      block_barrier();
+      read_d(last_slot);
+      wait_lgkmcnt0();
+      block_barrier();
+      store_d(0);
+      stage_d(1, false, last_slot);
+      wait_lgkmcnt0();
+      block_barrier();
+      read_d(last_slot);
+      store_d(1);
     } else {
       // fp32 partial tile of this slice: ws[part][BM][BN], row-major (partials
       // past M or N are written too: the reduce reads only valid ones)

@@ -106,11 +106,11 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     // 4-slot 64x128 shape beats the 3-slot ones at M = 64 and 128)
     if (splits > 1 && full == 0) intensity = tc.stages;
     // The 256x256 tile: measured on MI355X against the 256x128 / 128x256 tiles
-    // at equal fill, about 12 % faster per K block on long K loops, but its
-    // fixed costs per tile (pipeline fill, C staging, the stores) weigh twice as
-    // much: relative speed about 1.12 kb / (kb + 2), below 1 up to K = 2048
-    // (0.75 at K = 512, 0.96 at 1536, 1.08 at 7168)
-    else if (id == kWideTileId) intensity = 256.0 * 128.0 / 384.0 * 1.12 * kb / (kb + 2.0);
+    // at equal fill (dense, with C), 10-20 % faster from K = 1024 on (a third
+    // fewer copy bytes per matrix instruction, whole-row D stores), even at
+    // K = 512, where a tile's fixed costs (pipeline fill, C and D through LDS)
+    // weigh most: relative speed about 1.15 kb / (kb + 0.6)
+    else if (id == kWideTileId) intensity = 256.0 * 128.0 / 384.0 * 1.15 * kb / (kb + 0.6);
     double score = util * fill * intensity;
     // wide tiles store longer rows of D (512 bytes): measured 2-7 % faster than
     // the tall tile of the same area up to K = 8192 (the shorter the K loop, the

@@ -181,10 +181,11 @@ def test_planner_is_host_only_and_fills_the_chip():
     assert p["num_tiles"] % 256 == 0 and p["splits"] == 1
 
 
-@pytest.mark.parametrize("m,n,k", [(4096, 7168, 16384), (4096, 2112, 7168), (2304, 3840, 4096)])
+@pytest.mark.parametrize("m,n,k", [(3072, 6144, 16384), (4096, 2112, 7168), (2304, 3840, 4096)])
 def test_planner_splits_only_the_last_partial_round(m, n, k):
     """Long K with a partial last round: the whole rounds run unsplit and only the
-    remainder is split, into slices that together fit in one round."""
+    remainder is split, into slices that together fit in one round (the first
+    shape on the 256 x 256 tile: 288 tiles, 32 of them split)."""
     slots = 256
     p = dgm.dg_query_plan(m, n, k, 1, slots)
     tiles, full, s = p["num_tiles"], p["full_tiles"], p["splits"]

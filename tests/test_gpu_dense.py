@@ -191,22 +191,22 @@ def test_wide_tile_matches_square_tiles_bitwise(dg, monkeypatch):
     check_parity(outs[4], R.fp8_gemm_nt(a, sfa, b, sfb, c), what="256x256 1000x1040x2048")
 
 
-@pytest.mark.parametrize("mi,nki,with_c", [(1, 0, True), (1, 3, True), (1, 4, False), (0, 5, False)])
-def test_wide_tile_full_size_sampled(dg, monkeypatch, mi, nki, with_c):
-    """The 256 x 256 tile, pinned, on dense sweep shapes at full size (every
-    output tile sampled as in the sweep test), with and without C."""
+@pytest.mark.parametrize("M,N,K,with_c", [(4096, 2112, 7168, True), (4096, 7168, 16384, True),
+                                           (4096, 4096, 7168, False), (64, 7168, 2048, False),
+                                           (3072, 6144, 7168, True)])
+def test_wide_tile_full_size_sampled(dg, monkeypatch, M, N, K, with_c):
+    """The 256 x 256 tile, pinned, at full size (every output tile sampled as in
+    the sweep test), with and without C; the last shape's plan splits only its
+    partial last round (32 of 288 tiles, in 8 slices each)."""
     monkeypatch.setenv("DG_FORCE_KERNEL", "4")
-    M = synth.DENSE_M[mi]
-    N, K = synth.DENSE_NK[nki]
     assert dg.dg_query_plan_form(0, M, N, K)["kernel_id"] == 4
-    g = synth.gen_dense(M, N, K, seed=synth.seed_for(1, mi * 6 + nki) + 7, with_c=with_c, backend="torch",
-                        device="cuda")
+    g = synth.gen_dense(M, N, K, seed=M + N + K + 7, with_c=with_c, backend="torch", device="cuda")
     d = sentinel_like((M, N))
     dg.dg_fp8_gemm_nt(g["a"], g["sfa"], g["b"], g["sfb"], g["c"], d)
     torch.cuda.synchronize()
     db = bits(d)
     assert not (db == 0xFFFF).any()
-    rng = np.random.default_rng(100 + mi * 6 + nki)
+    rng = np.random.default_rng(100 + M + N + K)
     rows, cols = stratified_entries(M, N, rng)
     a, sfa, b, sfb = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb"))
     c = None if g["c"] is None else synth.to_numpy(g["c"])
