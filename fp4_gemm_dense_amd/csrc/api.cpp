@@ -92,7 +92,7 @@ static CallPlan plan_call(Fp8GemmParams& p, int mode, int expected_m, int flags,
   // K-grouped: plan for a group's mean K
   const int k_plan = mode == MODE_KGROUP ? std::max(128, p.k / p.num_groups / 128 * 128) : p.k;
   GemmPlan plan = plan_fp8_gemm(p.m, p.n, k_plan, p.num_groups, mode, cus, expected_m, bm_multiple,
-                                mode == MODE_DENSE && flags == 0 && wide_fits(p.m, p.n, p.k));
+                                flags == 0 && wide_fits(p.m, p.n, p.k));
   if (plan.kernel_id < 0) {
     cp.plan = plan;
     return cp;
@@ -102,7 +102,7 @@ static CallPlan plan_call(Fp8GemmParams& p, int mode, int expected_m, int flags,
   if (fk) {
     int id = std::atoi(fk);
     if (id >= 0 && id < num_tile_configs() &&
-        !(id == kWideTileId && (mode != MODE_DENSE || flags != 0 || !wide_fits(p.m, p.n, p.k))) &&
+        !(is_wide_tile(id) && (!wide_serves(id, mode) || flags != 0 || !wide_fits(p.m, p.n, p.k))) &&
         !(mode == MODE_CONTIG && (128 % tile_config(id).block_m) != 0) &&
         !(bm_multiple > 0 && tile_config(id).block_m % bm_multiple != 0))
       plan = plan_with_kernel(p.m, p.n, p.k, p.num_groups, mode, cus, id);

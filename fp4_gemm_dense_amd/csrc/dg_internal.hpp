@@ -81,14 +81,20 @@ struct TileConfig {
 };
 int num_tile_configs();
 TileConfig tile_config(int kernel_id);
-// The 256x256 tile (fp8_gemm_wide.hip): dense NT with fp32 scales only.  Its
-// copies form (row) * K offsets in 32 bits for rows up to 255 past the last.
-constexpr int kWideTileId = 4;
+// The tiles of 65536 outputs (fp8_gemm_wide.hip), NT with fp32 scales only:
+// 256x256 (dense) and 128x512 (dense and contiguous).  Their copies form
+// (row) * K offsets in 32 bits for rows up to a tile past the last.
+constexpr int kTile256x256Id = 4, kTile128x512Id = 5;
+inline bool is_wide_tile(int kernel_id) { return kernel_id == kTile256x256Id || kernel_id == kTile128x512Id; }
 inline bool wide_fits(int m, int n, int k) {
-  return (long long)(m + 256) * k < (1LL << 32) && (long long)(n + 256) * k < (1LL << 32);
+  return (long long)(m + 256) * k < (1LL << 32) && (long long)(n + 512) * k < (1LL << 32);
 }
-TileConfig wide_tile_config();
-hipError_t launch_fp8_gemm_wide(const Fp8GemmParams& p, int grid, hipStream_t stream);
+// the forms (MODE_*) a wide tile serves
+inline bool wide_serves(int kernel_id, int mode) {
+  return mode == MODE_DENSE || (kernel_id == kTile128x512Id && mode == MODE_CONTIG);
+}
+TileConfig wide_tile_config(int kernel_id);
+hipError_t launch_fp8_gemm_wide(const Fp8GemmParams& p, int kernel_id, int mode, int grid, hipStream_t stream);
 
 // Device facts the planner and launchers need (cached per device).
 struct DeviceInfo {
@@ -118,7 +124,7 @@ constexpr int kSkinnyIdBase = 100;
 GemmPlan plan_skinny(int m, int n, int k, int num_cus, bool has_c, int force_id = -1, int force_splits = -1);
 // bm_multiple > 0: only tile shapes whose height is a multiple of it (an A stored
 // [K][M] is staged in 128-row sub-tiles)
-// allow_wide: the 256x256 tile may be chosen (dense NT with fp32 scales)
+// allow_wide: the wide tiles may be chosen (NT with fp32 scales, offsets that fit)
 GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cus, int expected_m,
                        int bm_multiple = 0, bool allow_wide = false);
 GemmPlan plan_with_kernel(int m, int n, int k, int num_groups, int mode, int num_cus, int kernel_id);

@@ -873,9 +873,9 @@ static const TileConfig kTileConfigs[] = {
 #undef X
 };
 
-// ids 0-3: this file's template; id 4 (kWideTileId): the 256x256 kernel of fp8_gemm_wide.hip
-int num_tile_configs() { return (int)(sizeof(kTileConfigs) / sizeof(kTileConfigs[0])) + 1; }
-TileConfig tile_config(int id) { return id == kWideTileId ? wide_tile_config() : kTileConfigs[id]; }
+// ids 0-3: this file's template; ids 4 and 5: the 256x256 and 128x512 tiles of fp8_gemm_wide.hip
+int num_tile_configs() { return (int)(sizeof(kTileConfigs) / sizeof(kTileConfigs[0])) + 2; }
+TileConfig tile_config(int id) { return is_wide_tile(id) ? wide_tile_config(id) : kTileConfigs[id]; }
 
 template <int MODE>
 static hipError_t launch_mode(const Fp8GemmParams& p, int kernel_id, int grid, hipStream_t stream) {
@@ -907,7 +907,7 @@ static hipError_t launch_mode(const Fp8GemmParams& p, int kernel_id, int grid, h
 hipError_t launch_fp8_gemm(const Fp8GemmParams& p, const GemmPlan& plan, int mode, hipStream_t stream) {
   if (plan.num_workgroups <= 0) return hipSuccess;
   const int g = plan.num_workgroups, id = plan.kernel_id;
-  if (id == kWideTileId) return mode == MODE_DENSE ? launch_fp8_gemm_wide(p, g, stream) : hipErrorInvalidValue;
+  if (is_wide_tile(id)) return launch_fp8_gemm_wide(p, id, mode, g, stream);
   switch (mode) {
     case MODE_DENSE: return launch_mode<MODE_DENSE>(p, id, g, stream);
     case MODE_CONTIG: return launch_mode<MODE_CONTIG>(p, id, g, stream);

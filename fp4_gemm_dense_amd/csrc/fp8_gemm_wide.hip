@@ -49,24 +49,47 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-constexpr int W_BM = 256, W_BN = 256, W_MT = 4, W_NT = 8, W_NW = 8;
-constexpr int W_A_BYTES = W_BM * 128, W_B_BYTES = W_BN * 128, W_SA_BYTES = W_BM * 4;
-constexpr int W_STAGE = W_A_BYTES + W_B_BYTES + W_SA_BYTES;
-constexpr int W_LDS = 2 * W_STAGE;
+extern "C" __device__ int dg_raw_buffer_load_i32(v4i rsrc, int voffset, int soffset,
+                                                 int aux) __asm("llvm.amdgcn.raw.buffer.load.i32");
+
+constexpr int W_MT = 4, W_NT = 8, W_NW = 8;   // a wave's 64 x 128 sub-tile: 4 x 8 blocks of 16 x 16
 constexpr int W_LAG = 4;        // matrix instructions between a partial's issue and its promotion
-constexpr int W_RA = 4, W_RB = 4;   // 1-KB copy regions of A and B per wave per stage
-constexpr int W_LPS = W_RA + W_RB + 1;   // copy instructions per wave per stage (+ the row scales)
+constexpr int W_CPH = 8;        // copy (and store) instructions per wave per half tile of C or D
+
+// The two tile shapes of 65536 outputs: 256 x 256 (4 x 2 waves) and 128 x 512
+// (2 x 4 waves).  A stage holds the A and B tiles of one K block (and, for 256
+// rows, the A scales); two stages fill 130 KB or all 160 KB of LDS, so for 128
+// rows the A scales of the next K block are loaded into a register instead (one
+// row per lane) and handed to the lanes that need them by cross-lane reads.
+template <int BM>
+struct WideShape {
+  static constexpr int BN = 65536 / BM;
+  static constexpr int WN = BN / 128, WM = W_NW / WN;       // waves along N and M
+  static constexpr int RA = BM / 64, RB = BN / 64;          // 1-KB copy regions of A, B per wave per stage
+  static constexpr bool SA_LDS = BM == 256;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, SA_BYTES = SA_LDS ? BM * 4 : 0;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LPS = RA + RB + 1;                   // memory instructions per wave per stage
+  static constexpr int ROWB = BN * 2;                       // bytes of a staged C / D row
+  static constexpr int RPC = 1024 / ROWB;                   // staged rows per copy instruction
+  static_assert(LDS <= 160 * 1024 && LPS <= W_MT * W_NT, "tile shape");
+};
 }  // namespace
 
+// MODE: MODE_DENSE (C optional) or, for 128 rows, MODE_CONTIG (groups of rows
+// padded to 128, each with its own B; no C).
+template <int BM, int MODE>
 __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) {
+  using S = WideShape<BM>;
+  constexpr int BN = S::BN, WN = S::WN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   typedef const __attribute__((address_space(4))) float cfloat;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wave_m = wave >> 1, wave_n = wave & 1;
-  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int wave_m = wave / WN, wave_n = wave % WN;
   const int M = p.m, N = p.n, K = p.k;
   const int KB = K >> 7;
 
@@ -77,11 +100,12 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
   if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
   // Work units: [0, full_tiles) whole tiles; then unit full_tiles + u is K slice
-  // u % splits of tile full_tiles + u / splits.
+  // u % splits of tile full_tiles + u / splits.  Contiguous form: a tile whose
+  // first row is padding (group index out of range) is skipped.
   struct Unit {
-    int m0, n0, kb0, nkb, part;
+    int m0, n0, kb0, nkb, part, g;
   };
-  auto decode = [&](int t, Unit& w) {
+  auto decode = [&](int t, Unit& w) -> bool {
     w.kb0 = 0;
     w.nkb = KB;
     w.part = -1;
@@ -94,80 +118,104 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     }
     int tm, tn;
     raster_tile(t, p.tiles_m, p.tiles_n, p.group_m, &tm, &tn);
-    w.m0 = tm * W_BM;
-    w.n0 = tn * W_BN;
+    w.m0 = tm * BM;
+    w.n0 = tn * BN;
+    w.g = 0;
+    if constexpr (MODE == MODE_CONTIG) {
+      w.g = p.m_indices[w.m0];
+      if (w.g < 0 || w.g >= p.num_groups) return false;
+    }
+    return true;
+  };
+  // the first unit at or after t with work
+  auto next_unit = [&](int& t, Unit& w) -> bool {
+    for (; t < p.total_tiles; t += G)
+      if (decode(t, w)) return true;
+    return false;
   };
 
   const v4i rsA = make_buffer_rsrc(p.a, (uint32_t)M * (uint32_t)K);
-  const v4i rsB = make_buffer_rsrc(p.b, (uint32_t)N * (uint32_t)K);
   const v4i rsSA = make_buffer_rsrc(p.sfa, (uint32_t)KB * (uint32_t)M * 4u);
   cfloat* const SBc = (cfloat*)(uintptr_t)p.sfb;
+  const int NB = (N + 127) >> 7;   // 128-column blocks of B scales per group
 
   // Per-lane copy offsets of the unit whose stages are being copied.  Region j of
-  // a wave covers tile rows 8 (4 wave + j) .. + 7; lane l fills 16 bytes of row
-  // 8 (4 wave + j) + l / 8 at position l % 8, which holds chunk (l % 8) ^ swz(row).
-  // swz depends on the row modulo 16 only, so regions j and j + 2 (16 rows
-  // apart) share a lane's chunk and two offsets per operand serve the four
-  // regions.  A row past M (N) lies past the end of A (B): the buffer's range
-  // check makes it read zeros (its results are never stored).  Row scales:
-  // position q = g * 64 + r * 4 + mt of the slot's scale area holds row
-  // g * 64 + mt * 16 + r, so a lane's four scales are adjacent; waves w and w + 4
-  // copy the same 64 positions (identical bytes), so that every lane of every
-  // wave issues the same instructions.
+  // a wave's A (B) copies covers tile rows 8 (RA wave + j) .. + 7 (RB for B);
+  // lane l fills 16 bytes of row 8 (..) + l / 8 at position l % 8, which holds
+  // chunk (l % 8) ^ swz(row).  swz depends on the row modulo 16 only, so regions
+  // j and j + 2 (16 rows apart) share a lane's chunk and two offsets per operand
+  // serve all regions.  A row past M (N) lies past the end of A (B): the
+  // buffer's range check makes it read zeros (its results are never stored).
+  // Row scales, 256 rows: position q = g * 64 + r * 4 + mt of the slot's scale
+  // area holds row g * 64 + mt * 16 + r, so a lane's four scales are adjacent;
+  // waves w and w + 4 copy the same 64 positions (identical bytes), so that every
+  // lane of every wave issues the same instructions.  128 rows: lane l loads the
+  // scale of the wave's row l into a register (one coalesced load of 256 bytes);
+  // a row past M reads another K block's scale or zero, harmlessly.
   uint32_t a_off[2], b_off[2], sa_off = 0;
+  v4i rsB = make_buffer_rsrc(p.b, (uint32_t)N * (uint32_t)K);
+  float sa_nx = 0.f;   // 128 rows: the scale of the lane's row in the next K block
   int cp_kb0 = 0;   // first K block of that unit
   auto setup_copies = [&](const Unit& w) {
     cp_kb0 = w.kb0;
+    if constexpr (MODE == MODE_CONTIG)
+      rsB = make_buffer_rsrc(p.b + (size_t)w.g * (size_t)N * (size_t)K, (uint32_t)N * (uint32_t)K);
     const int ln = opaque(lane);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int row = (wave * W_RA + e) * 8 + (ln >> 3);
-      const uint32_t chunk = (uint32_t)(((ln & 7) ^ swz(row)) << 4);
-      a_off[e] = (uint32_t)(w.m0 + row) * (uint32_t)K + chunk;
-      b_off[e] = (uint32_t)(w.n0 + row) * (uint32_t)K + chunk;
+      const int ra = (wave * S::RA + e) * 8 + (ln >> 3), rb = (wave * S::RB + e) * 8 + (ln >> 3);
+      a_off[e] = (uint32_t)(w.m0 + ra) * (uint32_t)K + (uint32_t)(((ln & 7) ^ swz(ra)) << 4);
+      b_off[e] = (uint32_t)(w.n0 + rb) * (uint32_t)K + (uint32_t)(((ln & 7) ^ swz(rb)) << 4);
     }
-    const int row = (wave & 3) * 64 + (ln & 3) * 16 + (ln >> 2);
-    sa_off = w.m0 + row < M ? (uint32_t)(w.m0 + row) * 4u : kBufferOutOfRange;
+    if constexpr (S::SA_LDS) {
+      const int row = (wave & 3) * 64 + (ln & 3) * 16 + (ln >> 2);
+      sa_off = w.m0 + row < M ? (uint32_t)(w.m0 + row) * 4u : kBufferOutOfRange;
+    } else {
+      sa_off = (uint32_t)(w.m0 + wave_m * 64 + ln) * 4u;
+    }
   };
-  // Copy instruction idx (0-3 A regions, 4-7 B regions, 8 the row scales) of
-  // stage s (within the unit's K range) of the unit set up last, into the slot
-  // at byte offset slot.
+  // Memory instruction idx of stage s (within the unit's K range) of the unit
+  // set up last, into the slot at byte offset slot: A regions, then B regions,
+  // then the A scales (a copy into LDS, or a load into a register).
   auto issue = [&](int idx, int s, uint32_t slot) {
     const uint32_t kofs = (uint32_t)(cp_kb0 + s) * 128u;
-    if (idx < W_RA) {
+    if (idx < S::RA) {
       const uint32_t off = a_off[idx & 1] + (uint32_t)(idx >> 1) * 16u * (uint32_t)K;
-      buf16_to_lds(rsA, off, kofs, smem + slot + (wave * W_RA + idx) * 1024);
-    } else if (idx < W_RA + W_RB) {
-      const int j = idx - W_RA;
+      buf16_to_lds(rsA, off, kofs, smem + slot + (wave * S::RA + idx) * 1024);
+    } else if (idx < S::RA + S::RB) {
+      const int j = idx - S::RA;
       const uint32_t off = b_off[j & 1] + (uint32_t)(j >> 1) * 16u * (uint32_t)K;
-      buf16_to_lds(rsB, off, kofs, smem + slot + W_A_BYTES + (wave * W_RB + j) * 1024);
-    } else {
+      buf16_to_lds(rsB, off, kofs, smem + slot + S::A_BYTES + (wave * S::RB + j) * 1024);
+    } else if constexpr (S::SA_LDS) {
       buf4_to_lds(rsSA, sa_off, (uint32_t)(cp_kb0 + s) * (uint32_t)M * 4u,
-                  smem + slot + W_A_BYTES + W_B_BYTES + (wave & 3) * 256);
+                  smem + slot + S::A_BYTES + S::B_BYTES + (wave & 3) * 256);
+    } else {
+      sa_nx = __int_as_float(dg_raw_buffer_load_i32(rsSA, (int)sa_off, (int)((uint32_t)(cp_kb0 + s) * (uint32_t)M * 4u), 0));
     }
   };
-  // C of a whole tile is staged through a free LDS slot, half a tile at a time:
-  // half h holds row blocks 2h and 2h + 1 of every wave row, 128 rows of 512
-  // bytes; half row q is tile row (q / 32) * 64 + (2h + (q / 16) % 2) * 16 + q % 16
-  // and keeps its 16-byte chunk c at position c ^ (q % 16), so that the 16 rows a
-  // wave reads at once fall on distinct banks.  Copy j (0-7) of wave w fills half
-  // rows 16 w + 2 j and + 1 (lanes 0-31 and 32-63).  Elements past M or N read
-  // zeros (they are never stored).
+  // C of a whole tile (dense form) is staged through a free LDS slot, half a
+  // tile at a time: half h holds row blocks 2h and 2h + 1 of every wave row,
+  // WM * 32 rows of BN * 2 bytes; half row q = 32 wm + 16 i + r is tile row
+  // 64 wm + 16 (2h + i) + r and keeps its 16-byte chunk c at position c ^ r, so
+  // that the 16 rows a wave reads at once fall on distinct banks.  Copy j (0-7)
+  // of wave w fills the 1024 bytes at (8 w + j) KB: one row, or two (lanes 0-31
+  // and 32-63).  Elements past M or N read zeros (they are never stored).
   const v4i rsC = make_buffer_rsrc(p.c, (uint32_t)M * (uint32_t)N * 2u);
+  // (half row, position) of copy j's lane ln
+  auto staged_q = [&](int j, int ln) -> int { return S::RPC == 1 ? wave * 8 + j : (wave * 8 + j) * 2 + (ln >> 5); };
+  auto staged_row = [&](int q, int h) -> int { return (q >> 5) * 64 + (2 * h + ((q >> 4) & 1)) * 16 + (q & 15); };
+  auto staged_col = [&](int q, int ln) -> int { return (((S::RPC == 1 ? ln : ln & 31) ^ (q & 15)) << 3); };
   auto issue_c = [&](int j, int h, const Unit& w, uint32_t slot) {
     const int ln = opaque(lane);
-    const int r16 = 2 * j + (ln >> 5);
-    const int row = w.m0 + (wave >> 1) * 64 + (2 * h + (wave & 1)) * 16 + r16;
-    const int col = w.n0 + (((ln & 31) ^ r16) << 3);
+    const int q = staged_q(j, ln);
+    const int row = w.m0 + staged_row(q, h), col = w.n0 + staged_col(q, ln);
     const uint32_t off = row < M && col < N ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : kBufferOutOfRange;
     buf16_to_lds(rsC, off, 0u, smem + slot + (wave * 8 + j) * 1024);
   };
-  constexpr int W_CPH = 8;   // C copy instructions per wave per half tile
 
   int t = vb;
-  if (t >= p.total_tiles) return;
   Unit cur;
-  decode(t, cur);
+  if (!next_unit(t, cur)) return;
   setup_copies(cur);
   // The ring: stage s of a unit sits in slot s0 ^ (s & 1); K block kb copies
   // stage kb + 1 into the other slot right after its barrier (every wave is then
@@ -175,19 +223,18 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
   // the next unit's stage 0, or the first half of C, which then goes first.
   uint32_t s0 = 0;
 #pragma unroll
-  for (int idx = 0; idx < W_LPS; ++idx) issue(idx, 0, 0u);
+  for (int idx = 0; idx < S::LPS; ++idx) issue(idx, 0, 0u);
   bool stores_pending = false;   // the previous unit's stores were issued after this unit's stage 0
 
   while (true) {
     const int KT = cur.nkb;
     const int kb0 = cur.kb0;
     const int tn_col0 = min(cur.n0 + wave_n * 128, N - 1);
-    const int sb_idx = __builtin_amdgcn_readfirstlane((tn_col0 >> 7) * KB + kb0);
-    const int t_next = t + G;
-    const bool have_next = t_next < p.total_tiles;
+    const int sb_idx = __builtin_amdgcn_readfirstlane((cur.g * NB + (tn_col0 >> 7)) * KB + kb0);
+    int t_next = t + G;
     Unit nxt{};
-    if (have_next) decode(t_next, nxt);
-    const bool c_lds = cur.part < 0 && p.c != nullptr;   // C is added (staged through LDS)
+    const bool have_next = next_unit(t_next, nxt);
+    const bool c_lds = MODE == MODE_DENSE && cur.part < 0 && p.c != nullptr;   // C is added (through LDS)
 
     // LDS fragment read offsets (slot 0; block mt / nt adds mt * 2048 / nt *
     // 2048), derived anew for every unit so that they need no register through
@@ -196,9 +243,9 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     const int fr = lf & 15, fg = lf >> 4, sw = swz(fr);
     const uint32_t a_lo = (wave_m * 64 + fr) * 128 + (((2 * fg) ^ sw) << 4);
     const uint32_t a_hi = (wave_m * 64 + fr) * 128 + (((2 * fg + 1) ^ sw) << 4);
-    const uint32_t b_lo = W_A_BYTES + (wave_n * 128 + fr) * 128 + (((2 * fg) ^ sw) << 4);
-    const uint32_t b_hi = W_A_BYTES + (wave_n * 128 + fr) * 128 + (((2 * fg + 1) ^ sw) << 4);
-    const uint32_t sa_rd = W_A_BYTES + W_B_BYTES + (wave_m * 64 + fr * 4) * 4;
+    const uint32_t b_lo = S::A_BYTES + (wave_n * 128 + fr) * 128 + (((2 * fg) ^ sw) << 4);
+    const uint32_t b_hi = S::A_BYTES + (wave_n * 128 + fr) * 128 + (((2 * fg + 1) ^ sw) << 4);
+    const uint32_t sa_rd = S::A_BYTES + S::B_BYTES + (wave_m * 64 + fr * 4) * 4;
 
     v4f acc[W_MT][W_NT];
 #pragma unroll
@@ -211,8 +258,8 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     float sprev[W_MT] = {0.f, 0.f, 0.f, 0.f};
 
     // One K block from the slot at byte offset rd; copy(j) issues what goes
-    // after matrix instruction j (one copy instruction after each of the first
-    // nine).  Block j = nt * MT + mt goes into partial register j % LAG (= mt);
+    // after matrix instruction j (one memory instruction after each of the first
+    // LPS).  Block j = nt * MT + mt goes into partial register j % LAG (= mt);
     // the register's previous partial, of block (nt - 1, mt) -- for nt = 0 block
     // (NT - 1, mt) of the previous K block, scale sprev -- is promoted first.
     auto kblock = [&](int kb, uint32_t rd, auto&& copy) {
@@ -225,10 +272,16 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
       else wait_vmcnt<0>();
       block_barrier();
       const float sbv = SBc[sb_idx + kb];
-      const v4f sav = *reinterpret_cast<const v4f*>(smem + rd + sa_rd);
       float scur[W_MT];
+      if constexpr (S::SA_LDS) {
+        const v4f sav = *reinterpret_cast<const v4f*>(smem + rd + sa_rd);
 #pragma unroll
-      for (int i = 0; i < W_MT; ++i) scur[i] = sav[i] * sbv;
+        for (int i = 0; i < W_MT; ++i) scur[i] = sav[i] * sbv;
+      } else {
+        // row block i of the lane's rows: the wave's row 16 i + (lane % 16)
+#pragma unroll
+        for (int i = 0; i < W_MT; ++i) scur[i] = __shfl(sa_nx, 16 * i + (lane & 15), 64) * sbv;
+      }
       v8i af[W_MT];
 #pragma unroll
       for (int mt = 0; mt < W_MT; ++mt) {
@@ -252,10 +305,10 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
             for (int i = 0; i < 4; ++i) acc[mt][nt - 1][i] = fmaf(part[mt][i], scur[mt], acc[mt][nt - 1][i]);
           }
           part[mt] = mfma_e4m3_16x16x128(bf, af[mt], v4f{0.f, 0.f, 0.f, 0.f});
-          if (j < W_LPS) copy(j);
+          if (j < S::LPS) copy(j);
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU (promotion)
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-          if (j < W_LPS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM (copy)
+          if (j < S::LPS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM (copy)
         }
       }
 #pragma unroll
@@ -264,13 +317,13 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
 
 #pragma clang loop unroll(disable)
     for (int kb = 0; kb < KT - 1; ++kb) {
-      const uint32_t wr = (s0 ^ (uint32_t)((kb + 1) & 1)) * (uint32_t)W_STAGE;
-      kblock(kb, (s0 ^ (uint32_t)(kb & 1)) * (uint32_t)W_STAGE, [&](int j) { issue(j, kb + 1, wr); });
+      const uint32_t wr = (s0 ^ (uint32_t)((kb + 1) & 1)) * (uint32_t)S::STAGE;
+      kblock(kb, (s0 ^ (uint32_t)(kb & 1)) * (uint32_t)S::STAGE, [&](int j) { issue(j, kb + 1, wr); });
     }
     // the last K block: into the other slot goes half 0 of C, else the next
     // unit's stage 0
-    const uint32_t last_slot = (s0 ^ (uint32_t)((KT - 1) & 1)) * (uint32_t)W_STAGE;
-    const uint32_t other_slot = last_slot ^ (uint32_t)W_STAGE;
+    const uint32_t last_slot = (s0 ^ (uint32_t)((KT - 1) & 1)) * (uint32_t)S::STAGE;
+    const uint32_t other_slot = last_slot ^ (uint32_t)S::STAGE;
     const bool copy_next = have_next && !c_lds;
     if (copy_next) setup_copies(nxt);
     kblock(KT - 1, last_slot, [&](int j) {
@@ -295,7 +348,7 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     // in a staged half tile (C's layout)
     auto cd_addr = [&](int i, int nt, uint32_t slot) -> uint32_t {
       const int q = wave_m * 32 + i * 16 + (ln & 15);
-      return slot + q * 512 + wave_n * 256 + (((2 * nt + (ln >> 5)) ^ (ln & 15)) << 4) + ((ln >> 4) & 1) * 8;
+      return slot + q * S::ROWB + wave_n * 256 + (((2 * nt + (ln >> 5)) ^ (ln & 15)) << 4) + ((ln >> 4) & 1) * 8;
     };
     // half h of D as bf16 into the half tile staged at slot (over C, plus C)
     auto stage_d = [&](int h, bool add_c, uint32_t slot) {
@@ -317,10 +370,11 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
         }
     };
     // a staged half tile's rows into registers (copy j's place of issue_c), then
-    // to D: every store instruction writes two whole 512-byte rows, so the lines
+    // to D: every store instruction writes whole rows (1024 bytes), so the lines
     // are whole and the non-temporal hint lets them leave L2 first (stores of
     // 32 bytes in each of 16 rows, straight from the accumulators, measured 5-25 %
-    // slower: partial lines, and a wave's stores stall its next tile's K loop)
+    // slower: partial lines, and a wave's stores stall its next tile's K loop).
+    // Contiguous form: a row outside the tile's group (padding) is not written.
     v4i drow[W_CPH];
     auto read_d = [&](uint32_t slot) {
 #pragma unroll
@@ -329,10 +383,11 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     auto store_d = [&](int h) {
 #pragma unroll
       for (int j = 0; j < W_CPH; ++j) {
-        const int r16 = 2 * j + (ln >> 5);
-        const int row = done.m0 + (wave >> 1) * 64 + (2 * h + (wave & 1)) * 16 + r16;
-        const int col = done.n0 + (((ln & 31) ^ r16) << 3);
-        const uint32_t off = row < M && col < N ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : kBufferOutOfRange;
+        const int q = staged_q(j, ln);
+        const int row = done.m0 + staged_row(q, h), col = done.n0 + staged_col(q, ln);
+        bool ok = row < M && col < N;
+        if constexpr (MODE == MODE_CONTIG) ok = ok && p.m_indices[row] == done.g;   // (row is uniform: RPC = 1)
+        const uint32_t off = ok ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : kBufferOutOfRange;
         dg_raw_buffer_store_v4i32(drow[j], rsD, (int)off, 0, kStoreNonTemporal);
       }
     };
@@ -349,8 +404,8 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
       if (have_next) {
         setup_copies(nxt);
 #pragma unroll
-        for (int idx = 0; idx < W_LPS; ++idx) issue(idx, 0, last_slot);
-        wait_vmcnt<W_LPS>();   // half 0 has landed (only the next stage 0 was issued after it)
+        for (int idx = 0; idx < S::LPS; ++idx) issue(idx, 0, last_slot);
+        wait_vmcnt<S::LPS>();   // half 0 has landed (only the next stage 0 was issued after it)
       } else {
         wait_vmcnt<0>();
       }
@@ -392,16 +447,17 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
       store_d(1);
     } else {
       // fp32 partial tile of this slice: ws[part][BM][BN], row-major (partials
-      // past M or N are written too: the reduce reads only valid ones)
-      const v4i rsW = make_buffer_rsrc(p.ws + (size_t)done.part * (W_BM * W_BN), (uint32_t)(W_BM * W_BN * 4));
-      const int w_lane = ((wave_m * 64 + (ln & 15)) * W_BN + wave_n * 128 + 4 * (ln >> 4)) * 4;
+      // past M or N, or of padding rows, are written too: the reduce reads only
+      // valid ones)
+      const v4i rsW = make_buffer_rsrc(p.ws + (size_t)done.part * (BM * BN), (uint32_t)(BM * BN * 4));
+      const int w_lane = ((wave_m * 64 + (ln & 15)) * BN + wave_n * 128 + 4 * (ln >> 4)) * 4;
 #pragma unroll
       for (int mt = 0; mt < W_MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < W_NT; ++nt) {
           const v4i w = {__float_as_int(acc[mt][nt][0]), __float_as_int(acc[mt][nt][1]),
                          __float_as_int(acc[mt][nt][2]), __float_as_int(acc[mt][nt][3])};
-          dg_raw_buffer_store_v4i32(w, rsW, w_lane, (mt * 16 * W_BN + nt * 16) * 4, 0);
+          dg_raw_buffer_store_v4i32(w, rsW, w_lane, (mt * 16 * BN + nt * 16) * 4, 0);
         }
     }
     if (!have_next) break;
@@ -409,21 +465,33 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     cur = nxt;
     // the next unit's stage 0 sits in the last block's slot when C was staged,
     // else in the other one
-    s0 = (c_lds ? last_slot : other_slot) / (uint32_t)W_STAGE;
+    s0 = (c_lds ? last_slot : other_slot) / (uint32_t)S::STAGE;
     stores_pending = true;
   }
   wait_vmcnt<0>();
 }
 
-TileConfig wide_tile_config() { return TileConfig{W_BM, W_BN, 1, W_NW * 64, W_LDS, 2}; }
+TileConfig wide_tile_config(int kernel_id) {
+  if (kernel_id == kTile256x256Id) return TileConfig{256, 256, 1, W_NW * 64, WideShape<256>::LDS, 2};
+  return TileConfig{128, 512, 1, W_NW * 64, WideShape<128>::LDS, 2};
+}
 
-hipError_t launch_fp8_gemm_wide(const Fp8GemmParams& p, int grid, hipStream_t stream) {
-  if (!wide_fits(p.m, p.n, p.k)) return hipErrorInvalidValue;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fp8_gemm_wide_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, W_LDS);
+template <int BM, int MODE>
+static hipError_t launch_wide(const Fp8GemmParams& p, int grid, hipStream_t stream) {
+  constexpr int lds = WideShape<BM>::LDS;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fp8_gemm_wide_kernel<BM, MODE>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(fp8_gemm_wide_kernel, dim3(grid), dim3(W_NW * 64), W_LDS, stream, p);
+  hipLaunchKernelGGL((fp8_gemm_wide_kernel<BM, MODE>), dim3(grid), dim3(W_NW * 64), lds, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm_wide(const Fp8GemmParams& p, int kernel_id, int mode, int grid, hipStream_t stream) {
+  if (!wide_fits(p.m, p.n, p.k)) return hipErrorInvalidValue;
+  if (kernel_id == kTile256x256Id && mode == MODE_DENSE) return launch_wide<256, MODE_DENSE>(p, grid, stream);
+  if (kernel_id == kTile128x512Id && mode == MODE_DENSE) return launch_wide<128, MODE_DENSE>(p, grid, stream);
+  if (kernel_id == kTile128x512Id && mode == MODE_CONTIG) return launch_wide<128, MODE_CONTIG>(p, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dg

@@ -46,13 +46,16 @@ def _check_contig(d, ref, written, what):
     check_parity(d[written], ref[written], what=what)
 
 
+@pytest.mark.parametrize("kernel_id", [None, 5], ids=["planned", "128x512"])
 @pytest.mark.parametrize("G,total,N,K,counts", [
     (4, 500, 160, 256, None),
     (3, 300, 272, 384, [0, 300, 0]),          # empty groups around a full one
     (5, 700, 2112, 256, [1, 127, 128, 129, 315]),
     (1, 130, 144, 128, None),
 ])
-def test_contiguous_parity_and_padding(dg, G, total, N, K, counts):
+def test_contiguous_parity_and_padding(dg, monkeypatch, G, total, N, K, counts, kernel_id):
+    if kernel_id is not None:
+        monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
     g = synth.gen_contiguous(G, total, N, K, seed=G * 31 + N, counts=counts)
     a, sfa, b, sfb, mi = _np(g, "a", "sfa", "b", "sfb", "m_indices")
     d = _run_contig(dg, a, sfa, b, sfb, mi)
@@ -60,7 +63,10 @@ def test_contiguous_parity_and_padding(dg, G, total, N, K, counts):
     _check_contig(d, ref, written, f"contig G{G} N{N} K{K}")
 
 
-def test_contiguous_exact_integer_groups_bit_exact(dg):
+@pytest.mark.parametrize("kernel_id", [None, 5], ids=["planned", "128x512"])
+def test_contiguous_exact_integer_groups_bit_exact(dg, monkeypatch, kernel_id):
+    if kernel_id is not None:
+        monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
     rng = np.random.default_rng(5)
     N, K = 160, 384
     counts = [100, 0, 200]
@@ -81,11 +87,12 @@ def test_contiguous_exact_integer_groups_bit_exact(dg):
     check_bit_exact(d[written], ref[written], "contig exact")
 
 
-@pytest.mark.parametrize("kernel_id", [1, 2, 3])
+@pytest.mark.parametrize("kernel_id", [1, 2, 3, 5])
 def test_contiguous_many_tiles_per_workgroup(dg, monkeypatch, kernel_id):
     """Two workgroups walk every tile in turn (short K, so many tiles each): the
     rows' group indices are loaded when a tile is set up and tested after its K
-    loop, while the next tile's copies are already in flight."""
+    loop, while the next tile's copies are already in flight (kernel 5, the
+    128 x 512 tile, skips padding tiles while looking for its next unit)."""
     import fp4_gemm_dense_amd as dgm
     counts = [100, 0, 200, 7, 129]
     g = synth.gen_contiguous(len(counts), sum(counts), 400, 256, seed=77 + kernel_id, counts=counts)
@@ -100,7 +107,10 @@ def test_contiguous_many_tiles_per_workgroup(dg, monkeypatch, kernel_id):
     _check_contig(d, ref, written, f"contig many tiles per workgroup, kernel {kernel_id}")
 
 
-def test_contiguous_malformed_indices_are_skipped(dg):
+@pytest.mark.parametrize("kernel_id", [None, 5], ids=["planned", "128x512"])
+def test_contiguous_malformed_indices_are_skipped(dg, monkeypatch, kernel_id):
+    if kernel_id is not None:
+        monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
     g = synth.gen_contiguous(3, 256, 144, 256, seed=9, counts=[128, 64, 64])
     a, sfa, b, sfb, mi = _np(g, "a", "sfa", "b", "sfb", "m_indices")
     bad = mi.copy()
@@ -116,9 +126,13 @@ def test_contiguous_malformed_indices_are_skipped(dg):
     _check_contig(d, ref, written, "contig malformed")
 
 
+@pytest.mark.parametrize("kernel_id", [None, 1], ids=["planned", "128x256"])
 @pytest.mark.parametrize("nki", [0, 1])
-def test_contiguous_full_size_sampled(dg, nki):
-    """8 experts, 32768 routed rows (multinomial), padded to 128; full size on the device."""
+def test_contiguous_full_size_sampled(dg, monkeypatch, nki, kernel_id):
+    """8 experts, 32768 routed rows (multinomial), padded to 128; full size on the
+    device, with the planned tile and with the 128 x 256 tile pinned."""
+    if kernel_id is not None:
+        monkeypatch.setenv("DG_FORCE_KERNEL", str(kernel_id))
     N, K = synth.GROUPED_NK[nki]
     g = synth.gen_contiguous(8, 32768, N, K, seed=synth.seed_for(2, nki), backend="torch", device="cuda")
     M = g["M"]
