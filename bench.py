@@ -565,13 +565,13 @@ def summarize_counters(fetch_dir, write_dir, calib_fetch_dir, calib_write_dir, k
     write_scale = n / copy_bytes(per_kernel(calib_write_dir, "WRITE_SIZE"))
     kind = key.split(" ")[0]
     # one dispatch per call names the call: the FFN's routing kernel, else the GEMM
-    # kernel (square, skinny or FP8xFP4); split-K reduces and the K-grouped zeroing
-    # kernel ride along
-    primary = "route" if kind == "ffn" else "gemm_kernel"
+    # kernel (square, wide, skinny or FP8xFP4); split-K reduces and the K-grouped
+    # zeroing kernel ride along
+    primary = ("route",) if kind == "ffn" else ("gemm_kernel", "gemm_wide_kernel")
 
     def per_call(acc):
         lib = {k: v for k, v in acc.items() if "dg::" in k and "transpose" not in k}   # (weight set-up excluded)
-        calls = sum(len(v) for k, v in lib.items() if primary in k and "reduce" not in k)
+        calls = sum(len(v) for k, v in lib.items() if any(s in k for s in primary) and "reduce" not in k)
         return sum(sum(v) for v in lib.values()) / max(calls, 1), sorted(lib)
     fb, kernels = per_call(per_kernel(fetch_dir, "FETCH_SIZE"))
     wb, _ = per_call(per_kernel(write_dir, "WRITE_SIZE"))
