@@ -81,11 +81,11 @@ struct TileConfig {
 };
 int num_tile_configs();
 TileConfig tile_config(int kernel_id);
-// The tiles of 65536 outputs (fp8_gemm_wide.hip), NT with fp32 scales only:
-// 256x256 (dense) and 128x512 (dense and contiguous).  Their copies form
-// (row) * K offsets in 32 bits for rows up to a tile past the last.
-constexpr int kTile256x256Id = 4, kTile128x512Id = 5;
-inline bool is_wide_tile(int kernel_id) { return kernel_id == kTile256x256Id || kernel_id == kTile128x512Id; }
+// The wide tiles (fp8_gemm_wide.hip), NT with fp32 scales only: 256x256 and
+// 256x224 (dense), 128x512 (dense and contiguous).  Their copies form (row) * K
+// offsets in 32 bits for rows up to a tile past the last.
+constexpr int kTile256x256Id = 4, kTile128x512Id = 5, kTile256x224Id = 6;
+inline bool is_wide_tile(int kernel_id) { return kernel_id >= kTile256x256Id && kernel_id <= kTile256x224Id; }
 inline bool wide_fits(int m, int n, int k) {
   return (long long)(m + 256) * k < (1LL << 32) && (long long)(n + 512) * k < (1LL << 32);
 }

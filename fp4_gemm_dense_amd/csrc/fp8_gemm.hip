@@ -873,8 +873,8 @@ static const TileConfig kTileConfigs[] = {
 #undef X
 };
 
-// ids 0-3: this file's template; ids 4 and 5: the 256x256 and 128x512 tiles of fp8_gemm_wide.hip
-int num_tile_configs() { return (int)(sizeof(kTileConfigs) / sizeof(kTileConfigs[0])) + 2; }
+// ids 0-3: this file's template; ids 4-6: the 256x256, 128x512 and 256x224 tiles of fp8_gemm_wide.hip
+int num_tile_configs() { return (int)(sizeof(kTileConfigs) / sizeof(kTileConfigs[0])) + 3; }
 TileConfig tile_config(int id) { return is_wide_tile(id) ? wide_tile_config(id) : kTileConfigs[id]; }
 
 template <int MODE>

@@ -52,37 +52,43 @@ __device__ __forceinline__ int opaque(int x) {
 extern "C" __device__ int dg_raw_buffer_load_i32(v4i rsrc, int voffset, int soffset,
                                                  int aux) __asm("llvm.amdgcn.raw.buffer.load.i32");
 
-constexpr int W_MT = 4, W_NT = 8, W_NW = 8;   // a wave's 64 x 128 sub-tile: 4 x 8 blocks of 16 x 16
+constexpr int W_MT = 4, W_NW = 8;   // a wave: 64 rows (4 blocks of 16) of the tile; eight waves
 constexpr int W_LAG = 4;        // matrix instructions between a partial's issue and its promotion
 constexpr int W_CPH = 8;        // copy (and store) instructions per wave per half tile of C or D
 
-// The two tile shapes of 65536 outputs: 256 x 256 (4 x 2 waves) and 128 x 512
-// (2 x 4 waves).  A stage holds the A and B tiles of one K block (and, for 256
-// rows, the A scales); two stages fill 130 KB or all 160 KB of LDS, so for 128
-// rows the A scales of the next K block are loaded into a register instead (one
-// row per lane) and handed to the lanes that need them by cross-lane reads.
-template <int BM>
+// The tile shapes: 256 x 256 (4 x 2 waves of 64 x 128), 128 x 512 (2 x 4 waves
+// of 64 x 128) and 256 x 224 (4 x 2 waves of 64 x 112).  A stage holds the A and
+// B tiles of one K block (and, for 256 rows, the A scales); two stages fill 130
+// KB or all 160 KB of LDS, so for 128 rows the A scales of the next K block are
+// loaded into a register instead (one row per lane) and handed to the lanes that
+// need them by cross-lane reads.  The 224-wide tile copies and stages B and D as
+// if 256 wide (rows and columns past 224 read and write nothing); a wave's 112
+// columns may span two 128-column blocks of B scales.
+template <int BM, int BN_>
 struct WideShape {
-  static constexpr int BN = 65536 / BM;
-  static constexpr int WN = BN / 128, WM = W_NW / WN;       // waves along N and M
-  static constexpr int RA = BM / 64, RB = BN / 64;          // 1-KB copy regions of A, B per wave per stage
+  static constexpr int BN = BN_;
+  static constexpr int WN = BN == 512 ? 4 : 2, WM = W_NW / WN;   // waves along N and M
+  static constexpr int WC = BN / WN, NT = WC / 16;               // a wave's columns and 16-column blocks
+  static constexpr int BNP = BN == 224 ? 256 : BN;               // B rows copied, D columns staged
+  static constexpr int RA = BM / 64, RB = BNP / 64;              // 1-KB copy regions of A, B per wave per stage
   static constexpr bool SA_LDS = BM == 256;
-  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, SA_BYTES = SA_LDS ? BM * 4 : 0;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BNP * 128, SA_BYTES = SA_LDS ? BM * 4 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
   static constexpr int LDS = 2 * STAGE;
-  static constexpr int LPS = RA + RB + 1;                   // memory instructions per wave per stage
-  static constexpr int ROWB = BN * 2;                       // bytes of a staged C / D row
-  static constexpr int RPC = 1024 / ROWB;                   // staged rows per copy instruction
-  static_assert(LDS <= 160 * 1024 && LPS <= W_MT * W_NT, "tile shape");
+  static constexpr int LPS = RA + RB + 1;                        // memory instructions per wave per stage
+  static constexpr int ROWB = BNP * 2;                           // bytes of a staged C / D row
+  static constexpr int RPC = 1024 / ROWB;                        // staged rows per copy instruction
+  static constexpr bool SPLIT_SB = WC % 128 != 0;                // a wave's columns may span two scale blocks
+  static_assert(LDS <= 160 * 1024 && LPS <= W_MT * NT && WC % 16 == 0, "tile shape");
 };
 }  // namespace
 
 // MODE: MODE_DENSE (C optional) or, for 128 rows, MODE_CONTIG (groups of rows
 // padded to 128, each with its own B; no C).
-template <int BM, int MODE>
+template <int BM, int BN, int MODE>
 __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) {
-  using S = WideShape<BM>;
-  constexpr int BN = S::BN, WN = S::WN;
+  using S = WideShape<BM, BN>;
+  constexpr int WN = S::WN, WC = S::WC, NT = S::NT;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   typedef const __attribute__((address_space(4))) float cfloat;
 
@@ -165,7 +171,8 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     for (int e = 0; e < 2; ++e) {
       const int ra = (wave * S::RA + e) * 8 + (ln >> 3), rb = (wave * S::RB + e) * 8 + (ln >> 3);
       a_off[e] = (uint32_t)(w.m0 + ra) * (uint32_t)K + (uint32_t)(((ln & 7) ^ swz(ra)) << 4);
-      b_off[e] = (uint32_t)(w.n0 + rb) * (uint32_t)K + (uint32_t)(((ln & 7) ^ swz(rb)) << 4);
+      b_off[e] = wave * S::RB * 8 < BN ? (uint32_t)(w.n0 + rb) * (uint32_t)K + (uint32_t)(((ln & 7) ^ swz(rb)) << 4)
+                                       : kBufferOutOfRange;   // (224 wide: the last wave's rows are past the tile)
     }
     if constexpr (S::SA_LDS) {
       const int row = (wave & 3) * 64 + (ln & 3) * 16 + (ln >> 2);
@@ -205,11 +212,14 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
   auto staged_q = [&](int j, int ln) -> int { return S::RPC == 1 ? wave * 8 + j : (wave * 8 + j) * 2 + (ln >> 5); };
   auto staged_row = [&](int q, int h) -> int { return (q >> 5) * 64 + (2 * h + ((q >> 4) & 1)) * 16 + (q & 15); };
   auto staged_col = [&](int q, int ln) -> int { return (((S::RPC == 1 ? ln : ln & 31) ^ (q & 15)) << 3); };
+  // (a staged column past the tile's width holds nothing)
   auto issue_c = [&](int j, int h, const Unit& w, uint32_t slot) {
     const int ln = opaque(lane);
     const int q = staged_q(j, ln);
-    const int row = w.m0 + staged_row(q, h), col = w.n0 + staged_col(q, ln);
-    const uint32_t off = row < M && col < N ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : kBufferOutOfRange;
+    const int tc = staged_col(q, ln);
+    const int row = w.m0 + staged_row(q, h), col = w.n0 + tc;
+    const uint32_t off =
+        row < M && col < N && tc < BN ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : kBufferOutOfRange;
     buf16_to_lds(rsC, off, 0u, smem + slot + (wave * 8 + j) * 1024);
   };
 
@@ -229,8 +239,13 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
   while (true) {
     const int KT = cur.nkb;
     const int kb0 = cur.kb0;
-    const int tn_col0 = min(cur.n0 + wave_n * 128, N - 1);
-    const int sb_idx = __builtin_amdgcn_readfirstlane((cur.g * NB + (tn_col0 >> 7)) * KB + kb0);
+    // B scales: the wave's first 128-column block, and (224 wide) the next one,
+    // which column blocks nt >= nt_split fall in
+    const int bcol0 = cur.n0 + wave_n * WC;
+    const int blk0 = min(bcol0, N - 1) >> 7;
+    const int sb_idx = __builtin_amdgcn_readfirstlane((cur.g * NB + blk0) * KB + kb0);
+    const int sb_idx1 = __builtin_amdgcn_readfirstlane((cur.g * NB + min(blk0 + 1, NB - 1)) * KB + kb0);
+    const int nt_split = __builtin_amdgcn_readfirstlane(S::SPLIT_SB ? min(NT, ((blk0 + 1) * 128 - bcol0) >> 4) : NT);
     int t_next = t + G;
     Unit nxt{};
     const bool have_next = next_unit(t_next, nxt);
@@ -243,15 +258,15 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     const int fr = lf & 15, fg = lf >> 4, sw = swz(fr);
     const uint32_t a_lo = (wave_m * 64 + fr) * 128 + (((2 * fg) ^ sw) << 4);
     const uint32_t a_hi = (wave_m * 64 + fr) * 128 + (((2 * fg + 1) ^ sw) << 4);
-    const uint32_t b_lo = S::A_BYTES + (wave_n * 128 + fr) * 128 + (((2 * fg) ^ sw) << 4);
-    const uint32_t b_hi = S::A_BYTES + (wave_n * 128 + fr) * 128 + (((2 * fg + 1) ^ sw) << 4);
+    const uint32_t b_lo = S::A_BYTES + (wave_n * WC + fr) * 128 + (((2 * fg) ^ sw) << 4);
+    const uint32_t b_hi = S::A_BYTES + (wave_n * WC + fr) * 128 + (((2 * fg + 1) ^ sw) << 4);
     const uint32_t sa_rd = S::A_BYTES + S::B_BYTES + (wave_m * 64 + fr * 4) * 4;
 
-    v4f acc[W_MT][W_NT];
+    v4f acc[W_MT][NT];
 #pragma unroll
     for (int mt = 0; mt < W_MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < W_NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
     v4f part[W_LAG];
 #pragma unroll
     for (int r = 0; r < W_LAG; ++r) part[r] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -272,15 +287,23 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
       else wait_vmcnt<0>();
       block_barrier();
       const float sbv = SBc[sb_idx + kb];
-      float scur[W_MT];
+      const float sbv1 = S::SPLIT_SB ? SBc[sb_idx1 + kb] : sbv;
+      float sav[W_MT];
       if constexpr (S::SA_LDS) {
-        const v4f sav = *reinterpret_cast<const v4f*>(smem + rd + sa_rd);
+        const v4f v = *reinterpret_cast<const v4f*>(smem + rd + sa_rd);
 #pragma unroll
-        for (int i = 0; i < W_MT; ++i) scur[i] = sav[i] * sbv;
+        for (int i = 0; i < W_MT; ++i) sav[i] = v[i];
       } else {
         // row block i of the lane's rows: the wave's row 16 i + (lane % 16)
 #pragma unroll
-        for (int i = 0; i < W_MT; ++i) scur[i] = __shfl(sa_nx, 16 * i + (lane & 15), 64) * sbv;
+        for (int i = 0; i < W_MT; ++i) sav[i] = __shfl(sa_nx, 16 * i + (lane & 15), 64);
+      }
+      // the promotion scale of row block i in column blocks before / from nt_split
+      float scur[W_MT], scur1[W_MT];
+#pragma unroll
+      for (int i = 0; i < W_MT; ++i) {
+        scur[i] = sav[i] * sbv;
+        scur1[i] = S::SPLIT_SB ? sav[i] * sbv1 : scur[i];
       }
       v8i af[W_MT];
 #pragma unroll
@@ -290,7 +313,7 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
         af[mt] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
 #pragma unroll
-      for (int nt = 0; nt < W_NT; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const v4i lo = *reinterpret_cast<const v4i*>(smem + rd + b_lo + nt * 2048);
         const v4i hi = *reinterpret_cast<const v4i*>(smem + rd + b_hi + nt * 2048);
         const v8i bf = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -299,10 +322,11 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
           const int j = nt * W_MT + mt;
           if (nt == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][W_NT - 1][i] = fmaf(part[mt][i], sprev[mt], acc[mt][W_NT - 1][i]);
+            for (int i = 0; i < 4; ++i) acc[mt][NT - 1][i] = fmaf(part[mt][i], sprev[mt], acc[mt][NT - 1][i]);
           } else {
+            const float sc = S::SPLIT_SB && nt - 1 >= nt_split ? scur1[mt] : scur[mt];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][nt - 1][i] = fmaf(part[mt][i], scur[mt], acc[mt][nt - 1][i]);
+            for (int i = 0; i < 4; ++i) acc[mt][nt - 1][i] = fmaf(part[mt][i], sc, acc[mt][nt - 1][i]);
           }
           part[mt] = mfma_e4m3_16x16x128(bf, af[mt], v4f{0.f, 0.f, 0.f, 0.f});
           if (j < S::LPS) copy(j);
@@ -312,7 +336,7 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
         }
       }
 #pragma unroll
-      for (int i = 0; i < W_MT; ++i) sprev[i] = scur[i];
+      for (int i = 0; i < W_MT; ++i) sprev[i] = S::SPLIT_SB && NT - 1 >= nt_split ? scur1[i] : scur[i];
     };
 
 #pragma clang loop unroll(disable)
@@ -337,7 +361,7 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
 #pragma unroll
     for (int mt = 0; mt < W_MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mt][W_NT - 1][i] = fmaf(part[mt][i], sprev[mt], acc[mt][W_NT - 1][i]);
+      for (int i = 0; i < 4; ++i) acc[mt][NT - 1][i] = fmaf(part[mt][i], sprev[mt], acc[mt][NT - 1][i]);
 
     // ---------------- tile boundary ----------------
     const Unit done = cur;
@@ -348,14 +372,15 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
     // in a staged half tile (C's layout)
     auto cd_addr = [&](int i, int nt, uint32_t slot) -> uint32_t {
       const int q = wave_m * 32 + i * 16 + (ln & 15);
-      return slot + q * S::ROWB + wave_n * 256 + (((2 * nt + (ln >> 5)) ^ (ln & 15)) << 4) + ((ln >> 4) & 1) * 8;
+      const int c = (wave_n * WC >> 3) + 2 * nt + (ln >> 5);   // the lane's 16-byte chunk of the row
+      return slot + q * S::ROWB + ((c ^ (ln & 15)) << 4) + ((ln >> 4) & 1) * 8;
     };
     // half h of D as bf16 into the half tile staged at slot (over C, plus C)
     auto stage_d = [&](int h, bool add_c, uint32_t slot) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int nt = 0; nt < W_NT; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           const uint32_t addr = cd_addr(i, nt, slot);
           const v4f a = acc[2 * h + i][nt];
           float v0 = a[0], v1 = a[1], v2 = a[2], v3 = a[3];
@@ -384,8 +409,9 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
 #pragma unroll
       for (int j = 0; j < W_CPH; ++j) {
         const int q = staged_q(j, ln);
-        const int row = done.m0 + staged_row(q, h), col = done.n0 + staged_col(q, ln);
-        bool ok = row < M && col < N;
+        const int tc = staged_col(q, ln);
+        const int row = done.m0 + staged_row(q, h), col = done.n0 + tc;
+        bool ok = row < M && col < N && tc < BN;
         if constexpr (MODE == MODE_CONTIG) ok = ok && p.m_indices[row] == done.g;   // (row is uniform: RPC = 1)
         const uint32_t off = ok ? ((uint32_t)row * (uint32_t)N + (uint32_t)col) * 2u : kBufferOutOfRange;
         dg_raw_buffer_store_v4i32(drow[j], rsD, (int)off, 0, kStoreNonTemporal);
@@ -450,11 +476,11 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
       // past M or N, or of padding rows, are written too: the reduce reads only
       // valid ones)
       const v4i rsW = make_buffer_rsrc(p.ws + (size_t)done.part * (BM * BN), (uint32_t)(BM * BN * 4));
-      const int w_lane = ((wave_m * 64 + (ln & 15)) * BN + wave_n * 128 + 4 * (ln >> 4)) * 4;
+      const int w_lane = ((wave_m * 64 + (ln & 15)) * BN + wave_n * WC + 4 * (ln >> 4)) * 4;
 #pragma unroll
       for (int mt = 0; mt < W_MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < W_NT; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           const v4i w = {__float_as_int(acc[mt][nt][0]), __float_as_int(acc[mt][nt][1]),
                          __float_as_int(acc[mt][nt][2]), __float_as_int(acc[mt][nt][3])};
           dg_raw_buffer_store_v4i32(w, rsW, w_lane, (mt * 16 * BN + nt * 16) * 4, 0);
@@ -472,25 +498,27 @@ __global__ void __launch_bounds__(512, 1) fp8_gemm_wide_kernel(Fp8GemmParams p) 
 }
 
 TileConfig wide_tile_config(int kernel_id) {
-  if (kernel_id == kTile256x256Id) return TileConfig{256, 256, 1, W_NW * 64, WideShape<256>::LDS, 2};
-  return TileConfig{128, 512, 1, W_NW * 64, WideShape<128>::LDS, 2};
+  if (kernel_id == kTile256x256Id) return TileConfig{256, 256, 1, W_NW * 64, WideShape<256, 256>::LDS, 2};
+  if (kernel_id == kTile256x224Id) return TileConfig{256, 224, 1, W_NW * 64, WideShape<256, 224>::LDS, 2};
+  return TileConfig{128, 512, 1, W_NW * 64, WideShape<128, 512>::LDS, 2};
 }
 
-template <int BM, int MODE>
+template <int BM, int BN, int MODE>
 static hipError_t launch_wide(const Fp8GemmParams& p, int grid, hipStream_t stream) {
-  constexpr int lds = WideShape<BM>::LDS;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&fp8_gemm_wide_kernel<BM, MODE>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  constexpr int lds = WideShape<BM, BN>::LDS;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&fp8_gemm_wide_kernel<BM, BN, MODE>), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((fp8_gemm_wide_kernel<BM, MODE>), dim3(grid), dim3(W_NW * 64), lds, stream, p);
+  hipLaunchKernelGGL((fp8_gemm_wide_kernel<BM, BN, MODE>), dim3(grid), dim3(W_NW * 64), lds, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_fp8_gemm_wide(const Fp8GemmParams& p, int kernel_id, int mode, int grid, hipStream_t stream) {
   if (!wide_fits(p.m, p.n, p.k)) return hipErrorInvalidValue;
-  if (kernel_id == kTile256x256Id && mode == MODE_DENSE) return launch_wide<256, MODE_DENSE>(p, grid, stream);
-  if (kernel_id == kTile128x512Id && mode == MODE_DENSE) return launch_wide<128, MODE_DENSE>(p, grid, stream);
-  if (kernel_id == kTile128x512Id && mode == MODE_CONTIG) return launch_wide<128, MODE_CONTIG>(p, grid, stream);
+  if (kernel_id == kTile256x256Id && mode == MODE_DENSE) return launch_wide<256, 256, MODE_DENSE>(p, grid, stream);
+  if (kernel_id == kTile256x224Id && mode == MODE_DENSE) return launch_wide<256, 224, MODE_DENSE>(p, grid, stream);
+  if (kernel_id == kTile128x512Id && mode == MODE_DENSE) return launch_wide<128, 512, MODE_DENSE>(p, grid, stream);
+  if (kernel_id == kTile128x512Id && mode == MODE_CONTIG) return launch_wide<128, 512, MODE_CONTIG>(p, grid, stream);
   return hipErrorInvalidValue;
 }
 

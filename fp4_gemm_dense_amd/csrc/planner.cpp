@@ -105,17 +105,19 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     // HBM, and a deeper copy ring keeps more of it in flight (measured: the
     // 4-slot 64x128 shape beats the 3-slot ones at M = 64 and 128)
     if (splits > 1 && full == 0) intensity = tc.stages;
-    // The 256x256 and 128x512 tiles: measured on MI355X against the 256x128 /
-    // 128x256 tiles at equal fill (dense, with C), 10-20 % faster from K = 1024
-    // on (fewer copy bytes per matrix instruction, whole-row D stores), even at
-    // K = 512, where a tile's fixed costs (pipeline fill, C and D through LDS)
-    // weigh most: relative speed about 1.15 kb / (kb + 0.6).  The 128x512 tile
-    // measured 0-6 % behind the 256x256 one on dense shapes (its A scales come
-    // through a register and cross-lane reads, not LDS): it serves the
-    // contiguous form, whose 128-row groups the 256-row tile would straddle.
+    // The wide tiles: measured on MI355X against the 256x128 / 128x256 tiles at
+    // equal fill (dense, with C), 10-20 % faster from K = 1024 on (fewer copy
+    // bytes per matrix instruction, whole-row D stores), even at K = 512, where a
+    // tile's fixed costs (pipeline fill, C and D through LDS) weigh most:
+    // relative speed about 1.15 kb / (kb + 0.6).  The 128x512 tile measured 0-6 %
+    // behind the 256x256 one on dense shapes (its A scales come through a
+    // register and cross-lane reads, not LDS): it serves the contiguous form,
+    // whose 128-row groups the 256-row tile would straddle.  The 256x224 tile
+    // (N = 7168 in 32 column tiles) runs 28 matrix instructions per barrier
+    // instead of 32.
     else if (is_wide_tile(id))
       intensity = 256.0 * 128.0 / 384.0 * 1.15 * kb / (kb + 0.6) *
-                  (id == kTile128x512Id && mode == MODE_DENSE ? 0.97 : 1.0);
+                  ((id == kTile128x512Id && mode == MODE_DENSE) || id == kTile256x224Id ? 0.97 : 1.0);
     double score = util * fill * intensity;
     // wide tiles store longer rows of D (512 bytes): measured 2-7 % faster than
     // the tall tile of the same area up to K = 8192 (the shorter the K loop, the

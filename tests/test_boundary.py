@@ -273,12 +273,13 @@ def test_form_plan_query_names_each_forms_kernel():
 
 
 def test_wide_tile_is_dense_nt_only(monkeypatch):
-    """The 256 x 256 tile (kernel 4) serves the dense NT form with fp32 scales
-    only, the 128 x 512 tile (kernel 5) that and the contiguous NT form: pinned
+    """The 256 x 256 and 256 x 224 tiles (kernels 4, 6) serve the dense NT form
+    with fp32 scales only, the 128 x 512 tile (kernel 5) that and the contiguous
+    NT form: pinned
     on another form the pin is ignored; pinned on NT it is planned, with its
     workspace (split K) counted like any other tile's; a shape whose row offsets
     would pass 2^32 bytes keeps the square tiles."""
-    for kid in (4, 5):
+    for kid in (4, 5, 6):
         monkeypatch.setenv("DG_FORCE_KERNEL", str(kid))
         for form in (dgm.FORM_NN, dgm.FORM_TN, dgm.FORM_TT, dgm.FORM_NT_UE8M0):
             assert dgm.dg_query_plan_form(form, 1024, 1024, 1024, 1, 0, 256)["kernel_id"] != kid, form
@@ -288,10 +289,13 @@ def test_wide_tile_is_dense_nt_only(monkeypatch):
         p = dgm.dg_query_plan_form(dgm.FORM_NT, 1000, 1040, 2048, 1, 0, 256)
         assert p["kernel_id"] == kid
         _check_ws_bound(dgm.FORM_NT, 1000, 1040, 2048, 1, 256)
+    monkeypatch.setenv("DG_FORCE_KERNEL", "5")
     p = dgm.dg_query_plan_form(dgm.FORM_CONTIGUOUS_NT, 1024, 1024, 1024, 4, 0, 256)
     assert (p["kernel_id"], p["block_m"], p["block_n"]) == (5, 128, 512)
+    for kid in (4, 6):
+        monkeypatch.setenv("DG_FORCE_KERNEL", str(kid))
+        assert dgm.dg_query_plan_form(dgm.FORM_CONTIGUOUS_NT, 1024, 1024, 1024, 4, 0, 256)["kernel_id"] != kid
     monkeypatch.setenv("DG_FORCE_KERNEL", "4")
-    assert dgm.dg_query_plan_form(dgm.FORM_CONTIGUOUS_NT, 1024, 1024, 1024, 4, 0, 256)["kernel_id"] != 4
     p = dgm.dg_query_plan_form(dgm.FORM_NT, 1000, 1040, 2048, 1, 0, 256)
     assert (p["kernel_id"], p["block_m"], p["block_n"], p["num_tiles"]) == (4, 256, 256, 4 * 5)
     _check_ws_bound(dgm.FORM_NT, 1000, 1040, 2048, 1, 256)

@@ -79,7 +79,7 @@ def test_dense_identity_b_and_all_ones(dg):
     assert np.all(F.bf16_bits_to_f64(d) == K * 0.5 * 0.25 + 3.0)
 
 
-@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("K", [128, 256, 384, 640])
 @pytest.mark.parametrize("with_c", [True, False], ids=["c", "no_c"])
 def test_dense_many_tiles_per_workgroup_bit_exact(dg, monkeypatch, kernel_id, K, with_c):
@@ -87,9 +87,9 @@ def test_dense_many_tiles_per_workgroup_bit_exact(dg, monkeypatch, kernel_id, K,
     back, with and without C.  A tile starts its LDS ring in the slot of the
     previous tile's last K block and stages C (or D over C) in LDS; one to five K
     blocks per tile cover every step of the ring start (K blocks - 1 modulo the
-    slot count).  Kernels 4 and 5 are the 256 x 256 and 128 x 512 tiles, whose
-    next tile's first stage goes to a different slot with C than without.  Exact
-    integer inputs: the result is unique."""
+    slot count).  Kernels 4-6 are the 256 x 256, 128 x 512 and 256 x 224 tiles,
+    whose next tile's first stage goes to a different slot with C than without.
+    Exact integer inputs: the result is unique."""
     import fp4_gemm_dense_amd as dgm
     rng = np.random.default_rng(kernel_id * 10 + K + (0 if with_c else 5))
     M, N = 520, 784                     # ragged in both dimensions for every tile shape
@@ -115,7 +115,7 @@ def test_dense_random_parity(dg, M, N, K):
     check_parity(d, R.fp8_gemm_nt(a, sfa, b, sfb, c), what=f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("kernel_id", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("splits_wanted", [False, True])
 def test_dense_every_tile_random_parity(dg, monkeypatch, kernel_id, splits_wanted):
     """Every tile shape, pinned, on random inputs with C and ragged M and N:
@@ -126,7 +126,8 @@ def test_dense_every_tile_random_parity(dg, monkeypatch, kernel_id, splits_wante
     which sends the partials through the workspace and the reduce kernel; with 5
     CUs the workgroups walk several tiles each, unsplit."""
     import fp4_gemm_dense_amd as dgm
-    bm, bn = {0: (256, 128), 1: (128, 256), 2: (128, 128), 3: (64, 128), 4: (256, 256), 5: (128, 512)}[kernel_id]
+    bm, bn = {0: (256, 128), 1: (128, 256), 2: (128, 128), 3: (64, 128), 4: (256, 256), 5: (128, 512),
+              6: (256, 224)}[kernel_id]
     M, N, K = 2 * bm + bm // 2 + 3, 3 * bn + 48, 128 * 24
     g = synth.gen_dense(M, N, K, seed=500 + kernel_id * 2 + splits_wanted, with_c=True)
     a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
@@ -172,19 +173,21 @@ def test_dense_sweep_full_size_sampled(dg, mi, nki):
 
 
 def test_wide_tile_matches_square_tiles_bitwise(dg, monkeypatch):
-    """The 256 x 256 and 128 x 512 tiles promote each K block's partial with the
-    same fused multiply-add, in the same K order, as the square-tile template: on
-    random inputs with C their outputs are bit-identical to the 128 x 256 and
-    256 x 128 tiles' (a different accumulation order would differ in the last
-    bit of many elements)."""
+    """The 256 x 256, 128 x 512 and 256 x 224 tiles promote each K block's
+    partial with the same fused multiply-add, in the same K order, as the
+    square-tile template: on random inputs with C their outputs are bit-identical
+    to the 128 x 256 and 256 x 128 tiles' (a different accumulation order, or a
+    column block promoted with the neighbouring 128-column block's B scale, would
+    differ in many elements).  N = 1040 puts 224-wide tile edges at every offset
+    into a 128-column scale block that is a multiple of 32."""
     M, N, K = 1000, 1040, 2048
     g = synth.gen_dense(M, N, K, seed=4242, with_c=True)
     a, sfa, b, sfb, c = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb", "c"))
     outs = {}
-    for kid in (0, 1, 4, 5):
+    for kid in (0, 1, 4, 5, 6):
         monkeypatch.setenv("DG_FORCE_KERNEL", str(kid))
         outs[kid] = _run(dg, a, sfa, b, sfb, c)
-    for wide in (4, 5):
+    for wide in (4, 5, 6):
         assert not (outs[wide] == 0xFFFF).any()
         for kid in (0, 1):
             mism = outs[wide] != outs[kid]
@@ -195,12 +198,14 @@ def test_wide_tile_matches_square_tiles_bitwise(dg, monkeypatch):
 @pytest.mark.parametrize("kid,M,N,K,with_c", [(4, 4096, 2112, 7168, True), (4, 4096, 7168, 16384, True),
                                                (4, 4096, 4096, 7168, False), (4, 64, 7168, 2048, False),
                                                (4, 3072, 6144, 7168, True), (5, 4096, 7168, 2048, True),
-                                               (5, 1000, 4096, 7168, False), (5, 4096, 2112, 7168, True)])
+                                               (5, 1000, 4096, 7168, False), (5, 4096, 2112, 7168, True),
+                                               (6, 4096, 7168, 16384, True), (6, 4096, 7168, 2048, False),
+                                               (6, 3000, 2112, 7168, True)])
 def test_wide_tile_full_size_sampled(dg, monkeypatch, kid, M, N, K, with_c):
-    """The 256 x 256 (4) and 128 x 512 (5) tiles, pinned, at full size (every
-    output tile sampled as in the sweep test), with and without C; the fifth
-    shape's plan splits only its partial last round (32 of 288 tiles, in 8
-    slices each)."""
+    """The 256 x 256 (4), 128 x 512 (5) and 256 x 224 (6) tiles, pinned, at full
+    size (every output tile sampled as in the sweep test), with and without C;
+    the fifth shape's plan splits only its partial last round (32 of 288 tiles,
+    in 8 slices each)."""
     monkeypatch.setenv("DG_FORCE_KERNEL", str(kid))
     assert dg.dg_query_plan_form(0, M, N, K)["kernel_id"] == kid
     g = synth.gen_dense(M, N, K, seed=M + N + K + 7, with_c=with_c, backend="torch", device="cuda")
