@@ -1,13 +1,14 @@
-// Fine-grained-scaled FP8 GEMM for gfx950, 256x256 tiles: D = C + A.B^T (NT),
-// fp32 scales, bf16 out -- the dense form for problems large enough to fill the
-// chip with such tiles.
+// Fine-grained-scaled FP8 GEMM for gfx950 on wide tiles: D = C + A.B^T (NT),
+// fp32 scales, bf16 out.  Three tiles: 256x256 and 256x224 (dense form) and
+// 128x512 (dense and M-grouped contiguous forms), for problems large enough to
+// fill the chip with them.
 //
 // What is computed is the dense GEMM of the usage guide ("DeepGEMM：统一高性能张量
-// 核心 GEMM 计算库编译与使用指南", 五、使用方法) with the two-level accumulation of
-// the release article ("DeepSeek 开源第三弹 ... DeepGEMM", DeepGEMM section): one
-// matrix instruction per 128-wide K block into a fresh fp32 partial, promoted on
-// the vector ALUs by sa * sb -- exactly as the 128- and 256-row tiles of
-// fp8_gemm.hip, in the same per-element order.
+// 核心 GEMM 计算库编译与使用指南", 五、使用方法) and its M-grouped contiguous form,
+// with the two-level accumulation of the release article ("DeepSeek 开源第三弹 ...
+// DeepGEMM", DeepGEMM section): one matrix instruction per 128-wide K block into
+// a fresh fp32 partial, promoted on the vector ALUs by sa * sb -- exactly as the
+// tiles of fp8_gemm.hip, in the same per-element order.
 //
 // Why a second kernel: every K block of a tile is copied from L2 into LDS by
 // LDS-DMA loads, and on gfx950 the copy path (texture address unit, LDS writes)
@@ -15,12 +16,12 @@
 // 48 KB per 16 matrix instructions per wave.  A 256x256 tile moves 64 KB per 32:
 // a third fewer copy bytes and a quarter fewer LDS fragment bytes per matrix
 // instruction, half the barriers per instruction.  Its price is the LDS: a stage
-// is 65 KB, so the ring has two slots, and the stage copies of K block kb + 1
-// are issued right after block kb's barrier (one block of lead).
-//   * 8 waves as 4 x 2, each a 64 x 128 sub-tile of 16x16 blocks (MT = 4 row
-//     blocks, NT = 8 column blocks), computed transposed (B_nt . A_mt^T) so that
-//     a lane's four results lie in one row of D and share one A scale; a wave's
-//     128 columns lie in one 128-wide block of B scales;
+// is 65 KB (80 KB for 128x512), so the ring has two slots, and the stage copies
+// of K block kb + 1 are issued right after block kb's barrier (one block of
+// lead).
+//   * 8 waves, each a 64 x 128 (64 x 112) sub-tile of 16x16 blocks (MT = 4 row
+//     blocks, NT = 8 or 7 column blocks), computed transposed (B_nt . A_mt^T) so
+//     that a lane's four results lie in one row of D and share one A scale;
 //   * the four A fragments of a K block are read once, the B fragments one at a
 //     time, each feeding four matrix instructions (the register file holds 128
 //     accumulators per lane, which the promotion FMAs need in VGPRs);
@@ -28,7 +29,7 @@
 //     last K block (or, with C, right after it, the last block copying half of
 //     C instead); D leaves through a free LDS slot half a tile at a time, as
 //     bf16 (plus C, staged there in the same layout), and is stored from there
-//     in whole rows (two 512-byte rows per store instruction).
+//     in whole rows (1024 bytes per store instruction).
 //   * split K (a partial last round) writes fp32 partial tiles to the caller's
 //     workspace, summed by the split-K reduce kernel of fp8_gemm.hip.
 #include <algorithm>
