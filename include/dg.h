@@ -406,7 +406,9 @@ typedef struct dg_plan {
   int num_tiles;        /* output tiles */
   int num_workgroups;
   int kernel_id;        /* 0-3: the 256x128, 128x256, 128x128, 64x128 tiles; 4: the 256x256 tile
-                           (dense NT with fp32 scales only); >= 100: the skinny-M kernel */
+                           and 6: the 256x224 tile (dense NT with fp32 scales only); 5: the 128x512
+                           tile (dense and contiguous NT with fp32 scales); >= 100: the skinny-M
+                           kernel */
   int splits;           /* K slices per split tile (dense only; 1: no split) */
   int full_tiles;       /* tiles computed whole; the other num_tiles - full_tiles are split */
 } dg_plan;
