@@ -22,8 +22,11 @@
 //              round-to-nearest-even; writes the e4m3 intermediate and its UE8M0
 //              exponents.
 //   3. linear2 (persistent): (expert, 128-row block, 256 output columns) of the
-//              intermediate times W2 with the same scaled MFMA; writes fp32 per pair.
-//   4. combine: y[t] = sum over slots j (in order) of w[t,j] * o[pair(t,j)], bf16.
+//              intermediate times W2 with the same scaled MFMA; writes fp32 per pair,
+//              except for a token with a single local pair, whose output row it
+//              forms itself (bf16 of w * o, the combine's arithmetic for one slot).
+//   4. combine: y[t] = sum over slots j (in order) of w[t,j] * o[pair(t,j)], bf16,
+//              for the tokens with no local pair or with two or more.
 // Activations and weight-scale words are staged per 128-wide K block through a
 // 4-slot LDS ring, the weights per pair of K blocks through a 2-slot ring, and
 // the activation-scale words (four K blocks each) through a ring of their own,
@@ -58,6 +61,7 @@ struct FfnParams {
   int32_t* start;       // [E+1]
   int32_t* pair_token;  // [T*k]
   int32_t* pair_of;     // [T*k]
+  int32_t* pair_single; // [T*k]: (token, slot) entry of a pair that is its token's only local pair, else -1
   uint8_t* q;           // [T*k, I]
   uint8_t* sq;          // [T*k, sq_stride]
   float* o;             // [T*k, H]
@@ -71,7 +75,7 @@ struct FfnParams {
 };
 
 struct FfnLayout {
-  size_t cnt, start, pair_token, pair_of, q, sq, o, total;
+  size_t cnt, start, pair_token, pair_of, q, sq, o, pair_single, total;
   int sq_stride;
 };
 
@@ -91,6 +95,7 @@ static bool ffn_layout(int T, int k, int E, int H, int I, FfnLayout* L) {
   L->q = off;          off = align256(off + P * (size_t)I);
   L->sq = off;         off = align256(off + P * (size_t)L->sq_stride);
   L->o = off;          off = align256(off + P * (size_t)H * 4);
+  L->pair_single = off; off = align256(off + P * 4);
   L->total = off;
   return true;
 }
@@ -136,6 +141,13 @@ __global__ void __launch_bounds__(1024) ffn_route_kernel(FfnParams p) {
   __syncthreads();
   // The order of pairs inside an expert does not affect any result: each pair's
   // output row depends only on its token, and the combine sums slots in order.
+  // A pair whose token has no other local pair is marked (its entry index): its
+  // token's output row is then formed by linear2.  With k dividing 64 a token's k
+  // entries sit in k consecutive lanes of one wave (entry i = base + u * nt + tid,
+  // base and u * nt multiples of 64), so one ballot counts them; otherwise the
+  // token's entries are read again.
+  const bool wave_tokens = 64 % p.k == 0 && nt % 64 == 0;
+  const int lane = tid & 63;
   for (int base = 0; base < total; base += RU * nt) {
     int ev[RU];
 #pragma unroll
@@ -146,12 +158,27 @@ __global__ void __launch_bounds__(1024) ffn_route_kernel(FfnParams p) {
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
       const int i = base + u * nt + tid;
-      if (i >= total) continue;
       const int e = ev[u] - p.offset;
+      const bool local = i < total && e >= 0 && e < p.E;
+      int nloc = 0;
+      if (wave_tokens) {   // (uniform: every lane takes the ballot)
+        const unsigned long long m = __ballot(local);
+        const int first = lane - lane % p.k;
+        nloc = __popcll(p.k == 64 ? m : (m >> first) & ((1ull << p.k) - 1ull));
+      }
+      if (i >= total) continue;
       int pr = -1;
-      if (e >= 0 && e < p.E) {
+      if (local) {
         pr = atomicAdd(&cur[e], 1);
         p.pair_token[pr] = i / p.k;
+        if (!wave_tokens) {
+          const int i0 = i - i % p.k;
+          for (int j = 0; j < p.k; ++j) {
+            const int e2 = p.topk_idx[i0 + j] - p.offset;
+            nloc += (e2 >= 0 && e2 < p.E) ? 1 : 0;
+          }
+        }
+        p.pair_single[pr] = nloc == 1 ? i : -1;
       }
       p.pair_of[i] = pr;
     }
@@ -348,6 +375,15 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
       row0 = list_start(e) + tm * FFN_BM;        // first row (pair) of the tile
       rows = min(FFN_BM, cnt_e - tm * FFN_BM);   // valid rows in the tile
       last_pair = list_start(e) + cnt_e - 1;
+    }
+
+    // linear2: the (token, slot) entry of each of the lane's rows if it is its
+    // token's only local pair, else -1 (read before this tile's copies)
+    int single[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = wave_m * MT * 16 + mt * 16 + lrow;
+      single[mt] = MODE == 2 && r < rows ? p.pair_single[row0 + r] : -1;
     }
 
     // ---------------- copy sources (per-lane offsets, scalar K offsets) ----------------
@@ -572,14 +608,29 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
         }
       }
     } else if (MODE == 2) {
-      // fp32 output rows of the pairs: 4 consecutive columns (16 bytes) per lane and block
+      // fp32 output rows of the pairs: 4 consecutive columns (16 bytes) per lane
+      // and block; the only local pair of a token gives that token's bf16 output
+      // row instead, w * o rounded once as the combine does for a single slot
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = wave_m * MT * 16 + mt * 16 + lrow;
         if (r >= rows) continue;
-        float* orow = p.o + (size_t)(row0 + r) * H + tn * FFN_BN + wave_n * 128 + 4 * lgrp;
+        const int col = tn * FFN_BN + wave_n * 128 + 4 * lgrp;
+        if (single[mt] >= 0) {
+          const float w = p.topk_w[single[mt]];
+          uint16_t* yrow = p.y + (size_t)(single[mt] / p.k) * H + col;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<v4f*>(orow + nt * 16) = acc[mt][nt];
+          for (int nt = 0; nt < NT; ++nt) {
+            const v4f v = acc[mt][nt];
+            *reinterpret_cast<uint2*>(yrow + nt * 16) =
+                uint2{pack_bf16x2_rne(fmaf(w, v[0], 0.f), fmaf(w, v[1], 0.f)),
+                      pack_bf16x2_rne(fmaf(w, v[2], 0.f), fmaf(w, v[3], 0.f))};
+          }
+        } else {
+          float* orow = p.o + (size_t)(row0 + r) * H + col;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<v4f*>(orow + nt * 16) = acc[mt][nt];
+        }
       }
     } else {
       // SwiGLU in registers: gate block nt pairs with up block nt + 4 (same columns)
@@ -622,12 +673,16 @@ __global__ void __launch_bounds__(FFN_THREADS, 1) ffn_gemm_kernel(FfnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 4. combine: y[t] = bf16( sum_j w[t,j] * o[pair(t,j)] ), slots in order
+// 4. combine: y[t] = bf16( sum_j w[t,j] * o[pair(t,j)] ), slots in order (a
+// token with exactly one local pair has its row from linear2)
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) ffn_combine_kernel(FfnParams p) {
   const int t = blockIdx.y;
   const int c8 = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (c8 >= p.H) return;
+  int nloc = 0;
+  for (int j = 0; j < p.k; ++j) nloc += p.pair_of[(size_t)t * p.k + j] >= 0 ? 1 : 0;
+  if (nloc == 1) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < p.k; ++j) {
     const int pr = p.pair_of[(size_t)t * p.k + j];
@@ -831,6 +886,7 @@ int dg_fp8_fp4_expert_ffn(const uint8_t* x, const int32_t* x_sf, const int32_t* 
     p.start = reinterpret_cast<int32_t*>(ws + L.start);
     p.pair_token = reinterpret_cast<int32_t*>(ws + L.pair_token);
     p.pair_of = reinterpret_cast<int32_t*>(ws + L.pair_of);
+    p.pair_single = reinterpret_cast<int32_t*>(ws + L.pair_single);
     p.q = ws + L.q;
     p.sq = ws + L.sq;
     p.o = reinterpret_cast<float*>(ws + L.o);
