@@ -111,11 +111,14 @@ __global__ void __launch_bounds__(1024) ffn_route_kernel(FfnParams p) {
   const int nt = blockDim.x;
   // The entries are read RU per thread at a time, all loads issued before any
   // is used (one workgroup: the loop is bound by load latency, not bandwidth).
-  constexpr int RU = 16;
+  // When one batch covers every entry (T * k <= 32768) the second pass reuses
+  // the ids the first one read.
+  constexpr int RU = 32;
+  const bool one_batch = total <= RU * nt;
+  int ev[RU];
   for (int e = tid; e < p.E; e += nt) cnt[e] = 0;
   __syncthreads();
   for (int base = 0; base < total; base += RU * nt) {
-    int ev[RU];
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
       const int i = base + u * nt + tid;
@@ -149,11 +152,12 @@ __global__ void __launch_bounds__(1024) ffn_route_kernel(FfnParams p) {
   const bool wave_tokens = 64 % p.k == 0 && nt % 64 == 0;
   const int lane = tid & 63;
   for (int base = 0; base < total; base += RU * nt) {
-    int ev[RU];
+    if (!one_batch) {
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      const int i = base + u * nt + tid;
-      ev[u] = i < total ? p.topk_idx[i] : 0;
+      for (int u = 0; u < RU; ++u) {
+        const int i = base + u * nt + tid;
+        ev[u] = i < total ? p.topk_idx[i] : 0;
+      }
     }
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
