@@ -50,6 +50,28 @@ def test_ffn_small_parity(dg, T, H, I, E, n_exp, topk, offset):
     assert not np.any(y == 0xFFFF), "every row of y must be written"
 
 
+@pytest.mark.parametrize("T,E,n_exp,topk,offset", [
+    (40, 1, 64, 64, 0),     # every token picks every expert: one local pair each, a token spans a wave
+    (48, 2, 32, 16, 5),     # 16 entries per token (four tokens per wave), one or two local pairs
+    (64, 3, 24, 6, 2),      # 6 does not divide 64: local counts from re-reading the token's entries
+])
+def test_ffn_tokens_with_one_or_more_local_pairs(dg, T, E, n_exp, topk, offset):
+    """A token with exactly one local pair has its row formed by linear2, the
+    others go through the combine; both kinds must match the oracle (top-k counts
+    whose tokens fill a whole wave, a quarter of one, or do not divide it)."""
+    g = _to_dev(synth.gen_ffn(T=T, H=512, I=128, num_local=E, num_experts=n_exp, topk=topk,
+                              seed=T * 3 + topk, expert_offset=offset))
+    idx = synth.to_numpy(g["topk_idx"])
+    nloc = ((idx >= offset) & (idx < offset + E)).sum(axis=1)
+    assert (nloc == 1).any()
+    y, ws = _run(dg, g)
+    _, info = oracle_ffn(g)
+    hit = check_ffn_output(g, y, kernel_intermediate(g, ws, info), f"ffn T{T} k{topk}")
+    assert np.array_equal(hit, nloc > 0)
+    assert np.all(y[nloc == 0] == 0), "tokens without a local expert must be exactly zero"
+    assert not np.any(y == 0xFFFF), "every row of y must be written"
+
+
 def test_ffn_weight_doubling_is_bit_exact(dg):
     g = _to_dev(synth.gen_ffn(T=80, H=512, I=256, num_local=4, num_experts=8, topk=4, seed=5))
     y1, _ = _run(dg, g)
