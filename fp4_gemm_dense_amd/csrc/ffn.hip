@@ -149,8 +149,11 @@ __global__ void __launch_bounds__(1024) ffn_route_kernel(FfnParams p) {
   // entries sit in k consecutive lanes of one wave (entry i = base + u * nt + tid,
   // base and u * nt multiples of 64), so one ballot counts them; otherwise the
   // token's entries are read again.
-  const bool wave_tokens = 64 % p.k == 0 && nt % 64 == 0;
+  const bool wave_tokens = 64 % p.k == 0 && nt % 64 == 0;   // (k is then a power of two)
   const int lane = tid & 63;
+  const int ksh = wave_tokens ? __builtin_ctz((unsigned)p.k) : 0;
+  const int first = wave_tokens ? lane & ~(p.k - 1) : 0;   // the lane of the token's first entry
+  const unsigned long long kmask = p.k >= 64 ? ~0ull : (1ull << p.k) - 1ull;
   for (int base = 0; base < total; base += RU * nt) {
     if (!one_batch) {
 #pragma unroll
@@ -159,32 +162,37 @@ __global__ void __launch_bounds__(1024) ffn_route_kernel(FfnParams p) {
         ev[u] = i < total ? p.topk_idx[i] : 0;
       }
     }
+    // in chunks of CH entries: the pair indices first (the LDS atomics go out
+    // back to back), then the stores
+    constexpr int CH = 8;
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
-      const int i = base + u * nt + tid;
-      const int e = ev[u] - p.offset;
-      const bool local = i < total && e >= 0 && e < p.E;
-      int nloc = 0;
-      if (wave_tokens) {   // (uniform: every lane takes the ballot)
-        const unsigned long long m = __ballot(local);
-        const int first = lane - lane % p.k;
-        nloc = __popcll(p.k == 64 ? m : (m >> first) & ((1ull << p.k) - 1ull));
+    for (int c = 0; c < RU; c += CH) {
+      int pr[CH];
+#pragma unroll
+      for (int v = 0; v < CH; ++v) {
+        const int i = base + (c + v) * nt + tid;
+        const int e = ev[c + v] - p.offset;
+        pr[v] = i < total && e >= 0 && e < p.E ? atomicAdd(&cur[e], 1) : -1;
       }
-      if (i >= total) continue;
-      int pr = -1;
-      if (local) {
-        pr = atomicAdd(&cur[e], 1);
-        p.pair_token[pr] = i / p.k;
-        if (!wave_tokens) {
-          const int i0 = i - i % p.k;
-          for (int j = 0; j < p.k; ++j) {
-            const int e2 = p.topk_idx[i0 + j] - p.offset;
-            nloc += (e2 >= 0 && e2 < p.E) ? 1 : 0;
+#pragma unroll
+      for (int v = 0; v < CH; ++v) {
+        const int i = base + (c + v) * nt + tid;
+        int nloc = 0;
+        if (wave_tokens) nloc = __popcll((__ballot(pr[v] >= 0) >> first) & kmask);   // (uniform: every lane)
+        if (i >= total) continue;
+        if (pr[v] >= 0) {
+          const int t = wave_tokens ? i >> ksh : i / p.k;
+          p.pair_token[pr[v]] = t;
+          if (!wave_tokens) {
+            for (int j = 0; j < p.k; ++j) {
+              const int e2 = p.topk_idx[t * p.k + j] - p.offset;
+              nloc += (e2 >= 0 && e2 < p.E) ? 1 : 0;
+            }
           }
+          p.pair_single[pr[v]] = nloc == 1 ? i : -1;
         }
-        p.pair_single[pr] = nloc == 1 ? i : -1;
+        p.pair_of[i] = pr[v];
       }
-      p.pair_of[i] = pr;
     }
   }
 }
