@@ -317,6 +317,45 @@ def test_contiguous_split_tail_parity(dg, counts, N, K, cus):
     check_parity(db[written], ref[written], what=f"contig split tail {counts} on {cus} CUs")
 
 
+@pytest.mark.parametrize("N", [768, 1024])
+@pytest.mark.parametrize("exact", [False, True], ids=["random", "exact"])
+def test_contiguous_split_tail_on_the_128x512_tile(dg, monkeypatch, N, exact):
+    """The wide 128 x 512 tile's split path in the contiguous form: 16 whole tiles
+    and 6 split in two on 16 workgroups, with an empty group and padding rows in
+    split tiles (partial tiles summed by the split-K reduce, padding not written)."""
+    monkeypatch.setenv("DG_FORCE_KERNEL", "5")
+    counts, K, cus = [300, 0, 100, 500, 380], 128 * 48, 16
+    mi, _ = synth.padded_group_layout(counts)
+    mi = np.array(mi, np.int32)
+    M = mi.size
+    p = dgm.dg_query_plan_contiguous(M, N, K, len(counts), cus)
+    assert p["kernel_id"] == 5 and p["splits"] > 1 and 0 < p["full_tiles"] < p["num_tiles"], p
+    if exact:
+        rng = np.random.default_rng(N)
+        a, sfa, _, _, _, _ = make_exact_case(rng, M, N, K, with_c=False)
+        bs, sbs = [], []
+        for _ in counts:
+            _, _, b1, sfb1, _, _ = make_exact_case(rng, 1, N, K, with_c=False)
+            bs.append(b1)
+            sbs.append(sfb1)
+        b, sfb = np.stack(bs), np.stack(sbs)
+    else:
+        g = synth.gen_contiguous(len(counts), sum(counts), N, K, seed=N + 5, counts=counts)
+        a, sfa, b, sfb = (synth.to_numpy(g[k]) for k in ("a", "sfa", "b", "sfb"))
+    d = sentinel_like((M, N))
+    with _cu_cap(cus):
+        dg.dg_m_grouped_fp8_gemm_nt_contiguous(_dev(a), _dev(sfa), _dev(b), _dev(sfb), _dev(mi), d)
+        torch.cuda.synchronize()
+    db = bits(d)
+    ref, written = R.m_grouped_contiguous(a, sfa, b, sfb, mi)
+    assert np.all(db[~written] == 0xFFFF), "padding rows were written"
+    if exact:
+        check_bit_exact(db[written], ref[written], "contig 128x512 split tail exact")
+    else:
+        assert not np.any(db[written] == 0xFFFF), "group rows left unwritten"
+        check_parity(db[written], ref[written], what=f"contig 128x512 split tail N{N}")
+
+
 def test_contiguous_split_tail_exact_integer_bit_exact(dg):
     rng = np.random.default_rng(17)
     counts, N, K, cus = [300, 0, 100, 500, 380], 768, 128 * 48, 16
