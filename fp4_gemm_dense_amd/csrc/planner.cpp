@@ -116,13 +116,20 @@ GemmPlan plan_fp8_gemm(int m, int n, int k, int num_groups, int mode, int num_cu
     // tile's fixed costs (pipeline fill, C and D through LDS) weigh most:
     // relative speed about 1.15 kb / (kb + 0.6).  The 128x512 tile measured 0-6 %
     // behind the 256x256 one on dense shapes (its A scales come through a
-    // register and cross-lane reads, not LDS): it serves the contiguous form,
-    // whose 128-row groups the 256-row tile would straddle.  The 256x224 tile
-    // (N = 7168 in 32 column tiles) runs 28 matrix instructions per barrier
-    // instead of 32.
-    else if (is_wide_tile(id))
-      intensity = 256.0 * 128.0 / 384.0 * 1.15 * kb / (kb + 0.6) *
-                  ((id == kTile128x512Id && mode == MODE_DENSE) || id == kTile256x224Id ? 0.97 : 1.0);
+    // register and cross-lane reads, not LDS), except at K = 512, where the
+    // epilogue weighs most and its tile has half the boundaries of the 128x256
+    // one, with D and C rows of 1 KB (timed bench, operands from HBM, with C:
+    // 4096x32768x512 155 against 164 us; at K = 1024 and 1536 it measured even
+    // to 2 % behind).  It serves the contiguous form, whose 128-row groups the
+    // 256-row tile would straddle.  The
+    // 256x224 tile (N = 7168 in 32 column tiles) runs 28 matrix instructions per
+    // barrier instead of 32.
+    else if (is_wide_tile(id)) {
+      double shape = 1.0;
+      if (id == kTile128x512Id && mode == MODE_DENSE) shape = kb == 4 ? 1.1 : 0.97;
+      if (id == kTile256x224Id) shape = 0.97;
+      intensity = 256.0 * 128.0 / 384.0 * 1.15 * kb / (kb + 0.6) * shape;
+    }
     double score = util * fill * intensity;
     // wide tiles store longer rows of D (512 bytes): measured 2-7 % faster than
     // the tall tile of the same area up to K = 8192 (the shorter the K loop, the
